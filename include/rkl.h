@@ -1,0 +1,169 @@
+/*
+ * rkl.h -- C ABI of librkl.so: fused LM-head projection + exact
+ * full-vocabulary reverse KL (forward and backward) on one MI355X (gfx950).
+ *
+ * What is computed (NeMo-RL pull request "add full-vocabulary on-policy
+ * distillation to SingleController"):
+ *   - summary: per token t, over the whole vocabulary V,
+ *         L_t = sum_v p_s(v) (log p_s(v) - log p_t(v)),
+ *     p_s = softmax(z_s), p_t = softmax(z_t), natural log, no temperature;
+ *   - summary, payload paths: the teacher side arrives either as hidden
+ *     states h_t projected through the teacher LM-head weight W_t
+ *     (z_t = h_t W_t^T), or as precomputed full-vocabulary logits z_t;
+ *   - implementation notes: the shared backward is
+ *         dL/dz_s = p_s (w - L),  w = log p_s - log p_t,
+ *     with both log-softmaxes recomputed in the backward rather than cached.
+ * Loss-mask compaction (slime pull request "compact actor logits before
+ * projection", summary): only the N trainable rows of the T = B(S-1)
+ * positions are projected, and per-row scalars are scattered back to the
+ * [B, S-1] layout with zeros elsewhere; an empty mask still yields a (zero)
+ * gradient.
+ *
+ * Conventions shared by every entry point
+ *   - Pointers without a "host" note are device pointers (hipMalloc'd or
+ *     torch CUDA tensors) on the current device.  Every buffer is owned by
+ *     the caller; the library allocates no device memory, keeps no state
+ *     between calls, and may be called from several host threads.
+ *   - bf16 values are passed as raw 16-bit patterns (rkl_bf16).  Matrices are
+ *     row-major and densely packed: h [rows, H], W [V, H] (the nn.Linear /
+ *     output-layer layout), logits [rows, V].
+ *   - Device pointers must be 16-byte aligned.  H (Hs, Ht) must be a multiple
+ *     of 64, else RKL_UNSUPPORTED.
+ *   - Calls are asynchronous on `stream` (a hipStream_t; NULL = null stream),
+ *     except rkl_compact_rows when it returns the count to the host.
+ *   - Argument checks run before anything is launched.  On failure the call
+ *     returns a nonzero status, launches nothing, and rkl_last_error() (per
+ *     host thread) describes the problem.  Launch failures return
+ *     RKL_DEVICE_ERROR.  Nothing is thrown or aborted across this ABI.
+ *   - Outputs must not alias inputs.  Teacher inputs are read only; no
+ *     teacher gradient is produced (the teacher head is a frozen tensor).
+ *   - Results are bitwise reproducible for identical inputs and shapes.  A
+ *     row's loss, statistics, dz and dh do not depend on N or on the row's
+ *     position, so compacted rows and the same rows in full-row mode agree
+ *     bit for bit.
+ */
+#ifndef RKL_H
+#define RKL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef void* rkl_stream_t;   /* hipStream_t */
+typedef uint16_t rkl_bf16;    /* raw bfloat16 bits */
+
+#define RKL_OK 0
+#define RKL_INVALID_ARG 1
+#define RKL_UNSUPPORTED 2
+#define RKL_WORKSPACE_TOO_SMALL 3
+#define RKL_DEVICE_ERROR 4
+
+/* Message for the last nonzero status returned on this host thread. */
+const char* rkl_last_error(void);
+
+/* Library version string (static storage). */
+const char* rkl_version(void);
+
+/*
+ * Row compaction (slime page, summary: project only the loss-masked rows).
+ *   mask       [T] uint8, nonzero = trainable position (the [B, S-1] layout).
+ *   row_idx    [T] int32 capacity; receives the N selected positions in
+ *              ascending order (entries past N are left untouched).
+ *   n_rows_dev [1] int32 device; receives N.
+ *   n_rows_host optional host int64*; when non-NULL the call waits for the
+ *              stream and stores N there (the one host synchronisation of
+ *              the path).
+ * T = 0 is allowed (N = 0).  T must be < 2^31.
+ */
+int rkl_compact_rows(const uint8_t* mask, int64_t T, int32_t* row_idx, int32_t* n_rows_dev,
+                     int64_t* n_rows_host, rkl_stream_t stream);
+
+/*
+ * Gather: dst[i, :] = src[row_idx[i], :] for i < N, a bit copy of row_bytes
+ * bytes per row.  row_bytes must be a positive multiple of 4; every row_idx
+ * entry must lie in [0, T) (not checked on the device).  N = 0 is a no-op.
+ */
+int rkl_gather_rows(const void* src, int64_t T, int64_t row_bytes, const int32_t* row_idx, int64_t N,
+                    void* dst, rkl_stream_t stream);
+
+/*
+ * Scatter (slime page, summary: scalar results back to the response layout):
+ * every one of the T rows of dst is written -- rows named by row_idx get
+ * src[i, :], all others literal +0.0 (zero bytes).  Same constraints as
+ * gather; row_idx entries must be distinct.
+ */
+int rkl_scatter_rows(const void* src, int64_t N, int64_t row_bytes, const int32_t* row_idx, int64_t T,
+                     void* dst, rkl_stream_t stream);
+
+/*
+ * Device workspace (bytes) that rkl_forward_* and rkl_backward_* need for
+ * N rows, vocabulary V, student width Hs (0 = student given as logits) and
+ * teacher width Ht (0 = teacher given as logits).  Returns 0 on bad sizes.
+ */
+size_t rkl_workspace_bytes(int64_t N, int64_t V, int64_t Hs, int64_t Ht);
+
+/*
+ * Forward, hidden-state teacher (NeMo-RL page, summary: hidden_states payload).
+ *   h_s [N, Hs], W_s [V, Hs], h_t [N, Ht], W_t [V, Ht]   bf16
+ *   row_mask  NULL: all N rows are live (compacted input).
+ *             [N] uint8: full-row mode -- rows with 0 get loss 0 and stats 0.
+ *   loss      [N] fp32 out: L per row.
+ *   stats     [N, 3] fp32 out: (lse_s, lse_t, L) per row, the only state the
+ *             backward needs (the log-softmaxes themselves are recomputed).
+ * z_s and z_t are formed tile by tile in fp32 and never written to memory.
+ * N = 0 is allowed and launches nothing.
+ */
+int rkl_forward_hidden(int64_t N, int64_t V, int64_t Hs, int64_t Ht,
+                       const rkl_bf16* h_s, const rkl_bf16* W_s, const rkl_bf16* h_t, const rkl_bf16* W_t,
+                       const uint8_t* row_mask, float* loss, float* stats,
+                       void* workspace, size_t workspace_bytes, rkl_stream_t stream);
+
+/*
+ * Forward, logits teacher (NeMo-RL page, summary: logits payload).
+ *   z_t [N, V] fp32 teacher logits.
+ *   Student either as hidden states (h_s [N, Hs], W_s [V, Hs] bf16, z_s NULL)
+ *   or as fp32 logits (z_s [N, V], h_s = W_s = NULL, Hs = 0).
+ * Other arguments as rkl_forward_hidden.
+ */
+int rkl_forward_logits(int64_t N, int64_t V, int64_t Hs,
+                       const rkl_bf16* h_s, const rkl_bf16* W_s, const float* z_s, const float* z_t,
+                       const uint8_t* row_mask, float* loss, float* stats,
+                       void* workspace, size_t workspace_bytes, rkl_stream_t stream);
+
+/*
+ * Backward, hidden-state teacher (NeMo-RL page, implementation notes:
+ * dL/dz_s = p_s (w - L), log-softmaxes recomputed per vocabulary chunk).
+ * Inputs as rkl_forward_hidden, plus
+ *   grad_loss [N] fp32 upstream gradient g (NULL = all ones); the caller's
+ *             token reduction decides it.
+ *   stats     [N, 3] from the forward on the same inputs.
+ * Outputs (gradient of sum_i g_i L_i with respect to the student):
+ *   dh_s  [N, Hs] fp32, overwritten; rows with row_mask 0 are exactly 0.
+ *   dW_s  [V, Hs] fp32; overwritten, or added to when accumulate_dW != 0.
+ */
+int rkl_backward_hidden(int64_t N, int64_t V, int64_t Hs, int64_t Ht,
+                        const rkl_bf16* h_s, const rkl_bf16* W_s, const rkl_bf16* h_t, const rkl_bf16* W_t,
+                        const uint8_t* row_mask, const float* grad_loss, const float* stats,
+                        float* dh_s, float* dW_s, int accumulate_dW,
+                        void* workspace, size_t workspace_bytes, rkl_stream_t stream);
+
+/*
+ * Backward, logits teacher.  Student as hidden states: outputs dh_s, dW_s as
+ * in rkl_backward_hidden (dz_s must be NULL).  Student as logits (h_s = W_s
+ * = NULL, Hs = 0): output dz_s [N, V] fp32 = g p_s (w - L), rows with
+ * row_mask 0 exactly 0 (dh_s, dW_s must be NULL).
+ */
+int rkl_backward_logits(int64_t N, int64_t V, int64_t Hs,
+                        const rkl_bf16* h_s, const rkl_bf16* W_s, const float* z_s, const float* z_t,
+                        const uint8_t* row_mask, const float* grad_loss, const float* stats,
+                        float* dh_s, float* dW_s, int accumulate_dW, float* dz_s,
+                        void* workspace, size_t workspace_bytes, rkl_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RKL_H */

@@ -1,0 +1,314 @@
+"""lm_head_reverse_amd -- Python binding of librkl.so.
+
+Argument marshalling only: every step of the path (compaction, gather,
+projection, log-sum-exp / reverse-KL epilogue, dz, dh and dW GEMMs, scatter)
+runs in the HIP kernels of librkl.so.  PyTorch provides device memory and the
+current stream.  There is no fallback: if librkl.so is missing or the device
+is not a HIP device, calls raise.
+
+Function names mirror the C ABI in include/rkl.h (without the ``rkl_``
+prefix).  bf16 tensors are torch.bfloat16; every tensor must be contiguous
+and on the same CUDA (HIP) device.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+__all__ = [
+    "RKLError", "lib", "LIB_PATH", "version", "workspace_bytes", "compact_rows", "gather_rows",
+    "scatter_rows", "forward_hidden", "forward_logits", "backward_hidden", "backward_logits",
+    "ReverseKL",
+]
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librkl.so")
+
+RKL_OK, RKL_INVALID_ARG, RKL_UNSUPPORTED, RKL_WORKSPACE_TOO_SMALL, RKL_DEVICE_ERROR = range(5)
+
+
+class RKLError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"rkl status {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded librkl.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RKLError(-1, f"{LIB_PATH} not found; build it with `python -m lm_head_reverse_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    sig = {
+        "rkl_last_error": ([], ctypes.c_char_p),
+        "rkl_version": ([], ctypes.c_char_p),
+        "rkl_workspace_bytes": ([I64, I64, I64, I64], SZ),
+        "rkl_compact_rows": ([P, I64, P, P, P, P], I32),
+        "rkl_gather_rows": ([P, I64, I64, P, I64, P, P], I32),
+        "rkl_scatter_rows": ([P, I64, I64, P, I64, P, P], I32),
+        "rkl_forward_hidden": ([I64, I64, I64, I64, P, P, P, P, P, P, P, P, SZ, P], I32),
+        "rkl_forward_logits": ([I64, I64, I64, P, P, P, P, P, P, P, P, SZ, P], I32),
+        "rkl_backward_hidden": ([I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, I32, P, SZ, P], I32),
+        "rkl_backward_logits": ([I64, I64, I64, P, P, P, P, P, P, P, P, P, I32, P, P, SZ, P], I32),
+    }
+    for name, (args, res) in sig.items():
+        f = getattr(L, name)
+        f.argtypes = args
+        f.restype = res
+    _lib = L
+    return L
+
+
+def _check(rc: int):
+    if rc != RKL_OK:
+        raise RKLError(rc, lib().rkl_last_error().decode())
+
+
+def version() -> str:
+    return lib().rkl_version().decode()
+
+
+def workspace_bytes(N: int, V: int, Hs: int, Ht: int) -> int:
+    return int(lib().rkl_workspace_bytes(N, V, Hs, Ht))
+
+
+# ---------------------------------------------------------------- torch plumbing
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(dev):
+    torch = _torch()
+    return ctypes.c_void_p(torch.cuda.current_stream(dev).cuda_stream)
+
+
+def _need(t, name, dtype, dev=None, shape=None):
+    torch = _torch()
+    if t is None:
+        raise RKLError(RKL_INVALID_ARG, f"{name} is required")
+    if not t.is_cuda:
+        raise RKLError(RKL_INVALID_ARG, f"{name} must be a device tensor")
+    if t.dtype != dtype:
+        raise RKLError(RKL_INVALID_ARG, f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise RKLError(RKL_INVALID_ARG, f"{name} must be contiguous")
+    if dev is not None and t.device != dev:
+        raise RKLError(RKL_INVALID_ARG, f"{name} is on {t.device}, expected {dev}")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise RKLError(RKL_INVALID_ARG, f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    return t
+
+
+_ws_cache = {}
+
+
+def _workspace(dev, nbytes: int):
+    """A cached device byte buffer of at least nbytes (grown on demand)."""
+    torch = _torch()
+    key = str(dev)
+    buf = _ws_cache.get(key)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        _ws_cache[key] = buf
+    return buf
+
+
+# ---------------------------------------------------------------- entry points
+
+def compact_rows(mask):
+    """mask uint8 [T] -> (row_idx int32 [N] ascending, N).  Synchronises the stream."""
+    torch = _torch()
+    _need(mask, "mask", torch.uint8)
+    T = mask.numel()
+    row_idx = torch.empty(max(T, 1), dtype=torch.int32, device=mask.device)
+    n_dev = torch.empty(1, dtype=torch.int32, device=mask.device)
+    n_host = ctypes.c_int64(0)
+    _check(lib().rkl_compact_rows(_ptr(mask), T, _ptr(row_idx), _ptr(n_dev), ctypes.byref(n_host),
+                                  _stream(mask.device)))
+    return row_idx[: n_host.value], int(n_host.value)
+
+
+def gather_rows(src, row_idx):
+    """dst[i] = src[row_idx[i]] for a contiguous [T, ...] tensor (bit copy)."""
+    torch = _torch()
+    _need(row_idx, "row_idx", torch.int32, src.device)
+    T = src.shape[0]
+    N = row_idx.numel()
+    dst = torch.empty((N,) + tuple(src.shape[1:]), dtype=src.dtype, device=src.device)
+    row_bytes = src[0].numel() * src.element_size() if T > 0 else 4
+    _check(lib().rkl_gather_rows(_ptr(src), T, row_bytes, _ptr(row_idx), N, _ptr(dst), _stream(src.device)))
+    return dst
+
+
+def scatter_rows(src, row_idx, T: int):
+    """[T, ...] tensor with dst[row_idx[i]] = src[i] and +0 in every other row."""
+    torch = _torch()
+    _need(row_idx, "row_idx", torch.int32, src.device)
+    N = row_idx.numel()
+    dst = torch.empty((T,) + tuple(src.shape[1:]), dtype=src.dtype, device=src.device)
+    inner = 1
+    for d in src.shape[1:]:
+        inner *= d
+    row_bytes = inner * src.element_size()
+    _check(lib().rkl_scatter_rows(_ptr(src), N, row_bytes, _ptr(row_idx), T, _ptr(dst), _stream(src.device)))
+    return dst
+
+
+def forward_hidden(h_s, W_s, h_t, W_t, row_mask=None):
+    """Per-row reverse KL with the teacher given as hidden states.
+    Returns (loss fp32 [N], stats fp32 [N, 3] = (lse_s, lse_t, L))."""
+    torch = _torch()
+    dev = h_s.device
+    N, Hs = h_s.shape
+    V, Ht = W_t.shape
+    _need(h_s, "h_s", torch.bfloat16, dev)
+    _need(W_s, "W_s", torch.bfloat16, dev, (V, Hs))
+    _need(h_t, "h_t", torch.bfloat16, dev, (N, Ht))
+    _need(W_t, "W_t", torch.bfloat16, dev)
+    if row_mask is not None:
+        _need(row_mask, "row_mask", torch.uint8, dev, (N,))
+    loss = torch.empty(N, dtype=torch.float32, device=dev)
+    stats = torch.empty((N, 3), dtype=torch.float32, device=dev)
+    nb = workspace_bytes(N, V, Hs, Ht)
+    ws = _workspace(dev, nb)
+    _check(lib().rkl_forward_hidden(N, V, Hs, Ht, _ptr(h_s), _ptr(W_s), _ptr(h_t), _ptr(W_t), _ptr(row_mask),
+                                    _ptr(loss), _ptr(stats), _ptr(ws), ws.numel(), _stream(dev)))
+    return loss, stats
+
+
+def forward_logits(z_t, h_s=None, W_s=None, z_s=None, row_mask=None):
+    """Per-row reverse KL with the teacher given as fp32 logits z_t [N, V]; the
+    student as (h_s, W_s) bf16 or as fp32 logits z_s."""
+    torch = _torch()
+    dev = z_t.device
+    N, V = z_t.shape
+    _need(z_t, "z_t", torch.float32, dev)
+    Hs = 0
+    if z_s is None:
+        Hs = h_s.shape[1]
+        _need(h_s, "h_s", torch.bfloat16, dev, (N, Hs))
+        _need(W_s, "W_s", torch.bfloat16, dev, (V, Hs))
+    else:
+        _need(z_s, "z_s", torch.float32, dev, (N, V))
+    if row_mask is not None:
+        _need(row_mask, "row_mask", torch.uint8, dev, (N,))
+    loss = torch.empty(N, dtype=torch.float32, device=dev)
+    stats = torch.empty((N, 3), dtype=torch.float32, device=dev)
+    ws = _workspace(dev, workspace_bytes(N, V, Hs, 0))
+    _check(lib().rkl_forward_logits(N, V, Hs, _ptr(h_s), _ptr(W_s), _ptr(z_s), _ptr(z_t), _ptr(row_mask),
+                                    _ptr(loss), _ptr(stats), _ptr(ws), ws.numel(), _stream(dev)))
+    return loss, stats
+
+
+def backward_hidden(h_s, W_s, h_t, W_t, stats, grad_loss=None, row_mask=None, dW=None, accumulate_dW=False):
+    """Gradients of sum_i g_i L_i: returns (dh_s fp32 [N, Hs], dW_s fp32 [V, Hs])."""
+    torch = _torch()
+    dev = h_s.device
+    N, Hs = h_s.shape
+    V, Ht = W_t.shape
+    _need(h_s, "h_s", torch.bfloat16, dev)
+    _need(W_s, "W_s", torch.bfloat16, dev, (V, Hs))
+    _need(h_t, "h_t", torch.bfloat16, dev, (N, Ht))
+    _need(W_t, "W_t", torch.bfloat16, dev)
+    _need(stats, "stats", torch.float32, dev, (N, 3))
+    if grad_loss is not None:
+        _need(grad_loss, "grad_loss", torch.float32, dev, (N,))
+    if row_mask is not None:
+        _need(row_mask, "row_mask", torch.uint8, dev, (N,))
+    if dW is None:
+        if accumulate_dW:
+            raise RKLError(RKL_INVALID_ARG, "accumulate_dW needs a dW tensor")
+        dW = torch.empty((V, Hs), dtype=torch.float32, device=dev)
+    else:
+        _need(dW, "dW", torch.float32, dev, (V, Hs))
+    dh = torch.empty((N, Hs), dtype=torch.float32, device=dev)
+    ws = _workspace(dev, workspace_bytes(N, V, Hs, Ht))
+    _check(lib().rkl_backward_hidden(N, V, Hs, Ht, _ptr(h_s), _ptr(W_s), _ptr(h_t), _ptr(W_t), _ptr(row_mask),
+                                     _ptr(grad_loss), _ptr(stats), _ptr(dh), _ptr(dW), int(bool(accumulate_dW)),
+                                     _ptr(ws), ws.numel(), _stream(dev)))
+    return dh, dW
+
+
+def backward_logits(z_t, stats, h_s=None, W_s=None, z_s=None, grad_loss=None, row_mask=None, dW=None,
+                    accumulate_dW=False):
+    """Teacher as logits.  Student as (h_s, W_s): returns (dh_s, dW_s).
+    Student as logits z_s: returns dz_s fp32 [N, V]."""
+    torch = _torch()
+    dev = z_t.device
+    N, V = z_t.shape
+    _need(z_t, "z_t", torch.float32, dev)
+    _need(stats, "stats", torch.float32, dev, (N, 3))
+    if grad_loss is not None:
+        _need(grad_loss, "grad_loss", torch.float32, dev, (N,))
+    if row_mask is not None:
+        _need(row_mask, "row_mask", torch.uint8, dev, (N,))
+    if z_s is not None:
+        _need(z_s, "z_s", torch.float32, dev, (N, V))
+        dz = torch.empty((N, V), dtype=torch.float32, device=dev)
+        _check(lib().rkl_backward_logits(N, V, 0, None, None, _ptr(z_s), _ptr(z_t), _ptr(row_mask),
+                                         _ptr(grad_loss), _ptr(stats), None, None, 0, _ptr(dz), None, 0,
+                                         _stream(dev)))
+        return dz
+    Hs = h_s.shape[1]
+    _need(h_s, "h_s", torch.bfloat16, dev, (N, Hs))
+    _need(W_s, "W_s", torch.bfloat16, dev, (V, Hs))
+    if dW is None:
+        if accumulate_dW:
+            raise RKLError(RKL_INVALID_ARG, "accumulate_dW needs a dW tensor")
+        dW = torch.empty((V, Hs), dtype=torch.float32, device=dev)
+    else:
+        _need(dW, "dW", torch.float32, dev, (V, Hs))
+    dh = torch.empty((N, Hs), dtype=torch.float32, device=dev)
+    ws = _workspace(dev, workspace_bytes(N, V, Hs, 0))
+    _check(lib().rkl_backward_logits(N, V, Hs, _ptr(h_s), _ptr(W_s), None, _ptr(z_t), _ptr(row_mask),
+                                     _ptr(grad_loss), _ptr(stats), _ptr(dh), _ptr(dW), int(bool(accumulate_dW)),
+                                     None, _ptr(ws), ws.numel(), _stream(dev)))
+    return dh, dW
+
+
+class ReverseKL:
+    """Per-position reverse KL over a [B, S-1] loss mask with compaction:
+    compact -> gather -> fused forward -> scatter, and the matching backward.
+
+        rk = ReverseKL(W_s, W_t)                 # hidden-state teacher
+        loss_pos = rk.forward(h_s, h_t, mask)    # fp32 [T], zeros where mask == 0
+        dh_pos, dW = rk.backward(grad_pos)       # fp32 [T, Hs] and [V, Hs]
+    """
+
+    def __init__(self, W_s, W_t=None):
+        self.W_s, self.W_t = W_s, W_t
+
+    def forward(self, h_s, mask, h_t=None, z_t=None):
+        T = h_s.shape[0]
+        self.T = T
+        self.row_idx, self.N = compact_rows(mask)
+        self.h_s = gather_rows(h_s, self.row_idx)
+        if z_t is None:
+            self.h_t, self.z_t = gather_rows(h_t, self.row_idx), None
+            loss, self.stats = forward_hidden(self.h_s, self.W_s, self.h_t, self.W_t)
+        else:
+            self.h_t, self.z_t = None, gather_rows(z_t, self.row_idx)
+            loss, self.stats = forward_logits(self.z_t, h_s=self.h_s, W_s=self.W_s)
+        return scatter_rows(loss, self.row_idx, T)
+
+    def backward(self, grad_pos=None, dW=None, accumulate_dW=False):
+        g = None if grad_pos is None else gather_rows(grad_pos.contiguous(), self.row_idx)
+        if self.z_t is None:
+            dh, dW = backward_hidden(self.h_s, self.W_s, self.h_t, self.W_t, self.stats, g, dW=dW,
+                                     accumulate_dW=accumulate_dW)
+        else:
+            dh, dW = backward_logits(self.z_t, self.stats, h_s=self.h_s, W_s=self.W_s, grad_loss=g, dW=dW,
+                                     accumulate_dW=accumulate_dW)
+        return scatter_rows(dh, self.row_idx, self.T), dW

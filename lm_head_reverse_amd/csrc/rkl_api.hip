@@ -1,0 +1,334 @@
+// rkl_api.hip -- the C ABI declared in include/rkl.h: argument checks,
+// workspace layout and launch sequences.  No device memory is allocated here.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <string>
+
+#include "rkl.h"
+#include "rkl_internal.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define RKL_TRY(expr)                                                                   \
+  do {                                                                                  \
+    hipError_t e_ = (expr);                                                             \
+    if (e_ != hipSuccess) return fail(RKL_DEVICE_ERROR, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+constexpr int64_t kMaxDim = (int64_t)1 << 30;
+
+inline int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+inline int64_t ceil_div(int64_t x, int64_t m) { return (x + m - 1) / m; }
+inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+// Vocabulary columns per backward chunk (a multiple of 256).  Fixed for the
+// process so that a row's dh never depends on N.
+int64_t vocab_chunk() {
+  static const int64_t c = [] {
+    const char* s = std::getenv("RKL_VOCAB_CHUNK");
+    int64_t v = s ? std::atoll(s) : 16384;
+    if (v < 256) v = 256;
+    return round_up(v, 256);
+  }();
+  return c;
+}
+
+// Forward split plan: depends on V only (so a row's result never depends on N).
+struct Split {
+  int tiles_per_split, nsplit;
+};
+Split fwd_split(int64_t V) {
+  const int64_t ntv = ceil_div(V, rkl::kFwdTileV);
+  const int64_t tps = ceil_div(ntv, 160);
+  return Split{(int)tps, (int)ceil_div(ntv, tps)};
+}
+
+size_t fwd_ws_bytes(int64_t N, int64_t V, bool tiled) {
+  if (!tiled) return 0;
+  return align256((size_t)fwd_split(V).nsplit * 5 * (size_t)N * sizeof(float));
+}
+
+struct BwdLayout {
+  int64_t ldT, ldz;
+  size_t off_hT, off_dz, off_scale, total;
+};
+// [dz scale: 2 floats][hT: Hs x ldT fp16][dz chunk: N x ldz fp16]
+BwdLayout bwd_layout(int64_t N, int64_t V, int64_t Hs) {
+  BwdLayout L{};
+  L.ldT = round_up(N, 64);
+  const int64_t C = vocab_chunk();
+  L.ldz = round_up(V < C ? V : C, 64);
+  L.off_scale = 0;
+  L.off_hT = 256;
+  L.off_dz = L.off_hT + align256((size_t)Hs * L.ldT * 2);
+  L.total = L.off_dz + align256((size_t)N * L.ldz * 2);
+  return L;
+}
+
+size_t ws_bytes(int64_t N, int64_t V, int64_t Hs, int64_t Ht) {
+  (void)Ht;
+  if (Hs == 0) return 0;   // both sides as logits: row kernels need no workspace
+  const size_t f = fwd_ws_bytes(N, V, true);
+  const size_t b = bwd_layout(N, V, Hs).total;
+  return f > b ? f : b;
+}
+
+int check_dims(int64_t N, int64_t V, int64_t Hs, int64_t Ht, bool teacher_hidden, bool student_hidden) {
+  if (N < 0 || N > kMaxDim) return fail(RKL_INVALID_ARG, "N=%lld out of range [0, 2^30]", (long long)N);
+  if (V < 1 || V > kMaxDim) return fail(RKL_INVALID_ARG, "V=%lld out of range [1, 2^30]", (long long)V);
+  if (student_hidden) {
+    if (Hs <= 0 || Hs > 65536) return fail(RKL_INVALID_ARG, "Hs=%lld out of range", (long long)Hs);
+    if (Hs % 64) return fail(RKL_UNSUPPORTED, "Hs=%lld is not a multiple of 64", (long long)Hs);
+  } else if (Hs != 0) {
+    return fail(RKL_INVALID_ARG, "Hs must be 0 when the student is given as logits");
+  }
+  if (teacher_hidden) {
+    if (Ht <= 0 || Ht > 65536) return fail(RKL_INVALID_ARG, "Ht=%lld out of range", (long long)Ht);
+    if (Ht % 64) return fail(RKL_UNSUPPORTED, "Ht=%lld is not a multiple of 64", (long long)Ht);
+  }
+  if (N * V > ((int64_t)1 << 40)) return fail(RKL_INVALID_ARG, "N*V too large");
+  return RKL_OK;
+}
+
+#define NEED16(p, name)                                                                              \
+  do {                                                                                               \
+    if (!(p)) return fail(RKL_INVALID_ARG, "%s is NULL", name);                                      \
+    if (!aligned16(p)) return fail(RKL_INVALID_ARG, "%s is not 16-byte aligned", name);             \
+  } while (0)
+#define NEED4(p, name)                                                                               \
+  do {                                                                                               \
+    if (!(p)) return fail(RKL_INVALID_ARG, "%s is NULL", name);                                      \
+    if (!aligned4(p)) return fail(RKL_INVALID_ARG, "%s is not 4-byte aligned", name);               \
+  } while (0)
+#define OPT4(p, name)                                                                                \
+  do {                                                                                               \
+    if ((p) && !aligned4(p)) return fail(RKL_INVALID_ARG, "%s is not 4-byte aligned", name);        \
+  } while (0)
+
+// ---------------------------------------------------------------------------
+// forward / backward bodies shared by the hidden and logits entry points
+// ---------------------------------------------------------------------------
+int forward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* h_s, const rkl_bf16* W_s,
+                  const rkl_bf16* h_t, const rkl_bf16* W_t, const float* z_t, const uint8_t* row_mask, float* loss,
+                  float* stats, void* ws, size_t ws_bytes_given, hipStream_t s) {
+  const size_t need = fwd_ws_bytes(N, V, true);
+  if (ws_bytes_given < need)
+    return fail(RKL_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes_given, need);
+  if (N == 0) return RKL_OK;
+  NEED16(ws, "workspace");
+  const Split sp = fwd_split(V);
+  rkl::FwdParams p{};
+  p.N = (int)N; p.V = (int)V; p.Hs = (int)Hs; p.Ht = (int)Ht;
+  p.h_s = h_s; p.W_s = W_s; p.h_t = h_t; p.W_t = W_t; p.z_t = z_t;
+  p.partial = static_cast<float*>(ws);
+  p.tiles_per_split = sp.tiles_per_split;
+  p.nsplit = sp.nsplit;
+  p.ntok = (int)ceil_div(N, rkl::kFwdTileN);
+  RKL_TRY(rkl::launch_fwd_tiles(p, z_t != nullptr, s));
+  RKL_TRY(rkl::launch_fwd_combine(p.partial, p.nsplit, p.N, row_mask, loss, stats, s));
+  return RKL_OK;
+}
+
+int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* h_s, const rkl_bf16* W_s,
+                   const rkl_bf16* h_t, const rkl_bf16* W_t, const float* z_t, const uint8_t* row_mask,
+                   const float* grad, const float* stats, float* dh, float* dW, int accumulate, void* ws,
+                   size_t ws_bytes_given, hipStream_t s) {
+  const BwdLayout L = bwd_layout(N, V, Hs);
+  if (ws_bytes_given < L.total)
+    return fail(RKL_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes_given, L.total);
+  if (N == 0) {
+    // an empty selection still produces a (zero) dW unless the caller accumulates
+    if (!accumulate) RKL_TRY(rkl::launch_fill_zero(dW, V * Hs * (int64_t)sizeof(float), s));
+    return RKL_OK;
+  }
+  NEED16(ws, "workspace");
+  char* base = static_cast<char*>(ws);
+  float* gscale = reinterpret_cast<float*>(base + L.off_scale);
+  uint16_t* hT = reinterpret_cast<uint16_t*>(base + L.off_hT);
+  uint16_t* dz = reinterpret_cast<uint16_t*>(base + L.off_dz);
+  RKL_TRY(rkl::launch_grad_scale(grad, row_mask, (int)N, gscale, s));
+  RKL_TRY(rkl::launch_transpose_h(h_s, (int)N, (int)Hs, hT, (int)L.ldT, s));
+  const int64_t C = vocab_chunk();
+  for (int64_t c0 = 0; c0 < V; c0 += C) {
+    const int64_t width = (V - c0) < C ? (V - c0) : C;
+    const int64_t kpad = round_up(width, 64);
+    rkl::BwdParams b{};
+    b.N = (int)N; b.V = (int)V; b.Hs = (int)Hs; b.Ht = (int)Ht;
+    b.h_s = h_s; b.W_s = W_s; b.h_t = h_t; b.W_t = W_t; b.z_t = z_t;
+    b.row_mask = row_mask; b.grad = grad; b.stats = stats;
+    b.gscale = gscale; b.dz = dz; b.ldz = (int)L.ldz; b.c0 = (int)c0; b.kpad = (int)kpad;
+    b.ntv = (int)ceil_div(kpad, rkl::kFwdTileV);
+    b.ntok = (int)ceil_div(N, rkl::kFwdTileN);
+    RKL_TRY(rkl::launch_bwd_dz(b, z_t != nullptr, s));
+
+    rkl::DwParams w{};
+    w.gscale = gscale; w.dz = dz; w.ldz = (int)L.ldz; w.N = (int)N; w.kpad = (int)kpad; w.width = (int)width;
+    w.hT = hT; w.ldT = (int)L.ldT; w.H = (int)Hs;
+    w.dW = dW + c0 * Hs; w.accumulate = accumulate;
+    w.ntm = (int)ceil_div(width, rkl::kDwTileM);
+    w.ntn = (int)ceil_div(Hs, rkl::kDwTileN);
+    RKL_TRY(rkl::launch_dw(w, s));
+
+    rkl::DhParams h{};
+    h.gscale = gscale; h.dz = dz; h.ldz = (int)L.ldz; h.N = (int)N; h.kpad = (int)kpad; h.width = (int)width;
+    h.Wc = W_s + c0 * Hs; h.H = (int)Hs; h.dh = dh; h.accumulate = c0 > 0;
+    h.ntm = (int)ceil_div(N, rkl::kDhTileM);
+    h.ntn = (int)ceil_div(Hs, rkl::kDhTileN);
+    RKL_TRY(rkl::launch_dh(h, s));
+  }
+  return RKL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* rkl_last_error(void) { return g_err.c_str(); }
+
+const char* rkl_version(void) { return "rkl 0.1 gfx950"; }
+
+size_t rkl_workspace_bytes(int64_t N, int64_t V, int64_t Hs, int64_t Ht) {
+  if (N < 0 || N > kMaxDim || V < 1 || V > kMaxDim || Hs < 0 || Ht < 0) return 0;
+  return ws_bytes(N, V, Hs, Ht);
+}
+
+int rkl_compact_rows(const uint8_t* mask, int64_t T, int32_t* row_idx, int32_t* n_rows_dev, int64_t* n_rows_host,
+                     rkl_stream_t stream) {
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (T < 0 || T >= ((int64_t)1 << 31)) return fail(RKL_INVALID_ARG, "T=%lld out of range", (long long)T);
+  NEED4(n_rows_dev, "n_rows_dev");
+  if (T > 0) {
+    if (!mask) return fail(RKL_INVALID_ARG, "mask is NULL");
+    NEED4(row_idx, "row_idx");
+  }
+  RKL_TRY(rkl::launch_compact(mask, (int)T, row_idx, n_rows_dev, s));
+  if (n_rows_host) {
+    int32_t n = 0;
+    RKL_TRY(hipMemcpyAsync(&n, n_rows_dev, sizeof(n), hipMemcpyDeviceToHost, s));
+    RKL_TRY(hipStreamSynchronize(s));
+    *n_rows_host = n;
+  }
+  return RKL_OK;
+}
+
+int rkl_gather_rows(const void* src, int64_t T, int64_t row_bytes, const int32_t* row_idx, int64_t N, void* dst,
+                    rkl_stream_t stream) {
+  if (T < 0 || N < 0 || N > T) return fail(RKL_INVALID_ARG, "need 0 <= N <= T (N=%lld, T=%lld)", (long long)N, (long long)T);
+  if (N >= ((int64_t)1 << 31)) return fail(RKL_INVALID_ARG, "N too large");
+  if (row_bytes <= 0 || row_bytes % 4) return fail(RKL_INVALID_ARG, "row_bytes=%lld must be a positive multiple of 4", (long long)row_bytes);
+  if (N == 0) return RKL_OK;
+  if (!src || !dst || !row_idx) return fail(RKL_INVALID_ARG, "NULL pointer");
+  const bool need16 = row_bytes % 16 == 0;
+  if (need16 ? !(aligned16(src) && aligned16(dst)) : !(aligned4(src) && aligned4(dst)))
+    return fail(RKL_INVALID_ARG, "src/dst misaligned");
+  RKL_TRY(rkl::launch_gather(src, row_bytes, row_idx, N, dst, static_cast<hipStream_t>(stream)));
+  return RKL_OK;
+}
+
+int rkl_scatter_rows(const void* src, int64_t N, int64_t row_bytes, const int32_t* row_idx, int64_t T, void* dst,
+                     rkl_stream_t stream) {
+  if (T < 0 || N < 0 || N > T) return fail(RKL_INVALID_ARG, "need 0 <= N <= T (N=%lld, T=%lld)", (long long)N, (long long)T);
+  if (T >= ((int64_t)1 << 31)) return fail(RKL_INVALID_ARG, "T too large");
+  if (row_bytes <= 0 || row_bytes % 4) return fail(RKL_INVALID_ARG, "row_bytes=%lld must be a positive multiple of 4", (long long)row_bytes);
+  if (T == 0) return RKL_OK;
+  if (!dst || (N > 0 && (!src || !row_idx))) return fail(RKL_INVALID_ARG, "NULL pointer");
+  const bool need16 = row_bytes % 16 == 0;
+  if (need16 ? !(aligned16(dst) && (N == 0 || aligned16(src))) : !(aligned4(dst) && (N == 0 || aligned4(src))))
+    return fail(RKL_INVALID_ARG, "src/dst misaligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  RKL_TRY(rkl::launch_fill_zero(dst, T * row_bytes, s));
+  if (N > 0) RKL_TRY(rkl::launch_scatter(src, row_bytes, row_idx, N, dst, s));
+  return RKL_OK;
+}
+
+int rkl_forward_hidden(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* h_s, const rkl_bf16* W_s,
+                       const rkl_bf16* h_t, const rkl_bf16* W_t, const uint8_t* row_mask, float* loss, float* stats,
+                       void* workspace, size_t workspace_bytes, rkl_stream_t stream) {
+  if (int rc = check_dims(N, V, Hs, Ht, true, true)) return rc;
+  if (N > 0) {
+    NEED16(h_s, "h_s"); NEED16(W_s, "W_s"); NEED16(h_t, "h_t"); NEED16(W_t, "W_t");
+    NEED4(loss, "loss"); NEED4(stats, "stats");
+  }
+  return forward_tiled(N, V, Hs, Ht, h_s, W_s, h_t, W_t, nullptr, row_mask, loss, stats, workspace, workspace_bytes,
+                       static_cast<hipStream_t>(stream));
+}
+
+int rkl_forward_logits(int64_t N, int64_t V, int64_t Hs, const rkl_bf16* h_s, const rkl_bf16* W_s, const float* z_s,
+                       const float* z_t, const uint8_t* row_mask, float* loss, float* stats, void* workspace,
+                       size_t workspace_bytes, rkl_stream_t stream) {
+  const bool student_hidden = h_s != nullptr || W_s != nullptr;
+  if (student_hidden && z_s) return fail(RKL_INVALID_ARG, "give the student as (h_s, W_s) or as z_s, not both");
+  if (int rc = check_dims(N, V, Hs, 0, false, student_hidden)) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N > 0) {
+    NEED16(z_t, "z_t");
+    NEED4(loss, "loss"); NEED4(stats, "stats");
+    if (student_hidden) { NEED16(h_s, "h_s"); NEED16(W_s, "W_s"); }
+    else NEED16(z_s, "z_s");
+  }
+  if (student_hidden)
+    return forward_tiled(N, V, Hs, 0, h_s, W_s, nullptr, nullptr, z_t, row_mask, loss, stats, workspace,
+                         workspace_bytes, s);
+  if (N == 0) return RKL_OK;
+  RKL_TRY(rkl::launch_fwd_rows_logits(z_s, z_t, (int)N, (int)V, row_mask, loss, stats, s));
+  return RKL_OK;
+}
+
+int rkl_backward_hidden(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* h_s, const rkl_bf16* W_s,
+                        const rkl_bf16* h_t, const rkl_bf16* W_t, const uint8_t* row_mask, const float* grad_loss,
+                        const float* stats, float* dh_s, float* dW_s, int accumulate_dW, void* workspace,
+                        size_t workspace_bytes, rkl_stream_t stream) {
+  if (int rc = check_dims(N, V, Hs, Ht, true, true)) return rc;
+  NEED16(dW_s, "dW_s");
+  if (N > 0) {
+    NEED16(h_s, "h_s"); NEED16(W_s, "W_s"); NEED16(h_t, "h_t"); NEED16(W_t, "W_t");
+    NEED4(stats, "stats"); NEED16(dh_s, "dh_s"); OPT4(grad_loss, "grad_loss");
+  }
+  return backward_tiled(N, V, Hs, Ht, h_s, W_s, h_t, W_t, nullptr, row_mask, grad_loss, stats, dh_s, dW_s,
+                        accumulate_dW != 0, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int rkl_backward_logits(int64_t N, int64_t V, int64_t Hs, const rkl_bf16* h_s, const rkl_bf16* W_s, const float* z_s,
+                        const float* z_t, const uint8_t* row_mask, const float* grad_loss, const float* stats,
+                        float* dh_s, float* dW_s, int accumulate_dW, float* dz_s, void* workspace,
+                        size_t workspace_bytes, rkl_stream_t stream) {
+  const bool student_hidden = h_s != nullptr || W_s != nullptr;
+  if (student_hidden && z_s) return fail(RKL_INVALID_ARG, "give the student as (h_s, W_s) or as z_s, not both");
+  if (int rc = check_dims(N, V, Hs, 0, false, student_hidden)) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (student_hidden) {
+    if (dz_s) return fail(RKL_INVALID_ARG, "dz_s must be NULL when the student is given as hidden states");
+    NEED16(dW_s, "dW_s");
+    if (N > 0) {
+      NEED16(h_s, "h_s"); NEED16(W_s, "W_s"); NEED16(z_t, "z_t");
+      NEED4(stats, "stats"); NEED16(dh_s, "dh_s"); OPT4(grad_loss, "grad_loss");
+    }
+    return backward_tiled(N, V, Hs, 0, h_s, W_s, nullptr, nullptr, z_t, row_mask, grad_loss, stats, dh_s, dW_s,
+                          accumulate_dW != 0, workspace, workspace_bytes, s);
+  }
+  if (dh_s || dW_s) return fail(RKL_INVALID_ARG, "dh_s and dW_s must be NULL when the student is given as logits");
+  if (N == 0) return RKL_OK;
+  NEED16(z_s, "z_s"); NEED16(z_t, "z_t"); NEED4(stats, "stats"); NEED16(dz_s, "dz_s"); OPT4(grad_loss, "grad_loss");
+  RKL_TRY(rkl::launch_bwd_rows_logits(z_s, z_t, (int)N, (int)V, row_mask, grad_loss, stats, dz_s, s));
+  return RKL_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,89 @@
+// rkl_internal.h -- kernel parameter blocks and launchers shared by the C ABI
+// (rkl_api.hip) and the kernels (rkl_kernels.hip).  Not installed.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rkl {
+
+struct FwdParams {
+  int N, V, Hs, Ht;
+  const uint16_t* h_s;
+  const uint16_t* W_s;
+  const uint16_t* h_t;
+  const uint16_t* W_t;
+  const float* z_t;        // teacher logits [N, V] (teacher-logits payload)
+  float* partial;          // [nsplit][5][N]
+  int tiles_per_split;     // 256-row vocabulary tiles per split
+  int nsplit;
+  int ntok;                // 128-token tiles
+};
+
+struct BwdParams {
+  int N, V, Hs, Ht;
+  const uint16_t* h_s;
+  const uint16_t* W_s;
+  const uint16_t* h_t;
+  const uint16_t* W_t;
+  const float* z_t;
+  const uint8_t* row_mask;
+  const float* grad;
+  const float* stats;
+  const float* gscale;     // [2]: s, 1/s (powers of two); dz is stored as fp16(s * dz)
+  uint16_t* dz;            // [N, ldz] fp16 chunk workspace
+  int ldz;
+  int c0;                  // first vocabulary row of the chunk
+  int kpad;                // chunk width rounded up to 64 (columns written)
+  int ntv;                 // 256-row vocabulary tiles in the chunk
+  int ntok;
+};
+
+struct DwParams {
+  const float* gscale;
+  const uint16_t* dz;
+  int ldz, N, kpad, width;
+  const uint16_t* hT;      // [H, ldT] fp16
+  int ldT, H;
+  float* dW;               // dW_s + c0 * H
+  int accumulate;
+  int ntm, ntn;
+};
+
+struct DhParams {
+  const float* gscale;
+  const uint16_t* dz;
+  int ldz, N, kpad, width;
+  const uint16_t* Wc;      // W_s + c0 * H
+  int H;
+  float* dh;
+  int accumulate;
+  int ntm, ntn;
+};
+
+// Tile sizes the host needs for grids and workspace.
+constexpr int kFwdTileV = 256;
+constexpr int kFwdTileN = 128;
+constexpr int kDwTileM = 256, kDwTileN = 128;
+constexpr int kDhTileM = 128, kDhTileN = 128;
+
+hipError_t launch_fwd_tiles(const FwdParams& p, bool teacher_logits, hipStream_t s);
+hipError_t launch_fwd_combine(const float* partial, int nsplit, int N, const uint8_t* row_mask, float* loss,
+                              float* stats, hipStream_t s);
+hipError_t launch_bwd_dz(const BwdParams& p, bool teacher_logits, hipStream_t s);
+hipError_t launch_grad_scale(const float* grad, const uint8_t* row_mask, int N, float* out, hipStream_t s);
+hipError_t launch_transpose_h(const uint16_t* h, int N, int H, uint16_t* hT, int ldT, hipStream_t s);
+hipError_t launch_dw(const DwParams& p, hipStream_t s);
+hipError_t launch_dh(const DhParams& p, hipStream_t s);
+hipError_t launch_fwd_rows_logits(const float* z_s, const float* z_t, int N, int V, const uint8_t* row_mask,
+                                  float* loss, float* stats, hipStream_t s);
+hipError_t launch_bwd_rows_logits(const float* z_s, const float* z_t, int N, int V, const uint8_t* row_mask,
+                                  const float* grad, const float* stats, float* dz, hipStream_t s);
+hipError_t launch_compact(const uint8_t* mask, int T, int32_t* row_idx, int32_t* n_out, hipStream_t s);
+hipError_t launch_gather(const void* src, int64_t row_bytes, const int32_t* row_idx, int64_t N, void* dst,
+                         hipStream_t s);
+hipError_t launch_scatter(const void* src, int64_t row_bytes, const int32_t* row_idx, int64_t N, void* dst,
+                          hipStream_t s);
+hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t s);
+
+}  // namespace rkl

@@ -1,0 +1,696 @@
+// rkl_kernels.hip -- HIP kernels for gfx950 of the fused LM-head projection +
+// full-vocabulary reverse KL (forward, backward) and loss-mask compaction.
+//
+// Method (NeMo-RL pull request "add full-vocabulary on-policy distillation to
+// SingleController"): summary -- L = sum_v p_s (log p_s - log p_t) per token;
+// implementation notes -- dL/dz_s = p_s (w - L), w = log p_s - log p_t, with
+// the log-softmaxes recomputed in the backward.  Compaction (slime pull
+// request "compact actor logits before projection", summary): only the
+// loss-masked rows are projected and scalars are scattered back.
+//
+// Orientation: every projection tile is computed as C[v, t] = W[v, :] . h[t, :]
+// (vocabulary along MFMA rows, tokens along MFMA columns).  In the 32x32 MFMA
+// output layout one lane then holds one token and 16 vocabulary entries per
+// block, so the online log-sum-exp / KL statistics of a token live in that
+// lane's registers for the whole vocabulary sweep; lanes l and l^32 (the two
+// row halves) merge once at the end, then the two waves that share tokens
+// merge through LDS.
+#include "rkl_tile.h"
+#include "rkl_internal.h"
+
+namespace rkl {
+
+constexpr float kL2E = 1.4426950408889634f;
+constexpr float kNegBig = -1.0e30f;   // "no value seen yet" running max; exp2 of it underflows to 0
+
+__device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// Merge of two partial (max, sum of exp(z - max), sum of exp(z - max) * d) triples.
+__device__ __forceinline__ void merge3(float& m, float& s, float& a, float m2, float s2, float a2) {
+  const float M = fmaxf(m, m2);
+  const float f1 = ex2((m - M) * kL2E), f2 = ex2((m2 - M) * kL2E);
+  s = s * f1 + s2 * f2;
+  a = a * f1 + a2 * f2;
+  m = M;
+}
+__device__ __forceinline__ void merge2(float& m, float& s, float m2, float s2) {
+  const float M = fmaxf(m, m2);
+  const float f1 = ex2((m - M) * kL2E), f2 = ex2((m2 - M) * kL2E);
+  s = s * f1 + s2 * f2;
+  m = M;
+}
+
+// ===========================================================================
+// Fused forward: per (vocabulary split, token tile) workgroup, sweep the
+// split's vocabulary tiles; for each tile form z_s (and z_t) in registers with
+// MFMA and fold them into per-lane online statistics
+//   m_s, S_s = sum e^{z_s - m_s}, A = sum e^{z_s - m_s} (z_s - z_t), m_t, S_t.
+// Nothing of size [N, V] is written.
+// ===========================================================================
+constexpr int FBM = 256;   // vocabulary rows per tile
+constexpr int FBN = 128;   // tokens per tile
+constexpr int FFM = FBM / 2 / 32, FFN = FBN / 2 / 32;
+using FwdStages = Stages<FBM, FBN>;
+constexpr int kFwdRedBytes = 2 * FFN * 32 * 5 * 4;
+
+// Fold one tile's values of token column fn into the running statistics.
+template <bool TAIL>
+__device__ __forceinline__ void fold_tile(const f32x16 (&zs)[FFM][FFN], const f32x16 (&zt)[FFM][FFN], int fn,
+                                          int vrow, int V, float& ms, float& ss, float& aa, float& mt, float& st) {
+  // vrow = vocabulary index of fragment row 0 for this lane (block fm = 0)
+  float tms = kNegBig, tmt = kNegBig;
+#pragma unroll
+  for (int fm = 0; fm < FFM; ++fm)
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool ok = !TAIL || (vrow + fm * 32 + 8 * (i >> 2) + (i & 3) < V);
+      if (ok) {
+        tms = fmaxf(tms, zs[fm][fn][i]);
+        tmt = fmaxf(tmt, zt[fm][fn][i]);
+      }
+    }
+  const float nms = fmaxf(ms, tms), nmt = fmaxf(mt, tmt);
+  const float cs = nms * kL2E, ct = nmt * kL2E;
+  float ps[FFM], pt[FFM], pa[FFM];
+#pragma unroll
+  for (int fm = 0; fm < FFM; ++fm) {
+    ps[fm] = 0.f; pt[fm] = 0.f; pa[fm] = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool ok = !TAIL || (vrow + fm * 32 + 8 * (i >> 2) + (i & 3) < V);
+      if (ok) {
+        const float a = zs[fm][fn][i], b = zt[fm][fn][i];
+        const float es = ex2(fmaf(a, kL2E, -cs));
+        const float et = ex2(fmaf(b, kL2E, -ct));
+        ps[fm] += es;
+        pt[fm] += et;
+        pa[fm] = fmaf(es, a - b, pa[fm]);
+      }
+    }
+  }
+  float sum_s = ps[0], sum_t = pt[0], sum_a = pa[0];
+#pragma unroll
+  for (int fm = 1; fm < FFM; ++fm) { sum_s += ps[fm]; sum_t += pt[fm]; sum_a += pa[fm]; }
+  const float fs = ex2((ms - nms) * kL2E), ft = ex2((mt - nmt) * kL2E);
+  ss = fmaf(ss, fs, sum_s);
+  aa = fmaf(aa, fs, sum_a);
+  st = fmaf(st, ft, sum_t);
+  ms = nms;
+  mt = nmt;
+}
+
+// Teacher logits read into the accumulator layout (teacher-logits payload).
+template <bool VEC4>
+__device__ __forceinline__ void load_zt(f32x16 (&zt)[FFM][FFN], const float* __restrict__ z_t, int N, int V,
+                                        int vrow, int ncol, int lane) {
+  (void)lane;
+#pragma unroll
+  for (int fn = 0; fn < FFN; ++fn) {
+    const int n = ncol + fn * 32;
+    const float* row = z_t + (int64_t)n * V;
+#pragma unroll
+    for (int fm = 0; fm < FFM; ++fm)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int v = vrow + fm * 32 + 8 * g;
+        if (VEC4) {
+          float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
+          if (n < N && v < V) q = *reinterpret_cast<const float4*>(row + v);
+          zt[fm][fn][4 * g + 0] = q.x; zt[fm][fn][4 * g + 1] = q.y;
+          zt[fm][fn][4 * g + 2] = q.z; zt[fm][fn][4 * g + 3] = q.w;
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            zt[fm][fn][4 * g + e] = (n < N && v + e < V) ? row[v + e] : 0.f;
+        }
+      }
+  }
+}
+
+template <int MODE, bool VEC4>   // MODE 0: hidden teacher; 1: teacher logits
+__global__ __launch_bounds__(kThreads, 1) void fwd_tiles(FwdParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[FwdStages::kBytes + kFwdRedBytes];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int logical = xcd_logical(blockIdx.x, p.nsplit * p.ntok);
+  const int split = logical / p.ntok, tt = logical - split * p.ntok;
+  const int n0 = tt * FBN;
+  const int ntv = (p.V + FBM - 1) / FBM;
+  const int vt0 = split * p.tiles_per_split;
+  const int vt1 = min(vt0 + p.tiles_per_split, ntv);
+
+  float ms[FFN], ss[FFN], aa[FFN], mt[FFN], st[FFN];
+#pragma unroll
+  for (int fn = 0; fn < FFN; ++fn) { ms[fn] = kNegBig; ss[fn] = 0.f; aa[fn] = 0.f; mt[fn] = kNegBig; st[fn] = 0.f; }
+
+  KLoader<FBM> la;
+  KLoader<FBN> lb;
+  f32x16 zs[FFM][FFN], zt[FFM][FFN];
+  const int arow0 = wm * (FBM / 2), brow0 = wn * (FBN / 2);
+  const int lrow = 4 * (lane >> 5);
+
+  for (int vt = vt0; vt < vt1; ++vt) {
+    const int v0 = vt * FBM;
+    zero_acc(zs);
+    {
+      const uint16_t* Wb = p.W_s + (int64_t)v0 * p.Hs;
+      const uint16_t* hb = p.h_s + (int64_t)n0 * p.Hs;
+      auto fetch = [&](int kt) {
+        la.load(Wb + kt * kKT, p.Hs, p.V - v0, tid);
+        lb.load(hb + kt * kKT, p.Hs, p.N - n0, tid);
+      };
+      kloop<FBM, FBN>(zs, la, lb, fetch, p.Hs / kKT, lds, tid, arow0, brow0);
+    }
+    if (MODE == 0) {
+      zero_acc(zt);
+      const uint16_t* Wb = p.W_t + (int64_t)v0 * p.Ht;
+      const uint16_t* hb = p.h_t + (int64_t)n0 * p.Ht;
+      auto fetch = [&](int kt) {
+        la.load(Wb + kt * kKT, p.Ht, p.V - v0, tid);
+        lb.load(hb + kt * kKT, p.Ht, p.N - n0, tid);
+      };
+      kloop<FBM, FBN>(zt, la, lb, fetch, p.Ht / kKT, lds, tid, arow0, brow0);
+    } else {
+      load_zt<VEC4>(zt, p.z_t, p.N, p.V, v0 + arow0 + lrow, n0 + brow0 + (lane & 31), lane);
+    }
+    const int vrow = v0 + arow0 + lrow;
+    if (v0 + FBM <= p.V) {
+#pragma unroll
+      for (int fn = 0; fn < FFN; ++fn) fold_tile<false>(zs, zt, fn, vrow, p.V, ms[fn], ss[fn], aa[fn], mt[fn], st[fn]);
+    } else {
+#pragma unroll
+      for (int fn = 0; fn < FFN; ++fn) fold_tile<true>(zs, zt, fn, vrow, p.V, ms[fn], ss[fn], aa[fn], mt[fn], st[fn]);
+    }
+  }
+
+  // merge the two row halves of each 32x32 block (lanes l and l^32)
+#pragma unroll
+  for (int fn = 0; fn < FFN; ++fn) {
+    const float oms = __shfl_xor(ms[fn], 32), oss = __shfl_xor(ss[fn], 32), oaa = __shfl_xor(aa[fn], 32);
+    const float omt = __shfl_xor(mt[fn], 32), ost = __shfl_xor(st[fn], 32);
+    merge3(ms[fn], ss[fn], aa[fn], oms, oss, oaa);
+    merge2(mt[fn], st[fn], omt, ost);
+  }
+  // merge the two waves that hold the same tokens (wm = 0 and wm = 1)
+  float* red = reinterpret_cast<float*>(lds + FwdStages::kBytes);
+  if (wm == 1 && lane < 32) {
+#pragma unroll
+    for (int fn = 0; fn < FFN; ++fn) {
+      float* q = red + ((wn * FFN + fn) * 32 + lane) * 5;
+      q[0] = ms[fn]; q[1] = ss[fn]; q[2] = aa[fn]; q[3] = mt[fn]; q[4] = st[fn];
+    }
+  }
+  __syncthreads();
+  if (wm == 0 && lane < 32) {
+#pragma unroll
+    for (int fn = 0; fn < FFN; ++fn) {
+      const float* q = red + ((wn * FFN + fn) * 32 + lane) * 5;
+      merge3(ms[fn], ss[fn], aa[fn], q[0], q[1], q[2]);
+      merge2(mt[fn], st[fn], q[3], q[4]);
+      const int n = n0 + brow0 + fn * 32 + lane;
+      if (n < p.N) {
+        float* P = p.partial + (int64_t)split * 5 * p.N + n;
+        P[0] = ms[fn];
+        P[(int64_t)1 * p.N] = ss[fn];
+        P[(int64_t)2 * p.N] = aa[fn];
+        P[(int64_t)3 * p.N] = mt[fn];
+        P[(int64_t)4 * p.N] = st[fn];
+      }
+    }
+  }
+}
+
+// Split combine: lse = m + log S per side; L = A / S_s - (lse_s - lse_t).
+__global__ __launch_bounds__(256) void fwd_combine(const float* __restrict__ partial, int nsplit, int N,
+                                                   const uint8_t* __restrict__ row_mask, float* __restrict__ loss,
+                                                   float* __restrict__ stats) {
+  const int n = blockIdx.x * 256 + threadIdx.x;
+  if (n >= N) return;
+  float ms = kNegBig, ss = 0.f, aa = 0.f, mt = kNegBig, st = 0.f;
+  for (int s = 0; s < nsplit; ++s) {
+    const float* P = partial + (int64_t)s * 5 * N + n;
+    merge3(ms, ss, aa, P[0], P[(int64_t)N], P[(int64_t)2 * N]);
+    merge2(mt, st, P[(int64_t)3 * N], P[(int64_t)4 * N]);
+  }
+  float lse_s = ms + logf(ss);
+  float lse_t = mt + logf(st);
+  float L = aa / ss - (lse_s - lse_t);
+  if (row_mask && row_mask[n] == 0) { L = 0.f; lse_s = 0.f; lse_t = 0.f; }
+  loss[n] = L;
+  stats[3 * (int64_t)n + 0] = lse_s;
+  stats[3 * (int64_t)n + 1] = lse_t;
+  stats[3 * (int64_t)n + 2] = L;
+}
+
+// ===========================================================================
+// Backward, step 0: dz scale.  dz = g p_s (w - L) is stored as fp16(s * dz)
+// (11-bit significand; bf16's 8 bits alone can use up the gradient
+// tolerance when one vocabulary entry dominates a row).  s is the power of
+// two that puts max|g| (over live rows) in [1/16, 1/8), leaving fp16 headroom
+// for |w - L| up to ~5e5; dh and dW are multiplied by 1/s (exact).
+// ===========================================================================
+__global__ __launch_bounds__(1024) void grad_scale(const float* __restrict__ grad, const uint8_t* __restrict__ row_mask,
+                                                   int N, float* __restrict__ out) {
+  __shared__ float red[1024];
+  const int tid = threadIdx.x;
+  float m = 0.f;
+  for (int n = tid; n < N; n += 1024) {
+    const bool live = !row_mask || row_mask[n] != 0;
+    if (live) m = fmaxf(m, grad ? fabsf(grad[n]) : 1.0f);
+  }
+  red[tid] = m;
+  __syncthreads();
+  for (int off = 512; off > 0; off >>= 1) {
+    if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
+    __syncthreads();
+  }
+  if (tid == 0) {
+    int e = 0;
+    if (red[0] > 0.f) frexpf(red[0], &e);     // max|g| in [2^(e-1), 2^e)
+    e = e < -100 ? -100 : (e > 100 ? 100 : e);
+    out[0] = ldexpf(1.0f, -e - 3);
+    out[1] = ldexpf(1.0f, e + 3);
+  }
+}
+
+// ===========================================================================
+// Backward, step 1: recompute z_s, z_t for one (vocabulary tile, token tile)
+// of the current chunk and write s * dz, dz = g p_s ((z_s - z_t) - (lse_s -
+// lse_t + L)), rounded to fp16 into the chunk workspace dz[N, ldz]
+// (column = v - c0).  Columns in [width, kpad) are written as zero; rows with
+// row_mask 0 are zero.
+// ===========================================================================
+template <int MODE, bool VEC4>
+__global__ __launch_bounds__(kThreads, 1) void bwd_dz_tiles(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[FwdStages::kBytes];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int logical = xcd_logical(blockIdx.x, p.ntv * p.ntok);
+  const int vt = logical / p.ntok, tt = logical - vt * p.ntok;
+  const int v0 = p.c0 + vt * FBM, n0 = tt * FBN;
+  const int arow0 = wm * (FBM / 2), brow0 = wn * (FBN / 2);
+  const int lrow = 4 * (lane >> 5);
+
+  KLoader<FBM> la;
+  KLoader<FBN> lb;
+  f32x16 zs[FFM][FFN], zt[FFM][FFN];
+  zero_acc(zs);
+  {
+    const uint16_t* Wb = p.W_s + (int64_t)v0 * p.Hs;
+    const uint16_t* hb = p.h_s + (int64_t)n0 * p.Hs;
+    auto fetch = [&](int kt) {
+      la.load(Wb + kt * kKT, p.Hs, p.V - v0, tid);
+      lb.load(hb + kt * kKT, p.Hs, p.N - n0, tid);
+    };
+    kloop<FBM, FBN>(zs, la, lb, fetch, p.Hs / kKT, lds, tid, arow0, brow0);
+  }
+  if (MODE == 0) {
+    zero_acc(zt);
+    const uint16_t* Wb = p.W_t + (int64_t)v0 * p.Ht;
+    const uint16_t* hb = p.h_t + (int64_t)n0 * p.Ht;
+    auto fetch = [&](int kt) {
+      la.load(Wb + kt * kKT, p.Ht, p.V - v0, tid);
+      lb.load(hb + kt * kKT, p.Ht, p.N - n0, tid);
+    };
+    kloop<FBM, FBN>(zt, la, lb, fetch, p.Ht / kKT, lds, tid, arow0, brow0);
+  } else {
+    load_zt<VEC4>(zt, p.z_t, p.N, p.V, v0 + arow0 + lrow, n0 + brow0 + (lane & 31), lane);
+  }
+
+#pragma unroll
+  for (int fn = 0; fn < FFN; ++fn) {
+    const int n = n0 + brow0 + fn * 32 + (lane & 31);
+    if (n >= p.N) continue;
+    const bool live = !p.row_mask || p.row_mask[n] != 0;
+    const float lse_s = p.stats[3 * (int64_t)n + 0];
+    const float lse_t = p.stats[3 * (int64_t)n + 1];
+    const float L = p.stats[3 * (int64_t)n + 2];
+    const float g = (p.grad ? p.grad[n] : 1.0f) * p.gscale[0];
+    const float c = (lse_s - lse_t) + L;
+    const float cs = lse_s * kL2E;
+    uint16_t* drow = p.dz + (int64_t)n * p.ldz;
+#pragma unroll
+    for (int fm = 0; fm < FFM; ++fm)
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        const int v = v0 + arow0 + lrow + fm * 32 + 8 * gq;   // first of 4 consecutive entries
+        const int col = v - p.c0;
+        if (col >= p.kpad) continue;
+        _Float16 o[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float a = zs[fm][fn][4 * gq + e], b = zt[fm][fn][4 * gq + e];
+          float d = 0.f;
+          if (live && v + e < p.V) d = g * ex2(fmaf(a, kL2E, -cs)) * ((a - b) - c);
+          o[e] = (_Float16)d;
+        }
+        *reinterpret_cast<u32x2*>(drow + col) = u32x2{
+            (uint32_t)__builtin_bit_cast(uint16_t, o[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, o[1]) << 16),
+            (uint32_t)__builtin_bit_cast(uint16_t, o[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, o[3]) << 16)};
+      }
+  }
+}
+
+// h_s [N, H] bf16 -> hT [H, ldT] fp16 (exact for values in fp16's normal
+// range), zero for token columns in [N, ldT).
+__global__ __launch_bounds__(256) void transpose_h(const uint16_t* __restrict__ h, int N, int H,
+                                                   uint16_t* __restrict__ hT, int ldT) {
+  __shared__ uint16_t tile[64][66];
+  const int n0 = blockIdx.x * 64, j0 = blockIdx.y * 64, tid = threadIdx.x;
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    tile[r][c] = (n0 + r < N) ? h[(int64_t)(n0 + r) * H + j0 + c] : (uint16_t)0;
+  }
+  __syncthreads();
+  for (int e = tid; e < 64 * 64; e += 256) {
+    const int r = e >> 6, c = e & 63;
+    const float x = __builtin_bit_cast(float, (uint32_t)tile[c][r] << 16);
+    hT[(int64_t)(j0 + r) * ldT + n0 + c] = __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+}
+
+// ===========================================================================
+// Backward, step 2: dW_s[c0 + m, n] (+)= sum_t dz[t, m] h_s[t, n]
+// A = dz (MN-major: token rows, vocabulary contiguous), B = hT (K-major).
+// ===========================================================================
+constexpr int WBM = 256, WBN = 128;
+using DwStages = Stages<WBM, WBN>;
+
+__global__ __launch_bounds__(kThreads, 1) void dw_gemm(DwParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[DwStages::kBytes];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int logical = xcd_logical(blockIdx.x, p.ntm * p.ntn);
+  const int tm = logical / p.ntn, tn = logical - tm * p.ntn;
+  const int m0 = tm * WBM, n0 = tn * WBN;
+  constexpr int FM = WBM / 64, FN = WBN / 64;
+  MLoader<WBM> la;
+  KLoader<WBN> lb;
+  f32x16 acc[FM][FN];
+  zero_acc(acc);
+  auto fetch = [&](int kt) {
+    la.load(p.dz + (int64_t)kt * kKT * p.ldz + m0, p.ldz, p.N - kt * kKT, p.kpad - m0, tid);
+    lb.load(p.hT + (int64_t)n0 * p.ldT + kt * kKT, p.ldT, p.H - n0, tid);
+  };
+  kloop<WBM, WBN, f16x8>(acc, la, lb, fetch, p.ldT / kKT, lds, tid, wm * (WBM / 2), wn * (WBN / 2));
+  const float inv = p.gscale[1];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    const int n = n0 + wn * (WBN / 2) + fn * 32 + (lane & 31);
+    if (n >= p.H) continue;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = m0 + wm * (WBM / 2) + fm * 32 + frag_row(i, lane);
+        if (m < p.width) {
+          float* o = p.dW + (int64_t)m * p.H + n;
+          const float d = acc[fm][fn][i] * inv;
+          *o = p.accumulate ? *o + d : d;
+        }
+      }
+  }
+}
+
+// ===========================================================================
+// Backward, step 3: dh_s[m, n] (+)= sum_v dz[m, v] W_s[c0 + v, n]
+// A = dz (K-major rows), B = W_s chunk (MN-major: vocabulary rows, hidden contiguous).
+// ===========================================================================
+constexpr int HBM = 128, HBN = 128;
+using DhStages = Stages<HBM, HBN>;
+
+__global__ __launch_bounds__(kThreads, 2) void dh_gemm(DhParams p) {
+  __shared__ __attribute__((aligned(16))) char lds[DhStages::kBytes];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int logical = xcd_logical(blockIdx.x, p.ntm * p.ntn);
+  const int tm = logical / p.ntn, tn = logical - tm * p.ntn;
+  const int m0 = tm * HBM, n0 = tn * HBN;
+  constexpr int FM = HBM / 64, FN = HBN / 64;
+  KLoader<HBM> la;
+  MLoader<HBN, true> lb;
+  f32x16 acc[FM][FN];
+  zero_acc(acc);
+  auto fetch = [&](int kt) {
+    la.load(p.dz + (int64_t)m0 * p.ldz + kt * kKT, p.ldz, p.N - m0, tid);
+    lb.load(p.Wc + (int64_t)kt * kKT * p.H + n0, p.H, p.width - kt * kKT, p.H - n0, tid);
+  };
+  kloop<HBM, HBN, f16x8>(acc, la, lb, fetch, p.kpad / kKT, lds, tid, wm * (HBM / 2), wn * (HBN / 2));
+  const float inv = p.gscale[1];
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    const int n = n0 + wn * (HBN / 2) + fn * 32 + (lane & 31);
+    if (n >= p.H) continue;
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int m = m0 + wm * (HBM / 2) + fm * 32 + frag_row(i, lane);
+        if (m < p.N) {
+          float* o = p.dh + (int64_t)m * p.H + n;
+          const float d = acc[fm][fn][i] * inv;
+          *o = p.accumulate ? *o + d : d;
+        }
+      }
+  }
+}
+
+// ===========================================================================
+// Both sides given as fp32 logits: one workgroup per row streams z_s, z_t.
+// ===========================================================================
+__global__ __launch_bounds__(256) void fwd_rows_logits(const float* __restrict__ z_s, const float* __restrict__ z_t,
+                                                       int N, int V, const uint8_t* __restrict__ row_mask,
+                                                       float* __restrict__ loss, float* __restrict__ stats) {
+  __shared__ float red[5][256];
+  const int n = blockIdx.x, tid = threadIdx.x;
+  const float* rs = z_s + (int64_t)n * V;
+  const float* rt = z_t + (int64_t)n * V;
+  float ms = kNegBig, ss = 0.f, aa = 0.f, mt = kNegBig, st = 0.f;
+  for (int v0 = 0; v0 < V; v0 += 4 * 256) {
+    float a[4], b[4];
+    bool ok[4];
+    float tms = kNegBig, tmt = kNegBig;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int v = v0 + e * 256 + tid;
+      ok[e] = v < V;
+      a[e] = ok[e] ? rs[v] : 0.f;
+      b[e] = ok[e] ? rt[v] : 0.f;
+      if (ok[e]) { tms = fmaxf(tms, a[e]); tmt = fmaxf(tmt, b[e]); }
+    }
+    const float nms = fmaxf(ms, tms), nmt = fmaxf(mt, tmt);
+    const float cs = nms * kL2E, ct = nmt * kL2E;
+    float ps = 0.f, pt = 0.f, pa = 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      if (ok[e]) {
+        const float es = ex2(fmaf(a[e], kL2E, -cs));
+        const float et = ex2(fmaf(b[e], kL2E, -ct));
+        ps += es;
+        pt += et;
+        pa = fmaf(es, a[e] - b[e], pa);
+      }
+    const float fs = ex2((ms - nms) * kL2E), ft = ex2((mt - nmt) * kL2E);
+    ss = fmaf(ss, fs, ps);
+    aa = fmaf(aa, fs, pa);
+    st = fmaf(st, ft, pt);
+    ms = nms;
+    mt = nmt;
+  }
+  red[0][tid] = ms; red[1][tid] = ss; red[2][tid] = aa; red[3][tid] = mt; red[4][tid] = st;
+  __syncthreads();
+  for (int off = 128; off > 0; off >>= 1) {
+    if (tid < off) {
+      float m1 = red[0][tid], s1 = red[1][tid], a1 = red[2][tid], m2 = red[3][tid], s2 = red[4][tid];
+      merge3(m1, s1, a1, red[0][tid + off], red[1][tid + off], red[2][tid + off]);
+      merge2(m2, s2, red[3][tid + off], red[4][tid + off]);
+      red[0][tid] = m1; red[1][tid] = s1; red[2][tid] = a1; red[3][tid] = m2; red[4][tid] = s2;
+    }
+    __syncthreads();
+  }
+  if (tid == 0) {
+    float lse_s = red[0][0] + logf(red[1][0]);
+    float lse_t = red[3][0] + logf(red[4][0]);
+    float L = red[2][0] / red[1][0] - (lse_s - lse_t);
+    if (row_mask && row_mask[n] == 0) { L = 0.f; lse_s = 0.f; lse_t = 0.f; }
+    loss[n] = L;
+    stats[3 * (int64_t)n + 0] = lse_s;
+    stats[3 * (int64_t)n + 1] = lse_t;
+    stats[3 * (int64_t)n + 2] = L;
+  }
+}
+
+__global__ __launch_bounds__(256) void bwd_rows_logits(const float* __restrict__ z_s, const float* __restrict__ z_t,
+                                                       int N, int V, const uint8_t* __restrict__ row_mask,
+                                                       const float* __restrict__ grad, const float* __restrict__ stats,
+                                                       float* __restrict__ dz) {
+  const int n = blockIdx.x;
+  const int v = blockIdx.y * 256 + threadIdx.x;
+  if (v >= V) return;
+  const bool live = !row_mask || row_mask[n] != 0;
+  float d = 0.f;
+  if (live) {
+    const float lse_s = stats[3 * (int64_t)n + 0], lse_t = stats[3 * (int64_t)n + 1], L = stats[3 * (int64_t)n + 2];
+    const float g = grad ? grad[n] : 1.0f;
+    const float a = z_s[(int64_t)n * V + v], b = z_t[(int64_t)n * V + v];
+    d = g * ex2(fmaf(a, kL2E, -(lse_s * kL2E))) * ((a - b) - ((lse_s - lse_t) + L));
+  }
+  dz[(int64_t)n * V + v] = d;
+}
+
+// ===========================================================================
+// Compaction, gather, scatter, fill.
+// ===========================================================================
+__global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict__ mask, int T,
+                                                       int32_t* __restrict__ row_idx, int32_t* __restrict__ n_out) {
+  __shared__ int wave_cnt[16];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  int base = 0;
+  for (int start = 0; start < T; start += 1024) {
+    const int t = start + tid;
+    const bool f = t < T && mask[t] != 0;
+    const unsigned long long bal = __ballot(f);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_cnt[w] = __popcll(bal);
+    __syncthreads();
+    int off = 0, total = 0;
+    for (int i = 0; i < 16; ++i) {
+      if (i < w) off += wave_cnt[i];
+      total += wave_cnt[i];
+    }
+    if (f) row_idx[base + off + before] = t;
+    base += total;
+    __syncthreads();
+  }
+  if (tid == 0) *n_out = base;
+}
+
+template <typename U>
+__global__ __launch_bounds__(256) void gather_kernel(const U* __restrict__ src, int64_t row_units,
+                                                     const int32_t* __restrict__ row_idx, U* __restrict__ dst) {
+  const int64_t i = blockIdx.x;
+  const U* s = src + (int64_t)row_idx[i] * row_units;
+  U* d = dst + i * row_units;
+  for (int64_t u = (int64_t)blockIdx.y * 256 + threadIdx.x; u < row_units; u += (int64_t)gridDim.y * 256) d[u] = s[u];
+}
+
+template <typename U>
+__global__ __launch_bounds__(256) void scatter_kernel(const U* __restrict__ src, int64_t row_units,
+                                                      const int32_t* __restrict__ row_idx, U* __restrict__ dst) {
+  const int64_t i = blockIdx.x;
+  const U* s = src + i * row_units;
+  U* d = dst + (int64_t)row_idx[i] * row_units;
+  for (int64_t u = (int64_t)blockIdx.y * 256 + threadIdx.x; u < row_units; u += (int64_t)gridDim.y * 256) d[u] = s[u];
+}
+
+__global__ __launch_bounds__(256) void fill_zero_u32(uint32_t* __restrict__ p, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0u;
+}
+
+// ===========================================================================
+// Launchers
+// ===========================================================================
+static inline unsigned grid1(int64_t n, int64_t per, int64_t cap) {
+  int64_t g = (n + per - 1) / per;
+  if (g < 1) g = 1;
+  if (g > cap) g = cap;
+  return (unsigned)g;
+}
+
+hipError_t launch_fwd_tiles(const FwdParams& p, bool teacher_logits, hipStream_t s) {
+  const unsigned nb = (unsigned)(p.nsplit * p.ntok);
+  const bool vec4 = (p.V % 4) == 0;
+  if (!teacher_logits)
+    fwd_tiles<0, true><<<nb, kThreads, 0, s>>>(p);
+  else if (vec4)
+    fwd_tiles<1, true><<<nb, kThreads, 0, s>>>(p);
+  else
+    fwd_tiles<1, false><<<nb, kThreads, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_combine(const float* partial, int nsplit, int N, const uint8_t* row_mask, float* loss,
+                              float* stats, hipStream_t s) {
+  fwd_combine<<<(N + 255) / 256, 256, 0, s>>>(partial, nsplit, N, row_mask, loss, stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dz(const BwdParams& p, bool teacher_logits, hipStream_t s) {
+  const unsigned nb = (unsigned)(p.ntv * p.ntok);
+  const bool vec4 = (p.V % 4) == 0;
+  if (!teacher_logits)
+    bwd_dz_tiles<0, true><<<nb, kThreads, 0, s>>>(p);
+  else if (vec4)
+    bwd_dz_tiles<1, true><<<nb, kThreads, 0, s>>>(p);
+  else
+    bwd_dz_tiles<1, false><<<nb, kThreads, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_grad_scale(const float* grad, const uint8_t* row_mask, int N, float* out, hipStream_t s) {
+  grad_scale<<<1, 1024, 0, s>>>(grad, row_mask, N, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_h(const uint16_t* h, int N, int H, uint16_t* hT, int ldT, hipStream_t s) {
+  dim3 g((unsigned)(ldT / 64), (unsigned)(H / 64));
+  transpose_h<<<g, 256, 0, s>>>(h, N, H, hT, ldT);
+  return hipGetLastError();
+}
+
+hipError_t launch_dw(const DwParams& p, hipStream_t s) {
+  dw_gemm<<<(unsigned)(p.ntm * p.ntn), kThreads, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_dh(const DhParams& p, hipStream_t s) {
+  dh_gemm<<<(unsigned)(p.ntm * p.ntn), kThreads, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_rows_logits(const float* z_s, const float* z_t, int N, int V, const uint8_t* row_mask,
+                                  float* loss, float* stats, hipStream_t s) {
+  fwd_rows_logits<<<(unsigned)N, 256, 0, s>>>(z_s, z_t, N, V, row_mask, loss, stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_rows_logits(const float* z_s, const float* z_t, int N, int V, const uint8_t* row_mask,
+                                  const float* grad, const float* stats, float* dz, hipStream_t s) {
+  dim3 g((unsigned)N, (unsigned)((V + 255) / 256));
+  bwd_rows_logits<<<g, 256, 0, s>>>(z_s, z_t, N, V, row_mask, grad, stats, dz);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact(const uint8_t* mask, int T, int32_t* row_idx, int32_t* n_out, hipStream_t s) {
+  compact_kernel<<<1, 1024, 0, s>>>(mask, T, row_idx, n_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const void* src, int64_t row_bytes, const int32_t* row_idx, int64_t N, void* dst,
+                         hipStream_t s) {
+  const bool v16 = (row_bytes % 16) == 0;
+  const int64_t units = v16 ? row_bytes / 16 : row_bytes / 4;
+  dim3 g((unsigned)N, grid1(units, 256, 64));
+  if (v16)
+    gather_kernel<u32x4><<<g, 256, 0, s>>>((const u32x4*)src, units, row_idx, (u32x4*)dst);
+  else
+    gather_kernel<uint32_t><<<g, 256, 0, s>>>((const uint32_t*)src, units, row_idx, (uint32_t*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter(const void* src, int64_t row_bytes, const int32_t* row_idx, int64_t N, void* dst,
+                          hipStream_t s) {
+  const bool v16 = (row_bytes % 16) == 0;
+  const int64_t units = v16 ? row_bytes / 16 : row_bytes / 4;
+  dim3 g((unsigned)N, grid1(units, 256, 64));
+  if (v16)
+    scatter_kernel<u32x4><<<g, 256, 0, s>>>((const u32x4*)src, units, row_idx, (u32x4*)dst);
+  else
+    scatter_kernel<uint32_t><<<g, 256, 0, s>>>((const uint32_t*)src, units, row_idx, (uint32_t*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t s) {
+  const int64_t n = bytes / 4;
+  if (n == 0) return hipSuccess;
+  fill_zero_u32<<<grid1(n, 256, 8192), 256, 0, s>>>((uint32_t*)p, n);
+  return hipGetLastError();
+}
+
+}  // namespace rkl

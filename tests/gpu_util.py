@@ -1,0 +1,45 @@
+"""Shared helpers for the GPU parity tests (HIP path vs the fp64 oracle)."""
+import sys
+
+import numpy as np
+
+from oracle import rkl_oracle as O
+
+
+def torch_dev():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return torch, torch.device("cuda:0")
+
+
+def bf16(bits, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+def f32(a, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to(dev)
+
+
+def u8(a, dev):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.uint8)).to(dev)
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def say(*a):
+    """Name the case before a GPU step (flushed, so it survives a lost box)."""
+    print("[case]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def oracle_full(case, rows, g=None, want_dz=False):
+    """Oracle loss/stats and gradients over the given positions."""
+    inp = O.Inputs.from_case(case)
+    L, ls, lt = O.forward(inp, rows)
+    b = O.backward(inp, rows, g, want_dz=want_dz)
+    return inp, (L, ls, lt), b

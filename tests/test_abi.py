@@ -1,0 +1,125 @@
+"""C-ABI checks that need no GPU: the library loads, exports every entry point
+declared in include/rkl.h, sizes its workspace, and rejects bad arguments
+with a status and a message before anything is launched."""
+import ctypes
+import os
+import re
+import threading
+
+import pytest
+
+import lm_head_reverse_amd as R
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "rkl.h")
+
+# A non-null, 16-byte aligned address that is never dereferenced: every call
+# below fails its host-side checks before any launch.
+FAKE = ctypes.c_void_p(0x10000)
+MISALIGNED = ctypes.c_void_p(0x10002)
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(rkl_[a-z_]+)\s*\(", src)))
+
+
+def test_header_declares_the_path():
+    names = declared_functions()
+    for want in ("rkl_compact_rows", "rkl_gather_rows", "rkl_scatter_rows", "rkl_workspace_bytes",
+                 "rkl_forward_hidden", "rkl_forward_logits", "rkl_backward_hidden", "rkl_backward_logits",
+                 "rkl_last_error", "rkl_version"):
+        assert want in names
+
+
+def test_library_exports_every_declared_symbol():
+    L = R.lib()
+    missing = [n for n in declared_functions() if not hasattr(L, n)]
+    assert not missing, missing
+    assert "gfx950" in R.version()
+
+
+def test_workspace_sizes():
+    # both sides as logits: row kernels need no workspace
+    assert R.workspace_bytes(64, 1024, 0, 0) == 0
+    a = R.workspace_bytes(2048, 151936, 2048, 2048)
+    b = R.workspace_bytes(4096, 151936, 2048, 2048)
+    assert 0 < a < b
+    # bounded: the [N, V] logits are never materialised (4096 x 151936 fp32 = 2.49 GB)
+    assert b < 4096 * 151936 * 4 / 8
+    assert R.workspace_bytes(-1, 10, 64, 64) == 0
+
+
+def _fwd_hidden(N=4, V=100, Hs=64, Ht=64, p=FAKE, ws=FAKE, nbytes=1 << 30):
+    return R.lib().rkl_forward_hidden(N, V, Hs, Ht, p, p, p, p, None, p, p, ws, nbytes, None)
+
+
+@pytest.mark.parametrize("kw,code,msg", [
+    (dict(N=-1), 1, "N="),
+    (dict(V=0), 1, "V="),
+    (dict(Hs=100), 2, "multiple of 64"),
+    (dict(Ht=96), 2, "multiple of 64"),
+    (dict(Hs=0), 1, "Hs="),
+    (dict(p=None), 1, "NULL"),
+    (dict(p=MISALIGNED), 1, "aligned"),
+    (dict(nbytes=0), 3, "workspace"),
+])
+def test_forward_hidden_rejects(kw, code, msg):
+    assert _fwd_hidden(**kw) == code
+    assert msg in R.lib().rkl_last_error().decode()
+
+
+def test_forward_logits_rejects():
+    L = R.lib()
+    # student given both ways
+    assert L.rkl_forward_logits(4, 100, 64, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 20, None) == 1
+    # student as logits but Hs != 0
+    assert L.rkl_forward_logits(4, 100, 64, None, None, FAKE, FAKE, None, FAKE, FAKE, None, 0, None) == 1
+    # teacher logits missing
+    assert L.rkl_forward_logits(4, 100, 0, None, None, FAKE, None, None, FAKE, FAKE, None, 0, None) == 1
+    assert "z_t" in L.rkl_last_error().decode()
+
+
+def test_backward_rejects():
+    L = R.lib()
+    # student as logits: dh/dW must be NULL
+    assert L.rkl_backward_logits(4, 100, 0, None, None, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 0, FAKE,
+                                 None, 0, None) == 1
+    # student hidden: dz must be NULL
+    assert L.rkl_backward_logits(4, 100, 64, FAKE, FAKE, None, FAKE, None, None, FAKE, FAKE, FAKE, 0, FAKE,
+                                 FAKE, 1 << 30, None) == 1
+    # workspace too small
+    assert L.rkl_backward_hidden(4, 100, 64, 64, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 0,
+                                 FAKE, 16, None) == 3
+    # dW missing
+    assert L.rkl_backward_hidden(4, 100, 64, 64, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None, 0,
+                                 FAKE, 1 << 30, None) == 1
+
+
+def test_compaction_and_copies_reject():
+    L = R.lib()
+    assert L.rkl_compact_rows(FAKE, -1, FAKE, FAKE, None, None) == 1
+    assert L.rkl_compact_rows(None, 10, FAKE, FAKE, None, None) == 1
+    assert L.rkl_compact_rows(FAKE, 10, FAKE, None, None, None) == 1
+    assert L.rkl_gather_rows(FAKE, 5, 16, FAKE, 6, FAKE, None) == 1       # N > T
+    assert L.rkl_gather_rows(FAKE, 5, 6, FAKE, 2, FAKE, None) == 1        # row_bytes % 4
+    assert L.rkl_gather_rows(MISALIGNED, 5, 16, FAKE, 2, FAKE, None) == 1
+    assert L.rkl_scatter_rows(FAKE, 3, 8, FAKE, 2, FAKE, None) == 1       # N > T
+    assert L.rkl_scatter_rows(FAKE, 1, 8, None, 2, FAKE, None) == 1       # row_idx NULL
+
+
+def test_last_error_is_per_thread():
+    _fwd_hidden(N=-1)
+    main_msg = R.lib().rkl_last_error().decode()
+    seen = {}
+
+    def other():
+        _fwd_hidden(Hs=100)
+        seen["msg"] = R.lib().rkl_last_error().decode()
+
+    t = threading.Thread(target=other)
+    t.start()
+    t.join()
+    assert "multiple of 64" in seen["msg"]
+    assert R.lib().rkl_last_error().decode() == main_msg

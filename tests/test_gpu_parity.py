@@ -1,0 +1,274 @@
+"""GPU parity of the HIP path (through the C ABI) against the fp64 oracle, at
+sizes the oracle finishes in seconds: several tiles, ragged token and
+vocabulary tails, multi-chunk backward, both payload paths, full-row mode.
+
+Bars: per-token |dL| <= 1e-4 + 1e-3|L|; gradients max|d| <= 2e-3 max|ref|;
+compaction, gather and scatter bit-exact; exact zeros where the method gives
+exact zeros (unmasked rows, self-distillation).
+"""
+import numpy as np
+import pytest
+
+import lm_head_reverse_amd as R
+import synth
+from gpu_util import bf16, f32, host, oracle_full, say, torch_dev, u8
+from oracle import rkl_oracle as O
+from tolerances import assert_grad_close, assert_loss_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tdev():
+    torch, dev = torch_dev()
+    R.lib()
+    return torch, dev
+
+
+# ------------------------------------------------------------------ compaction
+
+def _masks():
+    rng = np.random.default_rng(0)
+    yield "empty", np.zeros(0, np.uint8)
+    yield "one_on", np.ones(1, np.uint8)
+    yield "one_off", np.zeros(1, np.uint8)
+    yield "bern0.3_T1000", (rng.random(1000) < 0.3).astype(np.uint8)
+    yield "all_T2049", np.ones(2049, np.uint8)
+    yield "none_T5000", np.zeros(5000, np.uint8)
+    m = np.zeros((2, 16384), np.uint8)
+    m[:, -2048:] = 1
+    yield "last2048_T32768", m.reshape(-1)
+    yield "bytes_T3001", rng.integers(0, 3, 3001).astype(np.uint8) * 77
+
+
+@pytest.mark.parametrize("name,mask", list(_masks()), ids=[n for n, _ in _masks()])
+def test_compact_rows_bitexact(tdev, name, mask):
+    torch, dev = tdev
+    say("compact", name, mask.shape)
+    idx, n = R.compact_rows(u8(mask, dev))
+    want = O.compact_rows(mask)
+    assert n == want.shape[0]
+    assert np.array_equal(host(idx), want)
+
+
+def test_gather_scatter_bitexact(tdev):
+    torch, dev = tdev
+    rng = np.random.default_rng(1)
+    T = 777
+    mask = (rng.random(T) < 0.4).astype(np.uint8)
+    idx_np = O.compact_rows(mask)
+    idx = torch.from_numpy(idx_np).to(dev)
+    for shape, kind in (((T, 192), "bf16"), ((T,), "f32"), ((T, 3), "f32"), ((T, 2048), "bf16")):
+        say("gather/scatter", shape, kind)
+        if kind == "bf16":
+            bits = rng.integers(0, 65536, size=shape, dtype=np.uint16)
+            src = bf16(bits, dev)
+            ref = bits
+        else:
+            ref = rng.standard_normal(shape).astype(np.float32)
+            src = f32(ref, dev)
+        g = R.gather_rows(src, idx)
+        gh = host(g.view(torch.int16)).view(np.uint16) if kind == "bf16" else host(g)
+        assert np.array_equal(gh.view(np.uint8), O.gather_rows(ref, idx_np).view(np.uint8))
+        back = R.scatter_rows(g, idx, T)
+        bh = host(back.view(torch.int16)).view(np.uint16) if kind == "bf16" else host(back)
+        assert np.array_equal(bh.view(np.uint8), O.scatter_rows(O.gather_rows(ref, idx_np), idx_np, T).view(np.uint8))
+
+
+# ------------------------------------------------------------------ logits path (both sides as logits)
+
+def test_logits_both_sides_tiny(tdev):
+    """64 positions, V = 1024, N(0, 2^2) logits, Bernoulli(0.7) mask."""
+    torch, dev = tdev
+    case = synth.config("c1")
+    T, V = case.T, case.V
+    say("c1 logits tiny", T, V)
+    mask = u8(case.mask, dev)
+    zs_all, zt_all = f32(case.z_s, dev), f32(case.z_t, dev)
+    idx, N = R.compact_rows(mask)
+    zs, zt = R.gather_rows(zs_all, idx), R.gather_rows(zt_all, idx)
+    loss, stats = R.forward_logits(zt, z_s=zs)
+    dz = R.backward_logits(zt, stats, z_s=zs)
+    loss_pos = host(R.scatter_rows(loss, idx, T))
+    torch.cuda.synchronize()
+
+    rows = O.compact_rows(case.mask)
+    inp, (L, ls, lt), b = oracle_full(case, rows, want_dz=True)
+    assert_loss_close(loss_pos[rows], L)
+    assert np.all(loss_pos[case.mask == 0] == 0.0)
+    assert_loss_close(host(stats)[:, 0], ls, "lse_s")
+    assert_loss_close(host(stats)[:, 1], lt, "lse_t")
+    assert_grad_close(host(dz), b["dz"], "dz")
+
+    # full-row mode over all T positions: unmasked rows exactly zero, masked rows identical
+    say("c1 full-row")
+    loss_f, stats_f = R.forward_logits(zt_all, z_s=zs_all, row_mask=mask)
+    dz_f = R.backward_logits(zt_all, stats_f, z_s=zs_all, row_mask=mask)
+    lf, dzf = host(loss_f), host(dz_f)
+    assert np.array_equal(lf[rows], host(loss))
+    assert np.all(lf[case.mask == 0] == 0.0)
+    assert np.array_equal(dzf[rows], host(dz))
+    assert np.all(dzf[case.mask == 0] == 0.0)
+
+
+# ------------------------------------------------------------------ hidden-state path
+
+def _run_hidden(case, dev, g=None, teacher_logits=False, full_row=False):
+    """Compaction -> gather -> forward -> backward through the binding."""
+    torch = __import__("torch")
+    mask = u8(case.mask, dev)
+    idx, N = R.compact_rows(mask)
+    if full_row:
+        idx = torch.arange(case.T, dtype=torch.int32, device=dev)
+        N = case.T
+    hs = R.gather_rows(bf16(case.h_s, dev), idx)
+    Ws = bf16(case.W_s, dev)
+    gg = None if g is None else R.gather_rows(f32(g, dev), idx)
+    rm = mask if full_row else None
+    if teacher_logits:
+        zt = R.gather_rows(f32(case.z_t, dev), idx)
+        loss, stats = R.forward_logits(zt, h_s=hs, W_s=Ws, row_mask=rm)
+        dh, dW = R.backward_logits(zt, stats, h_s=hs, W_s=Ws, grad_loss=gg, row_mask=rm)
+    else:
+        ht = R.gather_rows(bf16(case.h_t, dev), idx)
+        Wt = bf16(case.W_t, dev)
+        loss, stats = R.forward_hidden(hs, Ws, ht, Wt, row_mask=rm)
+        dh, dW = R.backward_hidden(hs, Ws, ht, Wt, stats, grad_loss=gg, row_mask=rm)
+    torch.cuda.synchronize()
+    return host(idx), host(loss), host(stats), host(dh), host(dW)
+
+
+def _check_against_oracle(case, out, g=None):
+    idx, loss, stats, dh, dW = out
+    rows = O.compact_rows(case.mask)
+    assert np.array_equal(idx, rows)
+    gr = None if g is None else g[rows]
+    inp, (L, ls, lt), b = oracle_full(case, rows, gr)
+    assert_loss_close(loss, L)
+    assert_loss_close(stats[:, 2], L, "stats L")
+    assert_loss_close(stats[:, 0], ls, "lse_s")
+    if case.h_t is not None:
+        assert_loss_close(stats[:, 1], lt, "lse_t")
+    assert_grad_close(dh, b["dh"], "dh")
+    assert_grad_close(dW, b["dW"], "dW")
+
+
+def test_hidden_small(tdev):
+    """B=2, S=129, Hs=Ht=256, V=8192, response spans from random offsets."""
+    torch, dev = tdev
+    case = synth.config("c2")
+    say("c2 hidden small", case.T, case.V, case.Hs)
+    _check_against_oracle(case, _run_hidden(case, dev))
+
+
+@pytest.mark.parametrize("T,V,Hs,Ht", [(300, 1000, 128, 192), (129, 257, 64, 64), (517, 2053, 192, 128)])
+def test_hidden_ragged_with_grad(tdev, T, V, Hs, Ht):
+    """Ragged N and V tails, unequal widths, an upstream per-token gradient."""
+    torch, dev = tdev
+    case = synth.random_case(10 + T, T=T, V=V, Hs=Hs, Ht=Ht, p_mask=0.5, with_grad=True)
+    say("ragged hidden", T, V, Hs, Ht)
+    _check_against_oracle(case, _run_hidden(case, dev, g=case.grad), g=case.grad)
+
+
+def test_hidden_multi_chunk_backward(tdev):
+    """V = 40000 spans three 16384-column backward chunks (the last one ragged)."""
+    torch, dev = tdev
+    case = synth.random_case(31, T=150, V=40000, Hs=64, Ht=64, p_mask=0.6)
+    say("multi-chunk", case.T, case.V)
+    _check_against_oracle(case, _run_hidden(case, dev))
+
+
+@pytest.mark.parametrize("V", [3000, 1001])
+def test_student_hidden_teacher_logits(tdev, V):
+    """Teacher logits payload with the student projected; V = 1001 takes the unvectorised z_t reads."""
+    torch, dev = tdev
+    case = synth.random_case(40 + V, T=200, V=V, Hs=128, Ht=0, teacher_logits=True, p_mask=0.7, with_grad=True)
+    say("teacher logits", case.T, V)
+    _check_against_oracle(case, _run_hidden(case, dev, g=case.grad, teacher_logits=True), g=case.grad)
+
+
+def test_logits_payload_equals_hidden_payload(tdev):
+    """Teacher logits = fp32 rounding of h_t W_t^T: both payload paths agree."""
+    torch, dev = tdev
+    case = synth.random_case(50, T=160, V=4000, Hs=128, Ht=128, p_mask=0.8)
+    say("logits == hidden", case.T, case.V)
+    hid = _run_hidden(case, dev)
+    case.z_t = O.project_f32(case.h_t, case.W_t)
+    lg = _run_hidden(case, dev, teacher_logits=True)
+    assert_loss_close(lg[1], hid[1], "loss logits vs hidden")
+    assert_grad_close(lg[3], hid[3], "dh logits vs hidden")
+    assert_grad_close(lg[4], hid[4], "dW logits vs hidden")
+
+
+def test_full_row_equals_compact(tdev):
+    """Full-row mode (all T rows projected, mask applied in the epilogues) gives
+    bit-identical loss and dh on masked rows, exact zeros elsewhere."""
+    torch, dev = tdev
+    case = synth.config("c2")
+    say("full-row vs compact", case.T)
+    c = _run_hidden(case, dev)
+    f = _run_hidden(case, dev, full_row=True)
+    rows = c[0]
+    m = case.mask != 0
+    assert np.array_equal(f[1][rows], c[1])
+    assert np.all(f[1][~m] == 0.0)
+    assert np.array_equal(f[2][rows], c[2])
+    assert np.array_equal(f[3][rows], c[3])
+    assert np.all(f[3][~m] == 0.0)
+    assert_grad_close(f[4], c[4], "dW full-row vs compact")
+
+
+def test_self_distillation_is_exactly_zero(tdev):
+    torch, dev = tdev
+    case = synth.random_case(60, T=100, V=3000, Hs=128, Ht=128, p_mask=0.9)
+    case.h_t, case.W_t = case.h_s, case.W_s
+    say("self-distillation small")
+    idx, loss, stats, dh, dW = _run_hidden(case, dev)
+    assert np.all(loss == 0.0)
+    assert np.all(dh == 0.0) and np.all(dW == 0.0)
+
+
+def test_bitwise_deterministic(tdev):
+    torch, dev = tdev
+    case = synth.random_case(70, T=300, V=5000, Hs=128, Ht=64, p_mask=0.5)
+    say("determinism")
+    a = _run_hidden(case, dev)
+    b = _run_hidden(case, dev)
+    for x, y in zip(a, b):
+        assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+
+
+def test_empty_mask(tdev):
+    torch, dev = tdev
+    case = synth.random_case(80, T=40, V=600, Hs=64, Ht=64, p_mask=0.0)
+    say("empty mask")
+    mask = u8(case.mask, dev)
+    idx, N = R.compact_rows(mask)
+    assert N == 0
+    hs = R.gather_rows(bf16(case.h_s, dev), idx)
+    ht = R.gather_rows(bf16(case.h_t, dev), idx)
+    Ws, Wt = bf16(case.W_s, dev), bf16(case.W_t, dev)
+    loss, stats = R.forward_hidden(hs, Ws, ht, Wt)
+    assert loss.shape == (0,)
+    assert np.all(host(R.scatter_rows(loss, idx, case.T)) == 0.0)
+    dh, dW = R.backward_hidden(hs, Ws, ht, Wt, stats)
+    assert dh.shape == (0, 64) and np.all(host(dW) == 0.0)
+    prev = torch.full((600, 64), 3.5, device=dev)
+    _, dW2 = R.backward_hidden(hs, Ws, ht, Wt, stats, dW=prev, accumulate_dW=True)
+    assert np.all(host(dW2) == 3.5)
+
+
+def test_accumulate_dW(tdev):
+    torch, dev = tdev
+    case = synth.random_case(90, T=120, V=1500, Hs=128, Ht=128, p_mask=0.6)
+    say("accumulate dW")
+    mask = u8(case.mask, dev)
+    idx, N = R.compact_rows(mask)
+    hs = R.gather_rows(bf16(case.h_s, dev), idx)
+    ht = R.gather_rows(bf16(case.h_t, dev), idx)
+    Ws, Wt = bf16(case.W_s, dev), bf16(case.W_t, dev)
+    loss, stats = R.forward_hidden(hs, Ws, ht, Wt)
+    _, dW = R.backward_hidden(hs, Ws, ht, Wt, stats)
+    base = np.random.default_rng(3).standard_normal((1500, 128)).astype(np.float32)
+    _, dW2 = R.backward_hidden(hs, Ws, ht, Wt, stats, dW=f32(base, dev), accumulate_dW=True)
+    assert np.array_equal(host(dW2), base + host(dW))
