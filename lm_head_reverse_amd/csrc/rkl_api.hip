@@ -51,6 +51,16 @@ int64_t vocab_chunk() {
   return c;
 }
 
+// Vocabulary tiles one backward workgroup sweeps (does not change results).
+int bwd_tiles_per_group() {
+  static const int t = [] {
+    const char* s = std::getenv("RKL_BWD_TILES");
+    int v = s ? std::atoi(s) : 4;
+    return v < 1 ? 1 : v;
+  }();
+  return t;
+}
+
 // Forward split plan: depends on V only (so a row's result never depends on N).
 struct Split {
   int tiles_per_split, nsplit;
@@ -176,6 +186,8 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
     b.row_mask = row_mask; b.grad = grad; b.stats = stats;
     b.gscale = gscale; b.dz = dz; b.ldz = (int)L.ldz; b.c0 = (int)c0; b.kpad = (int)kpad;
     b.ntv = (int)ceil_div(kpad, rkl::kFwdTileV);
+    b.tiles_per_group = bwd_tiles_per_group();
+    b.ngroups = (int)ceil_div(b.ntv, b.tiles_per_group);
     b.ntok = (int)ceil_div(N, rkl::kFwdTileN);
     RKL_TRY(rkl::launch_bwd_dz(b, z_t != nullptr, s));
 

@@ -36,6 +36,8 @@ struct BwdParams {
   int c0;                  // first vocabulary row of the chunk
   int kpad;                // chunk width rounded up to 64 (columns written)
   int ntv;                 // 256-row vocabulary tiles in the chunk
+  int tiles_per_group;     // vocabulary tiles one workgroup sweeps
+  int ngroups;             // ceil(ntv / tiles_per_group)
   int ntok;
 };
 
@@ -64,8 +66,8 @@ struct DhParams {
 // Tile sizes the host needs for grids and workspace.
 constexpr int kFwdTileV = 256;
 constexpr int kFwdTileN = 128;
-constexpr int kDwTileM = 256, kDwTileN = 128;
-constexpr int kDhTileM = 128, kDhTileN = 128;
+constexpr int kDwTileM = 256, kDwTileN = 256;
+constexpr int kDhTileM = 256, kDhTileN = 128;
 
 hipError_t launch_fwd_tiles(const FwdParams& p, bool teacher_logits, hipStream_t s);
 hipError_t launch_fwd_combine(const float* partial, int nsplit, int N, const uint8_t* row_mask, float* loss,

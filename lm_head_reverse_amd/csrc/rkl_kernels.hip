@@ -53,14 +53,18 @@ constexpr int FFM = FBM / 2 / 32, FFN = FBN / 2 / 32;
 using FwdStages = Stages<FBM, FBN>;
 constexpr int kFwdRedBytes = 2 * FFN * 32 * 5 * 4;
 
-// Fold one tile's values of token column fn into the running statistics.
+// Fold one tile's values of token column fn into the running statistics, one
+// 32x32 block (16 values per side) at a time: block max, rescale of the
+// running sums, then the block's exponentials.  Student and teacher go
+// through the same operations, so identical logits give identical
+// statistics (and A = 0 exactly).
 template <bool TAIL>
 __device__ __forceinline__ void fold_tile(const f32x16 (&zs)[FFM][FFN], const f32x16 (&zt)[FFM][FFN], int fn,
                                           int vrow, int V, float& ms, float& ss, float& aa, float& mt, float& st) {
   // vrow = vocabulary index of fragment row 0 for this lane (block fm = 0)
-  float tms = kNegBig, tmt = kNegBig;
 #pragma unroll
-  for (int fm = 0; fm < FFM; ++fm)
+  for (int fm = 0; fm < FFM; ++fm) {
+    float tms = kNegBig, tmt = kNegBig;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const bool ok = !TAIL || (vrow + fm * 32 + 8 * (i >> 2) + (i & 3) < V);
@@ -69,34 +73,30 @@ __device__ __forceinline__ void fold_tile(const f32x16 (&zs)[FFM][FFN], const f3
         tmt = fmaxf(tmt, zt[fm][fn][i]);
       }
     }
-  const float nms = fmaxf(ms, tms), nmt = fmaxf(mt, tmt);
-  const float cs = nms * kL2E, ct = nmt * kL2E;
-  float ps[FFM], pt[FFM], pa[FFM];
-#pragma unroll
-  for (int fm = 0; fm < FFM; ++fm) {
-    ps[fm] = 0.f; pt[fm] = 0.f; pa[fm] = 0.f;
+    const float nms = fmaxf(ms, tms), nmt = fmaxf(mt, tmt);
+    const float fs = ex2((ms - nms) * kL2E), ft = ex2((mt - nmt) * kL2E);
+    const float cs = nms * kL2E, ct = nmt * kL2E;
+    float ps0 = 0.f, ps1 = 0.f, pt0 = 0.f, pt1 = 0.f, pa0 = 0.f, pa1 = 0.f;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const bool ok = !TAIL || (vrow + fm * 32 + 8 * (i >> 2) + (i & 3) < V);
       if (ok) {
-        const float a = zs[fm][fn][i], b = zt[fm][fn][i];
-        const float es = ex2(fmaf(a, kL2E, -cs));
-        const float et = ex2(fmaf(b, kL2E, -ct));
-        ps[fm] += es;
-        pt[fm] += et;
-        pa[fm] = fmaf(es, a - b, pa[fm]);
+        const float x = zs[fm][fn][i], y = zt[fm][fn][i];
+        const float es = ex2(fmaf(x, kL2E, -cs));
+        const float et = ex2(fmaf(y, kL2E, -ct));
+        if (i & 1) {
+          ps1 += es; pt1 += et; pa1 = fmaf(es, x - y, pa1);
+        } else {
+          ps0 += es; pt0 += et; pa0 = fmaf(es, x - y, pa0);
+        }
       }
     }
+    ss = fmaf(ss, fs, ps0 + ps1);
+    aa = fmaf(aa, fs, pa0 + pa1);
+    st = fmaf(st, ft, pt0 + pt1);
+    ms = nms;
+    mt = nmt;
   }
-  float sum_s = ps[0], sum_t = pt[0], sum_a = pa[0];
-#pragma unroll
-  for (int fm = 1; fm < FFM; ++fm) { sum_s += ps[fm]; sum_t += pt[fm]; sum_a += pa[fm]; }
-  const float fs = ex2((ms - nms) * kL2E), ft = ex2((mt - nmt) * kL2E);
-  ss = fmaf(ss, fs, sum_s);
-  aa = fmaf(aa, fs, sum_a);
-  st = fmaf(st, ft, sum_t);
-  ms = nms;
-  mt = nmt;
 }
 
 // Teacher logits read into the accumulator layout (teacher-logits payload).
@@ -127,9 +127,106 @@ __device__ __forceinline__ void load_zt(f32x16 (&zt)[FFM][FFN], const float* __r
   }
 }
 
+// ---------------------------------------------------------------------------
+// Dual-projection stream.  A workgroup owns one 128-token tile and a run of
+// 256-row vocabulary tiles ("jobs").  For each job it computes z_s (Hs/64
+// k-tiles) and, with a hidden-state teacher, z_t (Ht/64 k-tiles), then calls
+// the epilogue.  All k-tiles of all jobs form one stream through a 3-stage
+// LDS ring fed by DMA two k-tiles ahead, so neither the switch between the
+// projections nor the next job restarts the pipeline, and an epilogue
+// overlaps the loads of the next job's first tiles.
+// ---------------------------------------------------------------------------
+struct DualOps {
+  const uint16_t* W[2];
+  const uint16_t* h[2];
+  int H[2];
+  int nk[2];        // k-tiles per projection; nk[1] = 0 when the teacher is given as logits
+  int V, N, n0, v0;  // v0: first row of job 0
+};
+
+struct StreamPos {
+  int job, phase, kt;
+};
+
+__device__ __forceinline__ void stream_advance(StreamPos& q, const DualOps& o) {
+  if (++q.kt == (q.phase ? o.nk[1] : o.nk[0])) {
+    q.kt = 0;
+    if (q.phase == 0 && o.nk[1] > 0) {
+      q.phase = 1;
+    } else {
+      q.phase = 0;
+      ++q.job;
+    }
+  }
+}
+
+constexpr int kStreamA = DmaRows<FBM>::kPerWave, kStreamB = DmaRows<FBN>::kPerWave;
+constexpr int kStreamND = kStreamA + kStreamB;
+
+template <class Epi>
+__device__ __forceinline__ void dual_stream(const DualOps& o, int njobs, char* lds, f32x16 (&zs)[FFM][FFN],
+                                            f32x16 (&zt)[FFM][FFN], int tid, int arow0, int brow0, Epi epi) {
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int total = njobs * (o.nk[0] + o.nk[1]);
+  char* cur = lds;
+  char* nxt = lds + FwdStages::kStage;
+  char* pre = lds + 2 * FwdStages::kStage;
+  StreamPos dp{0, 0, 0};
+  int dissued = 0;
+  // DMA of stream position dp into stage dst; past the end it repeats the last
+  // position (loads that are never consumed)
+  auto dma_all = [&](char* dst, int q) {
+    const bool t = dp.phase != 0;
+    const int64_t ld = t ? o.H[1] : o.H[0];
+    const int v0 = o.v0 + dp.job * FBM;
+    if (q < kStreamA)
+      DmaRows<FBM>::issue((t ? o.W[1] : o.W[0]) + (int64_t)v0 * ld, ld, o.V - v0, dp.kt, dst, q, lane, wave);
+    else
+      DmaRows<FBN>::issue((t ? o.h[1] : o.h[0]) + (int64_t)o.n0 * ld, ld, o.N - o.n0, dp.kt, dst + FwdStages::kA,
+                          q - kStreamA, lane, wave);
+  };
+  auto dma_next = [&]() {
+    if (dissued + 1 < total) stream_advance(dp, o);
+    ++dissued;
+  };
+#pragma unroll
+  for (int q = 0; q < kStreamND; ++q) dma_all(cur, q);
+  dma_next();
+#pragma unroll
+  for (int q = 0; q < kStreamND; ++q) dma_all(nxt, q);
+  dma_next();
+  dma_barrier<kStreamND>();
+  bf16x8 a[2][FFM], b[2][FFN];
+#pragma unroll
+  for (int f = 0; f < FFM + FFN; ++f)
+    load_frag<bf16x8, FFM, FFN>(a[0], b[0], cur, cur + FwdStages::kA, arow0, brow0, lane, 0, f);
+
+  auto step = [&](f32x16 (&acc)[FFM][FFN]) {
+    char* target = pre;
+    dma_iter<FBM, FBN, bf16x8, FFM, FFN, kStreamND>(acc, a, b, [&](int q) { dma_all(target, q); }, cur, nxt, lane,
+                                                   arow0, brow0);
+    dma_next();
+    char* t = cur;
+    cur = nxt;
+    nxt = pre;
+    pre = t;
+  };
+  for (int job = 0; job < njobs; ++job) {
+    zero_acc(zs);
+    for (int kt = 0; kt < o.nk[0]; ++kt) step(zs);
+    if (o.nk[1] > 0) {
+      zero_acc(zt);
+      for (int kt = 0; kt < o.nk[1]; ++kt) step(zt);
+    }
+    epi(job);
+  }
+  dma_barrier<0>();
+}
+
 template <int MODE, bool VEC4>   // MODE 0: hidden teacher; 1: teacher logits
 __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(FwdParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[FwdStages::kBytes + kFwdRedBytes];
+  __shared__ __attribute__((aligned(1024))) char lds[3 * FwdStages::kStage];
+  __shared__ __attribute__((aligned(16))) float red[kFwdRedBytes / 4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int logical = xcd_logical(blockIdx.x, p.nsplit * p.ntok);
   const int split = logical / p.ntok, tt = logical - split * p.ntok;
@@ -142,36 +239,17 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(FwdParams p) {
 #pragma unroll
   for (int fn = 0; fn < FFN; ++fn) { ms[fn] = kNegBig; ss[fn] = 0.f; aa[fn] = 0.f; mt[fn] = kNegBig; st[fn] = 0.f; }
 
-  KLoader<FBM> la;
-  KLoader<FBN> lb;
   f32x16 zs[FFM][FFN], zt[FFM][FFN];
   const int arow0 = wm * (FBM / 2), brow0 = wn * (FBN / 2);
   const int lrow = 4 * (lane >> 5);
+  DualOps o;
+  o.W[0] = p.W_s; o.h[0] = p.h_s; o.H[0] = p.Hs; o.nk[0] = p.Hs / kKT;
+  o.W[1] = p.W_t; o.h[1] = p.h_t; o.H[1] = p.Ht; o.nk[1] = MODE == 0 ? p.Ht / kKT : 0;
+  o.V = p.V; o.N = p.N; o.n0 = n0; o.v0 = vt0 * FBM;
 
-  for (int vt = vt0; vt < vt1; ++vt) {
-    const int v0 = vt * FBM;
-    zero_acc(zs);
-    {
-      const uint16_t* Wb = p.W_s + (int64_t)v0 * p.Hs;
-      const uint16_t* hb = p.h_s + (int64_t)n0 * p.Hs;
-      auto fetch = [&](int kt) {
-        la.load(Wb + kt * kKT, p.Hs, p.V - v0, tid);
-        lb.load(hb + kt * kKT, p.Hs, p.N - n0, tid);
-      };
-      kloop<FBM, FBN>(zs, la, lb, fetch, p.Hs / kKT, lds, tid, arow0, brow0);
-    }
-    if (MODE == 0) {
-      zero_acc(zt);
-      const uint16_t* Wb = p.W_t + (int64_t)v0 * p.Ht;
-      const uint16_t* hb = p.h_t + (int64_t)n0 * p.Ht;
-      auto fetch = [&](int kt) {
-        la.load(Wb + kt * kKT, p.Ht, p.V - v0, tid);
-        lb.load(hb + kt * kKT, p.Ht, p.N - n0, tid);
-      };
-      kloop<FBM, FBN>(zt, la, lb, fetch, p.Ht / kKT, lds, tid, arow0, brow0);
-    } else {
-      load_zt<VEC4>(zt, p.z_t, p.N, p.V, v0 + arow0 + lrow, n0 + brow0 + (lane & 31), lane);
-    }
+  dual_stream(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, [&](int job) {
+    const int v0 = (vt0 + job) * FBM;
+    if (MODE == 1) load_zt<VEC4>(zt, p.z_t, p.N, p.V, v0 + arow0 + lrow, n0 + brow0 + (lane & 31), lane);
     const int vrow = v0 + arow0 + lrow;
     if (v0 + FBM <= p.V) {
 #pragma unroll
@@ -180,7 +258,7 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(FwdParams p) {
 #pragma unroll
       for (int fn = 0; fn < FFN; ++fn) fold_tile<true>(zs, zt, fn, vrow, p.V, ms[fn], ss[fn], aa[fn], mt[fn], st[fn]);
     }
-  }
+  });
 
   // merge the two row halves of each 32x32 block (lanes l and l^32)
 #pragma unroll
@@ -191,7 +269,6 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(FwdParams p) {
     merge2(mt[fn], st[fn], omt, ost);
   }
   // merge the two waves that hold the same tokens (wm = 0 and wm = 1)
-  float* red = reinterpret_cast<float*>(lds + FwdStages::kBytes);
   if (wm == 1 && lane < 32) {
 #pragma unroll
     for (int fn = 0; fn < FFN; ++fn) {
@@ -281,72 +358,67 @@ __global__ __launch_bounds__(1024) void grad_scale(const float* __restrict__ gra
 // ===========================================================================
 template <int MODE, bool VEC4>
 __global__ __launch_bounds__(kThreads, 1) void bwd_dz_tiles(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[FwdStages::kBytes];
+  __shared__ __attribute__((aligned(1024))) char lds[3 * FwdStages::kStage];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
-  const int logical = xcd_logical(blockIdx.x, p.ntv * p.ntok);
-  const int vt = logical / p.ntok, tt = logical - vt * p.ntok;
-  const int v0 = p.c0 + vt * FBM, n0 = tt * FBN;
+  const int logical = xcd_logical(blockIdx.x, p.ngroups * p.ntok);
+  const int grp = logical / p.ntok, tt = logical - grp * p.ntok;
+  const int vt0 = grp * p.tiles_per_group;
+  const int vt1 = min(vt0 + p.tiles_per_group, p.ntv);
+  const int n0 = tt * FBN;
   const int arow0 = wm * (FBM / 2), brow0 = wn * (FBN / 2);
   const int lrow = 4 * (lane >> 5);
 
-  KLoader<FBM> la;
-  KLoader<FBN> lb;
-  f32x16 zs[FFM][FFN], zt[FFM][FFN];
-  zero_acc(zs);
-  {
-    const uint16_t* Wb = p.W_s + (int64_t)v0 * p.Hs;
-    const uint16_t* hb = p.h_s + (int64_t)n0 * p.Hs;
-    auto fetch = [&](int kt) {
-      la.load(Wb + kt * kKT, p.Hs, p.V - v0, tid);
-      lb.load(hb + kt * kKT, p.Hs, p.N - n0, tid);
-    };
-    kloop<FBM, FBN>(zs, la, lb, fetch, p.Hs / kKT, lds, tid, arow0, brow0);
-  }
-  if (MODE == 0) {
-    zero_acc(zt);
-    const uint16_t* Wb = p.W_t + (int64_t)v0 * p.Ht;
-    const uint16_t* hb = p.h_t + (int64_t)n0 * p.Ht;
-    auto fetch = [&](int kt) {
-      la.load(Wb + kt * kKT, p.Ht, p.V - v0, tid);
-      lb.load(hb + kt * kKT, p.Ht, p.N - n0, tid);
-    };
-    kloop<FBM, FBN>(zt, la, lb, fetch, p.Ht / kKT, lds, tid, arow0, brow0);
-  } else {
-    load_zt<VEC4>(zt, p.z_t, p.N, p.V, v0 + arow0 + lrow, n0 + brow0 + (lane & 31), lane);
-  }
-
+  // per-token constants of this lane's token columns
+  bool live[FFN];
+  float gs[FFN], cst[FFN], css[FFN];
 #pragma unroll
   for (int fn = 0; fn < FFN; ++fn) {
     const int n = n0 + brow0 + fn * 32 + (lane & 31);
-    if (n >= p.N) continue;
-    const bool live = !p.row_mask || p.row_mask[n] != 0;
-    const float lse_s = p.stats[3 * (int64_t)n + 0];
-    const float lse_t = p.stats[3 * (int64_t)n + 1];
-    const float L = p.stats[3 * (int64_t)n + 2];
-    const float g = (p.grad ? p.grad[n] : 1.0f) * p.gscale[0];
-    const float c = (lse_s - lse_t) + L;
-    const float cs = lse_s * kL2E;
-    uint16_t* drow = p.dz + (int64_t)n * p.ldz;
-#pragma unroll
-    for (int fm = 0; fm < FFM; ++fm)
-#pragma unroll
-      for (int gq = 0; gq < 4; ++gq) {
-        const int v = v0 + arow0 + lrow + fm * 32 + 8 * gq;   // first of 4 consecutive entries
-        const int col = v - p.c0;
-        if (col >= p.kpad) continue;
-        _Float16 o[4];
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const float a = zs[fm][fn][4 * gq + e], b = zt[fm][fn][4 * gq + e];
-          float d = 0.f;
-          if (live && v + e < p.V) d = g * ex2(fmaf(a, kL2E, -cs)) * ((a - b) - c);
-          o[e] = (_Float16)d;
-        }
-        *reinterpret_cast<u32x2*>(drow + col) = u32x2{
-            (uint32_t)__builtin_bit_cast(uint16_t, o[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, o[1]) << 16),
-            (uint32_t)__builtin_bit_cast(uint16_t, o[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, o[3]) << 16)};
-      }
+    live[fn] = n < p.N && (!p.row_mask || p.row_mask[n] != 0);
+    const int nc = min(n, p.N - 1);
+    const float lse_s = p.stats[3 * (int64_t)nc + 0];
+    const float lse_t = p.stats[3 * (int64_t)nc + 1];
+    const float L = p.stats[3 * (int64_t)nc + 2];
+    gs[fn] = (p.grad ? p.grad[nc] : 1.0f) * p.gscale[0];
+    cst[fn] = (lse_s - lse_t) + L;
+    css[fn] = lse_s * kL2E;
   }
+
+  f32x16 zs[FFM][FFN], zt[FFM][FFN];
+  DualOps o;
+  o.W[0] = p.W_s; o.h[0] = p.h_s; o.H[0] = p.Hs; o.nk[0] = p.Hs / kKT;
+  o.W[1] = p.W_t; o.h[1] = p.h_t; o.H[1] = p.Ht; o.nk[1] = MODE == 0 ? p.Ht / kKT : 0;
+  o.V = p.V; o.N = p.N; o.n0 = n0; o.v0 = p.c0 + vt0 * FBM;
+
+  dual_stream(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, [&](int job) {
+    const int v0 = p.c0 + (vt0 + job) * FBM;
+    if (MODE == 1) load_zt<VEC4>(zt, p.z_t, p.N, p.V, v0 + arow0 + lrow, n0 + brow0 + (lane & 31), lane);
+#pragma unroll
+    for (int fn = 0; fn < FFN; ++fn) {
+      const int n = n0 + brow0 + fn * 32 + (lane & 31);
+      if (n >= p.N) continue;
+      uint16_t* drow = p.dz + (int64_t)n * p.ldz;
+#pragma unroll
+      for (int fm = 0; fm < FFM; ++fm)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq) {
+          const int v = v0 + arow0 + lrow + fm * 32 + 8 * gq;   // first of 4 consecutive entries
+          const int col = v - p.c0;
+          if (col >= p.kpad) continue;
+          _Float16 oh[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float a = zs[fm][fn][4 * gq + e], bb = zt[fm][fn][4 * gq + e];
+            float d = 0.f;
+            if (live[fn] && v + e < p.V) d = gs[fn] * ex2(fmaf(a, kL2E, -css[fn])) * ((a - bb) - cst[fn]);
+            oh[e] = (_Float16)d;
+          }
+          *reinterpret_cast<u32x2*>(drow + col) = u32x2{
+              (uint32_t)__builtin_bit_cast(uint16_t, oh[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, oh[1]) << 16),
+              (uint32_t)__builtin_bit_cast(uint16_t, oh[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, oh[3]) << 16)};
+        }
+    }
+  });
 }
 
 // h_s [N, H] bf16 -> hT [H, ldT] fp16 (exact for values in fp16's normal
@@ -368,28 +440,30 @@ __global__ __launch_bounds__(256) void transpose_h(const uint16_t* __restrict__ 
 }
 
 // ===========================================================================
-// Backward, step 2: dW_s[c0 + m, n] (+)= sum_t dz[t, m] h_s[t, n]
-// A = dz (MN-major: token rows, vocabulary contiguous), B = hT (K-major).
+// Backward, step 2: dW_s[c0 + m, n] (+)= (1/s) sum_t dz[t, m] h_s[t, n]
+// A = dz (MN-major: token rows, vocabulary contiguous; read transposed),
+// B = hT (K-major).  256 x 256 tiles, 128 x 128 per wave.
 // ===========================================================================
-constexpr int WBM = 256, WBN = 128;
-using DwStages = Stages<WBM, WBN>;
+constexpr int WBM = 256, WBN = 256;
 
 __global__ __launch_bounds__(kThreads, 1) void dw_gemm(DwParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[DwStages::kBytes];
+  using TA = MN<WBM>;
+  using TB = KM<WBN>;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * (TA::kBytes + TB::kBytes)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int logical = xcd_logical(blockIdx.x, p.ntm * p.ntn);
   const int tm = logical / p.ntn, tn = logical - tm * p.ntn;
   const int m0 = tm * WBM, n0 = tn * WBN;
   constexpr int FM = WBM / 64, FN = WBN / 64;
-  MLoader<WBM> la;
-  KLoader<WBN> lb;
   f32x16 acc[FM][FN];
   zero_acc(acc);
-  auto fetch = [&](int kt) {
-    la.load(p.dz + (int64_t)kt * kKT * p.ldz + m0, p.ldz, p.N - kt * kKT, p.kpad - m0, tid);
-    lb.load(p.hT + (int64_t)n0 * p.ldT + kt * kKT, p.ldT, p.H - n0, tid);
-  };
-  kloop<WBM, WBN, f16x8>(acc, la, lb, fetch, p.ldT / kKT, lds, tid, wm * (WBM / 2), wn * (WBN / 2));
+  const uint16_t* abase = p.dz + m0;
+  const uint16_t* bbase = p.hT + (int64_t)n0 * p.ldT;
+  gemm_loop<TA, TB, f16x8, false>(
+      acc, p.ldT / kKT, lds,
+      [&](int kt, char* dst, int q, int ln, int wv) { TA::issue(abase, p.ldz, p.N, p.kpad - m0, kt, dst, q, ln, wv); },
+      [&](int kt, char* dst, int q, int ln, int wv) { TB::issue(bbase, p.ldT, p.H - n0, kt, dst, q, ln, wv); },
+      tid, wm * (WBM / 2), wn * (WBN / 2));
   const float inv = p.gscale[1];
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
@@ -410,28 +484,30 @@ __global__ __launch_bounds__(kThreads, 1) void dw_gemm(DwParams p) {
 }
 
 // ===========================================================================
-// Backward, step 3: dh_s[m, n] (+)= sum_v dz[m, v] W_s[c0 + v, n]
-// A = dz (K-major rows), B = W_s chunk (MN-major: vocabulary rows, hidden contiguous).
+// Backward, step 3: dh_s[m, n] (+)= (1/s) sum_v dz[m, v] W_s[c0 + v, n]
+// A = dz (K-major rows), B = W_s chunk (MN-major: vocabulary rows, hidden
+// contiguous; read transposed, bf16 converted to fp16).  256 x 128 tiles.
 // ===========================================================================
-constexpr int HBM = 128, HBN = 128;
-using DhStages = Stages<HBM, HBN>;
+constexpr int HBM = 256, HBN = 128;
 
-__global__ __launch_bounds__(kThreads, 2) void dh_gemm(DhParams p) {
-  __shared__ __attribute__((aligned(16))) char lds[DhStages::kBytes];
+__global__ __launch_bounds__(kThreads, 1) void dh_gemm(DhParams p) {
+  using TA = KM<HBM>;
+  using TB = MN<HBN>;
+  __shared__ __attribute__((aligned(1024))) char lds[2 * (TA::kBytes + TB::kBytes)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int logical = xcd_logical(blockIdx.x, p.ntm * p.ntn);
   const int tm = logical / p.ntn, tn = logical - tm * p.ntn;
   const int m0 = tm * HBM, n0 = tn * HBN;
   constexpr int FM = HBM / 64, FN = HBN / 64;
-  KLoader<HBM> la;
-  MLoader<HBN, true> lb;
   f32x16 acc[FM][FN];
   zero_acc(acc);
-  auto fetch = [&](int kt) {
-    la.load(p.dz + (int64_t)m0 * p.ldz + kt * kKT, p.ldz, p.N - m0, tid);
-    lb.load(p.Wc + (int64_t)kt * kKT * p.H + n0, p.H, p.width - kt * kKT, p.H - n0, tid);
-  };
-  kloop<HBM, HBN, f16x8>(acc, la, lb, fetch, p.kpad / kKT, lds, tid, wm * (HBM / 2), wn * (HBN / 2));
+  const uint16_t* abase = p.dz + (int64_t)m0 * p.ldz;
+  const uint16_t* bbase = p.Wc + n0;
+  gemm_loop<TA, TB, f16x8, true>(
+      acc, p.kpad / kKT, lds,
+      [&](int kt, char* dst, int q, int ln, int wv) { TA::issue(abase, p.ldz, p.N - m0, kt, dst, q, ln, wv); },
+      [&](int kt, char* dst, int q, int ln, int wv) { TB::issue(bbase, p.H, p.width, p.H - n0, kt, dst, q, ln, wv); },
+      tid, wm * (HBM / 2), wn * (HBN / 2));
   const float inv = p.gscale[1];
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
@@ -612,7 +688,7 @@ hipError_t launch_fwd_combine(const float* partial, int nsplit, int N, const uin
 }
 
 hipError_t launch_bwd_dz(const BwdParams& p, bool teacher_logits, hipStream_t s) {
-  const unsigned nb = (unsigned)(p.ntv * p.ntok);
+  const unsigned nb = (unsigned)(p.ngroups * p.ntok);
   const bool vec4 = (p.V % 4) == 0;
   if (!teacher_logits)
     bwd_dz_tiles<0, true><<<nb, kThreads, 0, s>>>(p);
