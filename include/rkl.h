@@ -111,8 +111,10 @@ size_t rkl_workspace_bytes(int64_t N, int64_t V, int64_t Hs, int64_t Ht);
  *   row_mask  NULL: all N rows are live (compacted input).
  *             [N] uint8: full-row mode -- rows with 0 get loss 0 and stats 0.
  *   loss      [N] fp32 out: L per row.
- *   stats     [N, 3] fp32 out: (lse_s, lse_t, L) per row, the only state the
- *             backward needs (the log-softmaxes themselves are recomputed).
+ *   stats     [N, 4] fp32 out: (lse_s, lse_t, L, lpmax) per row -- the two
+ *             log-sum-exps, the loss and the log of the row's largest student
+ *             probability; the only state the backward needs (the
+ *             log-softmaxes themselves are recomputed).
  * z_s and z_t are formed tile by tile in fp32 and never written to memory.
  * N = 0 is allowed and launches nothing.
  */
@@ -139,7 +141,7 @@ int rkl_forward_logits(int64_t N, int64_t V, int64_t Hs,
  * Inputs as rkl_forward_hidden, plus
  *   grad_loss [N] fp32 upstream gradient g (NULL = all ones); the caller's
  *             token reduction decides it.
- *   stats     [N, 3] from the forward on the same inputs.
+ *   stats     [N, 4] from the forward on the same inputs.
  * Outputs (gradient of sum_i g_i L_i with respect to the student):
  *   dh_s  [N, Hs] fp32, overwritten; rows with row_mask 0 are exactly 0.
  *   dW_s  [V, Hs] fp32; overwritten, or added to when accumulate_dW != 0.

@@ -168,7 +168,7 @@ def scatter_rows(src, row_idx, T: int):
 
 def forward_hidden(h_s, W_s, h_t, W_t, row_mask=None):
     """Per-row reverse KL with the teacher given as hidden states.
-    Returns (loss fp32 [N], stats fp32 [N, 3] = (lse_s, lse_t, L))."""
+    Returns (loss fp32 [N], stats fp32 [N, 4] = (lse_s, lse_t, L, lpmax))."""
     torch = _torch()
     dev = h_s.device
     N, Hs = h_s.shape
@@ -180,7 +180,7 @@ def forward_hidden(h_s, W_s, h_t, W_t, row_mask=None):
     if row_mask is not None:
         _need(row_mask, "row_mask", torch.uint8, dev, (N,))
     loss = torch.empty(N, dtype=torch.float32, device=dev)
-    stats = torch.empty((N, 3), dtype=torch.float32, device=dev)
+    stats = torch.empty((N, 4), dtype=torch.float32, device=dev)
     nb = workspace_bytes(N, V, Hs, Ht)
     ws = _workspace(dev, nb)
     _check(lib().rkl_forward_hidden(N, V, Hs, Ht, _ptr(h_s), _ptr(W_s), _ptr(h_t), _ptr(W_t), _ptr(row_mask),
@@ -205,7 +205,7 @@ def forward_logits(z_t, h_s=None, W_s=None, z_s=None, row_mask=None):
     if row_mask is not None:
         _need(row_mask, "row_mask", torch.uint8, dev, (N,))
     loss = torch.empty(N, dtype=torch.float32, device=dev)
-    stats = torch.empty((N, 3), dtype=torch.float32, device=dev)
+    stats = torch.empty((N, 4), dtype=torch.float32, device=dev)
     ws = _workspace(dev, workspace_bytes(N, V, Hs, 0))
     _check(lib().rkl_forward_logits(N, V, Hs, _ptr(h_s), _ptr(W_s), _ptr(z_s), _ptr(z_t), _ptr(row_mask),
                                     _ptr(loss), _ptr(stats), _ptr(ws), ws.numel(), _stream(dev)))
@@ -222,7 +222,7 @@ def backward_hidden(h_s, W_s, h_t, W_t, stats, grad_loss=None, row_mask=None, dW
     _need(W_s, "W_s", torch.bfloat16, dev, (V, Hs))
     _need(h_t, "h_t", torch.bfloat16, dev, (N, Ht))
     _need(W_t, "W_t", torch.bfloat16, dev)
-    _need(stats, "stats", torch.float32, dev, (N, 3))
+    _need(stats, "stats", torch.float32, dev, (N, 4))
     if grad_loss is not None:
         _need(grad_loss, "grad_loss", torch.float32, dev, (N,))
     if row_mask is not None:
@@ -249,7 +249,7 @@ def backward_logits(z_t, stats, h_s=None, W_s=None, z_s=None, grad_loss=None, ro
     dev = z_t.device
     N, V = z_t.shape
     _need(z_t, "z_t", torch.float32, dev)
-    _need(stats, "stats", torch.float32, dev, (N, 3))
+    _need(stats, "stats", torch.float32, dev, (N, 4))
     if grad_loss is not None:
         _need(grad_loss, "grad_loss", torch.float32, dev, (N,))
     if row_mask is not None:

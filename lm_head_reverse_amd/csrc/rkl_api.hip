@@ -44,7 +44,7 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 int64_t vocab_chunk() {
   static const int64_t c = [] {
     const char* s = std::getenv("RKL_VOCAB_CHUNK");
-    int64_t v = s ? std::atoll(s) : 16384;
+    int64_t v = s ? std::atoll(s) : 65536;
     if (v < 256) v = 256;
     return round_up(v, 256);
   }();
@@ -174,7 +174,7 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
   float* gscale = reinterpret_cast<float*>(base + L.off_scale);
   uint16_t* hT = reinterpret_cast<uint16_t*>(base + L.off_hT);
   uint16_t* dz = reinterpret_cast<uint16_t*>(base + L.off_dz);
-  RKL_TRY(rkl::launch_grad_scale(grad, row_mask, (int)N, gscale, s));
+  RKL_TRY(rkl::launch_grad_scale(grad, row_mask, stats, (int)N, gscale, s));
   RKL_TRY(rkl::launch_transpose_h(h_s, (int)N, (int)Hs, hT, (int)L.ldT, s));
   const int64_t C = vocab_chunk();
   for (int64_t c0 = 0; c0 < V; c0 += C) {

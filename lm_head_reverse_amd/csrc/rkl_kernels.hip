@@ -308,31 +308,37 @@ __global__ __launch_bounds__(256) void fwd_combine(const float* __restrict__ par
     merge3(ms, ss, aa, P[0], P[(int64_t)N], P[(int64_t)2 * N]);
     merge2(mt, st, P[(int64_t)3 * N], P[(int64_t)4 * N]);
   }
-  float lse_s = ms + logf(ss);
+  const float log_ss = logf(ss);
+  float lse_s = ms + log_ss;
   float lse_t = mt + logf(st);
   float L = aa / ss - (lse_s - lse_t);
-  if (row_mask && row_mask[n] == 0) { L = 0.f; lse_s = 0.f; lse_t = 0.f; }
+  float lpmax = -log_ss;   // log of the largest student probability
+  if (row_mask && row_mask[n] == 0) { L = 0.f; lse_s = 0.f; lse_t = 0.f; lpmax = 0.f; }
   loss[n] = L;
-  stats[3 * (int64_t)n + 0] = lse_s;
-  stats[3 * (int64_t)n + 1] = lse_t;
-  stats[3 * (int64_t)n + 2] = L;
+  stats[4 * (int64_t)n + 0] = lse_s;
+  stats[4 * (int64_t)n + 1] = lse_t;
+  stats[4 * (int64_t)n + 2] = L;
+  stats[4 * (int64_t)n + 3] = lpmax;
 }
 
 // ===========================================================================
 // Backward, step 0: dz scale.  dz = g p_s (w - L) is stored as fp16(s * dz)
-// (11-bit significand; bf16's 8 bits alone can use up the gradient
-// tolerance when one vocabulary entry dominates a row).  s is the power of
-// two that puts max|g| (over live rows) in [1/16, 1/8), leaving fp16 headroom
-// for |w - L| up to ~5e5; dh and dW are multiplied by 1/s (exact).
+// (11-bit significand; bf16's 8 bits alone can use up the gradient tolerance
+// when one vocabulary entry dominates a row).  s is the power of two that
+// puts the largest g * p_s over live rows -- |g| exp(lpmax), lpmax = log of
+// a row's largest student probability, from the forward -- in [16, 32): the
+// bulk of dz then sits in fp16's normal range, and |w - L| up to ~2000 still
+// fits below fp16's maximum (larger values saturate).  dh and dW are
+// multiplied by 1/s (exact).
 // ===========================================================================
 __global__ __launch_bounds__(1024) void grad_scale(const float* __restrict__ grad, const uint8_t* __restrict__ row_mask,
-                                                   int N, float* __restrict__ out) {
+                                                   const float* __restrict__ stats, int N, float* __restrict__ out) {
   __shared__ float red[1024];
   const int tid = threadIdx.x;
   float m = 0.f;
   for (int n = tid; n < N; n += 1024) {
     const bool live = !row_mask || row_mask[n] != 0;
-    if (live) m = fmaxf(m, grad ? fabsf(grad[n]) : 1.0f);
+    if (live) m = fmaxf(m, (grad ? fabsf(grad[n]) : 1.0f) * expf(stats[4 * (int64_t)n + 3]));
   }
   red[tid] = m;
   __syncthreads();
@@ -342,10 +348,10 @@ __global__ __launch_bounds__(1024) void grad_scale(const float* __restrict__ gra
   }
   if (tid == 0) {
     int e = 0;
-    if (red[0] > 0.f) frexpf(red[0], &e);     // max|g| in [2^(e-1), 2^e)
+    if (red[0] > 0.f) frexpf(red[0], &e);     // max in [2^(e-1), 2^e)
     e = e < -100 ? -100 : (e > 100 ? 100 : e);
-    out[0] = ldexpf(1.0f, -e - 3);
-    out[1] = ldexpf(1.0f, e + 3);
+    out[0] = ldexpf(1.0f, 5 - e);
+    out[1] = ldexpf(1.0f, e - 5);
   }
 }
 
@@ -376,9 +382,9 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz_tiles(BwdParams p) {
     const int n = n0 + brow0 + fn * 32 + (lane & 31);
     live[fn] = n < p.N && (!p.row_mask || p.row_mask[n] != 0);
     const int nc = min(n, p.N - 1);
-    const float lse_s = p.stats[3 * (int64_t)nc + 0];
-    const float lse_t = p.stats[3 * (int64_t)nc + 1];
-    const float L = p.stats[3 * (int64_t)nc + 2];
+    const float lse_s = p.stats[4 * (int64_t)nc + 0];
+    const float lse_t = p.stats[4 * (int64_t)nc + 1];
+    const float L = p.stats[4 * (int64_t)nc + 2];
     gs[fn] = (p.grad ? p.grad[nc] : 1.0f) * p.gscale[0];
     cst[fn] = (lse_s - lse_t) + L;
     css[fn] = lse_s * kL2E;
@@ -411,7 +417,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz_tiles(BwdParams p) {
             const float a = zs[fm][fn][4 * gq + e], bb = zt[fm][fn][4 * gq + e];
             float d = 0.f;
             if (live[fn] && v + e < p.V) d = gs[fn] * ex2(fmaf(a, kL2E, -css[fn])) * ((a - bb) - cst[fn]);
-            oh[e] = (_Float16)d;
+            oh[e] = (_Float16)fminf(fmaxf(d, -65504.f), 65504.f);
           }
           *reinterpret_cast<u32x2*>(drow + col) = u32x2{
               (uint32_t)__builtin_bit_cast(uint16_t, oh[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, oh[1]) << 16),
@@ -581,14 +587,17 @@ __global__ __launch_bounds__(256) void fwd_rows_logits(const float* __restrict__
     __syncthreads();
   }
   if (tid == 0) {
-    float lse_s = red[0][0] + logf(red[1][0]);
+    const float log_ss = logf(red[1][0]);
+    float lse_s = red[0][0] + log_ss;
     float lse_t = red[3][0] + logf(red[4][0]);
     float L = red[2][0] / red[1][0] - (lse_s - lse_t);
-    if (row_mask && row_mask[n] == 0) { L = 0.f; lse_s = 0.f; lse_t = 0.f; }
+    float lpmax = -log_ss;
+    if (row_mask && row_mask[n] == 0) { L = 0.f; lse_s = 0.f; lse_t = 0.f; lpmax = 0.f; }
     loss[n] = L;
-    stats[3 * (int64_t)n + 0] = lse_s;
-    stats[3 * (int64_t)n + 1] = lse_t;
-    stats[3 * (int64_t)n + 2] = L;
+    stats[4 * (int64_t)n + 0] = lse_s;
+    stats[4 * (int64_t)n + 1] = lse_t;
+    stats[4 * (int64_t)n + 2] = L;
+    stats[4 * (int64_t)n + 3] = lpmax;
   }
 }
 
@@ -602,7 +611,7 @@ __global__ __launch_bounds__(256) void bwd_rows_logits(const float* __restrict__
   const bool live = !row_mask || row_mask[n] != 0;
   float d = 0.f;
   if (live) {
-    const float lse_s = stats[3 * (int64_t)n + 0], lse_t = stats[3 * (int64_t)n + 1], L = stats[3 * (int64_t)n + 2];
+    const float lse_s = stats[4 * (int64_t)n + 0], lse_t = stats[4 * (int64_t)n + 1], L = stats[4 * (int64_t)n + 2];
     const float g = grad ? grad[n] : 1.0f;
     const float a = z_s[(int64_t)n * V + v], b = z_t[(int64_t)n * V + v];
     d = g * ex2(fmaf(a, kL2E, -(lse_s * kL2E))) * ((a - b) - ((lse_s - lse_t) + L));
@@ -699,8 +708,9 @@ hipError_t launch_bwd_dz(const BwdParams& p, bool teacher_logits, hipStream_t s)
   return hipGetLastError();
 }
 
-hipError_t launch_grad_scale(const float* grad, const uint8_t* row_mask, int N, float* out, hipStream_t s) {
-  grad_scale<<<1, 1024, 0, s>>>(grad, row_mask, N, out);
+hipError_t launch_grad_scale(const float* grad, const uint8_t* row_mask, const float* stats, int N, float* out,
+                             hipStream_t s) {
+  grad_scale<<<1, 1024, 0, s>>>(grad, row_mask, stats, N, out);
   return hipGetLastError();
 }
 

@@ -171,9 +171,9 @@ def test_hidden_ragged_with_grad(tdev, T, V, Hs, Ht):
 
 
 def test_hidden_multi_chunk_backward(tdev):
-    """V = 40000 spans three 16384-column backward chunks (the last one ragged)."""
+    """V = 140000 spans three 65536-column backward chunks (the last one ragged)."""
     torch, dev = tdev
-    case = synth.random_case(31, T=150, V=40000, Hs=64, Ht=64, p_mask=0.6)
+    case = synth.random_case(31, T=150, V=140000, Hs=64, Ht=64, p_mask=0.6)
     say("multi-chunk", case.T, case.V)
     _check_against_oracle(case, _run_hidden(case, dev))
 
@@ -272,3 +272,14 @@ def test_accumulate_dW(tdev):
     base = np.random.default_rng(3).standard_normal((1500, 128)).astype(np.float32)
     _, dW2 = R.backward_hidden(hs, Ws, ht, Wt, stats, dW=f32(base, dev), accumulate_dW=True)
     assert np.array_equal(host(dW2), base + host(dW))
+
+
+def test_token_mean_gradient_large_vocab(tdev):
+    """Upstream gradient 1/N with V = 60000: dz values around g/V must keep
+    their precision in the scaled fp16 workspace."""
+    torch, dev = tdev
+    case = synth.random_case(95, T=400, V=60000, Hs=128, Ht=64, p_mask=0.75)
+    rows = O.compact_rows(case.mask)
+    case.grad = np.full(case.T, 1.0 / rows.shape[0], np.float32)
+    say("token-mean gradient, V=60000")
+    _check_against_oracle(case, _run_hidden(case, dev, g=case.grad), g=case.grad)
