@@ -18,6 +18,7 @@ struct FwdParams {
   int tiles_per_split;     // 256-row vocabulary tiles per split
   int nsplit;
   int ntok;                // 128-token tiles
+  int order_gs, order_tg;  // workgroup order (panel_order)
 };
 
 struct BwdParams {
@@ -39,6 +40,7 @@ struct BwdParams {
   int tiles_per_group;     // vocabulary tiles one workgroup sweeps
   int ngroups;             // ceil(ntv / tiles_per_group)
   int ntok;
+  int order_gs, order_tg;  // workgroup order (panel_order)
 };
 
 struct DwParams {

@@ -229,7 +229,8 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(FwdParams p) {
   __shared__ __attribute__((aligned(16))) float red[kFwdRedBytes / 4];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int logical = xcd_logical(blockIdx.x, p.nsplit * p.ntok);
-  const int split = logical / p.ntok, tt = logical - split * p.ntok;
+  int split, tt;
+  panel_order(logical, p.nsplit, p.ntok, p.order_gs, p.order_tg, split, tt);
   const int n0 = tt * FBN;
   const int ntv = (p.V + FBM - 1) / FBM;
   const int vt0 = split * p.tiles_per_split;
@@ -297,16 +298,32 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(FwdParams p) {
 }
 
 // Split combine: lse = m + log S per side; L = A / S_s - (lse_s - lse_t).
+// 32 rows per workgroup; the 8 thread groups each merge every 8th split
+// (coalesced over rows), then group 0 merges the 8 results in a fixed order,
+// so the result depends on V (the split plan) only, never on N.
+constexpr int kCombRows = 32, kCombWays = 8;
+
 __global__ __launch_bounds__(256) void fwd_combine(const float* __restrict__ partial, int nsplit, int N,
                                                    const uint8_t* __restrict__ row_mask, float* __restrict__ loss,
                                                    float* __restrict__ stats) {
-  const int n = blockIdx.x * 256 + threadIdx.x;
-  if (n >= N) return;
+  __shared__ float red[kCombWays][5][kCombRows];
+  const int r = threadIdx.x % kCombRows, j = threadIdx.x / kCombRows;
+  const int n = blockIdx.x * kCombRows + r;
   float ms = kNegBig, ss = 0.f, aa = 0.f, mt = kNegBig, st = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float* P = partial + (int64_t)s * 5 * N + n;
-    merge3(ms, ss, aa, P[0], P[(int64_t)N], P[(int64_t)2 * N]);
-    merge2(mt, st, P[(int64_t)3 * N], P[(int64_t)4 * N]);
+  if (n < N) {
+    for (int s = j; s < nsplit; s += kCombWays) {
+      const float* P = partial + (int64_t)s * 5 * N + n;
+      merge3(ms, ss, aa, P[0], P[(int64_t)N], P[(int64_t)2 * N]);
+      merge2(mt, st, P[(int64_t)3 * N], P[(int64_t)4 * N]);
+    }
+  }
+  red[j][0][r] = ms; red[j][1][r] = ss; red[j][2][r] = aa; red[j][3][r] = mt; red[j][4][r] = st;
+  __syncthreads();
+  if (j != 0 || n >= N) return;
+#pragma unroll
+  for (int q = 1; q < kCombWays; ++q) {
+    merge3(ms, ss, aa, red[q][0][r], red[q][1][r], red[q][2][r]);
+    merge2(mt, st, red[q][3][r], red[q][4][r]);
   }
   const float log_ss = logf(ss);
   float lse_s = ms + log_ss;
@@ -367,7 +384,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz_tiles(BwdParams p) {
   __shared__ __attribute__((aligned(1024))) char lds[3 * FwdStages::kStage];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int logical = xcd_logical(blockIdx.x, p.ngroups * p.ntok);
-  const int grp = logical / p.ntok, tt = logical - grp * p.ntok;
+  int grp, tt;
+  panel_order(logical, p.ngroups, p.ntok, p.order_gs, p.order_tg, grp, tt);
   const int vt0 = grp * p.tiles_per_group;
   const int vt1 = min(vt0 + p.tiles_per_group, p.ntv);
   const int n0 = tt * FBN;
@@ -692,7 +710,7 @@ hipError_t launch_fwd_tiles(const FwdParams& p, bool teacher_logits, hipStream_t
 
 hipError_t launch_fwd_combine(const float* partial, int nsplit, int N, const uint8_t* row_mask, float* loss,
                               float* stats, hipStream_t s) {
-  fwd_combine<<<(N + 255) / 256, 256, 0, s>>>(partial, nsplit, N, row_mask, loss, stats);
+  fwd_combine<<<(N + kCombRows - 1) / kCombRows, 256, 0, s>>>(partial, nsplit, N, row_mask, loss, stats);
   return hipGetLastError();
 }
 

@@ -535,4 +535,21 @@ __device__ __forceinline__ int xcd_logical(int lin, int total) {
   return xcd < rem ? xcd * (per + 1) + idx : rem * (per + 1) + (xcd - rem) * per + idx;
 }
 
+// Workgroup order for L2 reuse in the fused kernels.  Logical ids walk
+// panels of GS vocabulary runs x all ntok token tiles; inside a panel,
+// rectangles of GS runs x TG token tiles are consecutive, so the workgroups
+// resident on one XCD at a time share both their weight k-slices (across
+// token tiles) and their hidden-state k-slices (across vocabulary runs).
+// A bijection of [0, nrun * ntok) for any GS, TG >= 1 (ragged last panel
+// and last token group included).
+__device__ __forceinline__ void panel_order(int logical, int nrun, int ntok, int GS, int TG, int& run, int& tt) {
+  const int panel = logical / (GS * ntok);
+  const int rem = logical - panel * GS * ntok;
+  const int gs = min(GS, nrun - panel * GS);
+  const int tg = rem / (gs * TG);
+  const int r2 = rem - tg * gs * TG;
+  run = panel * GS + r2 % gs;
+  tt = tg * TG + r2 / gs;
+}
+
 }  // namespace rkl
