@@ -417,18 +417,23 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz_tiles(BwdParams p) {
   dual_stream(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, [&](int job) {
     const int v0 = p.c0 + (vt0 + job) * FBM;
     if (MODE == 1) load_zt<VEC4>(zt, p.z_t, p.N, p.V, v0 + arow0 + lrow, n0 + brow0 + (lane & 31), lane);
+    // Lane l (l < 32) holds rows {0-3, 8-11, 16-19, 24-27} of each 32-row
+    // block, lane l + 32 rows {4-7, 12-15, 20-23, 28-31}, same token.  One
+    // permlane32 swap per dword leaves lane l with rows 0-7 and 16-23, lane
+    // l + 32 with rows 8-15 and 24-31: each lane then stores two runs of 8
+    // consecutive vocabulary entries (16 bytes each).
+    const int hi = lane >> 5;
 #pragma unroll
     for (int fn = 0; fn < FFN; ++fn) {
       const int n = n0 + brow0 + fn * 32 + (lane & 31);
-      if (n >= p.N) continue;
-      uint16_t* drow = p.dz + (int64_t)n * p.ldz;
+      uint16_t* drow = p.dz + (int64_t)min(n, p.N - 1) * p.ldz;
 #pragma unroll
-      for (int fm = 0; fm < FFM; ++fm)
+      for (int fm = 0; fm < FFM; ++fm) {
+        const int vb = v0 + arow0 + fm * 32;   // first vocabulary row of the block
+        uint32_t w[4][2];                       // [gq][dword] packed fp16 pairs
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
-          const int v = v0 + arow0 + lrow + fm * 32 + 8 * gq;   // first of 4 consecutive entries
-          const int col = v - p.c0;
-          if (col >= p.kpad) continue;
+          const int v = vb + lrow + 8 * gq;
           _Float16 oh[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
@@ -437,10 +442,22 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz_tiles(BwdParams p) {
             if (live[fn] && v + e < p.V) d = gs[fn] * ex2(fmaf(a, kL2E, -css[fn])) * ((a - bb) - cst[fn]);
             oh[e] = (_Float16)fminf(fmaxf(d, -65504.f), 65504.f);
           }
-          *reinterpret_cast<u32x2*>(drow + col) = u32x2{
-              (uint32_t)__builtin_bit_cast(uint16_t, oh[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, oh[1]) << 16),
-              (uint32_t)__builtin_bit_cast(uint16_t, oh[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, oh[3]) << 16)};
+          w[gq][0] = (uint32_t)__builtin_bit_cast(uint16_t, oh[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, oh[1]) << 16);
+          w[gq][1] = (uint32_t)__builtin_bit_cast(uint16_t, oh[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, oh[3]) << 16);
         }
+#pragma unroll
+        for (int pr = 0; pr < 2; ++pr) {
+#pragma unroll
+          for (int d = 0; d < 2; ++d) {
+            const auto r = __builtin_amdgcn_permlane32_swap(w[2 * pr][d], w[2 * pr + 1][d], false, false);
+            w[2 * pr][d] = r[0];
+            w[2 * pr + 1][d] = r[1];
+          }
+          const int col = vb + 16 * pr + 8 * hi - p.c0;
+          if (n < p.N && col < p.kpad)
+            *reinterpret_cast<u32x4*>(drow + col) = u32x4{w[2 * pr][0], w[2 * pr][1], w[2 * pr + 1][0], w[2 * pr + 1][1]};
+        }
+      }
     }
   });
 }
