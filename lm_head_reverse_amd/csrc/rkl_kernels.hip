@@ -483,14 +483,15 @@ __global__ __launch_bounds__(256) void transpose_h(const uint16_t* __restrict__ 
 // ===========================================================================
 // Backward, step 2: dW_s[c0 + m, n] (+)= (1/s) sum_t dz[t, m] h_s[t, n]
 // A = dz (MN-major: token rows, vocabulary contiguous; read transposed),
-// B = hT (K-major).  256 x 256 tiles, 128 x 128 per wave.
+// B = hT (K-major).  256 x 256 tiles (128 x 128 per wave), two LDS stages
+// (measured faster here than 256 x 128 tiles with three stages).
 // ===========================================================================
-constexpr int WBM = 256, WBN = 256;
+constexpr int WBM = kDwTileM, WBN = kDwTileN, WNST = 2;
 
 __global__ __launch_bounds__(kThreads, 1) void dw_gemm(DwParams p) {
   using TA = MN<WBM>;
   using TB = KM<WBN>;
-  __shared__ __attribute__((aligned(1024))) char lds[2 * (TA::kBytes + TB::kBytes)];
+  __shared__ __attribute__((aligned(1024))) char lds[WNST * (TA::kBytes + TB::kBytes)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int logical = xcd_logical(blockIdx.x, p.ntm * p.ntn);
   const int tm = logical / p.ntn, tn = logical - tm * p.ntn;
@@ -500,7 +501,7 @@ __global__ __launch_bounds__(kThreads, 1) void dw_gemm(DwParams p) {
   zero_acc(acc);
   const uint16_t* abase = p.dz + m0;
   const uint16_t* bbase = p.hT + (int64_t)n0 * p.ldT;
-  gemm_loop<TA, TB, f16x8, false>(
+  gemm_loop<TA, TB, f16x8, false, WNST>(
       acc, p.ldT / kKT, lds,
       [&](int kt, char* dst, int q, int ln, int wv) { TA::issue(abase, p.ldz, p.N, p.kpad - m0, kt, dst, q, ln, wv); },
       [&](int kt, char* dst, int q, int ln, int wv) { TB::issue(bbase, p.ldT, p.H - n0, kt, dst, q, ln, wv); },
@@ -527,14 +528,15 @@ __global__ __launch_bounds__(kThreads, 1) void dw_gemm(DwParams p) {
 // ===========================================================================
 // Backward, step 3: dh_s[m, n] (+)= (1/s) sum_v dz[m, v] W_s[c0 + v, n]
 // A = dz (K-major rows), B = W_s chunk (MN-major: vocabulary rows, hidden
-// contiguous; read transposed, bf16 converted to fp16).  256 x 128 tiles.
+// contiguous; read transposed, bf16 converted to fp16).  256 x 128 tiles,
+// three LDS stages.
 // ===========================================================================
-constexpr int HBM = 256, HBN = 128;
+constexpr int HBM = kDhTileM, HBN = kDhTileN, HNST = 3;
 
 __global__ __launch_bounds__(kThreads, 1) void dh_gemm(DhParams p) {
   using TA = KM<HBM>;
   using TB = MN<HBN>;
-  __shared__ __attribute__((aligned(1024))) char lds[2 * (TA::kBytes + TB::kBytes)];
+  __shared__ __attribute__((aligned(1024))) char lds[HNST * (TA::kBytes + TB::kBytes)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int logical = xcd_logical(blockIdx.x, p.ntm * p.ntn);
   const int tm = logical / p.ntn, tn = logical - tm * p.ntn;
@@ -544,7 +546,7 @@ __global__ __launch_bounds__(kThreads, 1) void dh_gemm(DhParams p) {
   zero_acc(acc);
   const uint16_t* abase = p.dz + (int64_t)m0 * p.ldz;
   const uint16_t* bbase = p.Wc + n0;
-  gemm_loop<TA, TB, f16x8, true>(
+  gemm_loop<TA, TB, f16x8, true, HNST>(
       acc, p.kpad / kKT, lds,
       [&](int kt, char* dst, int q, int ln, int wv) { TA::issue(abase, p.ldz, p.N - m0, kt, dst, q, ln, wv); },
       [&](int kt, char* dst, int q, int ln, int wv) { TB::issue(bbase, p.H, p.width, p.H - n0, kt, dst, q, ln, wv); },

@@ -455,24 +455,26 @@ __device__ __forceinline__ f16x8 bf16_to_f16(bf16x8 x) {
 }
 
 // ---------------------------------------------------------------------------
-// Generic GEMM main loop, both operands through the DMA, two LDS stages:
+// Generic GEMM main loop, both operands through the DMA, NST LDS stages:
 //   C[m, n] += sum_k A(m, k) B(n, k)   (fp32 accumulators)
 // TA / TB are KM<rows> (K-major, swizzled rows) or MN<cols> (MN-major, read
-// transposed).  Iteration kt: MFMAs of tile kt from stage kt&1 with the
-// fragments one step ahead; the DMA of tile kt+1 into the other stage during
-// step 0; between steps 2 and 3 a barrier that waits for that DMA, after
-// which step 3 reads the first fragments of tile kt+1.  The other stage was
-// last read before the previous iteration's barrier, so the DMA never races
-// a read.  CVT_B converts B fragments from bf16 to fp16.
+// transposed).  Iteration kt: MFMAs of tile kt from stage kt % NST with the
+// fragments one step ahead; the DMA of tile kt + NST - 1 into stage
+// (kt - 1) % NST during step 0; between steps 2 and 3 a barrier that waits
+// for tile kt + 1 (the DMA groups of the later tiles stay in flight), after
+// which step 3 reads the first fragments of tile kt + 1.  Stage (kt - 1) %
+// NST was last read before the previous iteration's barrier, so a DMA never
+// races a read.  Past the last tile the DMA repeats tile nk - 1 into stages
+// that are no longer read.  CVT_B converts B fragments from bf16 to fp16.
 // ---------------------------------------------------------------------------
-template <class TA, class TB, typename ELEM, bool CVT_B, int FM, int FN, class IssueA, class IssueB>
+template <class TA, class TB, typename ELEM, bool CVT_B, int NST, int FM, int FN, class IssueA, class IssueB>
 __device__ __forceinline__ void gemm_loop(f32x16 (&acc)[FM][FN], int nk, char* lds, IssueA issueA, IssueB issueB,
                                           int tid, int arow0, int brow0) {
+  static_assert(NST == 2 || NST == 3, "two or three stages");
   constexpr int kStage = TA::kBytes + TB::kBytes;
   constexpr int NA = TA::kPerWave, NB = TB::kPerWave, ND = NA + NB;
   constexpr int M = FM * FN, R = FM + FN;
   static_assert(R <= M, "fragment reads must fit the MFMA slots");
-  typedef __attribute__((ext_vector_type(8))) short s8;
   using BRAW = typename std::conditional<CVT_B, bf16x8, ELEM>::type;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   auto fragA = [&](const char* st, int fm, int ks) { return TA::template frag<ELEM>(st, arow0 + fm * 32, ks, lane); };
@@ -481,23 +483,31 @@ __device__ __forceinline__ void gemm_loop(f32x16 (&acc)[FM][FN], int nk, char* l
     if constexpr (CVT_B) return bf16_to_f16(r);
     else return r;
   };
+  auto issue_tile = [&](int t, char* st, int q) {
+    if (q < NA) issueA(t, st, q, lane, wave);
+    else issueB(t, st + TA::kBytes, q - NA, lane, wave);
+  };
 #pragma unroll
-  for (int q = 0; q < NA; ++q) issueA(0, lds, q, lane, wave);
+  for (int t = 0; t < NST - 1; ++t)
 #pragma unroll
-  for (int q = 0; q < NB; ++q) issueB(0, lds + TA::kBytes, q, lane, wave);
-  dma_barrier<0>();
+    for (int q = 0; q < ND; ++q) issue_tile(min(t, nk - 1), lds + t * kStage, q);
+  dma_barrier<(NST - 2) * ND>();
   ELEM a[2][FM], b[2][FN];
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) b[0][fn] = fragB(lds, fn, 0);
 #pragma unroll
   for (int fm = 0; fm < FM; ++fm) a[0][fm] = fragA(lds, fm, 0);
+  int scur = 0;
   for (int kt = 0; kt < nk; ++kt) {
-    const char* cur = lds + (kt & 1) * kStage;
-    char* nxt = lds + ((kt + 1) & 1) * kStage;
-    const int kn = min(kt + 1, nk - 1);
+    const int snxt = scur + 1 == NST ? 0 : scur + 1;
+    const int spre = scur == 0 ? NST - 1 : scur - 1;   // (kt + NST - 1) % NST
+    const char* cur = lds + scur * kStage;
+    const char* nxt = lds + snxt * kStage;
+    char* pre = lds + spre * kStage;
+    const int kn = min(kt + NST - 1, nk - 1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      if (ks == 3) dma_barrier<0>();
+      if (ks == 3) dma_barrier<(NST - 2) * ND>();
       const int fb = ks & 1, nb = fb ^ 1;
       const char* src = ks == 3 ? nxt : cur;
       const int nks = (ks + 1) & 3;
@@ -509,14 +519,12 @@ __device__ __forceinline__ void gemm_loop(f32x16 (&acc)[FM][FN], int nk, char* l
         else if (m < R) a[nb][m - FN] = fragA(src, m - FN, nks);
         if (ks == 0) {
 #pragma unroll
-          for (int q = share_lo(ND, M, m); q < share_lo(ND, M, m + 1); ++q) {
-            if (q < NA) issueA(kn, nxt, q, lane, wave);
-            else issueB(kn, nxt + TA::kBytes, q - NA, lane, wave);
-          }
+          for (int q = share_lo(ND, M, m); q < share_lo(ND, M, m + 1); ++q) issue_tile(kn, pre, q);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    scur = snxt;
   }
   dma_barrier<0>();
 }
