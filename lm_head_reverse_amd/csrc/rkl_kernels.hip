@@ -168,48 +168,78 @@ __device__ __forceinline__ void dual_stream(const DualOps& o, int njobs, char* l
                                             f32x16 (&zt)[FFM][FFN], int tid, int arow0, int brow0, Epi epi) {
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int total = njobs * (o.nk[0] + o.nk[1]);
-  char* cur = lds;
-  char* nxt = lds + FwdStages::kStage;
-  char* pre = lds + 2 * FwdStages::kStage;
+  const uint32_t lbase = lds_addr(lds);
+  // stage rotation as byte offsets: reads use lds + offset, the DMA lbase + offset
+  int ocur = 0, onxt = FwdStages::kStage, opre = 2 * FwdStages::kStage;
   StreamPos dp{0, 0, 0};
   int dissued = 0;
-  // DMA of stream position dp into stage dst; past the end it repeats the last
-  // position (loads that are never consumed)
-  auto dma_all = [&](char* dst, int q) {
+  // Per-lane DMA offsets of the current stream segment (one job's student or
+  // teacher k-tiles), relative to the segment's tile base at k-tile 0, with
+  // the ragged-tail clamp folded in (rows past the end repeat the last row).
+  // They only change when the stream enters a new segment, so each DMA is
+  // an SGPR base plus a table entry.
+  uint32_t offA[kStreamA], offB[kStreamB];
+  const uint16_t* segA = o.W[0];
+  const uint16_t* segB = o.h[0];
+  const int lr = lane >> 3, lc = lane & 7;
+  auto seg_setup = [&]() {
     const bool t = dp.phase != 0;
-    const int64_t ld = t ? o.H[1] : o.H[0];
+    const int ld = t ? o.H[1] : o.H[0];
     const int v0 = o.v0 + dp.job * FBM;
+    segA = (t ? o.W[1] : o.W[0]) + (int64_t)v0 * ld;
+    segB = (t ? o.h[1] : o.h[0]) + (int64_t)o.n0 * ld;
+    const int nA = o.V - v0, nB = o.N - o.n0;
+#pragma unroll
+    for (int q = 0; q < kStreamA; ++q) {
+      const int blk = wave * kStreamA + q;
+      const int row = min(8 * blk + lr, nA - 1);
+      offA[q] = (uint32_t)(row * ld + ((lc ^ ((lr ^ blk) & 7)) << 3)) * 2u;
+    }
+#pragma unroll
+    for (int q = 0; q < kStreamB; ++q) {
+      const int blk = wave * kStreamB + q;
+      const int row = min(8 * blk + lr, nB - 1);
+      offB[q] = (uint32_t)(row * ld + ((lc ^ ((lr ^ blk) & 7)) << 3)) * 2u;
+    }
+  };
+  seg_setup();
+  // DMA instruction q of stream position dp into the stage at LDS address dst;
+  // past the end it repeats the last position (loads that are never consumed)
+  auto dma_all = [&](uint32_t dst, int q) {
     if (q < kStreamA)
-      DmaRows<FBM>::issue((t ? o.W[1] : o.W[0]) + (int64_t)v0 * ld, ld, o.V - v0, dp.kt, dst, q, lane, wave);
+      dma16(segA + dp.kt * kKT, offA[q], dst + (uint32_t)((wave * kStreamA + q) * 1024));
     else
-      DmaRows<FBN>::issue((t ? o.h[1] : o.h[0]) + (int64_t)o.n0 * ld, ld, o.N - o.n0, dp.kt, dst + FwdStages::kA,
-                          q - kStreamA, lane, wave);
+      dma16(segB + dp.kt * kKT, offB[q - kStreamA],
+            dst + (uint32_t)(FwdStages::kA + (wave * kStreamB + q - kStreamA) * 1024));
   };
   auto dma_next = [&]() {
-    if (dissued + 1 < total) stream_advance(dp, o);
+    if (dissued + 1 < total) {
+      stream_advance(dp, o);
+      if (dp.kt == 0) seg_setup();
+    }
     ++dissued;
   };
 #pragma unroll
-  for (int q = 0; q < kStreamND; ++q) dma_all(cur, q);
+  for (int q = 0; q < kStreamND; ++q) dma_all(lbase + (uint32_t)ocur, q);
   dma_next();
 #pragma unroll
-  for (int q = 0; q < kStreamND; ++q) dma_all(nxt, q);
+  for (int q = 0; q < kStreamND; ++q) dma_all(lbase + (uint32_t)onxt, q);
   dma_next();
   dma_barrier<kStreamND>();
   bf16x8 a[2][FFM], b[2][FFN];
 #pragma unroll
   for (int f = 0; f < FFM + FFN; ++f)
-    load_frag<bf16x8, FFM, FFN>(a[0], b[0], cur, cur + FwdStages::kA, arow0, brow0, lane, 0, f);
+    load_frag<bf16x8, FFM, FFN>(a[0], b[0], lds, lds + FwdStages::kA, arow0, brow0, lane, 0, f);
 
   auto step = [&](f32x16 (&acc)[FFM][FFN]) {
-    char* target = pre;
-    dma_iter<FBM, FBN, bf16x8, FFM, FFN, kStreamND>(acc, a, b, [&](int q) { dma_all(target, q); }, cur, nxt, lane,
-                                                   arow0, brow0);
+    const uint32_t target = lbase + (uint32_t)opre;
+    dma_iter<FBM, FBN, bf16x8, FFM, FFN, kStreamND>(acc, a, b, [&](int q) { dma_all(target, q); }, lds + ocur,
+                                                   lds + onxt, lane, arow0, brow0);
     dma_next();
-    char* t = cur;
-    cur = nxt;
-    nxt = pre;
-    pre = t;
+    const int t = ocur;
+    ocur = onxt;
+    onxt = opre;
+    opre = t;
   };
   for (int job = 0; job < njobs; ++job) {
     zero_acc(zs);
@@ -503,8 +533,8 @@ __global__ __launch_bounds__(kThreads, 1) void dw_gemm(DwParams p) {
   const uint16_t* bbase = p.hT + (int64_t)n0 * p.ldT;
   gemm_loop<TA, TB, f16x8, false, WNST>(
       acc, p.ldT / kKT, lds,
-      [&](int kt, char* dst, int q, int ln, int wv) { TA::issue(abase, p.ldz, p.N, p.kpad - m0, kt, dst, q, ln, wv); },
-      [&](int kt, char* dst, int q, int ln, int wv) { TB::issue(bbase, p.ldT, p.H - n0, kt, dst, q, ln, wv); },
+      [&](int kt, uint32_t dst, int q, int ln, int wv) { TA::issue(abase, p.ldz, p.N, p.kpad - m0, kt, dst, q, ln, wv); },
+      [&](int kt, uint32_t dst, int q, int ln, int wv) { TB::issue(bbase, p.ldT, p.H - n0, kt, dst, q, ln, wv); },
       tid, wm * (WBM / 2), wn * (WBN / 2));
   const float inv = p.gscale[1];
 #pragma unroll
@@ -548,8 +578,8 @@ __global__ __launch_bounds__(kThreads, 1) void dh_gemm(DhParams p) {
   const uint16_t* bbase = p.Wc + n0;
   gemm_loop<TA, TB, f16x8, true, HNST>(
       acc, p.kpad / kKT, lds,
-      [&](int kt, char* dst, int q, int ln, int wv) { TA::issue(abase, p.ldz, p.N - m0, kt, dst, q, ln, wv); },
-      [&](int kt, char* dst, int q, int ln, int wv) { TB::issue(bbase, p.H, p.width, p.H - n0, kt, dst, q, ln, wv); },
+      [&](int kt, uint32_t dst, int q, int ln, int wv) { TA::issue(abase, p.ldz, p.N - m0, kt, dst, q, ln, wv); },
+      [&](int kt, uint32_t dst, int q, int ln, int wv) { TB::issue(bbase, p.H, p.width, p.H - n0, kt, dst, q, ln, wv); },
       tid, wm * (HBM / 2), wn * (HBN / 2));
   const float inv = p.gscale[1];
 #pragma unroll

@@ -41,104 +41,6 @@ __device__ __forceinline__ int lds_off(int r, int chunk) {
 }
 
 // ---------------------------------------------------------------------------
-// K-major operand: R rows (m or n), 64 consecutive k per row in memory.
-// load_one(kt, i) / store_one(i) issue instruction i of k-tile kt, so the k
-// loop can place each one between MFMAs.
-// ---------------------------------------------------------------------------
-template <int R>
-struct KLoader {
-  static constexpr int kPer = R * 8 / kThreads;
-  static_assert(kPer >= 1 && (R * 8) % kThreads == 0, "tile too small");
-  static constexpr int kVmem = kPer, kDsWrite = kPer;   // instructions per stage
-  u32x4 v[kPer];
-  const uint16_t* base;
-  int64_t ld;
-  int nrows;
-
-  // src -> element (row 0, k 0) of the operand; rows >= nrows (nrows >= 1)
-  // repeat row nrows-1: such rows only ever meet outputs that are discarded,
-  // or zero padding of the other operand, so no branch or zero fill is needed.
-  __device__ __forceinline__ void init(const uint16_t* src, int64_t ld_, int nrows_) {
-    base = src; ld = ld_; nrows = nrows_;
-  }
-  __device__ __forceinline__ void load_one(int kt, int i, int tid) {
-    const int c = tid + i * kThreads;
-    const int r = min(c >> 3, nrows - 1), ch = c & 7;
-    v[i] = *reinterpret_cast<const u32x4*>(base + (int64_t)r * ld + kt * kKT + ch * 8);
-  }
-  __device__ __forceinline__ void store_one(char* lds, int i, int tid) const {
-    const int c = tid + i * kThreads;
-    *reinterpret_cast<u32x4*>(lds + lds_off(c >> 3, c & 7)) = v[i];
-  }
-};
-
-// ---------------------------------------------------------------------------
-// MN-major operand: k-rows in memory, each holding consecutive m (or n).
-// Thread work unit = 4 k x 8 mn; lanes 0-7 read one 128-byte row segment.
-// ---------------------------------------------------------------------------
-template <int R, bool TO_F16 = false>
-struct MLoader {
-  static constexpr int kBlocks = (kKT / 4) * (R / 8);
-  static constexpr int kPer = kBlocks / kThreads;
-  static_assert(kPer >= 1 && kBlocks % kThreads == 0, "tile too small");
-  static constexpr int kVmem = 4 * kPer, kDsWrite = 8 * kPer;
-  u32x4 v[kPer][4];
-  const uint16_t* base;
-  int64_t ld;
-  int kvalid, nmn;
-
-  __device__ __forceinline__ static void decode(int blk, int& bk, int& bm) {
-    constexpr int MH = R / 64;
-    const int rest = blk >> 4;
-    bm = (blk & 7) + 8 * (rest % MH);
-    bk = ((blk >> 3) & 1) + 2 * (rest / MH);
-  }
-  // src -> element (k 0, mn 0).  k rows >= kvalid and mn >= nmn (kvalid >= 1,
-  // nmn >= 8, nmn % 8 == 0) repeat the last valid row / 8-column group: every
-  // caller pairs such k rows with zero padding of the other operand and
-  // discards such mn outputs.
-  __device__ __forceinline__ void init(const uint16_t* src, int64_t ld_, int kvalid_, int nmn_) {
-    base = src; ld = ld_; kvalid = kvalid_; nmn = nmn_;
-  }
-  __device__ __forceinline__ void load_one(int kt, int i, int tid) {
-    const int blk = i >> 2, rr = i & 3;
-    int bk, bm;
-    decode(tid + blk * kThreads, bk, bm);
-    const int col = min(8 * bm, nmn - 8);
-    const int k = min(kt * kKT + 4 * bk + rr, kvalid - 1);
-    v[blk][rr] = *reinterpret_cast<const u32x4*>(base + (int64_t)k * ld + col);
-  }
-  __device__ __forceinline__ void store_one(char* lds, int i, int tid) const {
-    const int blk = i >> 3, j = i & 7;
-    int bk, bm;
-    decode(tid + blk * kThreads, bk, bm);
-    const int r = 8 * bm + j;
-    u32x2 out;
-    if (TO_F16) {
-      // bf16 -> fp32 is a shift; fp32 -> fp16 is exact for bf16 values in
-      // fp16's normal range (only the rounding of tiny values depends on the
-      // truncating pack)
-      const int sh = (j & 1) ? 0 : 16;
-      const uint32_t msk = (j & 1) ? 0xFFFF0000u : 0xFFFFFFFFu;
-      const float f0 = __builtin_bit_cast(float, (v[blk][0][j >> 1] << sh) & msk);
-      const float f1 = __builtin_bit_cast(float, (v[blk][1][j >> 1] << sh) & msk);
-      const float f2 = __builtin_bit_cast(float, (v[blk][2][j >> 1] << sh) & msk);
-      const float f3 = __builtin_bit_cast(float, (v[blk][3][j >> 1] << sh) & msk);
-      out = u32x2{__builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f0, f1)),
-                  __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f2, f3))};
-    } else {
-      const int sh = (j & 1) * 16;
-      const uint32_t e0 = (v[blk][0][j >> 1] >> sh) & 0xFFFFu;
-      const uint32_t e1 = (v[blk][1][j >> 1] >> sh) & 0xFFFFu;
-      const uint32_t e2 = (v[blk][2][j >> 1] >> sh) & 0xFFFFu;
-      const uint32_t e3 = (v[blk][3][j >> 1] >> sh) & 0xFFFFu;
-      out = u32x2{e0 | (e1 << 16), e2 | (e3 << 16)};
-    }
-    *reinterpret_cast<u32x2*>(lds + lds_off(r, bk >> 1) + (bk & 1) * 8) = out;
-  }
-};
-
-// ---------------------------------------------------------------------------
 // One 64-deep stage of MFMAs for a wave: FM x FN blocks of 32 x 32.
 // arow0/brow0: first LDS row of this wave's A / B sub-tile.
 // ---------------------------------------------------------------------------
@@ -181,112 +83,34 @@ struct Stages {
   static constexpr int kA = BM * kLdsRow;
   static constexpr int kB = BN * kLdsRow;
   static constexpr int kStage = kA + kB;
-  static constexpr int kBytes = 2 * kStage;
 };
-
-// Wait for this wave's LDS traffic, then the workgroup barrier.  Unlike
-// __syncthreads() it does not drain outstanding global loads (the prefetch of
-// the tile after next stays in flight); the memory clobber keeps the compiler
-// from moving LDS accesses across it.
-__device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_sched_barrier(0);
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-  __builtin_amdgcn_sched_barrier(0);
-}
 
 constexpr int share_lo(int total, int slots, int i) { return (total * i) / slots; }
 
 // ---------------------------------------------------------------------------
-// k loop over 64-deep tiles: two LDS stages, staging registers one tile
-// ahead, fragment registers one 16-deep step ahead.  Iteration kt, in the
-// order the instructions are issued (each MFMA followed by its extras; the
-// order is pinned with scheduling barriers):
-//   step 0: MFMAs of (kt, 0) | fragments (kt, 1) | LDS writes of tile kt+1
-//   step 1: MFMAs of (kt, 1) | fragments (kt, 2) | global loads of tile kt+2
-//   step 2: MFMAs of (kt, 2) | fragments (kt, 3)
-//   barrier (LDS only)
-//   step 3: MFMAs of (kt, 3) | fragments (kt+1, 0) from the other stage
-// The barrier sits between steps 2 and 3: by then every wave has written
-// stage (kt+1)&1 and read its last fragments of stage kt&1, so step 3 can
-// already read tile kt+1 and iteration kt+1 can overwrite stage kt&1.  The
-// 8 MFMAs of step 3 cover the latency of those reads.  Tiles past the end are
-// clamped to the last one (never consumed), so the body is branch free.
-// ---------------------------------------------------------------------------
-template <int BM, int BN, typename ELEM = bf16x8, int FM, int FN, class LA, class LB>
-__device__ __forceinline__ void kloop(f32x16 (&acc)[FM][FN], LA& la, LB& lb, int nk, char* lds, int tid,
-                                      int arow0, int brow0) {
-  using St = Stages<BM, BN>;
-  static_assert(kKT / 16 == 4, "the schedule assumes 4 MFMA steps per tile");
-  constexpr int M = FM * FN, R = FM + FN;
-  constexpr int NW = LA::kDsWrite + LB::kDsWrite, NV = LA::kVmem + LB::kVmem;
-  static_assert(R <= M, "fragment reads must fit the MFMA slots");
-  const int lane = tid & 63;
-
-#pragma unroll
-  for (int i = 0; i < LA::kVmem; ++i) la.load_one(0, i, tid);
-#pragma unroll
-  for (int i = 0; i < LB::kVmem; ++i) lb.load_one(0, i, tid);
-#pragma unroll
-  for (int i = 0; i < LA::kDsWrite; ++i) la.store_one(lds, i, tid);
-#pragma unroll
-  for (int i = 0; i < LB::kDsWrite; ++i) lb.store_one(lds + St::kA, i, tid);
-  {
-    const int k1 = min(1, nk - 1);
-#pragma unroll
-    for (int i = 0; i < LA::kVmem; ++i) la.load_one(k1, i, tid);
-#pragma unroll
-    for (int i = 0; i < LB::kVmem; ++i) lb.load_one(k1, i, tid);
-  }
-  lds_barrier();
-  ELEM a[2][FM], b[2][FN];
-#pragma unroll
-  for (int f = 0; f < R; ++f) load_frag<ELEM, FM, FN>(a[0], b[0], lds, lds + St::kA, arow0, brow0, lane, 0, f);
-
-  for (int kt = 0; kt < nk; ++kt) {
-    const char* cur = lds + (kt & 1) * St::kStage;
-    char* nxt = lds + ((kt + 1) & 1) * St::kStage;
-    const int kpre = min(kt + 2, nk - 1);
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks == 3) lds_barrier();
-      const int fb = ks & 1, nb = fb ^ 1;
-      const char* src = ks == 3 ? nxt : cur;
-      const int nks = (ks + 1) & 3;
-#pragma unroll
-      for (int m = 0; m < M; ++m) {
-        const int fm = m / FN, fn = m % FN;
-        acc[fm][fn] = mfma32<ELEM>(a[fb][fm], b[fb][fn], acc[fm][fn]);
-        if (m < R) load_frag<ELEM, FM, FN>(a[nb], b[nb], src, src + St::kA, arow0, brow0, lane, nks, m);
-        if (ks == 0) {
-#pragma unroll
-          for (int w = share_lo(NW, M, m); w < share_lo(NW, M, m + 1); ++w) {
-            if (w < LA::kDsWrite) la.store_one(nxt, w, tid);
-            else lb.store_one(nxt + St::kA, w - LA::kDsWrite, tid);
-          }
-        }
-        if (ks == 1) {
-#pragma unroll
-          for (int q = share_lo(NV, M, m); q < share_lo(NV, M, m + 1); ++q) {
-            if (q < LA::kVmem) la.load_one(kpre, q, tid);
-            else lb.load_one(kpre, q - LA::kVmem, tid);
-          }
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    }
-  }
-  lds_barrier();
-}
-
-// ---------------------------------------------------------------------------
-// Direct-to-LDS loads for K-major operands (gfx950 global_load_lds_dwordx4:
-// each lane's 16 bytes land at the wave's LDS block + 16 * lane, no VGPRs).
-// A wave instruction fills one 1 KB block = 8 LDS rows of 128 bytes; lane l
-// covers LDS row 8*blk + l/8, physical chunk l%8, so it loads logical chunk
-// (l%8) ^ swizzle(row) of that row: the swizzled layout comes out of the DMA
-// as is.  Rows past nrows repeat row nrows-1 (see KLoader).
+// Direct-to-LDS loads (gfx950 global_load_lds_dwordx4: each lane's 16 bytes
+// land at the wave-uniform LDS address in M0 + 16 * lane, no VGPRs).  The
+// global address is a wave-uniform 64-bit base in SGPRs plus a per-lane
+// 32-bit offset; the issue paths below keep everything that depends on the
+// k-tile or the block in the scalar base, so the per-lane part is a few
+// full-rate integer ops.
 // ---------------------------------------------------------------------------
 #define RKL_LDS_PTR(p) ((__attribute__((address_space(3))) void*)(p))
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)RKL_LDS_PTR(p); }
+
+__device__ __forceinline__ void dma16(const void* sbase, uint32_t voff, uint32_t lds) {
+  const uint64_t gp = (uint64_t)(uintptr_t)sbase;
+  // (readfirstlane returns int: go through uint32_t so nothing is sign-extended)
+  const uint32_t g_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(gp >> 32));
+  const uint32_t g_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)gp);
+  const uint64_t g = ((uint64_t)g_hi << 32) | (uint64_t)g_lo;
+  const uint32_t l = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds);
+  // M0 is only ever written right before the instruction that reads it on
+  // gfx9+, so setting it here does not disturb compiler-generated code.
+  asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(voff), "s"(g), "s"(l) : "memory", "m0");
+}
 
 // s_waitcnt immediate for gfx9: vmcnt in bits [3:0] and [15:14], expcnt [6:4]
 // (left at 7 = no wait), lgkmcnt [11:8].
@@ -308,9 +132,11 @@ __device__ __forceinline__ void dma_barrier() {
 
 // One k-tile of the DMA pipeline: MFMAs of the tile in stage `cur`, its
 // fragments one step ahead, the ND DMA instructions of the tile two ahead
-// (issue(q), q < ND, into stage `pre`) spread over step 0, and between steps
-// 2 and 3 the barrier after which step 3 reads the first fragments of the
-// next tile from stage `nxt`.
+// (issue(q), q < ND, into stage `pre`) spread evenly over steps 0-2 (a burst
+// of them fills the memory pipeline's queue and stalls the MFMAs behind it),
+// and between steps 2 and 3 the barrier -- by then every DMA of the tile two
+// ahead is issued, so "at most ND in flight" means the next tile has landed --
+// after which step 3 reads the first fragments of the next tile from `nxt`.
 template <int BM, int BN, typename ELEM, int FM, int FN, int ND, class Issue>
 __device__ __forceinline__ void dma_iter(f32x16 (&acc)[FM][FN], ELEM (&a)[2][FM], ELEM (&b)[2][FN], Issue issue,
                                          const char* __restrict__ cur, const char* __restrict__ nxt, int lane,
@@ -328,39 +154,39 @@ __device__ __forceinline__ void dma_iter(f32x16 (&acc)[FM][FN], ELEM (&a)[2][FM]
       const int fm = m / FN, fn = m % FN;
       acc[fm][fn] = mfma32<ELEM>(a[fb][fm], b[fb][fn], acc[fm][fn]);
       if (m < R) load_frag<ELEM, FM, FN>(a[nb], b[nb], src, src + kA, arow0, brow0, lane, nks, m);
-      if (ks == 0) {
+      if (ks < 3) {
 #pragma unroll
-        for (int q = share_lo(ND, M, m); q < share_lo(ND, M, m + 1); ++q) issue(q);
+        for (int q = share_lo(ND, 3 * M, ks * M + m); q < share_lo(ND, 3 * M, ks * M + m + 1); ++q) issue(q);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
-// DMA of one K-major operand tile (R rows x 64 k) into the swizzled layout;
-// per-lane addresses are computed at issue time.
+// K-major operand tile (R rows x 64 k) into the swizzled layout.  A wave
+// instruction fills one 1 KB block = 8 LDS rows of 128 bytes; lane l covers
+// LDS row 8*blk + l/8, physical chunk l%8, so it loads logical chunk
+// (l%8) ^ swizzle(row) of that row: the swizzled layout comes out of the DMA
+// as is.  Rows past nrows (nrows >= 1) repeat row nrows-1: such rows only
+// meet outputs that are discarded or zero padding of the other operand.
 template <int R>
 struct DmaRows {
   static constexpr int kPerWave = R * kLdsRow / 1024 / (kThreads / 64);
   static_assert(kPerWave >= 1, "tile too small");
-  __device__ __forceinline__ static void issue(const uint16_t* base, int64_t ld, int nrows, int kt, char* dst, int i,
-                                               int lane, int wave) {
-    const int blk = wave * kPerWave + i;
-    const int row = 8 * blk + (lane >> 3);
-    const int chunk = (lane & 7) ^ (((lane >> 3) ^ blk) & 7);
-    const uint32_t off = (uint32_t)(((int64_t)min(row, nrows - 1) * ld + chunk * 8) * 2);
-    // base, kt and dst are wave-uniform: keep them in SGPRs
-    const uint64_t gp = (uint64_t)(uintptr_t)(base + kt * kKT);
-    // (readfirstlane returns int: go through uint32_t so nothing is sign-extended)
-    const uint32_t g_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(gp >> 32));
-    const uint32_t g_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)gp);
-    const uint64_t g = ((uint64_t)g_hi << 32) | (uint64_t)g_lo;
-    const uint32_t lds =
-        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)RKL_LDS_PTR(dst + blk * 1024));
-    // M0 is only ever written right before the instruction that reads it on
-    // gfx9+, so setting it here does not disturb compiler-generated code.
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(g), "s"(lds)
-                 : "memory", "m0");
+  __device__ __forceinline__ static void issue(const uint16_t* base, int64_t ld, int nrows, int kt, uint32_t dst,
+                                               int i, int lane, int wave) {
+    const int blk = wave * kPerWave + i;   // wave-uniform
+    const int row0 = 8 * blk;
+    const int lr = lane >> 3;
+    const int chunk = (lane & 7) ^ ((lr ^ blk) & 7);
+    int rb = row0;
+    int lrow = lr;
+    if (row0 + 8 > nrows) {                // ragged tail: wave-uniform test
+      rb = min(row0, nrows - 1);
+      lrow = min(row0 + lr, nrows - 1) - rb;
+    }
+    const uint32_t voff = (__umul24((uint32_t)lrow, (uint32_t)ld) + (uint32_t)chunk * 8u) * 2u;
+    dma16(base + ((int64_t)rb * ld + kt * kKT), voff, dst + (uint32_t)blk * 1024u);
   }
 };
 
@@ -385,27 +211,29 @@ struct MN {
   __device__ __forceinline__ static int off(int k, int chunk) {
     return k * kRowBytes + ((chunk ^ ((k & 3) << 2)) << 4);
   }
-  // DMA instruction i of k-tile kt: 1 KB block blk covers rows (blk*1024)/rowbytes ..
+  // DMA instruction i of k-tile kt: 1 KB block blk covers kRowsPerBlk k-rows.
+  // k rows >= kvalid (kvalid >= 1) repeat the last valid row and columns
+  // >= nmn (nmn >= 8, a multiple of 8) repeat the last 8-column group: every
+  // caller pairs such k rows with zero padding of the other operand and
+  // discards such outputs.
   __device__ __forceinline__ static void issue(const uint16_t* base, int64_t ld, int kvalid, int nmn, int kt,
-                                               char* dst, int i, int lane, int wave) {
-    constexpr int kLanesPerRow = kRowBytes / 16;   // chunks per row
-    const int blk = wave * kPerWave + i;
-    const int byte = blk * 1024 + lane * 16;
-    const int k = byte / kRowBytes;
-    const int pc = (byte % kRowBytes) >> 4;
-    const int c = pc ^ ((k & 3) << 2);
-    (void)kLanesPerRow;
-    const int row = min(kt * kKT + k, kvalid - 1);
-    const int col = min(c * 8, nmn - 8);
-    const uint32_t goff = (uint32_t)(((int64_t)row * ld + col) * 2);
-    const uint64_t gp = (uint64_t)(uintptr_t)base;
-    const uint32_t g_hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(gp >> 32));
-    const uint32_t g_lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)gp);
-    const uint64_t g = ((uint64_t)g_hi << 32) | (uint64_t)g_lo;
-    const uint32_t lds =
-        (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(uintptr_t)RKL_LDS_PTR(dst + blk * 1024));
-    asm volatile("s_mov_b32 m0, %2\n\tglobal_load_lds_dwordx4 %0, %1" ::"v"(goff), "s"(g), "s"(lds)
-                 : "memory", "m0");
+                                               uint32_t dst, int i, int lane, int wave) {
+    constexpr int kRowsPerBlk = 1024 / kRowBytes;
+    constexpr int kLanesPerRow = kRowBytes / 16;
+    const int blk = wave * kPerWave + i;   // wave-uniform
+    const int kl = lane / kLanesPerRow;
+    const int k = blk * kRowsPerBlk + kl;
+    const int c = (lane % kLanesPerRow) ^ ((k & 3) << 2);
+    int rb = kt * kKT + blk * kRowsPerBlk;
+    int lrow = kl, col = c * 8;
+    if (rb + kRowsPerBlk > kvalid || nmn < R) {   // ragged tail: wave-uniform test
+      const int r = min(rb + kl, kvalid - 1);
+      rb = min(rb, kvalid - 1);
+      lrow = r - rb;
+      col = min(col, nmn - 8);
+    }
+    const uint32_t voff = (__umul24((uint32_t)lrow, (uint32_t)ld) + (uint32_t)col) * 2u;
+    dma16(base + (int64_t)rb * ld, voff, dst + (uint32_t)blk * 1024u);
   }
   // MFMA operand for columns mn0 + 0..31 (lane%32), k = 16 ks + 8 (lane/32) .. +7
   template <typename ELEM>
@@ -431,8 +259,8 @@ template <int R>
 struct KM {
   static constexpr int kBytes = R * kLdsRow;
   static constexpr int kPerWave = DmaRows<R>::kPerWave;
-  __device__ __forceinline__ static void issue(const uint16_t* base, int64_t ld, int nrows, int kt, char* dst, int i,
-                                               int lane, int wave) {
+  __device__ __forceinline__ static void issue(const uint16_t* base, int64_t ld, int nrows, int kt, uint32_t dst,
+                                               int i, int lane, int wave) {
     DmaRows<R>::issue(base, ld, nrows, kt, dst, i, lane, wave);
   }
   template <typename ELEM>
@@ -460,8 +288,8 @@ __device__ __forceinline__ f16x8 bf16_to_f16(bf16x8 x) {
 // TA / TB are KM<rows> (K-major, swizzled rows) or MN<cols> (MN-major, read
 // transposed).  Iteration kt: MFMAs of tile kt from stage kt % NST with the
 // fragments one step ahead; the DMA of tile kt + NST - 1 into stage
-// (kt - 1) % NST during step 0; between steps 2 and 3 a barrier that waits
-// for tile kt + 1 (the DMA groups of the later tiles stay in flight), after
+// (kt - 1) % NST spread over steps 0-2; between steps 2 and 3 a barrier that
+// waits for tile kt + 1 (the DMA group of the later tile stays in flight), after
 // which step 3 reads the first fragments of tile kt + 1.  Stage (kt - 1) %
 // NST was last read before the previous iteration's barrier, so a DMA never
 // races a read.  Past the last tile the DMA repeats tile nk - 1 into stages
@@ -483,14 +311,15 @@ __device__ __forceinline__ void gemm_loop(f32x16 (&acc)[FM][FN], int nk, char* l
     if constexpr (CVT_B) return bf16_to_f16(r);
     else return r;
   };
-  auto issue_tile = [&](int t, char* st, int q) {
+  const uint32_t lbase = lds_addr(lds);
+  auto issue_tile = [&](int t, uint32_t st, int q) {
     if (q < NA) issueA(t, st, q, lane, wave);
-    else issueB(t, st + TA::kBytes, q - NA, lane, wave);
+    else issueB(t, st + (uint32_t)TA::kBytes, q - NA, lane, wave);
   };
 #pragma unroll
   for (int t = 0; t < NST - 1; ++t)
 #pragma unroll
-    for (int q = 0; q < ND; ++q) issue_tile(min(t, nk - 1), lds + t * kStage, q);
+    for (int q = 0; q < ND; ++q) issue_tile(min(t, nk - 1), lbase + (uint32_t)(t * kStage), q);
   dma_barrier<(NST - 2) * ND>();
   ELEM a[2][FM], b[2][FN];
 #pragma unroll
@@ -503,7 +332,7 @@ __device__ __forceinline__ void gemm_loop(f32x16 (&acc)[FM][FN], int nk, char* l
     const int spre = scur == 0 ? NST - 1 : scur - 1;   // (kt + NST - 1) % NST
     const char* cur = lds + scur * kStage;
     const char* nxt = lds + snxt * kStage;
-    char* pre = lds + spre * kStage;
+    const uint32_t pre = lbase + (uint32_t)(spre * kStage);
     const int kn = min(kt + NST - 1, nk - 1);
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
@@ -517,9 +346,10 @@ __device__ __forceinline__ void gemm_loop(f32x16 (&acc)[FM][FN], int nk, char* l
         acc[fm][fn] = mfma32<ELEM>(a[fb][fm], b[fb][fn], acc[fm][fn]);
         if (m < FN) b[nb][m] = fragB(src, m, nks);
         else if (m < R) a[nb][m - FN] = fragA(src, m - FN, nks);
-        if (ks == 0) {
+        if (ks < 3) {
 #pragma unroll
-          for (int q = share_lo(ND, M, m); q < share_lo(ND, M, m + 1); ++q) issue_tile(kn, pre, q);
+          for (int q = share_lo(ND, 3 * M, ks * M + m); q < share_lo(ND, 3 * M, ks * M + m + 1); ++q)
+            issue_tile(kn, pre, q);
         }
         __builtin_amdgcn_sched_barrier(0);
       }
