@@ -96,6 +96,9 @@ __device__ __forceinline__ void fold_tile(const f32x16 (&zs)[FFM][FFN], const f3
     st = fmaf(st, ft, pt0 + pt1);
     ms = nms;
     mt = nmt;
+    // one block at a time: keeps the accumulator reads of later blocks from
+    // being hoisted (which would need more registers than the wave has)
+    __builtin_amdgcn_sched_barrier(0);
   }
 }
 
@@ -189,17 +192,18 @@ __device__ __forceinline__ void dual_stream(const DualOps& o, int njobs, char* l
     segA = (t ? o.W[1] : o.W[0]) + (int64_t)v0 * ld;
     segB = (t ? o.h[1] : o.h[0]) + (int64_t)o.n0 * ld;
     const int nA = o.V - v0, nB = o.N - o.n0;
+    const uint32_t ld2 = 2u * (uint32_t)ld;
 #pragma unroll
     for (int q = 0; q < kStreamA; ++q) {
       const int blk = wave * kStreamA + q;
       const int row = min(8 * blk + lr, nA - 1);
-      offA[q] = (uint32_t)(row * ld + ((lc ^ ((lr ^ blk) & 7)) << 3)) * 2u;
+      offA[q] = __umul24((uint32_t)row, ld2) + ((uint32_t)(lc ^ ((lr ^ blk) & 7)) << 4);
     }
 #pragma unroll
     for (int q = 0; q < kStreamB; ++q) {
       const int blk = wave * kStreamB + q;
       const int row = min(8 * blk + lr, nB - 1);
-      offB[q] = (uint32_t)(row * ld + ((lc ^ ((lr ^ blk) & 7)) << 3)) * 2u;
+      offB[q] = __umul24((uint32_t)row, ld2) + ((uint32_t)(lc ^ ((lr ^ blk) & 7)) << 4);
     }
   };
   seg_setup();

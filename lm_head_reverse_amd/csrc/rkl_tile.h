@@ -132,20 +132,23 @@ __device__ __forceinline__ void dma_barrier() {
 
 // One k-tile of the DMA pipeline: MFMAs of the tile in stage `cur`, its
 // fragments one step ahead, the ND DMA instructions of the tile two ahead
-// (issue(q), q < ND, into stage `pre`) spread evenly over steps 0-2 (a burst
-// of them fills the memory pipeline's queue and stalls the MFMAs behind it),
-// and between steps 2 and 3 the barrier -- by then every DMA of the tile two
-// ahead is issued, so "at most ND in flight" means the next tile has landed --
-// after which step 3 reads the first fragments of the next tile from `nxt`.
+// (issue(q), q < ND, into stage `pre`) spread evenly over all 32 MFMA slots
+// (a burst of them fills the memory pipeline's queue and stalls the MFMAs
+// behind it), and between steps 2 and 3 the barrier, after which step 3 reads
+// the first fragments of the next tile from `nxt`.  The barrier lets exactly
+// the kBefore DMAs of the tile two ahead issued so far stay in flight: every
+// older one -- all of the next tile's -- has landed.  The caller's prologue
+// issues two whole tiles and waits with ND in flight.
 template <int BM, int BN, typename ELEM, int FM, int FN, int ND, class Issue>
 __device__ __forceinline__ void dma_iter(f32x16 (&acc)[FM][FN], ELEM (&a)[2][FM], ELEM (&b)[2][FN], Issue issue,
                                          const char* __restrict__ cur, const char* __restrict__ nxt, int lane,
                                          int arow0, int brow0) {
   constexpr int M = FM * FN, R = FM + FN;
   constexpr int kA = BM * kLdsRow;
+  constexpr int kBefore = share_lo(ND, 4 * M, 3 * M);   // DMAs of this call issued before its barrier
 #pragma unroll
   for (int ks = 0; ks < 4; ++ks) {
-    if (ks == 3) dma_barrier<ND>();
+    if (ks == 3) dma_barrier<kBefore>();
     const int fb = ks & 1, nb = fb ^ 1;
     const char* src = ks == 3 ? nxt : cur;
     const int nks = (ks + 1) & 3;
@@ -154,10 +157,8 @@ __device__ __forceinline__ void dma_iter(f32x16 (&acc)[FM][FN], ELEM (&a)[2][FM]
       const int fm = m / FN, fn = m % FN;
       acc[fm][fn] = mfma32<ELEM>(a[fb][fm], b[fb][fn], acc[fm][fn]);
       if (m < R) load_frag<ELEM, FM, FN>(a[nb], b[nb], src, src + kA, arow0, brow0, lane, nks, m);
-      if (ks < 3) {
 #pragma unroll
-        for (int q = share_lo(ND, 3 * M, ks * M + m); q < share_lo(ND, 3 * M, ks * M + m + 1); ++q) issue(q);
-      }
+      for (int q = share_lo(ND, 4 * M, ks * M + m); q < share_lo(ND, 4 * M, ks * M + m + 1); ++q) issue(q);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
