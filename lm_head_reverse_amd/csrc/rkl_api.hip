@@ -100,19 +100,21 @@ size_t fwd_ws_bytes(int64_t N, int64_t V, bool tiled) {
 }
 
 struct BwdLayout {
-  int64_t ldT, ldz;
+  int64_t ldT, ldz, npad;
   size_t off_hT, off_dz, off_scale, total;
 };
-// [dz scale: 2 floats][hT: Hs x ldT fp16][dz chunk: N x ldz fp16]
+// [dz scale: 2 floats][hT: Hs x ldT fp16][dz chunk: npad x ldz fp16]; npad =
+// N rounded up to the 128-token tile (the dz kernel writes those rows as zero)
 BwdLayout bwd_layout(int64_t N, int64_t V, int64_t Hs) {
   BwdLayout L{};
   L.ldT = round_up(N, 64);
+  L.npad = round_up(N, rkl::kFwdTileN);
   const int64_t C = vocab_chunk();
   L.ldz = round_up(V < C ? V : C, 64);
   L.off_scale = 0;
   L.off_hT = 256;
   L.off_dz = L.off_hT + align256((size_t)Hs * L.ldT * 2);
-  L.total = L.off_dz + align256((size_t)N * L.ldz * 2);
+  L.total = L.off_dz + align256((size_t)L.npad * L.ldz * 2);
   return L;
 }
 
@@ -227,11 +229,12 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
     RKL_TRY(rkl::launch_dw(w, s));
 
     rkl::DhParams h{};
-    h.gscale = gscale; h.dz = dz; h.ldz = (int)L.ldz; h.N = (int)N; h.kpad = (int)kpad; h.width = (int)width;
+    h.gscale = gscale; h.dz = dz; h.ldz = (int)L.ldz; h.N = (int)N; h.npad = (int)L.npad; h.kpad = (int)kpad;
+    h.width = (int)width;
     h.Wc = W_s + c0 * Hs; h.H = (int)Hs; h.dh = dh; h.accumulate = c0 > 0;
     h.ntm = (int)ceil_div(N, rkl::kDhTileM);
     h.ntn = (int)ceil_div(Hs, rkl::kDhTileN);
-    RKL_TRY(rkl::launch_dh(h, s));
+    RKL_TRY(rkl::launch_dh(h, c0 + kpad > V, s));
   }
   return RKL_OK;
 }

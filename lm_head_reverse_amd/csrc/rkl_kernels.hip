@@ -184,7 +184,6 @@ __device__ __forceinline__ void dual_stream(const DualOps& o, int njobs, char* l
   uint32_t offA[kStreamA], offB[kStreamB];
   const uint16_t* segA = o.W[0];
   const uint16_t* segB = o.h[0];
-  const int lr = lane >> 3, lc = lane & 7;
   auto seg_setup = [&]() {
     const bool t = dp.phase != 0;
     const int ld = t ? o.H[1] : o.H[0];
@@ -194,17 +193,9 @@ __device__ __forceinline__ void dual_stream(const DualOps& o, int njobs, char* l
     const int nA = o.V - v0, nB = o.N - o.n0;
     const uint32_t ld2 = 2u * (uint32_t)ld;
 #pragma unroll
-    for (int q = 0; q < kStreamA; ++q) {
-      const int blk = wave * kStreamA + q;
-      const int row = min(8 * blk + lr, nA - 1);
-      offA[q] = __umul24((uint32_t)row, ld2) + ((uint32_t)(lc ^ ((lr ^ blk) & 7)) << 4);
-    }
+    for (int q = 0; q < kStreamA; ++q) offA[q] = DmaRows<FBM>::lane_off(q, ld2, nA, lane, wave);
 #pragma unroll
-    for (int q = 0; q < kStreamB; ++q) {
-      const int blk = wave * kStreamB + q;
-      const int row = min(8 * blk + lr, nB - 1);
-      offB[q] = __umul24((uint32_t)row, ld2) + ((uint32_t)(lc ^ ((lr ^ blk) & 7)) << 4);
-    }
+    for (int q = 0; q < kStreamB; ++q) offB[q] = DmaRows<FBN>::lane_off(q, ld2, nB, lane, wave);
   };
   seg_setup();
   // DMA instruction q of stream position dp into the stage at LDS address dst;
@@ -459,8 +450,8 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz_tiles(BwdParams p) {
     const int hi = lane >> 5;
 #pragma unroll
     for (int fn = 0; fn < FFN; ++fn) {
-      const int n = n0 + brow0 + fn * 32 + (lane & 31);
-      uint16_t* drow = p.dz + (int64_t)min(n, p.N - 1) * p.ldz;
+      const int n = n0 + brow0 + fn * 32 + (lane & 31);   // < ntok * 128 = rows of the dz workspace
+      uint16_t* drow = p.dz + (int64_t)n * p.ldz;
 #pragma unroll
       for (int fm = 0; fm < FFM; ++fm) {
         const int vb = v0 + arow0 + fm * 32;   // first vocabulary row of the block
@@ -488,7 +479,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz_tiles(BwdParams p) {
             w[2 * pr + 1][d] = r[1];
           }
           const int col = vb + 16 * pr + 8 * hi - p.c0;
-          if (n < p.N && col < p.kpad)
+          if (col < p.kpad)
             *reinterpret_cast<u32x4*>(drow + col) = u32x4{w[2 * pr][0], w[2 * pr][1], w[2 * pr + 1][0], w[2 * pr + 1][1]};
         }
       }
@@ -533,13 +524,14 @@ __global__ __launch_bounds__(kThreads, 1) void dw_gemm(DwParams p) {
   constexpr int FM = WBM / 64, FN = WBN / 64;
   f32x16 acc[FM][FN];
   zero_acc(acc);
-  const uint16_t* abase = p.dz + m0;
-  const uint16_t* bbase = p.hT + (int64_t)n0 * p.ldT;
-  gemm_loop<TA, TB, f16x8, false, WNST>(
-      acc, p.ldT / kKT, lds,
-      [&](int kt, uint32_t dst, int q, int ln, int wv) { TA::issue(abase, p.ldz, p.N, p.kpad - m0, kt, dst, q, ln, wv); },
-      [&](int kt, uint32_t dst, int q, int ln, int wv) { TB::issue(bbase, p.ldT, p.H - n0, kt, dst, q, ln, wv); },
-      tid, wm * (WBM / 2), wn * (WBN / 2));
+  // A: dz rows are tokens (k, zero-padded to the workspace's row count >=
+  // ldT), columns vocabulary (m); B: hT rows are hidden units (n), columns
+  // tokens (k, zero past N)
+  TA ta;
+  ta.init(p.dz + m0, p.ldz, p.kpad - m0, lane, __builtin_amdgcn_readfirstlane(w));
+  TB tb;
+  tb.init(p.hT + (int64_t)n0 * p.ldT, p.ldT, p.H - n0, lane, __builtin_amdgcn_readfirstlane(w));
+  gemm_loop<TA, TB, f16x8, false, WNST>(acc, p.ldT / kKT, lds, ta, tb, 0, tid, wm * (WBM / 2), wn * (WBN / 2));
   const float inv = p.gscale[1];
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
@@ -567,6 +559,7 @@ __global__ __launch_bounds__(kThreads, 1) void dw_gemm(DwParams p) {
 // ===========================================================================
 constexpr int HBM = kDhTileM, HBN = kDhTileN, HNST = 3;
 
+template <bool RAGGED>
 __global__ __launch_bounds__(kThreads, 1) void dh_gemm(DhParams p) {
   using TA = KM<HBM>;
   using TB = MN<HBN>;
@@ -578,13 +571,15 @@ __global__ __launch_bounds__(kThreads, 1) void dh_gemm(DhParams p) {
   constexpr int FM = HBM / 64, FN = HBN / 64;
   f32x16 acc[FM][FN];
   zero_acc(acc);
-  const uint16_t* abase = p.dz + (int64_t)m0 * p.ldz;
-  const uint16_t* bbase = p.Wc + n0;
-  gemm_loop<TA, TB, f16x8, true, HNST>(
-      acc, p.kpad / kKT, lds,
-      [&](int kt, uint32_t dst, int q, int ln, int wv) { TA::issue(abase, p.ldz, p.N - m0, kt, dst, q, ln, wv); },
-      [&](int kt, uint32_t dst, int q, int ln, int wv) { TB::issue(bbase, p.H, p.width, p.H - n0, kt, dst, q, ln, wv); },
-      tid, wm * (HBM / 2), wn * (HBN / 2));
+  // A: dz rows are tokens (m; npad zero-padded rows), columns vocabulary (k,
+  // zero past the chunk width); B: the W_s chunk, rows vocabulary (k),
+  // columns hidden units (n).  RAGGED: the chunk's last k-tile runs past V.
+  TA ta;
+  ta.init(p.dz + (int64_t)m0 * p.ldz, p.ldz, p.npad - m0, lane, __builtin_amdgcn_readfirstlane(w));
+  TB tb;
+  tb.init(p.Wc + n0, p.H, p.H - n0, lane, __builtin_amdgcn_readfirstlane(w));
+  gemm_loop<TA, TB, f16x8, true, HNST, RAGGED>(acc, p.kpad / kKT, lds, ta, tb, p.width, tid, wm * (HBM / 2),
+                                              wn * (HBN / 2));
   const float inv = p.gscale[1];
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
@@ -796,8 +791,11 @@ hipError_t launch_dw(const DwParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_dh(const DhParams& p, hipStream_t s) {
-  dh_gemm<<<(unsigned)(p.ntm * p.ntn), kThreads, 0, s>>>(p);
+hipError_t launch_dh(const DhParams& p, bool ragged, hipStream_t s) {
+  if (ragged)
+    dh_gemm<true><<<(unsigned)(p.ntm * p.ntn), kThreads, 0, s>>>(p);
+  else
+    dh_gemm<false><<<(unsigned)(p.ntm * p.ntn), kThreads, 0, s>>>(p);
   return hipGetLastError();
 }
 

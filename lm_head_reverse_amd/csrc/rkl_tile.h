@@ -168,26 +168,20 @@ __device__ __forceinline__ void dma_iter(f32x16 (&acc)[FM][FN], ELEM (&a)[2][FM]
 // instruction fills one 1 KB block = 8 LDS rows of 128 bytes; lane l covers
 // LDS row 8*blk + l/8, physical chunk l%8, so it loads logical chunk
 // (l%8) ^ swizzle(row) of that row: the swizzled layout comes out of the DMA
-// as is.  Rows past nrows (nrows >= 1) repeat row nrows-1: such rows only
-// meet outputs that are discarded or zero padding of the other operand.
+// as is.
 template <int R>
 struct DmaRows {
   static constexpr int kPerWave = R * kLdsRow / 1024 / (kThreads / 64);
   static_assert(kPerWave >= 1, "tile too small");
-  __device__ __forceinline__ static void issue(const uint16_t* base, int64_t ld, int nrows, int kt, uint32_t dst,
-                                               int i, int lane, int wave) {
-    const int blk = wave * kPerWave + i;   // wave-uniform
-    const int row0 = 8 * blk;
+  // byte offset of this lane's 16 bytes for DMA instruction q, relative to
+  // (row 0, k-tile start); rows past nrows (nrows >= 1) repeat row nrows-1:
+  // such rows only meet outputs that are discarded or zero padding of the
+  // other operand.
+  __device__ __forceinline__ static uint32_t lane_off(int q, uint32_t ld2, int nrows, int lane, int wave) {
+    const int blk = wave * kPerWave + q;
     const int lr = lane >> 3;
-    const int chunk = (lane & 7) ^ ((lr ^ blk) & 7);
-    int rb = row0;
-    int lrow = lr;
-    if (row0 + 8 > nrows) {                // ragged tail: wave-uniform test
-      rb = min(row0, nrows - 1);
-      lrow = min(row0 + lr, nrows - 1) - rb;
-    }
-    const uint32_t voff = (__umul24((uint32_t)lrow, (uint32_t)ld) + (uint32_t)chunk * 8u) * 2u;
-    dma16(base + ((int64_t)rb * ld + kt * kKT), voff, dst + (uint32_t)blk * 1024u);
+    const int row = min(8 * blk + lr, nrows - 1);
+    return __umul24((uint32_t)row, ld2) + ((uint32_t)((lane & 7) ^ ((lr ^ blk) & 7)) << 4);
   }
 };
 
@@ -209,32 +203,42 @@ struct MN {
   static constexpr int kRowBytes = R * 2;
   static constexpr int kBytes = kKT * kRowBytes;
   static constexpr int kPerWave = kBytes / 1024 / (kThreads / 64);
-  __device__ __forceinline__ static int off(int k, int chunk) {
+  __device__ __forceinline__ static int lds_pos(int k, int chunk) {
     return k * kRowBytes + ((chunk ^ ((k & 3) << 2)) << 4);
   }
-  // DMA instruction i of k-tile kt: 1 KB block blk covers kRowsPerBlk k-rows.
-  // k rows >= kvalid (kvalid >= 1) repeat the last valid row and columns
-  // >= nmn (nmn >= 8, a multiple of 8) repeat the last 8-column group: every
-  // caller pairs such k rows with zero padding of the other operand and
-  // discards such outputs.
-  __device__ __forceinline__ static void issue(const uint16_t* base, int64_t ld, int kvalid, int nmn, int kt,
-                                               uint32_t dst, int i, int lane, int wave) {
-    constexpr int kRowsPerBlk = 1024 / kRowBytes;
-    constexpr int kLanesPerRow = kRowBytes / 16;
-    const int blk = wave * kPerWave + i;   // wave-uniform
-    const int kl = lane / kLanesPerRow;
-    const int k = blk * kRowsPerBlk + kl;
-    const int c = (lane % kLanesPerRow) ^ ((k & 3) << 2);
-    int rb = kt * kKT + blk * kRowsPerBlk;
-    int lrow = kl, col = c * 8;
-    if (rb + kRowsPerBlk > kvalid || nmn < R) {   // ragged tail: wave-uniform test
-      const int r = min(rb + kl, kvalid - 1);
-      rb = min(rb, kvalid - 1);
-      lrow = r - rb;
-      col = min(col, nmn - 8);
+  static constexpr int kRowsPerBlk = 1024 / kRowBytes;
+  static constexpr int kLanesPerRow = kRowBytes / 16;
+  // DMA state of one operand: base = element (k 0, mn 0) of this tile's
+  // column block in a row-major [K, ld] matrix; off[q] = this lane's byte
+  // offset for DMA instruction q within a k-tile.  Columns past nmn (nmn >= 8,
+  // a multiple of 8) repeat the last 8-column group: every caller discards
+  // such outputs.
+  const uint16_t* base;
+  uint32_t ld2;
+  uint32_t off[kPerWave];
+  __device__ __forceinline__ void init(const uint16_t* b, int ld, int nmn, int lane, int wave) {
+    base = b;
+    ld2 = 2u * (uint32_t)ld;
+#pragma unroll
+    for (int q = 0; q < kPerWave; ++q) {
+      const int blk = wave * kPerWave + q;
+      const int kl = blk * kRowsPerBlk + lane / kLanesPerRow;
+      const int c = (lane % kLanesPerRow) ^ ((kl & 3) << 2);
+      off[q] = __umul24((uint32_t)kl, ld2) + 2u * (uint32_t)min(c * 8, nmn - 8);
     }
-    const uint32_t voff = (__umul24((uint32_t)lrow, (uint32_t)ld) + (uint32_t)col) * 2u;
-    dma16(base + (int64_t)rb * ld, voff, dst + (uint32_t)blk * 1024u);
+  }
+  __device__ __forceinline__ void issue(int kt, uint32_t dst, int q, int wave) const {
+    dma16(base + (int64_t)kt * kKT * (ld2 >> 1), off[q], dst + (uint32_t)((wave * kPerWave + q) * 1024));
+  }
+  // Same, for a k-tile that runs past the kvalid valid k rows: rows past it
+  // repeat row kvalid-1 (callers pair them with zero padding of the other
+  // operand).
+  __device__ __forceinline__ void issue_clamped(int kt, uint32_t dst, int q, int wave, int lane, int kvalid) const {
+    const int blk = wave * kPerWave + q;
+    const int kl = blk * kRowsPerBlk + lane / kLanesPerRow;
+    const int row = min(kt * kKT + kl, kvalid - 1) - kt * kKT;
+    const uint32_t voff = off[q] - __umul24((uint32_t)kl, ld2) + __umul24((uint32_t)row, ld2);
+    dma16(base + (int64_t)kt * kKT * (ld2 >> 1), voff, dst + (uint32_t)((wave * kPerWave + q) * 1024));
   }
   // MFMA operand for columns mn0 + 0..31 (lane%32), k = 16 ks + 8 (lane/32) .. +7
   template <typename ELEM>
@@ -245,8 +249,8 @@ struct MN {
     const int m = mn0 + (((lane >> 4) & 1) << 4) + ((j & 3) << 2);
     const int k = 16 * ks + ((lane >> 5) << 3) + (j >> 2);
     const int chunk = m >> 3, within = (m & 7) * 2;
-    const char* p0 = lds + off(k, chunk) + within;
-    const char* p1 = lds + off(k + 4, chunk) + within;
+    const char* p0 = lds + lds_pos(k, chunk) + within;
+    const char* p1 = lds + lds_pos(k + 4, chunk) + within;
     const s4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)RKL_LDS_PTR(p0));
     const s4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s4*)RKL_LDS_PTR(p1));
     typedef short s8 __attribute__((ext_vector_type(8)));
@@ -260,9 +264,17 @@ template <int R>
 struct KM {
   static constexpr int kBytes = R * kLdsRow;
   static constexpr int kPerWave = DmaRows<R>::kPerWave;
-  __device__ __forceinline__ static void issue(const uint16_t* base, int64_t ld, int nrows, int kt, uint32_t dst,
-                                               int i, int lane, int wave) {
-    DmaRows<R>::issue(base, ld, nrows, kt, dst, i, lane, wave);
+  // DMA state: base = element (row 0, k 0) of this tile's row block in a
+  // row-major [rows, ld] matrix, nrows valid rows from there.
+  const uint16_t* base;
+  uint32_t off[kPerWave];
+  __device__ __forceinline__ void init(const uint16_t* b, int ld, int nrows, int lane, int wave) {
+    base = b;
+#pragma unroll
+    for (int q = 0; q < kPerWave; ++q) off[q] = DmaRows<R>::lane_off(q, 2u * (uint32_t)ld, nrows, lane, wave);
+  }
+  __device__ __forceinline__ void issue(int kt, uint32_t dst, int q, int wave) const {
+    dma16(base + kt * kKT, off[q], dst + (uint32_t)((wave * kPerWave + q) * 1024));
   }
   template <typename ELEM>
   __device__ __forceinline__ static ELEM frag(const char* lds, int row0, int ks, int lane) {
@@ -296,9 +308,9 @@ __device__ __forceinline__ f16x8 bf16_to_f16(bf16x8 x) {
 // races a read.  Past the last tile the DMA repeats tile nk - 1 into stages
 // that are no longer read.  CVT_B converts B fragments from bf16 to fp16.
 // ---------------------------------------------------------------------------
-template <class TA, class TB, typename ELEM, bool CVT_B, int NST, int FM, int FN, class IssueA, class IssueB>
-__device__ __forceinline__ void gemm_loop(f32x16 (&acc)[FM][FN], int nk, char* lds, IssueA issueA, IssueB issueB,
-                                          int tid, int arow0, int brow0) {
+template <class TA, class TB, typename ELEM, bool CVT_B, int NST, bool RAGGED_B = false, int FM, int FN>
+__device__ __forceinline__ void gemm_loop(f32x16 (&acc)[FM][FN], int nk, char* lds, const TA& ta, const TB& tb,
+                                          int kvalid_b, int tid, int arow0, int brow0) {
   static_assert(NST == 2 || NST == 3, "two or three stages");
   constexpr int kStage = TA::kBytes + TB::kBytes;
   constexpr int NA = TA::kPerWave, NB = TB::kPerWave, ND = NA + NB;
@@ -313,9 +325,18 @@ __device__ __forceinline__ void gemm_loop(f32x16 (&acc)[FM][FN], int nk, char* l
     else return r;
   };
   const uint32_t lbase = lds_addr(lds);
+  // RAGGED_B: B's last k-tile runs past its kvalid_b valid k rows (MN-major B)
   auto issue_tile = [&](int t, uint32_t st, int q) {
-    if (q < NA) issueA(t, st, q, lane, wave);
-    else issueB(t, st + (uint32_t)TA::kBytes, q - NA, lane, wave);
+    if (q < NA) {
+      ta.issue(t, st, q, wave);
+    } else {
+      if constexpr (RAGGED_B) {
+        if (t == nk - 1) tb.issue_clamped(t, st + (uint32_t)TA::kBytes, q - NA, wave, lane, kvalid_b);
+        else tb.issue(t, st + (uint32_t)TA::kBytes, q - NA, wave);
+      } else {
+        tb.issue(t, st + (uint32_t)TA::kBytes, q - NA, wave);
+      }
+    }
   };
 #pragma unroll
   for (int t = 0; t < NST - 1; ++t)
