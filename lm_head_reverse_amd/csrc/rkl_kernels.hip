@@ -509,9 +509,11 @@ __global__ __launch_bounds__(256) void transpose_h(const uint16_t* __restrict__ 
 // Backward, step 2: dW_s[c0 + m, n] (+)= (1/s) sum_t dz[t, m] h_s[t, n]
 // A = dz (MN-major: token rows, vocabulary contiguous; read transposed),
 // B = hT (K-major).  256 x 256 tiles (128 x 128 per wave), two LDS stages
-// (measured faster here than 256 x 128 tiles with three stages).
+// (measured faster here than 256 x 128 tiles with three stages); with two
+// stages the next tile's DMA is issued during steps 0-1 only, leaving it half
+// a k-tile of MFMAs to land before the barrier.
 // ===========================================================================
-constexpr int WBM = kDwTileM, WBN = kDwTileN, WNST = 2;
+constexpr int WBM = kDwTileM, WBN = kDwTileN, WNST = 2, WDSTEPS = 2;
 
 __global__ __launch_bounds__(kThreads, 1) void dw_gemm(DwParams p) {
   using TA = MN<WBM>;
@@ -531,7 +533,8 @@ __global__ __launch_bounds__(kThreads, 1) void dw_gemm(DwParams p) {
   ta.init(p.dz + m0, p.ldz, p.kpad - m0, lane, __builtin_amdgcn_readfirstlane(w));
   TB tb;
   tb.init(p.hT + (int64_t)n0 * p.ldT, p.ldT, p.H - n0, lane, __builtin_amdgcn_readfirstlane(w));
-  gemm_loop<TA, TB, f16x8, false, WNST>(acc, p.ldT / kKT, lds, ta, tb, 0, tid, wm * (WBM / 2), wn * (WBN / 2));
+  gemm_loop<TA, TB, f16x8, false, WNST, false, WDSTEPS>(acc, p.ldT / kKT, lds, ta, tb, 0, tid, wm * (WBM / 2),
+                                                       wn * (WBN / 2));
   const float inv = p.gscale[1];
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {

@@ -308,10 +308,12 @@ __device__ __forceinline__ f16x8 bf16_to_f16(bf16x8 x) {
 // races a read.  Past the last tile the DMA repeats tile nk - 1 into stages
 // that are no longer read.  CVT_B converts B fragments from bf16 to fp16.
 // ---------------------------------------------------------------------------
-template <class TA, class TB, typename ELEM, bool CVT_B, int NST, bool RAGGED_B = false, int FM, int FN>
+template <class TA, class TB, typename ELEM, bool CVT_B, int NST, bool RAGGED_B = false, int DSTEPS = 3, int FM,
+          int FN>
 __device__ __forceinline__ void gemm_loop(f32x16 (&acc)[FM][FN], int nk, char* lds, const TA& ta, const TB& tb,
                                           int kvalid_b, int tid, int arow0, int brow0) {
   static_assert(NST == 2 || NST == 3, "two or three stages");
+  static_assert(DSTEPS >= 1 && DSTEPS <= 3, "the DMA is issued before the barrier of step 3");
   constexpr int kStage = TA::kBytes + TB::kBytes;
   constexpr int NA = TA::kPerWave, NB = TB::kPerWave, ND = NA + NB;
   constexpr int M = FM * FN, R = FM + FN;
@@ -368,9 +370,9 @@ __device__ __forceinline__ void gemm_loop(f32x16 (&acc)[FM][FN], int nk, char* l
         acc[fm][fn] = mfma32<ELEM>(a[fb][fm], b[fb][fn], acc[fm][fn]);
         if (m < FN) b[nb][m] = fragB(src, m, nks);
         else if (m < R) a[nb][m - FN] = fragA(src, m - FN, nks);
-        if (ks < 3) {
+        if (ks < DSTEPS) {
 #pragma unroll
-          for (int q = share_lo(ND, 3 * M, ks * M + m); q < share_lo(ND, 3 * M, ks * M + m + 1); ++q)
+          for (int q = share_lo(ND, DSTEPS * M, ks * M + m); q < share_lo(ND, DSTEPS * M, ks * M + m + 1); ++q)
             issue_tile(kn, pre, q);
         }
         __builtin_amdgcn_sched_barrier(0);
