@@ -157,11 +157,13 @@ def cpu_baseline(case, target_s: float):
         O.backward(inp, rows)
         return time.perf_counter() - t0
 
-    probe = 32
-    t = run(probe)
-    n = probe
-    if t < target_s / 3:
-        n = int(min(1024, max(probe, probe * target_s / t)) // 32 * 32)
+    # grow the row sample until it takes about target_s (the per-row cost of
+    # a small probe overstates the steady cost)
+    cap = min(4096, case.T)
+    n = 32
+    t = run(n)
+    while t < target_s / 2 and n < cap:
+        n = int(min(cap, max(n + 32, n * target_s / max(t, 1e-3))) // 32 * 32)
         t = run(n)
     return {"value": n / t, "unit": "masked tokens/s", "cores": int(cores), "kind": "oracle",
             "sample": f"fp64 numpy oracle, forward+backward (L, dh, dW) over the first {n} of the {case.T} "
