@@ -221,15 +221,17 @@ __device__ __forceinline__ void dual_stream(const DualOps& o, int njobs, char* l
   for (int q = 0; q < kStreamND; ++q) dma_all(lbase + (uint32_t)onxt, q);
   dma_next();
   dma_barrier<kStreamND>();
+  FragLanes fl;
+  fl.init(lane);
   bf16x8 a[2][FFM], b[2][FFN];
 #pragma unroll
   for (int f = 0; f < FFM + FFN; ++f)
-    load_frag<bf16x8, FFM, FFN>(a[0], b[0], lds, lds + FwdStages::kA, arow0, brow0, lane, 0, f);
+    load_frag<bf16x8, FFM, FFN>(a[0], b[0], lds + arow0 * kLdsRow, lds + FwdStages::kA + brow0 * kLdsRow, fl, 0, f);
 
   auto step = [&](f32x16 (&acc)[FFM][FFN]) {
     const uint32_t target = lbase + (uint32_t)opre;
     dma_iter<FBM, FBN, bf16x8, FFM, FFN, kStreamND>(acc, a, b, [&](int q) { dma_all(target, q); }, lds + ocur,
-                                                   lds + onxt, lane, arow0, brow0);
+                                                   lds + onxt, fl, arow0, brow0);
     dma_next();
     const int t = ocur;
     ocur = onxt;

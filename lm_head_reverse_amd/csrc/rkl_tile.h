@@ -56,16 +56,33 @@ __device__ __forceinline__ f32x16 mfma32<f16x8>(f16x8 a, f16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
 }
 
+// Per-lane LDS offsets of the MFMA fragments of a swizzled K-major tile.
+// Rows step by 32 between fragments, which flips bit 2 of the swizzle only,
+// so for a tile row block starting at a multiple of 64 the fragment of
+// 32-row block f at 16-deep step ks sits at
+//   block base + p[ks ^ 2 (f & 1)] + 4096 f,
+//   p[k] = (lane % 32) * 128 + 16 * ((2k + lane / 32) ^ (lane % 8) ^ (lane / 8 % 4)),
+// the same four offsets for every block and both operands (this equals
+// lds_off(row0 + 32 f + lane % 32, 2 ks + lane / 32) for row0 % 64 == 0).
+struct FragLanes {
+  uint32_t p[4];
+  __device__ __forceinline__ void init(int lane) {
+    const int lx = (lane & 7) ^ ((lane >> 3) & 3);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) p[k] = (uint32_t)((lane & 31) * kLdsRow + (((2 * k + (lane >> 5)) ^ lx) << 4));
+  }
+};
+
 // One MFMA fragment (B fragments first: the fm-major MFMA order needs every
-// b before the second a).  f < FN: b[f]; else a[f - FN].
+// b before the second a).  f < FN: b[f]; else a[f - FN].  ldsA / ldsB point
+// at this wave's row block (a multiple of 64 rows into the tile).
 template <typename ELEM, int FM, int FN>
 __device__ __forceinline__ void load_frag(ELEM (&a)[FM], ELEM (&b)[FN], const char* ldsA, const char* ldsB,
-                                          int arow0, int brow0, int lane, int ks, int f) {
-  const int chunk = ks * 2 + (lane >> 5);
+                                          const FragLanes& fl, int ks, int f) {
   if (f < FN)
-    b[f] = *reinterpret_cast<const ELEM*>(ldsB + lds_off(brow0 + f * 32 + (lane & 31), chunk));
+    b[f] = *reinterpret_cast<const ELEM*>(ldsB + fl.p[ks ^ ((f & 1) << 1)] + f * 32 * kLdsRow);
   else
-    a[f - FN] = *reinterpret_cast<const ELEM*>(ldsA + lds_off(arow0 + (f - FN) * 32 + (lane & 31), chunk));
+    a[f - FN] = *reinterpret_cast<const ELEM*>(ldsA + fl.p[ks ^ (((f - FN) & 1) << 1)] + (f - FN) * 32 * kLdsRow);
 }
 
 template <int FM, int FN>
@@ -141,8 +158,8 @@ __device__ __forceinline__ void dma_barrier() {
 // issues two whole tiles and waits with ND in flight.
 template <int BM, int BN, typename ELEM, int FM, int FN, int ND, class Issue>
 __device__ __forceinline__ void dma_iter(f32x16 (&acc)[FM][FN], ELEM (&a)[2][FM], ELEM (&b)[2][FN], Issue issue,
-                                         const char* __restrict__ cur, const char* __restrict__ nxt, int lane,
-                                         int arow0, int brow0) {
+                                         const char* __restrict__ cur, const char* __restrict__ nxt,
+                                         const FragLanes& fl, int arow0, int brow0) {
   constexpr int M = FM * FN, R = FM + FN;
   constexpr int kA = BM * kLdsRow;
   constexpr int kBefore = share_lo(ND, 4 * M, 3 * M);   // DMAs of this call issued before its barrier
@@ -156,7 +173,8 @@ __device__ __forceinline__ void dma_iter(f32x16 (&acc)[FM][FN], ELEM (&a)[2][FM]
     for (int m = 0; m < M; ++m) {
       const int fm = m / FN, fn = m % FN;
       acc[fm][fn] = mfma32<ELEM>(a[fb][fm], b[fb][fn], acc[fm][fn]);
-      if (m < R) load_frag<ELEM, FM, FN>(a[nb], b[nb], src, src + kA, arow0, brow0, lane, nks, m);
+      if (m < R)
+        load_frag<ELEM, FM, FN>(a[nb], b[nb], src + arow0 * kLdsRow, src + kA + brow0 * kLdsRow, fl, nks, m);
 #pragma unroll
       for (int q = share_lo(ND, 4 * M, ks * M + m); q < share_lo(ND, 4 * M, ks * M + m + 1); ++q) issue(q);
       __builtin_amdgcn_sched_barrier(0);
