@@ -10,6 +10,9 @@ Workload: Qwen3-1.7B-shaped hidden-state path, B=4 sequences of S=1025 tokens,
 every one of the T = B(S-1) = 4096 positions trainable (N = 4096), Hs = Ht =
 2048, V = 151936, bf16 inputs (synthetic, seeded), fp32 accumulation.
 
+--payload logits times the same step with the teacher given as fp32 logits
+[N, V] (formed once from the same tensors) instead of hidden states.
+
 Prints one JSON line (rank 0):
   value = masked tokens/s for forward + backward;
   roofline = the fused forward kernel against the dense bf16 MFMA peak;
@@ -41,6 +44,8 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU work for the oracle sample")
     ap.add_argument("--profile-copy", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
+    ap.add_argument("--payload", choices=("hidden", "logits"), default="hidden",
+                    help="teacher payload: hidden states (default, the headline) or fp32 logits [N, V]")
     ap.add_argument("--report-c5", action="store_true",
                     help="time compact vs full-row on the long-prompt workload (T=32768, N=4096, Ht=4096)")
     return ap.parse_args()
@@ -199,20 +204,36 @@ def main():
 
     h_s_all, h_t_all = bf(case.h_s), bf(case.h_t)
     W_s, W_t = bf(case.W_s), bf(case.W_t)
+    logits = args.payload == "logits"
+    if logits:
+        # teacher logits payload: z_t = h_t W_t^T formed once in fp32 (input
+        # preparation, outside the timed region); the library streams it
+        z_t_all = h_t_all.float() @ W_t.float().t()
+        del h_t_all, W_t
     mask = torch.from_numpy(case.mask).to(dev)
     N_expected = int(case.mask.sum())
     grad_pos = torch.full((T,), 1.0 / N_expected, dtype=torch.float32, device=dev)   # token-mean upstream
     dW = torch.empty((V, Hs), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
+    def fwd(h_s, t_in):
+        if logits:
+            return R.forward_logits(t_in, h_s=h_s, W_s=W_s)
+        return R.forward_hidden(h_s, W_s, t_in, W_t)
+
+    def bwd(h_s, t_in, stats, g):
+        if logits:
+            return R.backward_logits(t_in, stats, h_s=h_s, W_s=W_s, grad_loss=g, dW=dW)
+        return R.backward_hidden(h_s, W_s, t_in, W_t, stats, grad_loss=g, dW=dW)
+
     def step():
         idx, N = R.compact_rows(mask)
         h_s = R.gather_rows(h_s_all, idx)
-        h_t = R.gather_rows(h_t_all, idx)
+        t_in = R.gather_rows(z_t_all if logits else h_t_all, idx)
         g = R.gather_rows(grad_pos, idx)
-        loss, stats = R.forward_hidden(h_s, W_s, h_t, W_t)
+        loss, stats = fwd(h_s, t_in)
         loss_pos = R.scatter_rows(loss, idx, T)
-        dh, _ = R.backward_hidden(h_s, W_s, h_t, W_t, stats, grad_loss=g, dW=dW)
+        dh, _ = bwd(h_s, t_in, stats, g)
         dh_pos = R.scatter_rows(dh, idx, T)
         return N, loss_pos, dh_pos
 
@@ -235,27 +256,32 @@ def main():
     tok_s = N * args.steps / wall
 
     # per-call device time with events on the stream the library launches on
-    h_s = R.gather_rows(h_s_all, R.compact_rows(mask)[0])
-    h_t = R.gather_rows(h_t_all, R.compact_rows(mask)[0])
+    idx, _ = R.compact_rows(mask)
+    h_s = R.gather_rows(h_s_all, idx)
+    t_in = R.gather_rows(z_t_all if logits else h_t_all, idx)
     g = torch.full((N,), 1.0 / N, dtype=torch.float32, device=dev)
-    loss, stats = R.forward_hidden(h_s, W_s, h_t, W_t)
+    loss, stats = fwd(h_s, t_in)
     stream = torch.cuda.current_stream(dev)
     reps = max(args.steps, 5)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
     torch.cuda.synchronize()
     ev[0].record(stream)
     for _ in range(reps):
-        R.forward_hidden(h_s, W_s, h_t, W_t)
+        fwd(h_s, t_in)
     ev[1].record(stream)
     for _ in range(reps):
-        R.backward_hidden(h_s, W_s, h_t, W_t, stats, grad_loss=g, dW=dW)
+        bwd(h_s, t_in, stats, g)
     ev[2].record(stream)
     torch.cuda.synchronize()
     fwd_ms = ev[0].elapsed_time(ev[1]) / reps
     bwd_ms = ev[1].elapsed_time(ev[2]) / reps
 
-    flop_fwd = 2.0 * N * V * (Hs + Ht)
-    flop_step = 4.0 * N * V * (Hs + Ht) + 4.0 * N * V * Hs
+    if logits:
+        flop_fwd = 2.0 * N * V * Hs
+        flop_step = 8.0 * N * V * Hs
+    else:
+        flop_fwd = 2.0 * N * V * (Hs + Ht)
+        flop_step = 4.0 * N * V * (Hs + Ht) + 4.0 * N * V * Hs
     achieved_fwd = flop_fwd / (fwd_ms * 1e-3)
     out = {
         "metric": METRIC,
@@ -270,10 +296,11 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "Qwen3-1.7B-shaped hidden-state teacher, B=4 S=1025 (T=N=4096 trainable), "
-                               "Hs=Ht=2048, V=151936",
-                   "B": case.B, "S": case.S, "N": int(N), "Hs": Hs, "Ht": Ht, "V": V,
-                   "payload": "hidden_states", "parallelism": "single GPU"},
+        "config": {"workload": ("Qwen3-1.7B-shaped fp32 teacher logits [N, V], " if logits else
+                                "Qwen3-1.7B-shaped hidden-state teacher, ") +
+                               "B=4 S=1025 (T=N=4096 trainable), Hs=Ht=2048, V=151936",
+                   "B": case.B, "S": case.S, "N": int(N), "Hs": Hs, "Ht": 0 if logits else Ht, "V": V,
+                   "payload": "logits" if logits else "hidden_states", "parallelism": "single GPU"},
         "mfma_peak_frac_fwd_bwd": round(flop_step / (ms_step * 1e-3) / PEAK_BF16, 4),
         "fwd_tokens_per_s": round(N / (fwd_ms * 1e-3), 1),
         "fwd_ms": round(fwd_ms, 4),
@@ -281,8 +308,10 @@ def main():
         "mfma_peak_frac_fwd": round(achieved_fwd / PEAK_BF16, 4),
         "mfma_peak_frac_bwd": round((flop_step - flop_fwd) / (bwd_ms * 1e-3) / PEAK_BF16, 4),
         "roofline": {
-            "kernel": "fwd_tiles (fused forward: both projections + online LSE/KL epilogue; "
-                      "event time of the forward call, which adds the per-row split combine)",
+            "kernel": ("fwd_tiles<1> (fused forward: student projection + teacher-logit stream + online "
+                       "LSE/KL epilogue" if logits else
+                       "fwd_tiles (fused forward: both projections + online LSE/KL epilogue") +
+                      "; event time of the forward call, which adds the per-row split combine)",
             "bound": "mfma",
             "achieved": round(achieved_fwd / 1e12, 2),
             "peak": round(PEAK_BF16 / 1e12, 1),
@@ -291,10 +320,10 @@ def main():
             "traffic": None,
         },
     }
-    rec = recorded_traffic()
+    rec = None if logits else recorded_traffic()
     if rec is not None:
         out["roofline"]["traffic"] = rec["hbm_bytes_per_launch"]
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and not logits:
         print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(out), flush=True)

@@ -39,26 +39,26 @@ inline size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
 
-// Vocabulary columns per backward chunk (a multiple of 256).  Fixed for the
-// process so that a row's dh never depends on N.
+// Tuning knobs, read from the environment at every call (cheap next to a
+// launch) so that one process can exercise several settings.  The workgroup
+// orders and the tiles per backward workgroup never change a result bit.  The
+// backward chunk width changes where dh's fp32 sum over vocabulary chunks is
+// split, so it changes dh's rounding (never N-dependent for a fixed width);
+// the workspace size depends on it.
+
+// Vocabulary columns per backward chunk (a multiple of 256; default 65536).
 int64_t vocab_chunk() {
-  static const int64_t c = [] {
-    const char* s = std::getenv("RKL_VOCAB_CHUNK");
-    int64_t v = s ? std::atoll(s) : 65536;
-    if (v < 256) v = 256;
-    return round_up(v, 256);
-  }();
-  return c;
+  const char* s = std::getenv("RKL_VOCAB_CHUNK");
+  int64_t v = s ? std::atoll(s) : 65536;
+  if (v < 256) v = 256;
+  return round_up(v, 256);
 }
 
 // Vocabulary tiles one backward workgroup sweeps (does not change results).
 int bwd_tiles_per_group() {
-  static const int t = [] {
-    const char* s = std::getenv("RKL_BWD_TILES");
-    int v = s ? std::atoi(s) : 4;
-    return v < 1 ? 1 : v;
-  }();
-  return t;
+  const char* s = std::getenv("RKL_BWD_TILES");
+  const int v = s ? std::atoi(s) : 4;
+  return v < 1 ? 1 : (v > 64 ? 64 : v);
 }
 
 // Workgroup order of the fused kernels (panel_order): GS vocabulary runs x TG
@@ -71,18 +71,12 @@ struct Order {
 Order read_order(const char* env, Order dflt) {
   if (const char* s = std::getenv(env)) {
     int a = 0, b = 0;
-    if (std::sscanf(s, "%d,%d", &a, &b) == 2 && a >= 1 && b >= 1) return Order{a, b};
+    if (std::sscanf(s, "%d,%d", &a, &b) == 2 && a >= 1 && b >= 1 && a <= 4096 && b <= 4096) return Order{a, b};
   }
   return dflt;
 }
-Order fwd_order() {
-  static const Order o = read_order("RKL_FWD_ORDER", Order{2, 16});
-  return o;
-}
-Order bwd_order() {
-  static const Order o = read_order("RKL_BWD_ORDER", Order{4, 8});
-  return o;
-}
+Order fwd_order() { return read_order("RKL_FWD_ORDER", Order{2, 16}); }
+Order bwd_order() { return read_order("RKL_BWD_ORDER", Order{4, 8}); }
 
 // Forward split plan: depends on V only (so a row's result never depends on N).
 struct Split {

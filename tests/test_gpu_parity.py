@@ -178,6 +178,36 @@ def test_hidden_multi_chunk_backward(tdev):
     _check_against_oracle(case, _run_hidden(case, dev))
 
 
+@pytest.mark.parametrize("orders", [("1,1", "1,1", "1"), ("3,5", "7,2", "3"), ("64,64", "2,3", "64")],
+                         ids=["one_by_one", "ragged_panels", "oversized"])
+def test_tile_order_and_grouping_do_not_change_results(tdev, monkeypatch, orders):
+    """The workgroup order (panel sizes GS x TG) and the vocabulary tiles per
+    backward workgroup only reorder independent work: results are bitwise
+    those of the default settings, for ragged token and vocabulary tails."""
+    torch, dev = tdev
+    case = synth.random_case(77, T=700, V=5003, Hs=128, Ht=192, p_mask=0.8, with_grad=True)
+    say("orders", orders, case.T, case.V)
+    ref = _run_hidden(case, dev, g=case.grad)
+    fo, bo, bt = orders
+    monkeypatch.setenv("RKL_FWD_ORDER", fo)
+    monkeypatch.setenv("RKL_BWD_ORDER", bo)
+    monkeypatch.setenv("RKL_BWD_TILES", bt)
+    got = _run_hidden(case, dev, g=case.grad)
+    for a, b, what in zip(got[1:], ref[1:], ("loss", "stats", "dh", "dW")):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), what
+
+
+@pytest.mark.parametrize("chunk", [256, 768])
+def test_narrow_backward_chunks(tdev, monkeypatch, chunk):
+    """Backward vocabulary chunks of 256 and 768 columns over V = 3001: many
+    chunks, the last ragged and past V (the clamped dh variant)."""
+    torch, dev = tdev
+    monkeypatch.setenv("RKL_VOCAB_CHUNK", str(chunk))
+    case = synth.random_case(78, T=300, V=3001, Hs=128, Ht=64, p_mask=0.6, with_grad=True)
+    say("chunk", chunk, case.T, case.V)
+    _check_against_oracle(case, _run_hidden(case, dev, g=case.grad), g=case.grad)
+
+
 @pytest.mark.parametrize("V", [3000, 1001])
 def test_student_hidden_teacher_logits(tdev, V):
     """Teacher logits payload with the student projected; V = 1001 takes the unvectorised z_t reads."""
