@@ -76,6 +76,14 @@ Order read_order(const char* env, Order dflt) {
   return dflt;
 }
 Order fwd_order() { return read_order("RKL_FWD_ORDER", Order{2, 16}); }
+
+// Waves per workgroup of the fused kernels: 8 (two waves per SIMD, measured
+// faster) or 4 (RKL_FUSED_WAVES=4).  The fold order of the online statistics
+// follows the wave layout, so the two settings differ in rounding only.
+int fused_waves() {
+  const char* s = std::getenv("RKL_FUSED_WAVES");
+  return (s && std::atoi(s) == 4) ? 4 : 8;
+}
 Order bwd_order() { return read_order("RKL_BWD_ORDER", Order{4, 8}); }
 
 // Forward split plan: depends on V only (so a row's result never depends on N).
@@ -173,7 +181,7 @@ int forward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* 
   p.ntok = (int)ceil_div(N, rkl::kFwdTileN);
   p.order_gs = fwd_order().gs;
   p.order_tg = fwd_order().tg;
-  RKL_TRY(rkl::launch_fwd_tiles(p, z_t != nullptr, s));
+  RKL_TRY(rkl::launch_fwd_tiles(p, z_t != nullptr, fused_waves(), s));
   RKL_TRY(rkl::launch_fwd_combine(p.partial, p.nsplit, p.N, row_mask, loss, stats, s));
   return RKL_OK;
 }
@@ -212,7 +220,7 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
     b.ntok = (int)ceil_div(N, rkl::kFwdTileN);
     b.order_gs = bwd_order().gs;
     b.order_tg = bwd_order().tg;
-    RKL_TRY(rkl::launch_bwd_dz(b, z_t != nullptr, s));
+    RKL_TRY(rkl::launch_bwd_dz(b, z_t != nullptr, fused_waves(), s));
 
     rkl::DwParams w{};
     w.gscale = gscale; w.dz = dz; w.ldz = (int)L.ldz; w.N = (int)N; w.kpad = (int)kpad; w.width = (int)width;

@@ -71,10 +71,10 @@ constexpr int kFwdTileN = 128;
 constexpr int kDwTileM = 256, kDwTileN = 256;
 constexpr int kDhTileM = 256, kDhTileN = 128;
 
-hipError_t launch_fwd_tiles(const FwdParams& p, bool teacher_logits, hipStream_t s);
+hipError_t launch_fwd_tiles(const FwdParams& p, bool teacher_logits, int waves, hipStream_t s);
 hipError_t launch_fwd_combine(const float* partial, int nsplit, int N, const uint8_t* row_mask, float* loss,
                               float* stats, hipStream_t s);
-hipError_t launch_bwd_dz(const BwdParams& p, bool teacher_logits, hipStream_t s);
+hipError_t launch_bwd_dz(const BwdParams& p, bool teacher_logits, int waves, hipStream_t s);
 hipError_t launch_grad_scale(const float* grad, const uint8_t* row_mask, const float* stats, int N, float* out,
                              hipStream_t s);
 hipError_t launch_transpose_h(const uint16_t* h, int N, int H, uint16_t* hT, int ldT, hipStream_t s);

@@ -49,21 +49,34 @@ __device__ __forceinline__ void merge2(float& m, float& s, float m2, float s2) {
 // ===========================================================================
 constexpr int FBM = 256;   // vocabulary rows per tile
 constexpr int FBN = 128;   // tokens per tile
-constexpr int FFM = FBM / 2 / 32, FFN = FBN / 2 / 32;
 using FwdStages = Stages<FBM, FBN>;
-constexpr int kFwdRedBytes = 2 * FFN * 32 * 5 * 4;
+
+// Wave layout of the fused kernels: NW waves as NW/2 rows (vocabulary) x 2
+// columns (tokens) over the 256 x 128 tile; each wave holds FM x FN 32x32
+// blocks of z_s and of z_t.  Four waves: 128 x 64 per wave, 256 accumulator
+// registers, one wave per SIMD.  Eight waves: 64 x 64 per wave, 128
+// accumulator registers, two waves per SIMD (one can issue MFMAs while the
+// other waits on LDS or the DMA), for a third more fragment reads.
+template <int NW>
+struct Fused {
+  static constexpr int kThreads = 64 * NW;
+  static constexpr int kWM = NW / 2;
+  static constexpr int FM = FBM / kWM / 32, FN = FBN / 2 / 32;
+  static constexpr int kA = DmaRows<FBM, NW>::kPerWave, kB = DmaRows<FBN, NW>::kPerWave, ND = kA + kB;
+  static constexpr int kRedFloats = (kWM - 1) * 2 * FN * 32 * 5;
+};
 
 // Fold one tile's values of token column fn into the running statistics, one
 // 32x32 block (16 values per side) at a time: block max, rescale of the
 // running sums, then the block's exponentials.  Student and teacher go
 // through the same operations, so identical logits give identical
 // statistics (and A = 0 exactly).
-template <bool TAIL>
-__device__ __forceinline__ void fold_tile(const f32x16 (&zs)[FFM][FFN], const f32x16 (&zt)[FFM][FFN], int fn,
+template <bool TAIL, int FM, int FN>
+__device__ __forceinline__ void fold_tile(const f32x16 (&zs)[FM][FN], const f32x16 (&zt)[FM][FN], int fn,
                                           int vrow, int V, float& ms, float& ss, float& aa, float& mt, float& st) {
   // vrow = vocabulary index of fragment row 0 for this lane (block fm = 0)
 #pragma unroll
-  for (int fm = 0; fm < FFM; ++fm) {
+  for (int fm = 0; fm < FM; ++fm) {
     float tms = kNegBig, tmt = kNegBig;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
@@ -103,16 +116,16 @@ __device__ __forceinline__ void fold_tile(const f32x16 (&zs)[FFM][FFN], const f3
 }
 
 // Teacher logits read into the accumulator layout (teacher-logits payload).
-template <bool VEC4>
-__device__ __forceinline__ void load_zt(f32x16 (&zt)[FFM][FFN], const float* __restrict__ z_t, int N, int V,
+template <bool VEC4, int FM, int FN>
+__device__ __forceinline__ void load_zt(f32x16 (&zt)[FM][FN], const float* __restrict__ z_t, int N, int V,
                                         int vrow, int ncol, int lane) {
   (void)lane;
 #pragma unroll
-  for (int fn = 0; fn < FFN; ++fn) {
+  for (int fn = 0; fn < FN; ++fn) {
     const int n = ncol + fn * 32;
     const float* row = z_t + (int64_t)n * V;
 #pragma unroll
-    for (int fm = 0; fm < FFM; ++fm)
+    for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
         const int v = vrow + fm * 32 + 8 * g;
@@ -163,12 +176,13 @@ __device__ __forceinline__ void stream_advance(StreamPos& q, const DualOps& o) {
   }
 }
 
-constexpr int kStreamA = DmaRows<FBM>::kPerWave, kStreamB = DmaRows<FBN>::kPerWave;
-constexpr int kStreamND = kStreamA + kStreamB;
-
-template <class Epi>
-__device__ __forceinline__ void dual_stream(const DualOps& o, int njobs, char* lds, f32x16 (&zs)[FFM][FFN],
-                                            f32x16 (&zt)[FFM][FFN], int tid, int arow0, int brow0, Epi epi) {
+template <int NW, class Epi>
+__device__ __forceinline__ void dual_stream(const DualOps& o, int njobs, char* lds,
+                                            f32x16 (&zs)[Fused<NW>::FM][Fused<NW>::FN],
+                                            f32x16 (&zt)[Fused<NW>::FM][Fused<NW>::FN], int tid, int arow0, int brow0,
+                                            Epi epi) {
+  using F = Fused<NW>;
+  constexpr int FFM = F::FM, FFN = F::FN, kStreamA = F::kA, kStreamB = F::kB, kStreamND = F::ND;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int total = njobs * (o.nk[0] + o.nk[1]);
   const uint32_t lbase = lds_addr(lds);
@@ -193,9 +207,9 @@ __device__ __forceinline__ void dual_stream(const DualOps& o, int njobs, char* l
     const int nA = o.V - v0, nB = o.N - o.n0;
     const uint32_t ld2 = 2u * (uint32_t)ld;
 #pragma unroll
-    for (int q = 0; q < kStreamA; ++q) offA[q] = DmaRows<FBM>::lane_off(q, ld2, nA, lane, wave);
+    for (int q = 0; q < kStreamA; ++q) offA[q] = DmaRows<FBM, NW>::lane_off(q, ld2, nA, lane, wave);
 #pragma unroll
-    for (int q = 0; q < kStreamB; ++q) offB[q] = DmaRows<FBN>::lane_off(q, ld2, nB, lane, wave);
+    for (int q = 0; q < kStreamB; ++q) offB[q] = DmaRows<FBN, NW>::lane_off(q, ld2, nB, lane, wave);
   };
   seg_setup();
   // DMA instruction q of stream position dp into the stage at LDS address dst;
@@ -250,10 +264,12 @@ __device__ __forceinline__ void dual_stream(const DualOps& o, int njobs, char* l
   dma_barrier<0>();
 }
 
-template <int MODE, bool VEC4>   // MODE 0: hidden teacher; 1: teacher logits
-__global__ __launch_bounds__(kThreads, 1) void fwd_tiles(FwdParams p) {
+template <int MODE, bool VEC4, int NW>   // MODE 0: hidden teacher; 1: teacher logits
+__global__ __launch_bounds__(Fused<NW>::kThreads, 1) void fwd_tiles(FwdParams p) {
+  using F = Fused<NW>;
+  constexpr int FFM = F::FM, FFN = F::FN;
   __shared__ __attribute__((aligned(1024))) char lds[3 * FwdStages::kStage];
-  __shared__ __attribute__((aligned(16))) float red[kFwdRedBytes / 4];
+  __shared__ __attribute__((aligned(16))) float red[F::kRedFloats];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int logical = xcd_logical(blockIdx.x, p.nsplit * p.ntok);
   int split, tt;
@@ -268,23 +284,25 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(FwdParams p) {
   for (int fn = 0; fn < FFN; ++fn) { ms[fn] = kNegBig; ss[fn] = 0.f; aa[fn] = 0.f; mt[fn] = kNegBig; st[fn] = 0.f; }
 
   f32x16 zs[FFM][FFN], zt[FFM][FFN];
-  const int arow0 = wm * (FBM / 2), brow0 = wn * (FBN / 2);
+  const int arow0 = wm * (FBM / F::kWM), brow0 = wn * (FBN / 2);
   const int lrow = 4 * (lane >> 5);
   DualOps o;
   o.W[0] = p.W_s; o.h[0] = p.h_s; o.H[0] = p.Hs; o.nk[0] = p.Hs / kKT;
   o.W[1] = p.W_t; o.h[1] = p.h_t; o.H[1] = p.Ht; o.nk[1] = MODE == 0 ? p.Ht / kKT : 0;
   o.V = p.V; o.N = p.N; o.n0 = n0; o.v0 = vt0 * FBM;
 
-  dual_stream(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, [&](int job) {
+  dual_stream<NW>(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, [&](int job) {
     const int v0 = (vt0 + job) * FBM;
     if (MODE == 1) load_zt<VEC4>(zt, p.z_t, p.N, p.V, v0 + arow0 + lrow, n0 + brow0 + (lane & 31), lane);
     const int vrow = v0 + arow0 + lrow;
     if (v0 + FBM <= p.V) {
 #pragma unroll
-      for (int fn = 0; fn < FFN; ++fn) fold_tile<false>(zs, zt, fn, vrow, p.V, ms[fn], ss[fn], aa[fn], mt[fn], st[fn]);
+      for (int fn = 0; fn < FFN; ++fn)
+        fold_tile<false>(zs, zt, fn, vrow, p.V, ms[fn], ss[fn], aa[fn], mt[fn], st[fn]);
     } else {
 #pragma unroll
-      for (int fn = 0; fn < FFN; ++fn) fold_tile<true>(zs, zt, fn, vrow, p.V, ms[fn], ss[fn], aa[fn], mt[fn], st[fn]);
+      for (int fn = 0; fn < FFN; ++fn)
+        fold_tile<true>(zs, zt, fn, vrow, p.V, ms[fn], ss[fn], aa[fn], mt[fn], st[fn]);
     }
   });
 
@@ -296,11 +314,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(FwdParams p) {
     merge3(ms[fn], ss[fn], aa[fn], oms, oss, oaa);
     merge2(mt[fn], st[fn], omt, ost);
   }
-  // merge the two waves that hold the same tokens (wm = 0 and wm = 1)
-  if (wm == 1 && lane < 32) {
+  // merge the waves that hold the same tokens (wm = 1 .. kWM-1 into wm = 0,
+  // in that order)
+  if (wm > 0 && lane < 32) {
 #pragma unroll
     for (int fn = 0; fn < FFN; ++fn) {
-      float* q = red + ((wn * FFN + fn) * 32 + lane) * 5;
+      float* q = red + ((((wm - 1) * 2 + wn) * FFN + fn) * 32 + lane) * 5;
       q[0] = ms[fn]; q[1] = ss[fn]; q[2] = aa[fn]; q[3] = mt[fn]; q[4] = st[fn];
     }
   }
@@ -308,9 +327,12 @@ __global__ __launch_bounds__(kThreads, 1) void fwd_tiles(FwdParams p) {
   if (wm == 0 && lane < 32) {
 #pragma unroll
     for (int fn = 0; fn < FFN; ++fn) {
-      const float* q = red + ((wn * FFN + fn) * 32 + lane) * 5;
-      merge3(ms[fn], ss[fn], aa[fn], q[0], q[1], q[2]);
-      merge2(mt[fn], st[fn], q[3], q[4]);
+#pragma unroll
+      for (int r = 1; r < F::kWM; ++r) {
+        const float* q = red + ((((r - 1) * 2 + wn) * FFN + fn) * 32 + lane) * 5;
+        merge3(ms[fn], ss[fn], aa[fn], q[0], q[1], q[2]);
+        merge2(mt[fn], st[fn], q[3], q[4]);
+      }
       const int n = n0 + brow0 + fn * 32 + lane;
       if (n < p.N) {
         float* P = p.partial + (int64_t)split * 5 * p.N + n;
@@ -406,8 +428,10 @@ __global__ __launch_bounds__(1024) void grad_scale(const float* __restrict__ gra
 // (column = v - c0).  Columns in [width, kpad) are written as zero; rows with
 // row_mask 0 are zero.
 // ===========================================================================
-template <int MODE, bool VEC4>
-__global__ __launch_bounds__(kThreads, 1) void bwd_dz_tiles(BwdParams p) {
+template <int MODE, bool VEC4, int NW>
+__global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams p) {
+  using F = Fused<NW>;
+  constexpr int FFM = F::FM, FFN = F::FN;
   __shared__ __attribute__((aligned(1024))) char lds[3 * FwdStages::kStage];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int logical = xcd_logical(blockIdx.x, p.ngroups * p.ntok);
@@ -416,7 +440,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz_tiles(BwdParams p) {
   const int vt0 = grp * p.tiles_per_group;
   const int vt1 = min(vt0 + p.tiles_per_group, p.ntv);
   const int n0 = tt * FBN;
-  const int arow0 = wm * (FBM / 2), brow0 = wn * (FBN / 2);
+  const int arow0 = wm * (FBM / F::kWM), brow0 = wn * (FBN / 2);
   const int lrow = 4 * (lane >> 5);
 
   // per-token constants of this lane's token columns
@@ -441,7 +465,7 @@ __global__ __launch_bounds__(kThreads, 1) void bwd_dz_tiles(BwdParams p) {
   o.W[1] = p.W_t; o.h[1] = p.h_t; o.H[1] = p.Ht; o.nk[1] = MODE == 0 ? p.Ht / kKT : 0;
   o.V = p.V; o.N = p.N; o.n0 = n0; o.v0 = p.c0 + vt0 * FBM;
 
-  dual_stream(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, [&](int job) {
+  dual_stream<NW>(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, [&](int job) {
     const int v0 = p.c0 + (vt0 + job) * FBM;
     if (MODE == 1) load_zt<VEC4>(zt, p.z_t, p.N, p.V, v0 + arow0 + lrow, n0 + brow0 + (lane & 31), lane);
     // Lane l (l < 32) holds rows {0-3, 8-11, 16-19, 24-27} of each 32-row
@@ -749,15 +773,23 @@ static inline unsigned grid1(int64_t n, int64_t per, int64_t cap) {
   return (unsigned)g;
 }
 
-hipError_t launch_fwd_tiles(const FwdParams& p, bool teacher_logits, hipStream_t s) {
-  const unsigned nb = (unsigned)(p.nsplit * p.ntok);
-  const bool vec4 = (p.V % 4) == 0;
+template <int NW>
+static void fwd_tiles_launch(const FwdParams& p, bool teacher_logits, unsigned nb, hipStream_t s) {
+  constexpr unsigned nt = Fused<NW>::kThreads;
   if (!teacher_logits)
-    fwd_tiles<0, true><<<nb, kThreads, 0, s>>>(p);
-  else if (vec4)
-    fwd_tiles<1, true><<<nb, kThreads, 0, s>>>(p);
+    fwd_tiles<0, true, NW><<<nb, nt, 0, s>>>(p);
+  else if (p.V % 4 == 0)
+    fwd_tiles<1, true, NW><<<nb, nt, 0, s>>>(p);
   else
-    fwd_tiles<1, false><<<nb, kThreads, 0, s>>>(p);
+    fwd_tiles<1, false, NW><<<nb, nt, 0, s>>>(p);
+}
+
+hipError_t launch_fwd_tiles(const FwdParams& p, bool teacher_logits, int waves, hipStream_t s) {
+  const unsigned nb = (unsigned)(p.nsplit * p.ntok);
+  if (waves == 8)
+    fwd_tiles_launch<8>(p, teacher_logits, nb, s);
+  else
+    fwd_tiles_launch<4>(p, teacher_logits, nb, s);
   return hipGetLastError();
 }
 
@@ -767,15 +799,23 @@ hipError_t launch_fwd_combine(const float* partial, int nsplit, int N, const uin
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dz(const BwdParams& p, bool teacher_logits, hipStream_t s) {
-  const unsigned nb = (unsigned)(p.ngroups * p.ntok);
-  const bool vec4 = (p.V % 4) == 0;
+template <int NW>
+static void bwd_dz_launch(const BwdParams& p, bool teacher_logits, unsigned nb, hipStream_t s) {
+  constexpr unsigned nt = Fused<NW>::kThreads;
   if (!teacher_logits)
-    bwd_dz_tiles<0, true><<<nb, kThreads, 0, s>>>(p);
-  else if (vec4)
-    bwd_dz_tiles<1, true><<<nb, kThreads, 0, s>>>(p);
+    bwd_dz_tiles<0, true, NW><<<nb, nt, 0, s>>>(p);
+  else if (p.V % 4 == 0)
+    bwd_dz_tiles<1, true, NW><<<nb, nt, 0, s>>>(p);
   else
-    bwd_dz_tiles<1, false><<<nb, kThreads, 0, s>>>(p);
+    bwd_dz_tiles<1, false, NW><<<nb, nt, 0, s>>>(p);
+}
+
+hipError_t launch_bwd_dz(const BwdParams& p, bool teacher_logits, int waves, hipStream_t s) {
+  const unsigned nb = (unsigned)(p.ngroups * p.ntok);
+  if (waves == 8)
+    bwd_dz_launch<8>(p, teacher_logits, nb, s);
+  else
+    bwd_dz_launch<4>(p, teacher_logits, nb, s);
   return hipGetLastError();
 }
 

@@ -187,9 +187,9 @@ __device__ __forceinline__ void dma_iter(f32x16 (&acc)[FM][FN], ELEM (&a)[2][FM]
 // LDS row 8*blk + l/8, physical chunk l%8, so it loads logical chunk
 // (l%8) ^ swizzle(row) of that row: the swizzled layout comes out of the DMA
 // as is.
-template <int R>
+template <int R, int NW = kThreads / 64>
 struct DmaRows {
-  static constexpr int kPerWave = R * kLdsRow / 1024 / (kThreads / 64);
+  static constexpr int kPerWave = R * kLdsRow / 1024 / NW;
   static_assert(kPerWave >= 1, "tile too small");
   // byte offset of this lane's 16 bytes for DMA instruction q, relative to
   // (row 0, k-tile start); rows past nrows (nrows >= 1) repeat row nrows-1:
