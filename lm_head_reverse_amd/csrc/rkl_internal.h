@@ -78,8 +78,8 @@ hipError_t launch_bwd_dz(const BwdParams& p, bool teacher_logits, int waves, hip
 hipError_t launch_grad_scale(const float* grad, const uint8_t* row_mask, const float* stats, int N, float* out,
                              hipStream_t s);
 hipError_t launch_transpose_h(const uint16_t* h, int N, int H, uint16_t* hT, int ldT, hipStream_t s);
-hipError_t launch_dw(const DwParams& p, hipStream_t s);
-hipError_t launch_dh(const DhParams& p, bool ragged, hipStream_t s);
+hipError_t launch_dw(const DwParams& p, int waves, hipStream_t s);
+hipError_t launch_dh(const DhParams& p, bool ragged, int waves, hipStream_t s);
 hipError_t launch_fwd_rows_logits(const float* z_s, const float* z_t, int N, int V, const uint8_t* row_mask,
                                   float* loss, float* stats, hipStream_t s);
 hipError_t launch_bwd_rows_logits(const float* z_s, const float* z_t, int N, int V, const uint8_t* row_mask,

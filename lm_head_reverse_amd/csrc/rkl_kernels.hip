@@ -541,15 +541,19 @@ __global__ __launch_bounds__(256) void transpose_h(const uint16_t* __restrict__ 
 // ===========================================================================
 constexpr int WBM = kDwTileM, WBN = kDwTileN, WNST = 2, WDSTEPS = 2;
 
-__global__ __launch_bounds__(kThreads, 1) void dw_gemm(DwParams p) {
-  using TA = MN<WBM>;
-  using TB = KM<WBN>;
+template <int NW>
+__global__ __launch_bounds__(64 * NW, 1) void dw_gemm(DwParams p) {
+  // NW = 4: waves 2 x 2, 128 x 128 each; NW = 8: waves 4 (m) x 2 (n), 64 x 128
+  // each (A, read transposed, is the operand with fewer fragments)
+  constexpr int WGN = 2, WGM = NW / WGN;
+  using TA = MN<WBM, NW>;
+  using TB = KM<WBN, NW>;
   __shared__ __attribute__((aligned(1024))) char lds[WNST * (TA::kBytes + TB::kBytes)];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / WGN, wn = w % WGN;
   const int logical = xcd_logical(blockIdx.x, p.ntm * p.ntn);
   const int tm = logical / p.ntn, tn = logical - tm * p.ntn;
   const int m0 = tm * WBM, n0 = tn * WBN;
-  constexpr int FM = WBM / 64, FN = WBN / 64;
+  constexpr int FM = WBM / WGM / 32, FN = WBN / WGN / 32;
   f32x16 acc[FM][FN];
   zero_acc(acc);
   // A: dz rows are tokens (k, zero-padded to the workspace's row count >=
@@ -559,18 +563,18 @@ __global__ __launch_bounds__(kThreads, 1) void dw_gemm(DwParams p) {
   ta.init(p.dz + m0, p.ldz, p.kpad - m0, lane, __builtin_amdgcn_readfirstlane(w));
   TB tb;
   tb.init(p.hT + (int64_t)n0 * p.ldT, p.ldT, p.H - n0, lane, __builtin_amdgcn_readfirstlane(w));
-  gemm_loop<TA, TB, f16x8, false, WNST, false, WDSTEPS>(acc, p.ldT / kKT, lds, ta, tb, 0, tid, wm * (WBM / 2),
-                                                       wn * (WBN / 2));
+  gemm_loop<TA, TB, f16x8, false, WNST, false, WDSTEPS>(acc, p.ldT / kKT, lds, ta, tb, 0, tid, wm * (WBM / WGM),
+                                                       wn * (WBN / WGN));
   const float inv = p.gscale[1];
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
-    const int n = n0 + wn * (WBN / 2) + fn * 32 + (lane & 31);
+    const int n = n0 + wn * (WBN / WGN) + fn * 32 + (lane & 31);
     if (n >= p.H) continue;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int m = m0 + wm * (WBM / 2) + fm * 32 + frag_row(i, lane);
+        const int m = m0 + wm * (WBM / WGM) + fm * 32 + frag_row(i, lane);
         if (m < p.width) {
           float* o = p.dW + (int64_t)m * p.H + n;
           const float d = acc[fm][fn][i] * inv;
@@ -588,16 +592,18 @@ __global__ __launch_bounds__(kThreads, 1) void dw_gemm(DwParams p) {
 // ===========================================================================
 constexpr int HBM = kDhTileM, HBN = kDhTileN, HNST = 3;
 
-template <bool RAGGED>
-__global__ __launch_bounds__(kThreads, 1) void dh_gemm(DhParams p) {
-  using TA = KM<HBM>;
-  using TB = MN<HBN>;
+template <bool RAGGED, int NW>
+__global__ __launch_bounds__(64 * NW, 1) void dh_gemm(DhParams p) {
+  // NW = 4: waves 2 x 2, 128 x 64 each; NW = 8: waves 4 (m) x 2 (n), 64 x 64 each
+  constexpr int HGM = NW / 2, HGN = 2;
+  using TA = KM<HBM, NW>;
+  using TB = MN<HBN, NW>;
   __shared__ __attribute__((aligned(1024))) char lds[HNST * (TA::kBytes + TB::kBytes)];
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / HGN, wn = w % HGN;
   const int logical = xcd_logical(blockIdx.x, p.ntm * p.ntn);
   const int tm = logical / p.ntn, tn = logical - tm * p.ntn;
   const int m0 = tm * HBM, n0 = tn * HBN;
-  constexpr int FM = HBM / 64, FN = HBN / 64;
+  constexpr int FM = HBM / HGM / 32, FN = HBN / HGN / 32;
   f32x16 acc[FM][FN];
   zero_acc(acc);
   // A: dz rows are tokens (m; npad zero-padded rows), columns vocabulary (k,
@@ -607,18 +613,18 @@ __global__ __launch_bounds__(kThreads, 1) void dh_gemm(DhParams p) {
   ta.init(p.dz + (int64_t)m0 * p.ldz, p.ldz, p.npad - m0, lane, __builtin_amdgcn_readfirstlane(w));
   TB tb;
   tb.init(p.Wc + n0, p.H, p.H - n0, lane, __builtin_amdgcn_readfirstlane(w));
-  gemm_loop<TA, TB, f16x8, true, HNST, RAGGED>(acc, p.kpad / kKT, lds, ta, tb, p.width, tid, wm * (HBM / 2),
-                                              wn * (HBN / 2));
+  gemm_loop<TA, TB, f16x8, true, HNST, RAGGED>(acc, p.kpad / kKT, lds, ta, tb, p.width, tid, wm * (HBM / HGM),
+                                              wn * (HBN / HGN));
   const float inv = p.gscale[1];
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
-    const int n = n0 + wn * (HBN / 2) + fn * 32 + (lane & 31);
+    const int n = n0 + wn * (HBN / HGN) + fn * 32 + (lane & 31);
     if (n >= p.H) continue;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const int m = m0 + wm * (HBM / 2) + fm * 32 + frag_row(i, lane);
+        const int m = m0 + wm * (HBM / HGM) + fm * 32 + frag_row(i, lane);
         if (m < p.N) {
           float* o = p.dh + (int64_t)m * p.H + n;
           const float d = acc[fm][fn][i] * inv;
@@ -831,16 +837,23 @@ hipError_t launch_transpose_h(const uint16_t* h, int N, int H, uint16_t* hT, int
   return hipGetLastError();
 }
 
-hipError_t launch_dw(const DwParams& p, hipStream_t s) {
-  dw_gemm<<<(unsigned)(p.ntm * p.ntn), kThreads, 0, s>>>(p);
+hipError_t launch_dw(const DwParams& p, int waves, hipStream_t s) {
+  if (waves == 8)
+    dw_gemm<8><<<(unsigned)(p.ntm * p.ntn), 512, 0, s>>>(p);
+  else
+    dw_gemm<4><<<(unsigned)(p.ntm * p.ntn), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 
-hipError_t launch_dh(const DhParams& p, bool ragged, hipStream_t s) {
-  if (ragged)
-    dh_gemm<true><<<(unsigned)(p.ntm * p.ntn), kThreads, 0, s>>>(p);
-  else
-    dh_gemm<false><<<(unsigned)(p.ntm * p.ntn), kThreads, 0, s>>>(p);
+hipError_t launch_dh(const DhParams& p, bool ragged, int waves, hipStream_t s) {
+  const unsigned nb = (unsigned)(p.ntm * p.ntn);
+  if (waves == 8) {
+    if (ragged) dh_gemm<true, 8><<<nb, 512, 0, s>>>(p);
+    else dh_gemm<false, 8><<<nb, 512, 0, s>>>(p);
+  } else {
+    if (ragged) dh_gemm<true, 4><<<nb, 256, 0, s>>>(p);
+    else dh_gemm<false, 4><<<nb, 256, 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 

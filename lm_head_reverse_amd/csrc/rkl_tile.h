@@ -215,12 +215,12 @@ struct DmaRows {
 // sits at physical chunk c ^ 4(k & 3), so the 8 rows x 4 chunks that one
 // transposing read touches fall on distinct bank groups twice at most.
 // ---------------------------------------------------------------------------
-template <int R>
+template <int R, int NW = kThreads / 64>
 struct MN {
   static_assert(R >= 128 && R % 128 == 0, "MN-major tiles need >= 128 columns");
   static constexpr int kRowBytes = R * 2;
   static constexpr int kBytes = kKT * kRowBytes;
-  static constexpr int kPerWave = kBytes / 1024 / (kThreads / 64);
+  static constexpr int kPerWave = kBytes / 1024 / NW;
   __device__ __forceinline__ static int lds_pos(int k, int chunk) {
     return k * kRowBytes + ((chunk ^ ((k & 3) << 2)) << 4);
   }
@@ -278,10 +278,10 @@ struct MN {
 };
 
 // K-major tiles (R rows x 64 k, swizzled rows of 128 bytes) for the generic GEMM.
-template <int R>
+template <int R, int NW = kThreads / 64>
 struct KM {
   static constexpr int kBytes = R * kLdsRow;
-  static constexpr int kPerWave = DmaRows<R>::kPerWave;
+  static constexpr int kPerWave = DmaRows<R, NW>::kPerWave;
   // DMA state: base = element (row 0, k 0) of this tile's row block in a
   // row-major [rows, ld] matrix, nrows valid rows from there.
   const uint16_t* base;
@@ -289,7 +289,7 @@ struct KM {
   __device__ __forceinline__ void init(const uint16_t* b, int ld, int nrows, int lane, int wave) {
     base = b;
 #pragma unroll
-    for (int q = 0; q < kPerWave; ++q) off[q] = DmaRows<R>::lane_off(q, 2u * (uint32_t)ld, nrows, lane, wave);
+    for (int q = 0; q < kPerWave; ++q) off[q] = DmaRows<R, NW>::lane_off(q, 2u * (uint32_t)ld, nrows, lane, wave);
   }
   __device__ __forceinline__ void issue(int kt, uint32_t dst, int q, int wave) const {
     dma16(base + kt * kKT, off[q], dst + (uint32_t)((wave * kPerWave + q) * 1024));
