@@ -113,7 +113,7 @@ size_t fwd_ws_bytes(int64_t N, int64_t V, bool tiled) {
 
 struct BwdLayout {
   int64_t ldT, ldz, npad;
-  size_t off_hT, off_dz, off_scale, total;
+  size_t off_hT, off_dz, off_w16, off_scale, total;
 };
 // [dz scale: 2 floats][hT: Hs x ldT fp16][dz chunk: npad x ldz fp16]; npad =
 // N rounded up to the 128-token tile (the dz kernel writes those rows as zero)
@@ -126,7 +126,9 @@ BwdLayout bwd_layout(int64_t N, int64_t V, int64_t Hs) {
   L.off_scale = 0;
   L.off_hT = 256;
   L.off_dz = L.off_hT + align256((size_t)Hs * L.ldT * 2);
-  L.total = L.off_dz + align256((size_t)L.npad * L.ldz * 2);
+  L.off_w16 = L.off_dz + align256((size_t)L.npad * L.ldz * 2);
+  // the fp16 W_s copy covers every 256-row vocabulary tile of a chunk
+  L.total = L.off_w16 + align256((size_t)round_up(L.ldz, rkl::kFwdTileV) * Hs * 2);
   return L;
 }
 
@@ -213,6 +215,7 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
   float* gscale = reinterpret_cast<float*>(base + L.off_scale);
   uint16_t* hT = reinterpret_cast<uint16_t*>(base + L.off_hT);
   uint16_t* dz = reinterpret_cast<uint16_t*>(base + L.off_dz);
+  uint16_t* w16 = reinterpret_cast<uint16_t*>(base + L.off_w16);
   RKL_TRY(rkl::launch_grad_scale(grad, row_mask, stats, (int)N, gscale, s));
   RKL_TRY(rkl::launch_transpose_h(h_s, (int)N, (int)Hs, hT, (int)L.ldT, s));
   const int64_t C = vocab_chunk();
@@ -223,7 +226,7 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
     b.N = (int)N; b.V = (int)V; b.Hs = (int)Hs; b.Ht = (int)Ht;
     b.h_s = h_s; b.W_s = W_s; b.h_t = h_t; b.W_t = W_t; b.z_t = z_t;
     b.row_mask = row_mask; b.grad = grad; b.stats = stats;
-    b.gscale = gscale; b.dz = dz; b.ldz = (int)L.ldz; b.c0 = (int)c0; b.kpad = (int)kpad;
+    b.gscale = gscale; b.dz = dz; b.w16 = w16; b.ldz = (int)L.ldz; b.c0 = (int)c0; b.kpad = (int)kpad;
     b.ntv = (int)ceil_div(kpad, rkl::kFwdTileV);
     b.tiles_per_group = bwd_tiles_per_group();
     b.ngroups = (int)ceil_div(b.ntv, b.tiles_per_group);
@@ -243,10 +246,10 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
     rkl::DhParams h{};
     h.gscale = gscale; h.dz = dz; h.ldz = (int)L.ldz; h.N = (int)N; h.npad = (int)L.npad; h.kpad = (int)kpad;
     h.width = (int)width;
-    h.Wc = W_s + c0 * Hs; h.H = (int)Hs; h.dh = dh; h.accumulate = c0 > 0;
+    h.w16 = w16; h.H = (int)Hs; h.dh = dh; h.accumulate = c0 > 0;
     h.ntm = (int)ceil_div(N, rkl::kDhTileM);
     h.ntn = (int)ceil_div(Hs, rkl::kDhTileN);
-    RKL_TRY(rkl::launch_dh(h, c0 + kpad > V, gemm_waves("RKL_DH_WAVES", 4), s));
+    RKL_TRY(rkl::launch_dh(h, gemm_waves("RKL_DH_WAVES", 4), s));
   }
   return RKL_OK;
 }

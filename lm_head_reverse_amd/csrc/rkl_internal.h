@@ -33,6 +33,7 @@ struct BwdParams {
   const float* stats;
   const float* gscale;     // [2]: s, 1/s (powers of two); dz is stored as fp16(s * dz)
   uint16_t* dz;            // [ntok * 128, ldz] fp16 chunk workspace (rows past N written as zero)
+  uint16_t* w16;           // [ntv * 256, Hs] fp16 copy of the W_s chunk (for dh)
   int ldz;
   int c0;                  // first vocabulary row of the chunk
   int kpad;                // chunk width rounded up to 64 (columns written)
@@ -58,7 +59,7 @@ struct DhParams {
   const float* gscale;
   const uint16_t* dz;
   int ldz, N, npad, kpad, width;   // npad: dz workspace rows
-  const uint16_t* Wc;      // W_s + c0 * H
+  const uint16_t* w16;     // fp16 copy of the W_s chunk [>= kpad rows, H]
   int H;
   float* dh;
   int accumulate;
@@ -79,7 +80,7 @@ hipError_t launch_grad_scale(const float* grad, const uint8_t* row_mask, const f
                              hipStream_t s);
 hipError_t launch_transpose_h(const uint16_t* h, int N, int H, uint16_t* hT, int ldT, hipStream_t s);
 hipError_t launch_dw(const DwParams& p, int waves, hipStream_t s);
-hipError_t launch_dh(const DhParams& p, bool ragged, int waves, hipStream_t s);
+hipError_t launch_dh(const DhParams& p, int waves, hipStream_t s);
 hipError_t launch_fwd_rows_logits(const float* z_s, const float* z_t, int N, int V, const uint8_t* row_mask,
                                   float* loss, float* stats, hipStream_t s);
 hipError_t launch_bwd_rows_logits(const float* z_s, const float* z_t, int N, int V, const uint8_t* row_mask,

@@ -176,11 +176,20 @@ __device__ __forceinline__ void stream_advance(StreamPos& q, const DualOps& o) {
   }
 }
 
-template <int NW, class Epi>
+// No per-k-tile work besides the MFMAs.
+struct NoTileHook {
+  __device__ __forceinline__ void operator()(const char*, int, int) const {}
+};
+
+// hook(stage, job, kt) runs after each student k-tile: `stage` still holds
+// that tile, and every wave has passed the barrier after which the tile is
+// complete.  The next k-tile's DMA writes `stage`, so a hook that reads it
+// must end with a workgroup barrier whenever it reads.
+template <int NW, class Epi, class Hook = NoTileHook>
 __device__ __forceinline__ void dual_stream(const DualOps& o, int njobs, char* lds,
                                             f32x16 (&zs)[Fused<NW>::FM][Fused<NW>::FN],
                                             f32x16 (&zt)[Fused<NW>::FM][Fused<NW>::FN], int tid, int arow0, int brow0,
-                                            Epi epi) {
+                                            Epi epi, Hook hook = Hook{}) {
   using F = Fused<NW>;
   constexpr int FFM = F::FM, FFN = F::FN, kStreamA = F::kA, kStreamB = F::kB, kStreamND = F::ND;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -254,7 +263,11 @@ __device__ __forceinline__ void dual_stream(const DualOps& o, int njobs, char* l
   };
   for (int job = 0; job < njobs; ++job) {
     zero_acc(zs);
-    for (int kt = 0; kt < o.nk[0]; ++kt) step(zs);
+    for (int kt = 0; kt < o.nk[0]; ++kt) {
+      const char* consumed = lds + ocur;
+      step(zs);
+      hook(consumed, job, kt);
+    }
     if (o.nk[1] > 0) {
       zero_acc(zt);
       for (int kt = 0; kt < o.nk[1]; ++kt) step(zt);
@@ -465,6 +478,25 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
   o.W[1] = p.W_t; o.h[1] = p.h_t; o.H[1] = p.Ht; o.nk[1] = MODE == 0 ? p.Ht / kKT : 0;
   o.V = p.V; o.N = p.N; o.n0 = n0; o.v0 = p.c0 + vt0 * FBM;
 
+  // fp16 copy of this workgroup's share of the W_s chunk for the dh GEMM:
+  // of each vocabulary tile's Hs/64 student k-tiles, token tile tt converts
+  // those with kt = tt (mod ntok), so every (tile, k-tile) is written once.
+  // Rows past V hold the clamped copies of row V-1 the DMA brought in.
+  auto convert_w = [&](const char* stage, int job, int kt) {
+    if (kt % p.ntok != tt % p.ntok) return;
+    uint16_t* dst = p.w16 + (int64_t)(vt0 + job) * FBM * p.Hs + kt * kKT;
+#pragma unroll
+    for (int i = 0; i < FBM * 8 / F::kThreads; ++i) {
+      const int pr = tid + i * F::kThreads;
+      const int r = pr >> 3, c = pr & 7;
+      const u32x4 x = *reinterpret_cast<const u32x4*>(stage + lds_off(r, c));
+      *reinterpret_cast<f16x8*>(dst + (int64_t)r * p.Hs + c * 8) = bf16_to_f16(__builtin_bit_cast(bf16x8, x));
+    }
+    // the next k-tile's DMA writes this stage: every wave's reads first
+    // (the condition above is the same for the whole workgroup)
+    dma_barrier<63>();
+  };
+
   dual_stream<NW>(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, [&](int job) {
     const int v0 = p.c0 + (vt0 + job) * FBM;
     if (MODE == 1) load_zt<VEC4>(zt, p.z_t, p.N, p.V, v0 + arow0 + lrow, n0 + brow0 + (lane & 31), lane);
@@ -510,7 +542,7 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
         }
       }
     }
-  });
+  }, convert_w);
 }
 
 // h_s [N, H] bf16 -> hT [H, ldT] fp16 (exact for values in fp16's normal
@@ -592,7 +624,7 @@ __global__ __launch_bounds__(64 * NW, 1) void dw_gemm(DwParams p) {
 // ===========================================================================
 constexpr int HBM = kDhTileM, HBN = kDhTileN, HNST = 3;
 
-template <bool RAGGED, int NW>
+template <int NW>
 __global__ __launch_bounds__(64 * NW, 1) void dh_gemm(DhParams p) {
   // NW = 4: waves 2 x 2, 128 x 64 each; NW = 8: waves 4 (m) x 2 (n), 64 x 64 each
   constexpr int HGM = NW / 2, HGN = 2;
@@ -607,14 +639,13 @@ __global__ __launch_bounds__(64 * NW, 1) void dh_gemm(DhParams p) {
   f32x16 acc[FM][FN];
   zero_acc(acc);
   // A: dz rows are tokens (m; npad zero-padded rows), columns vocabulary (k,
-  // zero past the chunk width); B: the W_s chunk, rows vocabulary (k),
-  // columns hidden units (n).  RAGGED: the chunk's last k-tile runs past V.
+  // zero past the chunk width); B: the fp16 copy of the W_s chunk, rows
+  // vocabulary (k; the copy covers every k-tile), columns hidden units (n).
   TA ta;
   ta.init(p.dz + (int64_t)m0 * p.ldz, p.ldz, p.npad - m0, lane, __builtin_amdgcn_readfirstlane(w));
   TB tb;
-  tb.init(p.Wc + n0, p.H, p.H - n0, lane, __builtin_amdgcn_readfirstlane(w));
-  gemm_loop<TA, TB, f16x8, true, HNST, RAGGED>(acc, p.kpad / kKT, lds, ta, tb, p.width, tid, wm * (HBM / HGM),
-                                              wn * (HBN / HGN));
+  tb.init(p.w16 + n0, p.H, p.H - n0, lane, __builtin_amdgcn_readfirstlane(w));
+  gemm_loop<TA, TB, f16x8, false, HNST>(acc, p.kpad / kKT, lds, ta, tb, 0, tid, wm * (HBM / HGM), wn * (HBN / HGN));
   const float inv = p.gscale[1];
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
@@ -845,15 +876,12 @@ hipError_t launch_dw(const DwParams& p, int waves, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_dh(const DhParams& p, bool ragged, int waves, hipStream_t s) {
+hipError_t launch_dh(const DhParams& p, int waves, hipStream_t s) {
   const unsigned nb = (unsigned)(p.ntm * p.ntn);
-  if (waves == 8) {
-    if (ragged) dh_gemm<true, 8><<<nb, 512, 0, s>>>(p);
-    else dh_gemm<false, 8><<<nb, 512, 0, s>>>(p);
-  } else {
-    if (ragged) dh_gemm<true, 4><<<nb, 256, 0, s>>>(p);
-    else dh_gemm<false, 4><<<nb, 256, 0, s>>>(p);
-  }
+  if (waves == 8)
+    dh_gemm<8><<<nb, 512, 0, s>>>(p);
+  else
+    dh_gemm<4><<<nb, 256, 0, s>>>(p);
   return hipGetLastError();
 }
 

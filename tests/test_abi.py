@@ -47,8 +47,10 @@ def test_workspace_sizes():
     b = R.workspace_bytes(4096, 151936, 2048, 2048)
     assert 0 < a < b
     # bounded: the [N, V] logits are never materialised (4096 x 151936 fp32 =
-    # 2.49 GB); the backward keeps a 65536-column fp16 dz chunk
-    assert b < 4096 * 151936 * 4 / 4
+    # 2.49 GB); the backward keeps one 65536-column fp16 dz chunk and an fp16
+    # copy of that chunk of W_s (0.82 GB together at N = 4096)
+    assert b < 4096 * 151936 * 4 / 2
+    assert b < 4096 * 65536 * 2 + 65536 * 2048 * 2 + 2048 * 4096 * 2 + (1 << 20)
     assert R.workspace_bytes(4096, 151936, 2048, 2048) == R.workspace_bytes(4096, 151936, 2048, 4096)
     assert R.workspace_bytes(-1, 10, 64, 64) == 0
 
