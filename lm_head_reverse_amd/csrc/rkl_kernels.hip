@@ -181,6 +181,9 @@ struct NoTileHook {
   __device__ __forceinline__ void operator()(const char*, int, int) const {}
 };
 
+// epi(job, stage) runs after each job's last k-tile; `stage` is an LDS stage
+// it may use as scratch (it must end with a workgroup barrier if it does,
+// since the next k-tile's DMA writes it).
 // hook(stage, job, kt) runs after each student k-tile: `stage` still holds
 // that tile, and every wave has passed the barrier after which the tile is
 // complete.  The next k-tile's DMA writes `stage`, so a hook that reads it
@@ -272,7 +275,8 @@ __device__ __forceinline__ void dual_stream(const DualOps& o, int njobs, char* l
       zero_acc(zt);
       for (int kt = 0; kt < o.nk[1]; ++kt) step(zt);
     }
-    epi(job);
+    // the stage just consumed is free until the next k-tile's DMA
+    epi(job, lds + opre);
   }
   dma_barrier<0>();
 }
@@ -304,7 +308,7 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void fwd_tiles(FwdParams p)
   o.W[1] = p.W_t; o.h[1] = p.h_t; o.H[1] = p.Ht; o.nk[1] = MODE == 0 ? p.Ht / kKT : 0;
   o.V = p.V; o.N = p.N; o.n0 = n0; o.v0 = vt0 * FBM;
 
-  dual_stream<NW>(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, [&](int job) {
+  dual_stream<NW>(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, [&](int job, char*) {
     const int v0 = (vt0 + job) * FBM;
     if (MODE == 1) load_zt<VEC4>(zt, p.z_t, p.N, p.V, v0 + arow0 + lrow, n0 + brow0 + (lane & 31), lane);
     const int vrow = v0 + arow0 + lrow;
@@ -497,23 +501,22 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
     dma_barrier<63>();
   };
 
-  dual_stream<NW>(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, [&](int job) {
+  dual_stream<NW>(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, [&](int job, char* stage) {
     const int v0 = p.c0 + (vt0 + job) * FBM;
     if (MODE == 1) load_zt<VEC4>(zt, p.z_t, p.N, p.V, v0 + arow0 + lrow, n0 + brow0 + (lane & 31), lane);
-    // Lane l (l < 32) holds rows {0-3, 8-11, 16-19, 24-27} of each 32-row
-    // block, lane l + 32 rows {4-7, 12-15, 20-23, 28-31}, same token.  One
-    // permlane32 swap per dword leaves lane l with rows 0-7 and 16-23, lane
-    // l + 32 with rows 8-15 and 24-31: each lane then stores two runs of 8
-    // consecutive vocabulary entries (16 bytes each).
+    // dz of this lane's elements, rounded to fp16 and packed in pairs.  Lane
+    // l (l < 32) holds rows {0-3, 8-11, 16-19, 24-27} of each 32-row block,
+    // lane l + 32 rows {4-7, 12-15, 20-23, 28-31}, same token; one permlane32
+    // swap per dword leaves lane l with rows 0-7 and 16-23, lane l + 32 with
+    // rows 8-15 and 24-31: runs of 8 consecutive vocabulary entries.
     const int hi = lane >> 5;
+    uint32_t pk[FFM][FFN][2][4];   // [fm][fn][run][dword]
 #pragma unroll
     for (int fn = 0; fn < FFN; ++fn) {
-      const int n = n0 + brow0 + fn * 32 + (lane & 31);   // < ntok * 128 = rows of the dz workspace
-      uint16_t* drow = p.dz + (int64_t)n * p.ldz;
 #pragma unroll
       for (int fm = 0; fm < FFM; ++fm) {
         const int vb = v0 + arow0 + fm * 32;   // first vocabulary row of the block
-        uint32_t w[4][2];                       // [gq][dword] packed fp16 pairs
+        uint32_t w[4][2];                       // [gq][dword]
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
           const int v = vb + lrow + 8 * gq;
@@ -536,11 +539,44 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
             w[2 * pr][d] = r[0];
             w[2 * pr + 1][d] = r[1];
           }
-          const int col = vb + 16 * pr + 8 * hi - p.c0;
-          if (col < p.kpad)
-            *reinterpret_cast<u32x4*>(drow + col) = u32x4{w[2 * pr][0], w[2 * pr][1], w[2 * pr + 1][0], w[2 * pr + 1][1]};
+          pk[fm][fn][pr][0] = w[2 * pr][0];
+          pk[fm][fn][pr][1] = w[2 * pr][1];
+          pk[fm][fn][pr][2] = w[2 * pr + 1][0];
+          pk[fm][fn][pr][3] = w[2 * pr + 1][1];
         }
       }
+    }
+    // Stores go through the free LDS stage, 64 tokens per round: the waves
+    // holding those tokens write a [64 token][256 vocabulary] fp16 tile (16-byte
+    // chunk c of row t at chunk c ^ (t % 32), so neither side has bank
+    // conflicts), then every thread stores 16-byte pieces of whole rows: 512
+    // contiguous bytes per token row instead of 32 rows per store instruction.
+#pragma unroll
+    for (int round = 0; round < 2; ++round) {
+      if (wn == round) {
+#pragma unroll
+        for (int fn = 0; fn < FFN; ++fn) {
+          const int tl = fn * 32 + (lane & 31);   // token within the round
+#pragma unroll
+          for (int fm = 0; fm < FFM; ++fm)
+#pragma unroll
+            for (int pr = 0; pr < 2; ++pr) {
+              const int c = (arow0 + fm * 32 + 16 * pr + 8 * hi) >> 3;
+              *reinterpret_cast<u32x4*>(stage + tl * 512 + ((c ^ (tl & 31)) << 4)) =
+                  u32x4{pk[fm][fn][pr][0], pk[fm][fn][pr][1], pk[fm][fn][pr][2], pk[fm][fn][pr][3]};
+            }
+        }
+      }
+      dma_barrier<63>();
+#pragma unroll
+      for (int it = 0; it < 64 * 32 / F::kThreads; ++it) {
+        const int lin = it * F::kThreads + tid;
+        const int tr = lin >> 5, c = lin & 31;
+        const int col = v0 - p.c0 + c * 8;
+        const u32x4 x = *reinterpret_cast<const u32x4*>(stage + tr * 512 + ((c ^ (tr & 31)) << 4));
+        if (col < p.kpad) *reinterpret_cast<u32x4*>(p.dz + (int64_t)(n0 + round * 64 + tr) * p.ldz + col) = x;
+      }
+      dma_barrier<63>();
     }
   }, convert_w);
 }
