@@ -13,8 +13,8 @@
 // output layout one lane then holds one token and 16 vocabulary entries per
 // block, so the online log-sum-exp / KL statistics of a token live in that
 // lane's registers for the whole vocabulary sweep; lanes l and l^32 (the two
-// row halves) merge once at the end, then the two waves that share tokens
-// merge through LDS.
+// row halves) merge once at the end, then the waves that share tokens merge
+// through LDS.
 #include "rkl_tile.h"
 #include "rkl_internal.h"
 
