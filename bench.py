@@ -52,14 +52,20 @@ def parse():
 
 
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources: a recorded traffic measurement is only reused
-    while the kernels it was taken on are unchanged."""
+    """Hash of the HIP sources with comments and blank space removed: a
+    recorded traffic measurement is only reused while the code it was taken
+    on is unchanged."""
     import hashlib
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "lm_head_reverse_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + b"\0" + f.read())
+        with open(os.path.join(csrc, name)) as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", "", src)
+        src = "\n".join(line.strip() for line in src.splitlines() if line.strip())
+        h.update(name.encode() + b"\0" + src.encode())
     return h.hexdigest()[:16]
 
 
