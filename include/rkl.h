@@ -145,6 +145,7 @@ int rkl_forward_logits(int64_t N, int64_t V, int64_t Hs,
  * Outputs (gradient of sum_i g_i L_i with respect to the student):
  *   dh_s  [N, Hs] fp32, overwritten; rows with row_mask 0 are exactly 0.
  *   dW_s  [V, Hs] fp32; overwritten, or added to when accumulate_dW != 0.
+ * At most 2^22 rows per call (RKL_UNSUPPORTED beyond; split the batch).
  */
 int rkl_backward_hidden(int64_t N, int64_t V, int64_t Hs, int64_t Ht,
                         const rkl_bf16* h_s, const rkl_bf16* W_s, const rkl_bf16* h_t, const rkl_bf16* W_t,

@@ -46,11 +46,18 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 // split, so it changes dh's rounding (never N-dependent for a fixed width);
 // the workspace size depends on it.
 
+// The GEMM operands' per-lane DMA offsets are formed with 24-bit multiplies
+// (row < 256 times the row pitch in bytes), so a pitch must stay below 2^24
+// bytes: the dz chunk width and the token count of a backward call are capped
+// at 2^22.
+constexpr int64_t kMaxPitchElems = (int64_t)1 << 22;
+
 // Vocabulary columns per backward chunk (a multiple of 256; default 65536).
 int64_t vocab_chunk() {
   const char* s = std::getenv("RKL_VOCAB_CHUNK");
   int64_t v = s ? std::atoll(s) : 65536;
   if (v < 256) v = 256;
+  if (v > kMaxPitchElems) v = kMaxPitchElems;
   return round_up(v, 256);
 }
 
@@ -202,6 +209,8 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
                    const rkl_bf16* h_t, const rkl_bf16* W_t, const float* z_t, const uint8_t* row_mask,
                    const float* grad, const float* stats, float* dh, float* dW, int accumulate, void* ws,
                    size_t ws_bytes_given, hipStream_t s) {
+  if (N > kMaxPitchElems)
+    return fail(RKL_UNSUPPORTED, "N=%lld rows exceed the backward's limit of 2^22 per call", (long long)N);
   const BwdLayout L = bwd_layout(N, V, Hs);
   if (ws_bytes_given < L.total)
     return fail(RKL_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes_given, L.total);

@@ -99,6 +99,10 @@ def test_backward_rejects():
     # dW missing
     assert L.rkl_backward_hidden(4, 100, 64, 64, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, None, 0,
                                  FAKE, 1 << 30, None) == 1
+    # more rows than the backward's per-call limit (2^22): unsupported, nothing launched
+    assert L.rkl_backward_hidden((1 << 22) + 1, 100, 64, 64, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE,
+                                 0, FAKE, 1 << 62, None) == 2
+    assert "2^22" in L.rkl_last_error().decode()
 
 
 def test_compaction_and_copies_reject():
