@@ -602,20 +602,19 @@ __global__ __launch_bounds__(256) void transpose_h(const uint16_t* __restrict__ 
 // ===========================================================================
 // Backward, step 2: dW_s[c0 + m, n] (+)= (1/s) sum_t dz[t, m] h_s[t, n]
 // A = dz (MN-major: token rows, vocabulary contiguous; read transposed),
-// B = hT (K-major).  256 x 256 tiles (128 x 128 per wave), two LDS stages
-// (measured faster here than 256 x 128 tiles with three stages); with two
-// stages the next tile's DMA is issued during steps 0-1 only, leaving it half
-// a k-tile of MFMAs to land before the barrier.
+// B = hT (K-major).  256 x 256 tiles in 32-deep k-tiles through four LDS
+// stages (128 KB): the DMA runs three k-tiles ahead.  (Three 64-deep stages of
+// a 256 x 256 tile would need 192 KB; with two, memory latency showed.)
 // ===========================================================================
-constexpr int WBM = kDwTileM, WBN = kDwTileN, WNST = 2, WDSTEPS = 2;
+constexpr int WBM = kDwTileM, WBN = kDwTileN, WKT = 32, WNST = 4, WDSTEPS = 1;
 
 template <int NW>
 __global__ __launch_bounds__(64 * NW, 1) void dw_gemm(DwParams p) {
   // NW = 4: waves 2 x 2, 128 x 128 each; NW = 8: waves 4 (m) x 2 (n), 64 x 128
   // each (A, read transposed, is the operand with fewer fragments)
   constexpr int WGN = 2, WGM = NW / WGN;
-  using TA = MN<WBM, NW>;
-  using TB = KM<WBN, NW>;
+  using TA = MN<WBM, NW, WKT>;
+  using TB = KM<WBN, NW, WKT>;
   __shared__ __attribute__((aligned(1024))) char lds[WNST * (TA::kBytes + TB::kBytes)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / WGN, wn = w % WGN;
   const int logical = xcd_logical(blockIdx.x, p.ntm * p.ntn);
@@ -631,7 +630,7 @@ __global__ __launch_bounds__(64 * NW, 1) void dw_gemm(DwParams p) {
   ta.init(p.dz + m0, p.ldz, p.kpad - m0, lane, __builtin_amdgcn_readfirstlane(w));
   TB tb;
   tb.init(p.hT + (int64_t)n0 * p.ldT, p.ldT, p.H - n0, lane, __builtin_amdgcn_readfirstlane(w));
-  gemm_loop<TA, TB, f16x8, false, WNST, false, WDSTEPS>(acc, p.ldT / kKT, lds, ta, tb, 0, tid, wm * (WBM / WGM),
+  gemm_loop<TA, TB, f16x8, false, WNST, false, WDSTEPS>(acc, p.ldT / WKT, lds, ta, tb, 0, tid, wm * (WBM / WGM),
                                                        wn * (WBN / WGN));
   const float inv = p.gscale[1];
 #pragma unroll

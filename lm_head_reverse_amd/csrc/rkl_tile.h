@@ -215,11 +215,13 @@ struct DmaRows {
 // sits at physical chunk c ^ 4(k & 3), so the 8 rows x 4 chunks that one
 // transposing read touches fall on distinct bank groups twice at most.
 // ---------------------------------------------------------------------------
-template <int R, int NW = kThreads / 64>
+template <int R, int NW = kThreads / 64, int KT = kKT>
 struct MN {
   static_assert(R >= 128 && R % 128 == 0, "MN-major tiles need >= 128 columns");
+  static_assert(KT == 32 || KT == 64, "32- or 64-deep k-tiles");
+  static constexpr int kKTile = KT;
   static constexpr int kRowBytes = R * 2;
-  static constexpr int kBytes = kKT * kRowBytes;
+  static constexpr int kBytes = KT * kRowBytes;
   static constexpr int kPerWave = kBytes / 1024 / NW;
   __device__ __forceinline__ static int lds_pos(int k, int chunk) {
     return k * kRowBytes + ((chunk ^ ((k & 3) << 2)) << 4);
@@ -246,7 +248,7 @@ struct MN {
     }
   }
   __device__ __forceinline__ void issue(int kt, uint32_t dst, int q, int wave) const {
-    dma16(base + (int64_t)kt * kKT * (ld2 >> 1), off[q], dst + (uint32_t)((wave * kPerWave + q) * 1024));
+    dma16(base + (int64_t)kt * KT * (ld2 >> 1), off[q], dst + (uint32_t)((wave * kPerWave + q) * 1024));
   }
   // Same, for a k-tile that runs past the kvalid valid k rows: rows past it
   // repeat row kvalid-1 (callers pair them with zero padding of the other
@@ -254,9 +256,9 @@ struct MN {
   __device__ __forceinline__ void issue_clamped(int kt, uint32_t dst, int q, int wave, int lane, int kvalid) const {
     const int blk = wave * kPerWave + q;
     const int kl = blk * kRowsPerBlk + lane / kLanesPerRow;
-    const int row = min(kt * kKT + kl, kvalid - 1) - kt * kKT;
+    const int row = min(kt * KT + kl, kvalid - 1) - kt * KT;
     const uint32_t voff = off[q] - __umul24((uint32_t)kl, ld2) + __umul24((uint32_t)row, ld2);
-    dma16(base + (int64_t)kt * kKT * (ld2 >> 1), voff, dst + (uint32_t)((wave * kPerWave + q) * 1024));
+    dma16(base + (int64_t)kt * KT * (ld2 >> 1), voff, dst + (uint32_t)((wave * kPerWave + q) * 1024));
   }
   // MFMA operand for columns mn0 + 0..31 (lane%32), k = 16 ks + 8 (lane/32) .. +7
   template <typename ELEM>
@@ -277,26 +279,50 @@ struct MN {
   }
 };
 
-// K-major tiles (R rows x 64 k, swizzled rows of 128 bytes) for the generic GEMM.
-template <int R, int NW = kThreads / 64>
+// K-major tiles for the generic GEMM: R rows x KT k.
+//   KT = 64: rows of 128 bytes, chunk c of row r at c ^ ((r ^ r/8) % 8) (the
+//            fused kernels' layout, lds_off);
+//   KT = 32: rows of 64 bytes, chunk c of row r at c ^ (r/4 % 4): the 16 lanes
+//            of a quarter of a ds_read_b128 (rows r0..r0+15, one chunk) then
+//            cover all 64 banks once.  A DMA instruction fills 16 rows, lane l
+//            row l/4, physical chunk l%4.
+template <int R, int NW = kThreads / 64, int KT = kKT>
 struct KM {
-  static constexpr int kBytes = R * kLdsRow;
-  static constexpr int kPerWave = DmaRows<R, NW>::kPerWave;
+  static_assert(KT == 32 || KT == 64, "32- or 64-deep k-tiles");
+  static constexpr int kKTile = KT;
+  static constexpr int kRowB = KT * 2;
+  static constexpr int kBytes = R * kRowB;
+  static constexpr int kPerWave = kBytes / 1024 / NW;
+  static_assert(kPerWave >= 1, "tile too small");
   // DMA state: base = element (row 0, k 0) of this tile's row block in a
-  // row-major [rows, ld] matrix, nrows valid rows from there.
+  // row-major [rows, ld] matrix, nrows valid rows from there (rows past it
+  // repeat row nrows-1: such rows only meet outputs that are discarded).
   const uint16_t* base;
   uint32_t off[kPerWave];
   __device__ __forceinline__ void init(const uint16_t* b, int ld, int nrows, int lane, int wave) {
     base = b;
+    if constexpr (KT == 64) {
 #pragma unroll
-    for (int q = 0; q < kPerWave; ++q) off[q] = DmaRows<R, NW>::lane_off(q, 2u * (uint32_t)ld, nrows, lane, wave);
+      for (int q = 0; q < kPerWave; ++q) off[q] = DmaRows<R, NW>::lane_off(q, 2u * (uint32_t)ld, nrows, lane, wave);
+    } else {
+#pragma unroll
+      for (int q = 0; q < kPerWave; ++q) {
+        const int row = min(16 * (wave * kPerWave + q) + (lane >> 2), nrows - 1);
+        off[q] = __umul24((uint32_t)row, 2u * (uint32_t)ld) + ((uint32_t)((lane & 3) ^ ((row >> 2) & 3)) << 4);
+      }
+    }
   }
   __device__ __forceinline__ void issue(int kt, uint32_t dst, int q, int wave) const {
-    dma16(base + kt * kKT, off[q], dst + (uint32_t)((wave * kPerWave + q) * 1024));
+    dma16(base + kt * KT, off[q], dst + (uint32_t)((wave * kPerWave + q) * 1024));
   }
   template <typename ELEM>
   __device__ __forceinline__ static ELEM frag(const char* lds, int row0, int ks, int lane) {
-    return *reinterpret_cast<const ELEM*>(lds + lds_off(row0 + (lane & 31), ks * 2 + (lane >> 5)));
+    if constexpr (KT == 64) {
+      return *reinterpret_cast<const ELEM*>(lds + lds_off(row0 + (lane & 31), ks * 2 + (lane >> 5)));
+    } else {
+      const int r = row0 + (lane & 31);
+      return *reinterpret_cast<const ELEM*>(lds + r * 64 + (((ks * 2 + (lane >> 5)) ^ ((r >> 2) & 3)) << 4));
+    }
   }
 };
 
@@ -316,22 +342,25 @@ __device__ __forceinline__ f16x8 bf16_to_f16(bf16x8 x) {
 // ---------------------------------------------------------------------------
 // Generic GEMM main loop, both operands through the DMA, NST LDS stages:
 //   C[m, n] += sum_k A(m, k) B(n, k)   (fp32 accumulators)
-// TA / TB are KM<rows> (K-major, swizzled rows) or MN<cols> (MN-major, read
-// transposed).  Iteration kt: MFMAs of tile kt from stage kt % NST with the
-// fragments one step ahead; the DMA of tile kt + NST - 1 into stage
-// (kt - 1) % NST spread over steps 0-2; between steps 2 and 3 a barrier that
-// waits for tile kt + 1 (the DMA group of the later tile stays in flight), after
-// which step 3 reads the first fragments of tile kt + 1.  Stage (kt - 1) %
-// NST was last read before the previous iteration's barrier, so a DMA never
-// races a read.  Past the last tile the DMA repeats tile nk - 1 into stages
-// that are no longer read.  CVT_B converts B fragments from bf16 to fp16.
+// TA / TB are KM (K-major, swizzled rows) or MN (MN-major, read transposed)
+// with the same k-tile depth KT = 16 KS.  Iteration kt: MFMAs of tile kt
+// from stage kt % NST with the fragments one step ahead; the DMA of tile
+// kt + NST - 1 into stage (kt - 1) % NST spread over steps 0 .. DSTEPS-1;
+// before the last step a barrier that waits for tile kt + 1 (the NST - 2
+// later tiles' DMA stays in flight), after which the last step reads the
+// first fragments of tile kt + 1.  Stage (kt - 1) % NST was last read before
+// the previous iteration's barrier, so a DMA never races a read.  Past the
+// last tile the DMA repeats tile nk - 1 into stages that are no longer read.
+// CVT_B converts B fragments from bf16 to fp16.
 // ---------------------------------------------------------------------------
 template <class TA, class TB, typename ELEM, bool CVT_B, int NST, bool RAGGED_B = false, int DSTEPS = 3, int FM,
           int FN>
 __device__ __forceinline__ void gemm_loop(f32x16 (&acc)[FM][FN], int nk, char* lds, const TA& ta, const TB& tb,
                                           int kvalid_b, int tid, int arow0, int brow0) {
-  static_assert(NST == 2 || NST == 3, "two or three stages");
-  static_assert(DSTEPS >= 1 && DSTEPS <= 3, "the DMA is issued before the barrier of step 3");
+  static_assert(TA::kKTile == TB::kKTile, "both operands use one k-tile depth");
+  constexpr int KS = TA::kKTile / 16;
+  static_assert(NST >= 2 && NST <= 4, "two to four stages");
+  static_assert(DSTEPS >= 1 && DSTEPS <= KS - 1, "the DMA is issued before the barrier of the last step");
   constexpr int kStage = TA::kBytes + TB::kBytes;
   constexpr int NA = TA::kPerWave, NB = TB::kPerWave, ND = NA + NB;
   constexpr int M = FM * FN, R = FM + FN;
@@ -377,11 +406,11 @@ __device__ __forceinline__ void gemm_loop(f32x16 (&acc)[FM][FN], int nk, char* l
     const uint32_t pre = lbase + (uint32_t)(spre * kStage);
     const int kn = min(kt + NST - 1, nk - 1);
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      if (ks == 3) dma_barrier<(NST - 2) * ND>();
+    for (int ks = 0; ks < KS; ++ks) {
+      if (ks == KS - 1) dma_barrier<(NST - 2) * ND>();
       const int fb = ks & 1, nb = fb ^ 1;
-      const char* src = ks == 3 ? nxt : cur;
-      const int nks = (ks + 1) & 3;
+      const char* src = ks == KS - 1 ? nxt : cur;
+      const int nks = ks == KS - 1 ? 0 : ks + 1;
 #pragma unroll
       for (int m = 0; m < M; ++m) {
         const int fm = m / FN, fn = m % FN;
