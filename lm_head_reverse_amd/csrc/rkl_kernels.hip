@@ -657,14 +657,14 @@ __global__ __launch_bounds__(64 * NW, 1) void dw_gemm(DwParams p) {
 // contiguous; read transposed, bf16 converted to fp16).  256 x 128 tiles,
 // three LDS stages.
 // ===========================================================================
-constexpr int HBM = kDhTileM, HBN = kDhTileN, HNST = 3;
+constexpr int HBM = kDhTileM, HBN = kDhTileN, HKT = 64, HNST = 3, HDSTEPS = 3;
 
 template <int NW>
 __global__ __launch_bounds__(64 * NW, 1) void dh_gemm(DhParams p) {
   // NW = 4: waves 2 x 2, 128 x 64 each; NW = 8: waves 4 (m) x 2 (n), 64 x 64 each
   constexpr int HGM = NW / 2, HGN = 2;
-  using TA = KM<HBM, NW>;
-  using TB = MN<HBN, NW>;
+  using TA = KM<HBM, NW, HKT>;
+  using TB = MN<HBN, NW, HKT>;
   __shared__ __attribute__((aligned(1024))) char lds[HNST * (TA::kBytes + TB::kBytes)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / HGN, wn = w % HGN;
   const int logical = xcd_logical(blockIdx.x, p.ntm * p.ntn);
@@ -680,7 +680,8 @@ __global__ __launch_bounds__(64 * NW, 1) void dh_gemm(DhParams p) {
   ta.init(p.dz + (int64_t)m0 * p.ldz, p.ldz, p.npad - m0, lane, __builtin_amdgcn_readfirstlane(w));
   TB tb;
   tb.init(p.w16 + n0, p.H, p.H - n0, lane, __builtin_amdgcn_readfirstlane(w));
-  gemm_loop<TA, TB, f16x8, false, HNST>(acc, p.kpad / kKT, lds, ta, tb, 0, tid, wm * (HBM / HGM), wn * (HBN / HGN));
+  gemm_loop<TA, TB, f16x8, false, HNST, false, HDSTEPS>(acc, p.kpad / HKT, lds, ta, tb, 0, tid, wm * (HBM / HGM),
+                                                       wn * (HBN / HGN));
   const float inv = p.gscale[1];
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {

@@ -359,7 +359,8 @@ __device__ __forceinline__ void gemm_loop(f32x16 (&acc)[FM][FN], int nk, char* l
                                           int kvalid_b, int tid, int arow0, int brow0) {
   static_assert(TA::kKTile == TB::kKTile, "both operands use one k-tile depth");
   constexpr int KS = TA::kKTile / 16;
-  static_assert(NST >= 2 && NST <= 4, "two to four stages");
+  static_assert(NST >= 2 && NST <= 6, "two to six stages");
+  static_assert((NST - 2) * (TA::kPerWave + TB::kPerWave) <= 63, "wait count fits vmcnt");
   static_assert(DSTEPS >= 1 && DSTEPS <= KS - 1, "the DMA is issued before the barrier of the last step");
   constexpr int kStage = TA::kBytes + TB::kBytes;
   constexpr int NA = TA::kPerWave, NB = TB::kPerWave, ND = NA + NB;
