@@ -61,10 +61,11 @@ int64_t vocab_chunk() {
   return round_up(v, 256);
 }
 
-// Vocabulary tiles one backward workgroup sweeps (does not change results).
+// Vocabulary tiles one backward workgroup sweeps (does not change results;
+// one per workgroup measured fastest: the finer grain balances the last wave).
 int bwd_tiles_per_group() {
   const char* s = std::getenv("RKL_BWD_TILES");
-  const int v = s ? std::atoi(s) : 4;
+  const int v = s ? std::atoi(s) : 1;
   return v < 1 ? 1 : (v > 64 ? 64 : v);
 }
 
@@ -109,7 +110,11 @@ struct Split {
 };
 Split fwd_split(int64_t V) {
   const int64_t ntv = ceil_div(V, rkl::kFwdTileV);
-  const int64_t tps = ceil_div(ntv, 160);
+  int64_t tps = ceil_div(ntv, 200);   // 3 at V = 151936: 198 splits (measured fastest)
+  if (const char* s = std::getenv("RKL_FWD_TILES")) {   // tiles per split (changes rounding only)
+    const int v = std::atoi(s);
+    if (v >= 1 && v <= 1024) tps = v;
+  }
   return Split{(int)tps, (int)ceil_div(ntv, tps)};
 }
 
