@@ -438,6 +438,66 @@ __global__ __launch_bounds__(1024) void grad_scale(const float* __restrict__ gra
   }
 }
 
+// s * dz of this lane's accumulator elements, rounded to fp16 and packed in
+// pairs.  Lane l (l < 32) holds rows {0-3, 8-11, 16-19, 24-27} of each 32-row
+// block, lane l + 32 rows {4-7, 12-15, 20-23, 28-31}, same token; one
+// permlane32 swap per dword leaves lane l with rows 0-7 and 16-23, lane l + 32
+// with rows 8-15 and 24-31: runs of 8 consecutive vocabulary entries,
+// pk[fm][fn][run] = 4 dwords.  The arithmetic is branch-free: entries past V
+// (TAIL, the last vocabulary tile only) and dead token columns become zero by
+// selection, so a dead row stays exactly zero whatever its logits are.
+// vrow = vocabulary index of this lane's row 0 in block fm = 0.
+template <bool TAIL, int FM, int FN>
+__device__ __forceinline__ void dz_pack(const f32x16 (&zs)[FM][FN], const f32x16 (&zt)[FM][FN],
+                                        uint32_t (&pk)[FM][FN][2][4], const bool (&live)[FN], const float (&gs)[FN],
+                                        const float (&css)[FN], const float (&cst)[FN], int vrow, int V) {
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm) {
+      uint32_t w[4][2];   // [gq][dword]
+#pragma unroll
+      for (int gq = 0; gq < 4; ++gq) {
+        float dv[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float a = zs[fm][fn][4 * gq + e];
+          const float bb = zt[fm][fn][4 * gq + e];
+          // (the tail copy reads its input through an empty asm so that the
+          // compiler cannot merge the two copies' arithmetic above the branch
+          // that selects them -- that computes every entry at once and spills)
+          if (TAIL) asm volatile("" : "+v"(a));
+          float d = gs[fn] * ex2(fmaf(a, kL2E, -css[fn])) * ((a - bb) - cst[fn]);
+          d = __builtin_amdgcn_fmed3f(d, -65504.f, 65504.f);
+          if (TAIL) d = (vrow + fm * 32 + 8 * gq + e < V) ? d : 0.f;
+          dv[e] = d;
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          // both halves rounded to nearest in one packed conversion
+          const uint32_t x = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{dv[2 * h], dv[2 * h + 1]}, f16x2));
+          w[gq][h] = live[fn] ? x : 0u;
+        }
+        // four entries at a time: keeps the register peak down
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int pr = 0; pr < 2; ++pr) {
+#pragma unroll
+        for (int d = 0; d < 2; ++d) {
+          const auto r = __builtin_amdgcn_permlane32_swap(w[2 * pr][d], w[2 * pr + 1][d], false, false);
+          w[2 * pr][d] = r[0];
+          w[2 * pr + 1][d] = r[1];
+        }
+        pk[fm][fn][pr][0] = w[2 * pr][0];
+        pk[fm][fn][pr][1] = w[2 * pr][1];
+        pk[fm][fn][pr][2] = w[2 * pr + 1][0];
+        pk[fm][fn][pr][3] = w[2 * pr + 1][1];
+      }
+    }
+  }
+}
+
 // ===========================================================================
 // Backward, step 1: recompute z_s, z_t for one (vocabulary tile, token tile)
 // of the current chunk and write s * dz, dz = g p_s ((z_s - z_t) - (lse_s -
@@ -504,48 +564,12 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
   dual_stream<NW>(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, [&](int job, char* stage) {
     const int v0 = p.c0 + (vt0 + job) * FBM;
     if (MODE == 1) load_zt<VEC4>(zt, p.z_t, p.N, p.V, v0 + arow0 + lrow, n0 + brow0 + (lane & 31), lane);
-    // dz of this lane's elements, rounded to fp16 and packed in pairs.  Lane
-    // l (l < 32) holds rows {0-3, 8-11, 16-19, 24-27} of each 32-row block,
-    // lane l + 32 rows {4-7, 12-15, 20-23, 28-31}, same token; one permlane32
-    // swap per dword leaves lane l with rows 0-7 and 16-23, lane l + 32 with
-    // rows 8-15 and 24-31: runs of 8 consecutive vocabulary entries.
     const int hi = lane >> 5;
     uint32_t pk[FFM][FFN][2][4];   // [fm][fn][run][dword]
-#pragma unroll
-    for (int fn = 0; fn < FFN; ++fn) {
-#pragma unroll
-      for (int fm = 0; fm < FFM; ++fm) {
-        const int vb = v0 + arow0 + fm * 32;   // first vocabulary row of the block
-        uint32_t w[4][2];                       // [gq][dword]
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq) {
-          const int v = vb + lrow + 8 * gq;
-          _Float16 oh[4];
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            const float a = zs[fm][fn][4 * gq + e], bb = zt[fm][fn][4 * gq + e];
-            float d = 0.f;
-            if (live[fn] && v + e < p.V) d = gs[fn] * ex2(fmaf(a, kL2E, -css[fn])) * ((a - bb) - cst[fn]);
-            oh[e] = (_Float16)fminf(fmaxf(d, -65504.f), 65504.f);
-          }
-          w[gq][0] = (uint32_t)__builtin_bit_cast(uint16_t, oh[0]) | ((uint32_t)__builtin_bit_cast(uint16_t, oh[1]) << 16);
-          w[gq][1] = (uint32_t)__builtin_bit_cast(uint16_t, oh[2]) | ((uint32_t)__builtin_bit_cast(uint16_t, oh[3]) << 16);
-        }
-#pragma unroll
-        for (int pr = 0; pr < 2; ++pr) {
-#pragma unroll
-          for (int d = 0; d < 2; ++d) {
-            const auto r = __builtin_amdgcn_permlane32_swap(w[2 * pr][d], w[2 * pr + 1][d], false, false);
-            w[2 * pr][d] = r[0];
-            w[2 * pr + 1][d] = r[1];
-          }
-          pk[fm][fn][pr][0] = w[2 * pr][0];
-          pk[fm][fn][pr][1] = w[2 * pr][1];
-          pk[fm][fn][pr][2] = w[2 * pr + 1][0];
-          pk[fm][fn][pr][3] = w[2 * pr + 1][1];
-        }
-      }
-    }
+    if (v0 + FBM <= p.V)
+      dz_pack<false>(zs, zt, pk, live, gs, css, cst, v0 + arow0 + lrow, p.V);
+    else
+      dz_pack<true>(zs, zt, pk, live, gs, css, cst, v0 + arow0 + lrow, p.V);
     // Stores go through the free LDS stage, 64 tokens per round: the waves
     // holding those tokens write a [64 token][256 vocabulary] fp16 tile (16-byte
     // chunk c of row t at chunk c ^ (t % 32), so neither side has bank
