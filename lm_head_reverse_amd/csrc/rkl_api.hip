@@ -41,10 +41,10 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 
 // Tuning knobs, read from the environment at every call (cheap next to a
 // launch) so that one process can exercise several settings.  The workgroup
-// orders and the tiles per backward workgroup never change a result bit.  The
-// backward chunk width changes where dh's fp32 sum over vocabulary chunks is
-// split, so it changes dh's rounding (never N-dependent for a fixed width);
-// the workspace size depends on it.
+// orders and the tiles per backward workgroup never change a result bit, nor
+// does a backward chunk width that is a whole number of dh segments (the
+// default); other widths move where dh's fp32 sum is split, i.e. its
+// rounding.  The workspace size depends on the width.
 
 // The GEMM operands' per-lane DMA offsets are formed with 24-bit multiplies
 // (row < 256 times the row pitch in bytes), so a pitch must stay below 2^24
@@ -52,13 +52,25 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 // at 2^22.
 constexpr int64_t kMaxPitchElems = (int64_t)1 << 22;
 
-// Vocabulary columns per backward chunk (a multiple of 256; default 65536).
-int64_t vocab_chunk() {
-  const char* s = std::getenv("RKL_VOCAB_CHUNK");
-  int64_t v = s ? std::atoll(s) : 65536;
-  if (v < 256) v = 256;
-  if (v > kMaxPitchElems) v = kMaxPitchElems;
-  return round_up(v, 256);
+// Vocabulary columns per backward chunk for N rows: as many whole
+// kDhSegment-column segments as keep the chunk's fp16 dz within 2 GiB, at
+// least one (262144 columns at N <= 4096, one 65536-column segment for
+// N > 8192).  Fewer chunks mean fewer launches and no narrow tail
+// chunk; chunks on segment boundaries keep dh's bits independent of N.
+// RKL_VOCAB_CHUNK overrides it (a multiple of 256; widths that are not a
+// multiple of kDhSegment change where dh's sum is split, i.e. its rounding).
+int64_t vocab_chunk(int64_t N) {
+  if (const char* s = std::getenv("RKL_VOCAB_CHUNK")) {
+    int64_t v = std::atoll(s);
+    if (v < 256) v = 256;
+    if (v > kMaxPitchElems) v = kMaxPitchElems;
+    return round_up(v, 256);
+  }
+  const int64_t budget = (int64_t)1 << 31;   // bytes of fp16 dz per chunk
+  int64_t segs = budget / (2 * (N > 0 ? N : 1) * (int64_t)rkl::kDhSegment);
+  if (segs < 1) segs = 1;
+  const int64_t C = segs * rkl::kDhSegment;
+  return C < kMaxPitchElems ? C : kMaxPitchElems;
 }
 
 // Vocabulary tiles one backward workgroup sweeps (does not change results;
@@ -133,7 +145,7 @@ BwdLayout bwd_layout(int64_t N, int64_t V, int64_t Hs) {
   BwdLayout L{};
   L.ldT = round_up(N, 64);
   L.npad = round_up(N, rkl::kFwdTileN);
-  const int64_t C = vocab_chunk();
+  const int64_t C = vocab_chunk(N);
   L.ldz = round_up(V < C ? V : C, 64);
   L.off_scale = 0;
   L.off_hT = 256;
@@ -232,7 +244,7 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
   uint16_t* w16 = reinterpret_cast<uint16_t*>(base + L.off_w16);
   RKL_TRY(rkl::launch_grad_scale(grad, row_mask, stats, (int)N, gscale, s));
   RKL_TRY(rkl::launch_transpose_h(h_s, (int)N, (int)Hs, hT, (int)L.ldT, s));
-  const int64_t C = vocab_chunk();
+  const int64_t C = vocab_chunk(N);
   for (int64_t c0 = 0; c0 < V; c0 += C) {
     const int64_t width = (V - c0) < C ? (V - c0) : C;
     const int64_t kpad = round_up(width, 64);
@@ -259,7 +271,7 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
 
     rkl::DhParams h{};
     h.gscale = gscale; h.dz = dz; h.ldz = (int)L.ldz; h.N = (int)N; h.npad = (int)L.npad; h.kpad = (int)kpad;
-    h.width = (int)width;
+    h.width = (int)width; h.c0 = (int)c0;
     h.w16 = w16; h.H = (int)Hs; h.dh = dh; h.accumulate = c0 > 0;
     h.ntm = (int)ceil_div(N, rkl::kDhTileM);
     h.ntn = (int)ceil_div(Hs, rkl::kDhTileN);

@@ -59,6 +59,7 @@ struct DhParams {
   const float* gscale;
   const uint16_t* dz;
   int ldz, N, npad, kpad, width;   // npad: dz workspace rows
+  int c0;                          // first vocabulary column of the chunk
   const uint16_t* w16;     // fp16 copy of the W_s chunk [>= kpad rows, H]
   int H;
   float* dh;
@@ -71,6 +72,9 @@ constexpr int kFwdTileV = 256;
 constexpr int kFwdTileN = 128;
 constexpr int kDwTileM = 256, kDwTileN = 256;
 constexpr int kDhTileM = 256, kDhTileN = 128;
+// dh's fp32 sum over the vocabulary is split at multiples of this column
+// index (absolute), whatever the backward's chunk width.
+constexpr int kDhSegment = 65536;
 
 hipError_t launch_fwd_tiles(const FwdParams& p, bool teacher_logits, int waves, hipStream_t s);
 hipError_t launch_fwd_combine(const float* partial, int nsplit, int N, const uint8_t* row_mask, float* loss,

@@ -677,9 +677,14 @@ __global__ __launch_bounds__(64 * NW, 1) void dw_gemm(DwParams p) {
 
 // ===========================================================================
 // Backward, step 3: dh_s[m, n] (+)= (1/s) sum_v dz[m, v] W_s[c0 + v, n]
-// A = dz (K-major rows), B = W_s chunk (MN-major: vocabulary rows, hidden
-// contiguous; read transposed, bf16 converted to fp16).  256 x 128 tiles,
-// three LDS stages.
+// A = dz (K-major rows), B = the fp16 copy of the W_s chunk (MN-major:
+// vocabulary rows, hidden contiguous; read transposed).  256 x 128 tiles,
+// three LDS stages.  The sum over v runs in segments that end at multiples
+// of kDhSegment (absolute column): each segment's fp32 sum is added to the
+// running total in order.  Chunks that start on segment boundaries thus give
+// the same bits whatever their width (a chunk's total leaves through memory,
+// scaled by the power of two 1/s, which commutes with the additions), so dh
+// does not depend on N through the chunk plan.
 // ===========================================================================
 constexpr int HBM = kDhTileM, HBN = kDhTileN, HKT = 64, HNST = 3, HDSTEPS = 3;
 
@@ -695,17 +700,27 @@ __global__ __launch_bounds__(64 * NW, 1) void dh_gemm(DhParams p) {
   const int tm = logical / p.ntn, tn = logical - tm * p.ntn;
   const int m0 = tm * HBM, n0 = tn * HBN;
   constexpr int FM = HBM / HGM / 32, FN = HBN / HGN / 32;
-  f32x16 acc[FM][FN];
-  zero_acc(acc);
+  f32x16 acc[FM][FN], tot[FM][FN];
   // A: dz rows are tokens (m; npad zero-padded rows), columns vocabulary (k,
   // zero past the chunk width); B: the fp16 copy of the W_s chunk, rows
   // vocabulary (k; the copy covers every k-tile), columns hidden units (n).
-  TA ta;
-  ta.init(p.dz + (int64_t)m0 * p.ldz, p.ldz, p.npad - m0, lane, __builtin_amdgcn_readfirstlane(w));
-  TB tb;
-  tb.init(p.w16 + n0, p.H, p.H - n0, lane, __builtin_amdgcn_readfirstlane(w));
-  gemm_loop<TA, TB, f16x8, false, HNST, false, HDSTEPS>(acc, p.kpad / HKT, lds, ta, tb, 0, tid, wm * (HBM / HGM),
-                                                       wn * (HBN / HGN));
+  for (int k0 = 0; k0 < p.kpad;) {
+    const int k1 = min(p.kpad, ((p.c0 + k0) / kDhSegment + 1) * kDhSegment - p.c0);
+    zero_acc(acc);
+    TA ta;
+    ta.init(p.dz + (int64_t)m0 * p.ldz + k0, p.ldz, p.npad - m0, lane, __builtin_amdgcn_readfirstlane(w));
+    TB tb;
+    tb.init(p.w16 + (int64_t)k0 * p.H + n0, p.H, p.H - n0, lane, __builtin_amdgcn_readfirstlane(w));
+    gemm_loop<TA, TB, f16x8, false, HNST, false, HDSTEPS>(acc, (k1 - k0) / HKT, lds, ta, tb, 0, tid,
+                                                         wm * (HBM / HGM), wn * (HBN / HGN));
+#pragma unroll
+    for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) tot[fm][fn][i] = k0 == 0 ? acc[fm][fn][i] : tot[fm][fn][i] + acc[fm][fn][i];
+    k0 = k1;
+  }
   const float inv = p.gscale[1];
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
@@ -718,7 +733,7 @@ __global__ __launch_bounds__(64 * NW, 1) void dh_gemm(DhParams p) {
         const int m = m0 + wm * (HBM / HGM) + fm * 32 + frag_row(i, lane);
         if (m < p.N) {
           float* o = p.dh + (int64_t)m * p.H + n;
-          const float d = acc[fm][fn][i] * inv;
+          const float d = tot[fm][fn][i] * inv;
           *o = p.accumulate ? *o + d : d;
         }
       }

@@ -46,11 +46,15 @@ def test_workspace_sizes():
     a = R.workspace_bytes(2048, 151936, 2048, 2048)
     b = R.workspace_bytes(4096, 151936, 2048, 2048)
     assert 0 < a < b
-    # bounded: the [N, V] logits are never materialised (4096 x 151936 fp32 =
-    # 2.49 GB); the backward keeps one 65536-column fp16 dz chunk and an fp16
-    # copy of that chunk of W_s (0.82 GB together at N = 4096)
-    assert b < 4096 * 151936 * 4 / 2
-    assert b < 4096 * 65536 * 2 + 65536 * 2048 * 2 + 2048 * 4096 * 2 + (1 << 20)
+    # no fp32 [N, V] logits (4096 x 151936 x 4 B = 2.49 GB) are ever held; the
+    # backward keeps an fp16 dz chunk of whole 65536-column segments within
+    # 2 GiB (the whole vocabulary at N = 4096), an fp16 copy of that chunk of
+    # W_s and the transposed fp16 h_s
+    assert b < 4096 * 151936 * 4
+    assert b <= 4096 * 151936 * 2 + 152064 * 2048 * 2 + 2048 * 4096 * 2 + (1 << 20)
+    # N = 8192: two segments (2 GiB of dz); N = 32768: one segment
+    assert R.workspace_bytes(8192, 151936, 2048, 2048) <= 8192 * 131072 * 2 + 131072 * 2048 * 2 + 2048 * 8192 * 2 + (1 << 20)
+    assert R.workspace_bytes(32768, 151936, 2048, 2048) <= 32768 * 65536 * 2 + 65536 * 2048 * 2 + 2048 * 32768 * 2 + (1 << 20)
     assert R.workspace_bytes(4096, 151936, 2048, 2048) == R.workspace_bytes(4096, 151936, 2048, 4096)
     assert R.workspace_bytes(-1, 10, 64, 64) == 0
 

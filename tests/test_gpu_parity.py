@@ -170,12 +170,21 @@ def test_hidden_ragged_with_grad(tdev, T, V, Hs, Ht):
     _check_against_oracle(case, _run_hidden(case, dev, g=case.grad), g=case.grad)
 
 
-def test_hidden_multi_chunk_backward(tdev):
-    """V = 140000 spans three 65536-column backward chunks (the last one ragged)."""
+def test_hidden_multi_chunk_backward(tdev, monkeypatch):
+    """V = 140000 spans three 65536-column dh segments (the last one ragged):
+    one backward chunk by default at this N, three chunks of 65536 columns
+    when the chunk width is forced.  Both match the oracle, and bit for bit
+    each other: dh's sum is split at the same segment boundaries either way
+    (the chunk plan depends on N, the result must not)."""
     torch, dev = tdev
-    case = synth.random_case(31, T=150, V=140000, Hs=64, Ht=64, p_mask=0.6)
+    case = synth.random_case(31, T=150, V=140000, Hs=64, Ht=64, p_mask=0.6, with_grad=True)
     say("multi-chunk", case.T, case.V)
-    _check_against_oracle(case, _run_hidden(case, dev))
+    one = _run_hidden(case, dev, g=case.grad)
+    _check_against_oracle(case, one, g=case.grad)
+    monkeypatch.setenv("RKL_VOCAB_CHUNK", "65536")
+    three = _run_hidden(case, dev, g=case.grad)
+    for a, b, what in zip(three[1:], one[1:], ("loss", "stats", "dh", "dW")):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), what
 
 
 @pytest.mark.parametrize("orders", [("1,1", "1,1", "1"), ("3,5", "7,2", "3"), ("64,64", "2,3", "64")],
