@@ -313,6 +313,30 @@ def test_accumulate_dW(tdev):
     assert np.array_equal(host(dW2), base + host(dW))
 
 
+@pytest.mark.parametrize("T,V", [(1, 1), (3, 1), (2, 2), (5, 63), (1, 300)])
+def test_tiny_vocabulary_and_single_rows(tdev, T, V):
+    """Vocabularies far below one 256-row tile (down to V = 1) and batches of
+    one row: clamped rows and padded columns everywhere.  With V = 1 both
+    distributions are the point mass: L and every gradient are 0 in exact
+    arithmetic (the oracle gives exact zeros), so the relative gradient bar
+    does not apply; the GPU values must be zero up to fp32 rounding of the
+    log-sum-exps (exp of the max entry is 1 only to within an ulp)."""
+    torch, dev = tdev
+    case = synth.random_case(200 + 10 * T + V, T=T, V=V, Hs=64, Ht=128, p_mask=1.0, with_grad=True)
+    say("tiny vocabulary", T, V)
+    out = _run_hidden(case, dev, g=case.grad)
+    if V > 1:
+        _check_against_oracle(case, out, g=case.grad)
+        return
+    idx, loss, stats, dh, dW = out
+    assert np.array_equal(idx, np.arange(T))
+    assert np.all(np.abs(loss) <= 1e-6)
+    # z_s of the single entry: lse_s equals it up to rounding
+    z_s = O.project(O.widen_bf16(case.h_s), O.widen_bf16(case.W_s))
+    assert np.allclose(stats[:, 0], z_s[:, 0], rtol=1e-5, atol=1e-5)
+    assert np.max(np.abs(dh)) <= 1e-6 and np.max(np.abs(dW)) <= 1e-6
+
+
 def test_token_mean_gradient_large_vocab(tdev):
     """Upstream gradient 1/N with V = 60000: dz values around g/V must keep
     their precision in the scaled fp16 workspace."""
