@@ -165,6 +165,44 @@ int rkl_backward_logits(int64_t N, int64_t V, int64_t Hs,
                         float* dh_s, float* dW_s, int accumulate_dW, float* dz_s,
                         void* workspace, size_t workspace_bytes, rkl_stream_t stream);
 
+/*
+ * Log-probability of the sampled token and entropy of one projection (slime
+ * page, summary: the log-probability / entropy computation of the compact
+ * actor path takes the [N, V] logits of the loss-masked rows and returns
+ * per-row scalars; the top-p masks it also builds are not covered).  Per row
+ * i, z_i = h_i W^T formed tile by tile in fp32 and never written to memory:
+ *     logp[i]    = z_i[y_i] - lse(z_i)
+ *     entropy[i] = -sum_v p_i(v) log p_i(v) = lse(z_i) - sum_v p_i(v) z_i[v]
+ *   h [N, H], W [V, H]   bf16; H a multiple of 64.
+ *   y [N] int32 device   sampled token per row, in [0, V) (not checked on
+ *                        the device; a row whose y lies outside gets
+ *                        logp of about -1e30).
+ *   row_mask             as rkl_forward_hidden (rows with 0: all outputs 0).
+ *   logp, entropy [N] fp32 out.
+ *   stats [N, 4] fp32 out: (lse, entropy, logp, lpmax) -- all the backward
+ *                        needs.
+ * Workspace: rkl_workspace_bytes(N, V, H, 0).  N = 0 launches nothing.
+ */
+int rkl_forward_logprob_entropy(int64_t N, int64_t V, int64_t H, const rkl_bf16* h, const rkl_bf16* W,
+                                const int32_t* y, const uint8_t* row_mask, float* logp, float* entropy, float* stats,
+                                void* workspace, size_t workspace_bytes, rkl_stream_t stream);
+
+/*
+ * Backward of sum_i (g_lp,i logp_i + g_H,i entropy_i) (NeMo-RL page,
+ * implementation notes: like the entropy kernel there, the log-softmax is
+ * recomputed from h and W instead of cached):
+ *     dz_i[v] = g_lp,i (1[v = y_i] - p_i(v)) - g_H,i p_i(v) (log p_i(v) + entropy_i)
+ *     dh = dz W (overwritten),  dW = sum_i dz_i^T h_i (overwritten, or added
+ *     to when accumulate_dW != 0).
+ *   grad_logp [N] fp32 (NULL = all ones), grad_entropy [N] fp32 (NULL = all
+ *   zeros); stats from rkl_forward_logprob_entropy on the same inputs.
+ * Other arguments, limits and the workspace as rkl_backward_hidden with Ht = 0.
+ */
+int rkl_backward_logprob_entropy(int64_t N, int64_t V, int64_t H, const rkl_bf16* h, const rkl_bf16* W,
+                                 const int32_t* y, const uint8_t* row_mask, const float* grad_logp,
+                                 const float* grad_entropy, const float* stats, float* dh, float* dW,
+                                 int accumulate_dW, void* workspace, size_t workspace_bytes, rkl_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -56,6 +56,8 @@ def lib() -> ctypes.CDLL:
         "rkl_forward_logits": ([I64, I64, I64, P, P, P, P, P, P, P, P, SZ, P], I32),
         "rkl_backward_hidden": ([I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, I32, P, SZ, P], I32),
         "rkl_backward_logits": ([I64, I64, I64, P, P, P, P, P, P, P, P, P, I32, P, P, SZ, P], I32),
+        "rkl_forward_logprob_entropy": ([I64, I64, I64, P, P, P, P, P, P, P, P, SZ, P], I32),
+        "rkl_backward_logprob_entropy": ([I64, I64, I64, P, P, P, P, P, P, P, P, P, I32, P, SZ, P], I32),
     }
     for name, (args, res) in sig.items():
         f = getattr(L, name)
@@ -312,3 +314,57 @@ class ReverseKL:
             dh, dW = backward_logits(self.z_t, self.stats, h_s=self.h_s, W_s=self.W_s, grad_loss=g, dW=dW,
                                      accumulate_dW=accumulate_dW)
         return scatter_rows(dh, self.row_idx, self.T), dW
+
+
+def forward_logprob_entropy(h, W, y, row_mask=None):
+    """Log-probability of the sampled token and entropy per row of the
+    projection h W^T.  Returns (logp fp32 [N], entropy fp32 [N], stats fp32
+    [N, 4] = (lse, entropy, logp, lpmax))."""
+    torch = _torch()
+    dev = h.device
+    N, H = h.shape
+    V = W.shape[0]
+    _need(h, "h", torch.bfloat16, dev)
+    _need(W, "W", torch.bfloat16, dev, (V, H))
+    _need(y, "y", torch.int32, dev, (N,))
+    if row_mask is not None:
+        _need(row_mask, "row_mask", torch.uint8, dev, (N,))
+    logp = torch.empty(N, dtype=torch.float32, device=dev)
+    ent = torch.empty(N, dtype=torch.float32, device=dev)
+    stats = torch.empty((N, 4), dtype=torch.float32, device=dev)
+    ws = _workspace(dev, workspace_bytes(N, V, H, 0))
+    _check(lib().rkl_forward_logprob_entropy(N, V, H, _ptr(h), _ptr(W), _ptr(y), _ptr(row_mask), _ptr(logp),
+                                             _ptr(ent), _ptr(stats), _ptr(ws), ws.numel(), _stream(dev)))
+    return logp, ent, stats
+
+
+def backward_logprob_entropy(h, W, y, stats, grad_logp=None, grad_entropy=None, row_mask=None, dW=None,
+                             accumulate_dW=False):
+    """Gradients of sum_i (g_lp,i logp_i + g_H,i entropy_i) (grad_logp
+    defaults to ones, grad_entropy to zeros): returns (dh fp32 [N, H], dW fp32
+    [V, H])."""
+    torch = _torch()
+    dev = h.device
+    N, H = h.shape
+    V = W.shape[0]
+    _need(h, "h", torch.bfloat16, dev)
+    _need(W, "W", torch.bfloat16, dev, (V, H))
+    _need(y, "y", torch.int32, dev, (N,))
+    _need(stats, "stats", torch.float32, dev, (N, 4))
+    for g, name in ((grad_logp, "grad_logp"), (grad_entropy, "grad_entropy")):
+        if g is not None:
+            _need(g, name, torch.float32, dev, (N,))
+    if row_mask is not None:
+        _need(row_mask, "row_mask", torch.uint8, dev, (N,))
+    if dW is None:
+        if accumulate_dW:
+            raise RKLError(RKL_INVALID_ARG, "accumulate_dW needs a dW tensor")
+        dW = torch.empty((V, H), dtype=torch.float32, device=dev)
+    else:
+        _need(dW, "dW", torch.float32, dev, (V, H))
+    dh = torch.empty((N, H), dtype=torch.float32, device=dev)
+    ws = _workspace(dev, workspace_bytes(N, V, H, 0))
+    _check(lib().rkl_backward_logprob_entropy(N, V, H, _ptr(h), _ptr(W), _ptr(y), _ptr(row_mask), _ptr(grad_logp),
+                                              _ptr(grad_entropy), _ptr(stats), _ptr(dh), _ptr(dW),
+                                              int(bool(accumulate_dW)), _ptr(ws), ws.numel(), _stream(dev)))
+    return dh, dW

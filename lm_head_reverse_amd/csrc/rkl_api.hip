@@ -199,9 +199,17 @@ int check_dims(int64_t N, int64_t V, int64_t Hs, int64_t Ht, bool teacher_hidden
 // ---------------------------------------------------------------------------
 // forward / backward bodies shared by the hidden and logits entry points
 // ---------------------------------------------------------------------------
+// mode: y != NULL -> log-probability / entropy (out0 = log p(y), out1 =
+// entropy); else reverse KL (out0 = loss) with the teacher as hidden states
+// (z_t NULL) or as logits.
+int mode_of(const float* z_t, const int32_t* y) {
+  return y ? rkl::kModeLogprobEntropy : (z_t ? rkl::kModeTeacherLogits : rkl::kModeHidden);
+}
+
 int forward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* h_s, const rkl_bf16* W_s,
-                  const rkl_bf16* h_t, const rkl_bf16* W_t, const float* z_t, const uint8_t* row_mask, float* loss,
-                  float* stats, void* ws, size_t ws_bytes_given, hipStream_t s) {
+                  const rkl_bf16* h_t, const rkl_bf16* W_t, const float* z_t, const int32_t* y,
+                  const uint8_t* row_mask, float* out0, float* out1, float* stats, void* ws, size_t ws_bytes_given,
+                  hipStream_t s) {
   const size_t need = fwd_ws_bytes(N, V, true);
   if (ws_bytes_given < need)
     return fail(RKL_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes_given, need);
@@ -210,22 +218,25 @@ int forward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* 
   const Split sp = fwd_split(V);
   rkl::FwdParams p{};
   p.N = (int)N; p.V = (int)V; p.Hs = (int)Hs; p.Ht = (int)Ht;
-  p.h_s = h_s; p.W_s = W_s; p.h_t = h_t; p.W_t = W_t; p.z_t = z_t;
+  p.h_s = h_s; p.W_s = W_s; p.h_t = h_t; p.W_t = W_t; p.z_t = z_t; p.y = y;
   p.partial = static_cast<float*>(ws);
   p.tiles_per_split = sp.tiles_per_split;
   p.nsplit = sp.nsplit;
   p.ntok = (int)ceil_div(N, rkl::kFwdTileN);
   p.order_gs = fwd_order().gs;
   p.order_tg = fwd_order().tg;
-  RKL_TRY(rkl::launch_fwd_tiles(p, z_t != nullptr, fused_waves(), s));
-  RKL_TRY(rkl::launch_fwd_combine(p.partial, p.nsplit, p.N, row_mask, loss, stats, s));
+  const int mode = mode_of(z_t, y);
+  RKL_TRY(rkl::launch_fwd_tiles(p, mode, fused_waves(), s));
+  RKL_TRY(rkl::launch_fwd_combine(p.partial, p.nsplit, p.N, row_mask, mode == rkl::kModeLogprobEntropy, out0, out1,
+                                  stats, s));
   return RKL_OK;
 }
 
 int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* h_s, const rkl_bf16* W_s,
-                   const rkl_bf16* h_t, const rkl_bf16* W_t, const float* z_t, const uint8_t* row_mask,
-                   const float* grad, const float* stats, float* dh, float* dW, int accumulate, void* ws,
-                   size_t ws_bytes_given, hipStream_t s) {
+                   const rkl_bf16* h_t, const rkl_bf16* W_t, const float* z_t, const int32_t* y,
+                   const uint8_t* row_mask, const float* grad, const float* grad_h, const float* stats, float* dh,
+                   float* dW, int accumulate, void* ws, size_t ws_bytes_given, hipStream_t s) {
+  const int mode = mode_of(z_t, y);
   if (N > kMaxPitchElems)
     return fail(RKL_UNSUPPORTED, "N=%lld rows exceed the backward's limit of 2^22 per call", (long long)N);
   const BwdLayout L = bwd_layout(N, V, Hs);
@@ -242,7 +253,7 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
   uint16_t* hT = reinterpret_cast<uint16_t*>(base + L.off_hT);
   uint16_t* dz = reinterpret_cast<uint16_t*>(base + L.off_dz);
   uint16_t* w16 = reinterpret_cast<uint16_t*>(base + L.off_w16);
-  RKL_TRY(rkl::launch_grad_scale(grad, row_mask, stats, (int)N, gscale, s));
+  RKL_TRY(rkl::launch_grad_scale(grad, grad_h, row_mask, stats, (int)N, mode == rkl::kModeLogprobEntropy, gscale, s));
   RKL_TRY(rkl::launch_transpose_h(h_s, (int)N, (int)Hs, hT, (int)L.ldT, s));
   const int64_t C = vocab_chunk(N);
   for (int64_t c0 = 0; c0 < V; c0 += C) {
@@ -251,7 +262,7 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
     rkl::BwdParams b{};
     b.N = (int)N; b.V = (int)V; b.Hs = (int)Hs; b.Ht = (int)Ht;
     b.h_s = h_s; b.W_s = W_s; b.h_t = h_t; b.W_t = W_t; b.z_t = z_t;
-    b.row_mask = row_mask; b.grad = grad; b.stats = stats;
+    b.row_mask = row_mask; b.grad = grad; b.grad_h = grad_h; b.y = y; b.stats = stats;
     b.gscale = gscale; b.dz = dz; b.w16 = w16; b.ldz = (int)L.ldz; b.c0 = (int)c0; b.kpad = (int)kpad;
     b.ntv = (int)ceil_div(kpad, rkl::kFwdTileV);
     b.tiles_per_group = bwd_tiles_per_group();
@@ -259,7 +270,7 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
     b.ntok = (int)ceil_div(N, rkl::kFwdTileN);
     b.order_gs = bwd_order().gs;
     b.order_tg = bwd_order().tg;
-    RKL_TRY(rkl::launch_bwd_dz(b, z_t != nullptr, fused_waves(), s));
+    RKL_TRY(rkl::launch_bwd_dz(b, mode, fused_waves(), s));
 
     rkl::DwParams w{};
     w.gscale = gscale; w.dz = dz; w.ldz = (int)L.ldz; w.N = (int)N; w.kpad = (int)kpad; w.width = (int)width;
@@ -350,8 +361,8 @@ int rkl_forward_hidden(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_b
     NEED16(h_s, "h_s"); NEED16(W_s, "W_s"); NEED16(h_t, "h_t"); NEED16(W_t, "W_t");
     NEED4(loss, "loss"); NEED4(stats, "stats");
   }
-  return forward_tiled(N, V, Hs, Ht, h_s, W_s, h_t, W_t, nullptr, row_mask, loss, stats, workspace, workspace_bytes,
-                       static_cast<hipStream_t>(stream));
+  return forward_tiled(N, V, Hs, Ht, h_s, W_s, h_t, W_t, nullptr, nullptr, row_mask, loss, nullptr, stats, workspace,
+                       workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 int rkl_forward_logits(int64_t N, int64_t V, int64_t Hs, const rkl_bf16* h_s, const rkl_bf16* W_s, const float* z_s,
@@ -368,8 +379,8 @@ int rkl_forward_logits(int64_t N, int64_t V, int64_t Hs, const rkl_bf16* h_s, co
     else NEED16(z_s, "z_s");
   }
   if (student_hidden)
-    return forward_tiled(N, V, Hs, 0, h_s, W_s, nullptr, nullptr, z_t, row_mask, loss, stats, workspace,
-                         workspace_bytes, s);
+    return forward_tiled(N, V, Hs, 0, h_s, W_s, nullptr, nullptr, z_t, nullptr, row_mask, loss, nullptr, stats,
+                         workspace, workspace_bytes, s);
   if (N == 0) return RKL_OK;
   RKL_TRY(rkl::launch_fwd_rows_logits(z_s, z_t, (int)N, (int)V, row_mask, loss, stats, s));
   return RKL_OK;
@@ -385,8 +396,8 @@ int rkl_backward_hidden(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_
     NEED16(h_s, "h_s"); NEED16(W_s, "W_s"); NEED16(h_t, "h_t"); NEED16(W_t, "W_t");
     NEED4(stats, "stats"); NEED16(dh_s, "dh_s"); OPT4(grad_loss, "grad_loss");
   }
-  return backward_tiled(N, V, Hs, Ht, h_s, W_s, h_t, W_t, nullptr, row_mask, grad_loss, stats, dh_s, dW_s,
-                        accumulate_dW != 0, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+  return backward_tiled(N, V, Hs, Ht, h_s, W_s, h_t, W_t, nullptr, nullptr, row_mask, grad_loss, nullptr, stats, dh_s,
+                        dW_s, accumulate_dW != 0, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 int rkl_backward_logits(int64_t N, int64_t V, int64_t Hs, const rkl_bf16* h_s, const rkl_bf16* W_s, const float* z_s,
@@ -404,14 +415,40 @@ int rkl_backward_logits(int64_t N, int64_t V, int64_t Hs, const rkl_bf16* h_s, c
       NEED16(h_s, "h_s"); NEED16(W_s, "W_s"); NEED16(z_t, "z_t");
       NEED4(stats, "stats"); NEED16(dh_s, "dh_s"); OPT4(grad_loss, "grad_loss");
     }
-    return backward_tiled(N, V, Hs, 0, h_s, W_s, nullptr, nullptr, z_t, row_mask, grad_loss, stats, dh_s, dW_s,
-                          accumulate_dW != 0, workspace, workspace_bytes, s);
+    return backward_tiled(N, V, Hs, 0, h_s, W_s, nullptr, nullptr, z_t, nullptr, row_mask, grad_loss, nullptr, stats,
+                          dh_s, dW_s, accumulate_dW != 0, workspace, workspace_bytes, s);
   }
   if (dh_s || dW_s) return fail(RKL_INVALID_ARG, "dh_s and dW_s must be NULL when the student is given as logits");
   if (N == 0) return RKL_OK;
   NEED16(z_s, "z_s"); NEED16(z_t, "z_t"); NEED4(stats, "stats"); NEED16(dz_s, "dz_s"); OPT4(grad_loss, "grad_loss");
   RKL_TRY(rkl::launch_bwd_rows_logits(z_s, z_t, (int)N, (int)V, row_mask, grad_loss, stats, dz_s, s));
   return RKL_OK;
+}
+
+int rkl_forward_logprob_entropy(int64_t N, int64_t V, int64_t H, const rkl_bf16* h, const rkl_bf16* W,
+                                const int32_t* y, const uint8_t* row_mask, float* logp, float* entropy, float* stats,
+                                void* workspace, size_t workspace_bytes, rkl_stream_t stream) {
+  if (int rc = check_dims(N, V, H, 0, false, true)) return rc;
+  if (N > 0) {
+    NEED16(h, "h"); NEED16(W, "W"); NEED4(y, "y");
+    NEED4(logp, "logp"); NEED4(entropy, "entropy"); NEED4(stats, "stats");
+  }
+  return forward_tiled(N, V, H, 0, h, W, nullptr, nullptr, nullptr, y, row_mask, logp, entropy, stats, workspace,
+                       workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int rkl_backward_logprob_entropy(int64_t N, int64_t V, int64_t H, const rkl_bf16* h, const rkl_bf16* W,
+                                 const int32_t* y, const uint8_t* row_mask, const float* grad_logp,
+                                 const float* grad_entropy, const float* stats, float* dh, float* dW,
+                                 int accumulate_dW, void* workspace, size_t workspace_bytes, rkl_stream_t stream) {
+  if (int rc = check_dims(N, V, H, 0, false, true)) return rc;
+  NEED16(dW, "dW");
+  if (N > 0) {
+    NEED16(h, "h"); NEED16(W, "W"); NEED4(y, "y"); NEED4(stats, "stats"); NEED16(dh, "dh");
+    OPT4(grad_logp, "grad_logp"); OPT4(grad_entropy, "grad_entropy");
+  }
+  return backward_tiled(N, V, H, 0, h, W, nullptr, nullptr, nullptr, y, row_mask, grad_logp, grad_entropy, stats, dh,
+                        dW, accumulate_dW != 0, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
 }  // extern "C"

@@ -14,6 +14,7 @@ struct FwdParams {
   const uint16_t* h_t;
   const uint16_t* W_t;
   const float* z_t;        // teacher logits [N, V] (teacher-logits payload)
+  const int32_t* y;        // sampled token per row (log-probability / entropy)
   float* partial;          // [nsplit][5][N]
   int tiles_per_split;     // 256-row vocabulary tiles per split
   int nsplit;
@@ -29,7 +30,9 @@ struct BwdParams {
   const uint16_t* W_t;
   const float* z_t;
   const uint8_t* row_mask;
-  const float* grad;
+  const float* grad;       // g of L (reverse KL) or of log p(y) (log-probability / entropy)
+  const float* grad_h;     // g of the entropy (log-probability / entropy)
+  const int32_t* y;        // sampled token per row (log-probability / entropy)
   const float* stats;
   const float* gscale;     // [2]: s, 1/s (powers of two); dz is stored as fp16(s * dz)
   uint16_t* dz;            // [ntok * 128, ldz] fp16 chunk workspace (rows past N written as zero)
@@ -76,12 +79,20 @@ constexpr int kDhTileM = 256, kDhTileN = 128;
 // index (absolute), whatever the backward's chunk width.
 constexpr int kDhSegment = 65536;
 
-hipError_t launch_fwd_tiles(const FwdParams& p, bool teacher_logits, int waves, hipStream_t s);
-hipError_t launch_fwd_combine(const float* partial, int nsplit, int N, const uint8_t* row_mask, float* loss,
-                              float* stats, hipStream_t s);
-hipError_t launch_bwd_dz(const BwdParams& p, bool teacher_logits, int waves, hipStream_t s);
-hipError_t launch_grad_scale(const float* grad, const uint8_t* row_mask, const float* stats, int N, float* out,
-                             hipStream_t s);
+// What the fused kernels compute.
+enum Mode : int {
+  kModeHidden = 0,          // reverse KL, teacher projected from hidden states
+  kModeTeacherLogits = 1,   // reverse KL, teacher logits streamed
+  kModeLogprobEntropy = 2,  // log p(sampled token) and entropy of one projection
+};
+
+hipError_t launch_fwd_tiles(const FwdParams& p, int mode, int waves, hipStream_t s);
+// out0: loss (reverse KL) or log p(y); out1: entropy (log-probability / entropy only)
+hipError_t launch_fwd_combine(const float* partial, int nsplit, int N, const uint8_t* row_mask, bool logprob_entropy,
+                              float* out0, float* out1, float* stats, hipStream_t s);
+hipError_t launch_bwd_dz(const BwdParams& p, int mode, int waves, hipStream_t s);
+hipError_t launch_grad_scale(const float* grad, const float* grad_h, const uint8_t* row_mask, const float* stats,
+                             int N, bool logprob_entropy, float* out, hipStream_t s);
 hipError_t launch_transpose_h(const uint16_t* h, int N, int H, uint16_t* hT, int ldT, hipStream_t s);
 hipError_t launch_dw(const DwParams& p, int waves, hipStream_t s);
 hipError_t launch_dh(const DhParams& p, int waves, hipStream_t s);

@@ -115,6 +115,49 @@ __device__ __forceinline__ void fold_tile(const f32x16 (&zs)[FM][FN], const f32x
   }
 }
 
+// Log-probability / entropy fold of one tile's token column fn: running
+// m, S = sum e^{z - m}, B = sum e^{z - m} z (B rescales like S), and zy = the
+// logit of the row's sampled token yv when this lane holds it (kNegBig
+// otherwise, so a max merges it).  lse = m + log S, the entropy is
+// lse - B / S and log p(y) = zy - lse (slime page, summary: log-probability
+// and entropy of the compacted rows).
+template <bool TAIL, int FM, int FN>
+__device__ __forceinline__ void fold_lpe(const f32x16 (&zs)[FM][FN], int fn, int vrow, int V, int yv, float& ms,
+                                         float& ss, float& bb, float& zy) {
+#pragma unroll
+  for (int fm = 0; fm < FM; ++fm) {
+    float tms = kNegBig;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const bool ok = !TAIL || (vrow + fm * 32 + 8 * (i >> 2) + (i & 3) < V);
+      if (ok) tms = fmaxf(tms, zs[fm][fn][i]);
+    }
+    const float nms = fmaxf(ms, tms);
+    const float fs = ex2((ms - nms) * kL2E);
+    const float cs = nms * kL2E;
+    float ps0 = 0.f, ps1 = 0.f, pb0 = 0.f, pb1 = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int v = vrow + fm * 32 + 8 * (i >> 2) + (i & 3);
+      const bool ok = !TAIL || v < V;
+      if (ok) {
+        const float x = zs[fm][fn][i];
+        const float es = ex2(fmaf(x, kL2E, -cs));
+        if (i & 1) {
+          ps1 += es; pb1 = fmaf(es, x, pb1);
+        } else {
+          ps0 += es; pb0 = fmaf(es, x, pb0);
+        }
+        if (v == yv) zy = x;
+      }
+    }
+    ss = fmaf(ss, fs, ps0 + ps1);
+    bb = fmaf(bb, fs, pb0 + pb1);
+    ms = nms;
+    __builtin_amdgcn_sched_barrier(0);
+  }
+}
+
 // Teacher logits read into the accumulator layout (teacher-logits payload).
 template <bool VEC4, int FM, int FN>
 __device__ __forceinline__ void load_zt(f32x16 (&zt)[FM][FN], const float* __restrict__ z_t, int N, int V,
@@ -281,7 +324,9 @@ __device__ __forceinline__ void dual_stream(const DualOps& o, int njobs, char* l
   dma_barrier<0>();
 }
 
-template <int MODE, bool VEC4, int NW>   // MODE 0: hidden teacher; 1: teacher logits
+// MODE 0: hidden teacher; 1: teacher logits; 2: log-probability / entropy
+// (one projection; the statistics slots hold m, S, B, zy, 0).
+template <int MODE, bool VEC4, int NW>
 __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void fwd_tiles(FwdParams p) {
   using F = Fused<NW>;
   constexpr int FFM = F::FM, FFN = F::FN;
@@ -307,6 +352,12 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void fwd_tiles(FwdParams p)
   o.W[0] = p.W_s; o.h[0] = p.h_s; o.H[0] = p.Hs; o.nk[0] = p.Hs / kKT;
   o.W[1] = p.W_t; o.h[1] = p.h_t; o.H[1] = p.Ht; o.nk[1] = MODE == 0 ? p.Ht / kKT : 0;
   o.V = p.V; o.N = p.N; o.n0 = n0; o.v0 = vt0 * FBM;
+  int yv[FFN];   // sampled token of this lane's token columns (MODE 2)
+#pragma unroll
+  for (int fn = 0; fn < FFN; ++fn) {
+    const int n = n0 + brow0 + fn * 32 + (lane & 31);
+    yv[fn] = (MODE == 2 && n < p.N) ? p.y[n] : -1;
+  }
 
   dual_stream<NW>(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, [&](int job, char*) {
     const int v0 = (vt0 + job) * FBM;
@@ -314,12 +365,20 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void fwd_tiles(FwdParams p)
     const int vrow = v0 + arow0 + lrow;
     if (v0 + FBM <= p.V) {
 #pragma unroll
-      for (int fn = 0; fn < FFN; ++fn)
-        fold_tile<false>(zs, zt, fn, vrow, p.V, ms[fn], ss[fn], aa[fn], mt[fn], st[fn]);
+      for (int fn = 0; fn < FFN; ++fn) {
+        if (MODE == 2)
+          fold_lpe<false>(zs, fn, vrow, p.V, yv[fn], ms[fn], ss[fn], aa[fn], mt[fn]);
+        else
+          fold_tile<false>(zs, zt, fn, vrow, p.V, ms[fn], ss[fn], aa[fn], mt[fn], st[fn]);
+      }
     } else {
 #pragma unroll
-      for (int fn = 0; fn < FFN; ++fn)
-        fold_tile<true>(zs, zt, fn, vrow, p.V, ms[fn], ss[fn], aa[fn], mt[fn], st[fn]);
+      for (int fn = 0; fn < FFN; ++fn) {
+        if (MODE == 2)
+          fold_lpe<true>(zs, fn, vrow, p.V, yv[fn], ms[fn], ss[fn], aa[fn], mt[fn]);
+        else
+          fold_tile<true>(zs, zt, fn, vrow, p.V, ms[fn], ss[fn], aa[fn], mt[fn], st[fn]);
+      }
     }
   });
 
@@ -363,15 +422,19 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void fwd_tiles(FwdParams p)
   }
 }
 
-// Split combine: lse = m + log S per side; L = A / S_s - (lse_s - lse_t).
-// 32 rows per workgroup; the 8 thread groups each merge every 8th split
-// (coalesced over rows), then group 0 merges the 8 results in a fixed order,
-// so the result depends on V (the split plan) only, never on N.
+// Split combine.  Reverse KL: lse = m + log S per side, L = A / S_s -
+// (lse_s - lse_t), stats (lse_s, lse_t, L, log p_max).  Log-probability /
+// entropy (LPE): lse = m + log S, H = lse - B / S, log p(y) = zy - lse, stats
+// (lse, H, log p(y), log p_max).  32 rows per workgroup; the 8 thread groups
+// each merge every 8th split (coalesced over rows), then group 0 merges the 8
+// results in a fixed order, so the result depends on V (the split plan) only,
+// never on N.
 constexpr int kCombRows = 32, kCombWays = 8;
 
+template <bool LPE>
 __global__ __launch_bounds__(256) void fwd_combine(const float* __restrict__ partial, int nsplit, int N,
-                                                   const uint8_t* __restrict__ row_mask, float* __restrict__ loss,
-                                                   float* __restrict__ stats) {
+                                                   const uint8_t* __restrict__ row_mask, float* __restrict__ out0,
+                                                   float* __restrict__ out1, float* __restrict__ stats) {
   __shared__ float red[kCombWays][5][kCombRows];
   const int r = threadIdx.x % kCombRows, j = threadIdx.x / kCombRows;
   const int n = blockIdx.x * kCombRows + r;
@@ -392,16 +455,29 @@ __global__ __launch_bounds__(256) void fwd_combine(const float* __restrict__ par
     merge2(mt, st, red[q][3][r], red[q][4][r]);
   }
   const float log_ss = logf(ss);
+  const bool dead = row_mask && row_mask[n] == 0;
   float lse_s = ms + log_ss;
-  float lse_t = mt + logf(st);
-  float L = aa / ss - (lse_s - lse_t);
   float lpmax = -log_ss;   // log of the largest student probability
-  if (row_mask && row_mask[n] == 0) { L = 0.f; lse_s = 0.f; lse_t = 0.f; lpmax = 0.f; }
-  loss[n] = L;
-  stats[4 * (int64_t)n + 0] = lse_s;
-  stats[4 * (int64_t)n + 1] = lse_t;
-  stats[4 * (int64_t)n + 2] = L;
-  stats[4 * (int64_t)n + 3] = lpmax;
+  if (LPE) {
+    float H = lse_s - aa / ss;
+    float lpy = mt - lse_s;
+    if (dead) { lse_s = 0.f; H = 0.f; lpy = 0.f; lpmax = 0.f; }
+    out0[n] = lpy;
+    out1[n] = H;
+    stats[4 * (int64_t)n + 0] = lse_s;
+    stats[4 * (int64_t)n + 1] = H;
+    stats[4 * (int64_t)n + 2] = lpy;
+    stats[4 * (int64_t)n + 3] = lpmax;
+  } else {
+    float lse_t = mt + logf(st);
+    float L = aa / ss - (lse_s - lse_t);
+    if (dead) { L = 0.f; lse_s = 0.f; lse_t = 0.f; lpmax = 0.f; }
+    out0[n] = L;
+    stats[4 * (int64_t)n + 0] = lse_s;
+    stats[4 * (int64_t)n + 1] = lse_t;
+    stats[4 * (int64_t)n + 2] = L;
+    stats[4 * (int64_t)n + 3] = lpmax;
+  }
 }
 
 // ===========================================================================
@@ -413,15 +489,27 @@ __global__ __launch_bounds__(256) void fwd_combine(const float* __restrict__ par
 // bulk of dz then sits in fp16's normal range, and |w - L| up to ~2000 still
 // fits below fp16's maximum (larger values saturate).  dh and dW are
 // multiplied by 1/s (exact).
+// Log-probability / entropy: |dz_v| <= 2 |g_lp| + |g_H| (p_v |log p_v| +
+// p_v H) <= 2 |g_lp| + |g_H| (1 + H), so that bound takes the place of
+// g * p_max: s * dz stays below 32.
 // ===========================================================================
-__global__ __launch_bounds__(1024) void grad_scale(const float* __restrict__ grad, const uint8_t* __restrict__ row_mask,
+template <bool LPE>
+__global__ __launch_bounds__(1024) void grad_scale(const float* __restrict__ grad, const float* __restrict__ grad_h,
+                                                   const uint8_t* __restrict__ row_mask,
                                                    const float* __restrict__ stats, int N, float* __restrict__ out) {
   __shared__ float red[1024];
   const int tid = threadIdx.x;
   float m = 0.f;
   for (int n = tid; n < N; n += 1024) {
     const bool live = !row_mask || row_mask[n] != 0;
-    if (live) m = fmaxf(m, (grad ? fabsf(grad[n]) : 1.0f) * expf(stats[4 * (int64_t)n + 3]));
+    if (!live) continue;
+    const float g = grad ? fabsf(grad[n]) : 1.0f;
+    if (LPE) {
+      const float gh = grad_h ? fabsf(grad_h[n]) : 0.0f;
+      m = fmaxf(m, 2.0f * g + gh * (1.0f + fabsf(stats[4 * (int64_t)n + 1])));
+    } else {
+      m = fmaxf(m, g * expf(stats[4 * (int64_t)n + 3]));
+    }
   }
   red[tid] = m;
   __syncthreads();
@@ -446,11 +534,12 @@ __global__ __launch_bounds__(1024) void grad_scale(const float* __restrict__ gra
 // pk[fm][fn][run] = 4 dwords.  The arithmetic is branch-free: entries past V
 // (TAIL, the last vocabulary tile only) and dead token columns become zero by
 // selection, so a dead row stays exactly zero whatever its logits are.
-// vrow = vocabulary index of this lane's row 0 in block fm = 0.
-template <bool TAIL, int FM, int FN>
+// vrow = vocabulary index of this lane's row 0 in block fm = 0; elem(z_s,
+// z_t, fn, v) gives s * dz of one entry (v = its vocabulary index).
+template <bool TAIL, int FM, int FN, class Elem>
 __device__ __forceinline__ void dz_pack(const f32x16 (&zs)[FM][FN], const f32x16 (&zt)[FM][FN],
-                                        uint32_t (&pk)[FM][FN][2][4], const bool (&live)[FN], const float (&gs)[FN],
-                                        const float (&css)[FN], const float (&cst)[FN], int vrow, int V) {
+                                        uint32_t (&pk)[FM][FN][2][4], const bool (&live)[FN], int vrow, int V,
+                                        Elem elem) {
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
 #pragma unroll
@@ -467,9 +556,10 @@ __device__ __forceinline__ void dz_pack(const f32x16 (&zs)[FM][FN], const f32x16
           // compiler cannot merge the two copies' arithmetic above the branch
           // that selects them -- that computes every entry at once and spills)
           if (TAIL) asm volatile("" : "+v"(a));
-          float d = gs[fn] * ex2(fmaf(a, kL2E, -css[fn])) * ((a - bb) - cst[fn]);
+          const int v = vrow + fm * 32 + 8 * gq + e;
+          float d = elem(a, bb, fn, v);
           d = __builtin_amdgcn_fmed3f(d, -65504.f, 65504.f);
-          if (TAIL) d = (vrow + fm * 32 + 8 * gq + e < V) ? d : 0.f;
+          if (TAIL) d = v < V ? d : 0.f;
           dv[e] = d;
         }
 #pragma unroll
@@ -503,7 +593,8 @@ __device__ __forceinline__ void dz_pack(const f32x16 (&zs)[FM][FN], const f32x16
 // of the current chunk and write s * dz, dz = g p_s ((z_s - z_t) - (lse_s -
 // lse_t + L)), rounded to fp16 into the chunk workspace dz[N, ldz]
 // (column = v - c0).  Columns in [width, kpad) are written as zero; rows with
-// row_mask 0 are zero.
+// row_mask 0 are zero.  MODE 2 recomputes the one projection and writes the
+// log-probability / entropy gradient instead (see the per-token constants).
 // ===========================================================================
 template <int MODE, bool VEC4, int NW>
 __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams p) {
@@ -520,20 +611,35 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
   const int arow0 = wm * (FBM / F::kWM), brow0 = wn * (FBN / 2);
   const int lrow = 4 * (lane >> 5);
 
-  // per-token constants of this lane's token columns
+  // per-token constants of this lane's token columns.  Reverse KL:
+  //   s dz = gs p ((z_s - z_t) - cst),  gs = s g, cst = lse_s - lse_t + L;
+  // log-probability / entropy (MODE 2), lp = z - lse:
+  //   s dz = gs (1[v = y] - p) - ge p (lp + H) = -p (ge z + cst) + 1[v = y] gs,
+  //   gs = s g_lp, ge = s g_H, cst = gs + ge (H - lse).
+  // css = lse_s log2(e): p = 2^(z log2(e) - css).
   bool live[FFN];
-  float gs[FFN], cst[FFN], css[FFN];
+  float gs[FFN], ge[FFN], cst[FFN], css[FFN];
+  int yv[FFN];
 #pragma unroll
   for (int fn = 0; fn < FFN; ++fn) {
     const int n = n0 + brow0 + fn * 32 + (lane & 31);
     live[fn] = n < p.N && (!p.row_mask || p.row_mask[n] != 0);
     const int nc = min(n, p.N - 1);
     const float lse_s = p.stats[4 * (int64_t)nc + 0];
-    const float lse_t = p.stats[4 * (int64_t)nc + 1];
-    const float L = p.stats[4 * (int64_t)nc + 2];
     gs[fn] = (p.grad ? p.grad[nc] : 1.0f) * p.gscale[0];
-    cst[fn] = (lse_s - lse_t) + L;
     css[fn] = lse_s * kL2E;
+    if (MODE == 2) {
+      const float H = p.stats[4 * (int64_t)nc + 1];
+      ge[fn] = (p.grad_h ? p.grad_h[nc] : 0.0f) * p.gscale[0];
+      cst[fn] = gs[fn] + ge[fn] * (H - lse_s);
+      yv[fn] = p.y[nc];
+    } else {
+      const float lse_t = p.stats[4 * (int64_t)nc + 1];
+      const float L = p.stats[4 * (int64_t)nc + 2];
+      cst[fn] = (lse_s - lse_t) + L;
+      ge[fn] = 0.f;
+      yv[fn] = -1;
+    }
   }
 
   f32x16 zs[FFM][FFN], zt[FFM][FFN];
@@ -566,10 +672,24 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
     if (MODE == 1) load_zt<VEC4>(zt, p.z_t, p.N, p.V, v0 + arow0 + lrow, n0 + brow0 + (lane & 31), lane);
     const int hi = lane >> 5;
     uint32_t pk[FFM][FFN][2][4];   // [fm][fn][run][dword]
-    if (v0 + FBM <= p.V)
-      dz_pack<false>(zs, zt, pk, live, gs, css, cst, v0 + arow0 + lrow, p.V);
-    else
-      dz_pack<true>(zs, zt, pk, live, gs, css, cst, v0 + arow0 + lrow, p.V);
+    auto kl = [&](float a, float bb, int fn, int) {
+      return gs[fn] * ex2(fmaf(a, kL2E, -css[fn])) * ((a - bb) - cst[fn]);
+    };
+    auto lpe = [&](float a, float, int fn, int v) {
+      const float d = -ex2(fmaf(a, kL2E, -css[fn])) * fmaf(ge[fn], a, cst[fn]);
+      return v == yv[fn] ? d + gs[fn] : d;
+    };
+    if (MODE == 2) {
+      if (v0 + FBM <= p.V)
+        dz_pack<false>(zs, zt, pk, live, v0 + arow0 + lrow, p.V, lpe);
+      else
+        dz_pack<true>(zs, zt, pk, live, v0 + arow0 + lrow, p.V, lpe);
+    } else {
+      if (v0 + FBM <= p.V)
+        dz_pack<false>(zs, zt, pk, live, v0 + arow0 + lrow, p.V, kl);
+      else
+        dz_pack<true>(zs, zt, pk, live, v0 + arow0 + lrow, p.V, kl);
+    }
     // Stores go through the free LDS stage, 64 tokens per round: the waves
     // holding those tokens write a [64 token][256 vocabulary] fp16 tile (16-byte
     // chunk c of row t at chunk c ^ (t % 32), so neither side has bank
@@ -886,54 +1006,65 @@ static inline unsigned grid1(int64_t n, int64_t per, int64_t cap) {
 }
 
 template <int NW>
-static void fwd_tiles_launch(const FwdParams& p, bool teacher_logits, unsigned nb, hipStream_t s) {
+static void fwd_tiles_launch(const FwdParams& p, int mode, unsigned nb, hipStream_t s) {
   constexpr unsigned nt = Fused<NW>::kThreads;
-  if (!teacher_logits)
-    fwd_tiles<0, true, NW><<<nb, nt, 0, s>>>(p);
+  if (mode == kModeHidden)
+    fwd_tiles<kModeHidden, true, NW><<<nb, nt, 0, s>>>(p);
+  else if (mode == kModeLogprobEntropy)
+    fwd_tiles<kModeLogprobEntropy, true, NW><<<nb, nt, 0, s>>>(p);
   else if (p.V % 4 == 0)
-    fwd_tiles<1, true, NW><<<nb, nt, 0, s>>>(p);
+    fwd_tiles<kModeTeacherLogits, true, NW><<<nb, nt, 0, s>>>(p);
   else
-    fwd_tiles<1, false, NW><<<nb, nt, 0, s>>>(p);
+    fwd_tiles<kModeTeacherLogits, false, NW><<<nb, nt, 0, s>>>(p);
 }
 
-hipError_t launch_fwd_tiles(const FwdParams& p, bool teacher_logits, int waves, hipStream_t s) {
+hipError_t launch_fwd_tiles(const FwdParams& p, int mode, int waves, hipStream_t s) {
   const unsigned nb = (unsigned)(p.nsplit * p.ntok);
   if (waves == 8)
-    fwd_tiles_launch<8>(p, teacher_logits, nb, s);
+    fwd_tiles_launch<8>(p, mode, nb, s);
   else
-    fwd_tiles_launch<4>(p, teacher_logits, nb, s);
+    fwd_tiles_launch<4>(p, mode, nb, s);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_combine(const float* partial, int nsplit, int N, const uint8_t* row_mask, float* loss,
-                              float* stats, hipStream_t s) {
-  fwd_combine<<<(N + kCombRows - 1) / kCombRows, 256, 0, s>>>(partial, nsplit, N, row_mask, loss, stats);
+hipError_t launch_fwd_combine(const float* partial, int nsplit, int N, const uint8_t* row_mask, bool logprob_entropy,
+                              float* out0, float* out1, float* stats, hipStream_t s) {
+  const unsigned nb = (unsigned)((N + kCombRows - 1) / kCombRows);
+  if (logprob_entropy)
+    fwd_combine<true><<<nb, 256, 0, s>>>(partial, nsplit, N, row_mask, out0, out1, stats);
+  else
+    fwd_combine<false><<<nb, 256, 0, s>>>(partial, nsplit, N, row_mask, out0, out1, stats);
   return hipGetLastError();
 }
 
 template <int NW>
-static void bwd_dz_launch(const BwdParams& p, bool teacher_logits, unsigned nb, hipStream_t s) {
+static void bwd_dz_launch(const BwdParams& p, int mode, unsigned nb, hipStream_t s) {
   constexpr unsigned nt = Fused<NW>::kThreads;
-  if (!teacher_logits)
-    bwd_dz_tiles<0, true, NW><<<nb, nt, 0, s>>>(p);
+  if (mode == kModeHidden)
+    bwd_dz_tiles<kModeHidden, true, NW><<<nb, nt, 0, s>>>(p);
+  else if (mode == kModeLogprobEntropy)
+    bwd_dz_tiles<kModeLogprobEntropy, true, NW><<<nb, nt, 0, s>>>(p);
   else if (p.V % 4 == 0)
-    bwd_dz_tiles<1, true, NW><<<nb, nt, 0, s>>>(p);
+    bwd_dz_tiles<kModeTeacherLogits, true, NW><<<nb, nt, 0, s>>>(p);
   else
-    bwd_dz_tiles<1, false, NW><<<nb, nt, 0, s>>>(p);
+    bwd_dz_tiles<kModeTeacherLogits, false, NW><<<nb, nt, 0, s>>>(p);
 }
 
-hipError_t launch_bwd_dz(const BwdParams& p, bool teacher_logits, int waves, hipStream_t s) {
+hipError_t launch_bwd_dz(const BwdParams& p, int mode, int waves, hipStream_t s) {
   const unsigned nb = (unsigned)(p.ngroups * p.ntok);
   if (waves == 8)
-    bwd_dz_launch<8>(p, teacher_logits, nb, s);
+    bwd_dz_launch<8>(p, mode, nb, s);
   else
-    bwd_dz_launch<4>(p, teacher_logits, nb, s);
+    bwd_dz_launch<4>(p, mode, nb, s);
   return hipGetLastError();
 }
 
-hipError_t launch_grad_scale(const float* grad, const uint8_t* row_mask, const float* stats, int N, float* out,
-                             hipStream_t s) {
-  grad_scale<<<1, 1024, 0, s>>>(grad, row_mask, stats, N, out);
+hipError_t launch_grad_scale(const float* grad, const float* grad_h, const uint8_t* row_mask, const float* stats,
+                             int N, bool logprob_entropy, float* out, hipStream_t s) {
+  if (logprob_entropy)
+    grad_scale<true><<<1, 1024, 0, s>>>(grad, grad_h, row_mask, stats, N, out);
+  else
+    grad_scale<false><<<1, 1024, 0, s>>>(grad, grad_h, row_mask, stats, N, out);
   return hipGetLastError();
 }
 

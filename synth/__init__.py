@@ -30,7 +30,7 @@ from typing import Optional
 import numpy as np
 
 # tensor ids for the sub-streams
-_HS, _HT, _WS, _WT, _ZS, _ZT, _MASK, _PERT, _G = range(9)
+_HS, _HT, _WS, _WT, _ZS, _ZT, _MASK, _PERT, _G, _Y, _GH = range(11)
 
 _ROW_CHUNK = 4096
 
@@ -207,3 +207,21 @@ def config(name: str) -> Case:
     if name == "c5":
         return qwen_shaped(seed=5, B=2, S=16385, Hs=2048, Ht=4096, response=2048)
     raise KeyError(name)
+
+
+# ------------------------------------------------- log-probability / entropy
+
+def sampled_tokens(seed: int, T: int, V: int) -> np.ndarray:
+    """int32 [T] token ids, uniform on [0, V): stands in for the tokens a
+    policy sampled (any id is a valid input; uniform ids reach every
+    vocabulary tile, the ragged last one included)."""
+    return _rng(seed, _Y).integers(0, V, size=T, dtype=np.int64).astype(np.int32)
+
+
+def upstream_grads(seed: int, T: int):
+    """(g_logp, g_entropy) fp32 [T] each: per-token upstream gradients of the
+    log-probability and of the entropy, N(0, 1) and U(-0.1, 0.1) (an entropy
+    bonus is a small coefficient)."""
+    g = _rng(seed, _G).standard_normal(T).astype(np.float32)
+    gh = _rng(seed, _GH).uniform(-0.1, 0.1, size=T).astype(np.float32)
+    return g, gh

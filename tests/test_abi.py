@@ -29,6 +29,7 @@ def test_header_declares_the_path():
     names = declared_functions()
     for want in ("rkl_compact_rows", "rkl_gather_rows", "rkl_scatter_rows", "rkl_workspace_bytes",
                  "rkl_forward_hidden", "rkl_forward_logits", "rkl_backward_hidden", "rkl_backward_logits",
+                 "rkl_forward_logprob_entropy", "rkl_backward_logprob_entropy",
                  "rkl_last_error", "rkl_version"):
         assert want in names
 
@@ -107,6 +108,29 @@ def test_backward_rejects():
     assert L.rkl_backward_hidden((1 << 22) + 1, 100, 64, 64, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE,
                                  0, FAKE, 1 << 62, None) == 2
     assert "2^22" in L.rkl_last_error().decode()
+
+
+def test_logprob_entropy_rejects():
+    L = R.lib()
+    fwd = L.rkl_forward_logprob_entropy
+    # sampled tokens missing
+    assert fwd(4, 100, 64, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert "y" in L.rkl_last_error().decode()
+    # entropy output missing
+    assert fwd(4, 100, 64, FAKE, FAKE, FAKE, None, FAKE, None, FAKE, FAKE, 1 << 30, None) == 1
+    # width not a multiple of 64
+    assert fwd(4, 100, 96, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 2
+    # workspace too small
+    assert fwd(4, 100, 64, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, FAKE, 16, None) == 3
+    bwd = L.rkl_backward_logprob_entropy
+    # dW missing
+    assert bwd(4, 100, 64, FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, None, 0, FAKE, 1 << 30, None) == 1
+    # misaligned upstream gradient
+    assert bwd(4, 100, 64, FAKE, FAKE, FAKE, None, MISALIGNED, None, FAKE, FAKE, FAKE, 0, FAKE, 1 << 30, None) == 1
+    assert "grad_logp" in L.rkl_last_error().decode()
+    # more rows than the backward's per-call limit
+    assert bwd((1 << 22) + 1, 100, 64, FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, FAKE, 0, FAKE, 1 << 62,
+               None) == 2
 
 
 def test_compaction_and_copies_reject():
