@@ -13,6 +13,11 @@ every one of the T = B(S-1) = 4096 positions trainable (N = 4096), Hs = Ht =
 --payload logits times the same step with the teacher given as fp32 logits
 [N, V] (formed once from the same tensors) instead of hidden states.
 
+--workload logprob_entropy times the compact actor path instead: per row the
+log-probability of a sampled token and the entropy of softmax(h_s W_s^T)
+(forward), and the gradients dh, dW of g_lp logp + g_H H (backward), on the
+same student tensors.
+
 Prints one JSON line (rank 0):
   value = masked tokens/s for forward + backward;
   roofline = the fused forward kernel against the dense bf16 MFMA peak;
@@ -46,6 +51,8 @@ def parse():
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--payload", choices=("hidden", "logits"), default="hidden",
                     help="teacher payload: hidden states (default, the headline) or fp32 logits [N, V]")
+    ap.add_argument("--workload", choices=("reverse_kl", "logprob_entropy"), default="reverse_kl",
+                    help="reverse KL distillation step (default, the headline) or log-probability + entropy")
     ap.add_argument("--report-c5", action="store_true",
                     help="time compact vs full-row on the long-prompt workload (T=32768, N=4096, Ht=4096)")
     return ap.parse_args()
@@ -182,6 +189,151 @@ def cpu_baseline(case, target_s: float):
                       f"of the weights done once outside the timed region"}
 
 
+def cpu_baseline_lpe(case, y, target_s: float):
+    """Time the fp64 log-probability / entropy oracle (forward + backward) on a
+    bounded row sample."""
+    import numpy as np
+    from oracle import logprob_entropy_oracle as E
+    from oracle import rkl_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    W = O.widen_bf16(case.W_s)
+
+    def run(nrows):
+        h = O.widen_bf16(case.h_s[:nrows])
+        t0 = time.perf_counter()
+        E.forward(h, W, y[:nrows])
+        E.backward(h, W, y[:nrows])
+        return time.perf_counter() - t0
+
+    cap = min(4096, case.T)
+    n = 32
+    t = run(n)
+    while t < target_s / 2 and n < cap:
+        n = int(min(cap, max(n + 32, n * target_s / max(t, 1e-3))) // 32 * 32)
+        t = run(n)
+    return {"value": n / t, "unit": "masked tokens/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"fp64 numpy oracle, log-probability + entropy forward+backward (logp, H, dh, dW) over the "
+                      f"first {n} of the {case.T} positions of this workload, full V={case.V}; {t:.1f} s wall; "
+                      f"bf16->fp64 widening of the weights done once outside the timed region"}
+
+
+def bench_logprob_entropy(args):
+    """The compact actor log-probability / entropy step on the headline tensors."""
+    import numpy as np
+    import torch
+
+    import lm_head_reverse_amd as R
+    import synth
+
+    R.lib()
+    dev = torch.device("cuda:0")
+    print("[bench] generating inputs", file=sys.stderr, flush=True)
+    case = synth.config("headline")
+    T, V, H = case.T, case.V, case.Hs
+    y_np = synth.sampled_tokens(3, T, V)
+    h_all = torch.from_numpy(case.h_s.view(np.int16)).to(dev).view(torch.bfloat16)
+    W = torch.from_numpy(case.W_s.view(np.int16)).to(dev).view(torch.bfloat16)
+    y_all = torch.from_numpy(y_np).to(dev)
+    mask = torch.from_numpy(case.mask).to(dev)
+    N_expected = int(case.mask.sum())
+    # token-mean upstream gradients: policy term and a small entropy bonus
+    g_lp_all = torch.full((T,), 1.0 / N_expected, dtype=torch.float32, device=dev)
+    g_h_all = torch.full((T,), -0.01 / N_expected, dtype=torch.float32, device=dev)
+    dW = torch.empty((V, H), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        idx, N = R.compact_rows(mask)
+        h = R.gather_rows(h_all, idx)
+        y = R.gather_rows(y_all, idx)
+        gl, gh = R.gather_rows(g_lp_all, idx), R.gather_rows(g_h_all, idx)
+        logp, ent, stats = R.forward_logprob_entropy(h, W, y)
+        lp_pos, ent_pos = R.scatter_rows(logp, idx, T), R.scatter_rows(ent, idx, T)
+        dh, _ = R.backward_logprob_entropy(h, W, y, stats, grad_logp=gl, grad_entropy=gh, dW=dW)
+        return N, lp_pos, ent_pos, R.scatter_rows(dh, idx, T)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        N, lp_pos, ent_pos, _ = step()
+    torch.cuda.synchronize()
+    assert N == N_expected
+    assert np.all(np.isfinite(lp_pos.cpu().numpy())) and np.all(np.isfinite(ent_pos.cpu().numpy()))
+
+    print("[bench] timing", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        N, _, _, _ = step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+    tok_s = N * args.steps / wall
+
+    idx, _ = R.compact_rows(mask)
+    h, y = R.gather_rows(h_all, idx), R.gather_rows(y_all, idx)
+    gl, gh = R.gather_rows(g_lp_all, idx), R.gather_rows(g_h_all, idx)
+    _, _, stats = R.forward_logprob_entropy(h, W, y)
+    stream = torch.cuda.current_stream(dev)
+    reps = max(args.steps, 5)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(reps):
+        R.forward_logprob_entropy(h, W, y)
+    ev[1].record(stream)
+    for _ in range(reps):
+        R.backward_logprob_entropy(h, W, y, stats, grad_logp=gl, grad_entropy=gh, dW=dW)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = ev[0].elapsed_time(ev[1]) / reps
+    bwd_ms = ev[1].elapsed_time(ev[2]) / reps
+
+    flop_fwd = 2.0 * N * V * H
+    flop_step = 8.0 * N * V * H   # forward + recompute + dh + dW
+    achieved_fwd = flop_fwd / (fwd_ms * 1e-3)
+    out = {
+        "metric": "masked tokens/sec fwd+bwd log-prob + entropy (H2048,V152k); MFMA % peak",
+        "value": round(tok_s, 1),
+        "unit": "masked tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "Qwen3-1.7B-shaped actor log-probability + entropy, B=4 S=1025 (T=N=4096 "
+                               "trainable), H=2048, V=151936, uniform sampled tokens",
+                   "B": case.B, "S": case.S, "N": int(N), "H": H, "V": V, "parallelism": "single GPU"},
+        "mfma_peak_frac_fwd_bwd": round(flop_step / (ms_step * 1e-3) / PEAK_BF16, 4),
+        "fwd_tokens_per_s": round(N / (fwd_ms * 1e-3), 1),
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "mfma_peak_frac_fwd": round(achieved_fwd / PEAK_BF16, 4),
+        "mfma_peak_frac_bwd": round((flop_step - flop_fwd) / (bwd_ms * 1e-3) / PEAK_BF16, 4),
+        "roofline": {
+            "kernel": "fwd_tiles<2> (fused forward: one projection + online log-sum-exp / entropy / sampled-logit "
+                      "epilogue; event time of the forward call, which adds the per-row split combine)",
+            "bound": "mfma",
+            "achieved": round(achieved_fwd / 1e12, 2),
+            "peak": round(PEAK_BF16 / 1e12, 1),
+            "unit": "TFLOP/s",
+            "frac": round(achieved_fwd / PEAK_BF16, 4),
+            "traffic": None,
+        },
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_lpe(case, y_np, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.profile_copy:
@@ -192,6 +344,8 @@ def main():
         print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}); "
               f"the multi-GPU sharding is described but not built", file=sys.stderr)
         sys.exit(2)
+    if args.workload == "logprob_entropy":
+        return bench_logprob_entropy(args)
 
     import numpy as np
     import torch
