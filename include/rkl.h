@@ -166,6 +166,34 @@ int rkl_backward_logits(int64_t N, int64_t V, int64_t Hs,
                         void* workspace, size_t workspace_bytes, rkl_stream_t stream);
 
 /*
+ * Reverse KL with the teacher chosen per row (NeMo-RL page, first-version
+ * limits: one teacher checkpoint in that version, with the payload column
+ * shaped for a per-row teacher index).  As rkl_forward_hidden, except:
+ *   W_t [K, V, Ht] bf16   the K teachers' output-layer weights, back to back.
+ *   teacher [N] int32     device; row i is projected through W_t[teacher[i]].
+ *                         Ids outside [0, K) are not checked on the device: such
+ *                         a row gets teacher logits 0 (nothing is addressed
+ *                         with the id).
+ *   1 <= K <= 31.
+ * Rows of one teacher need not be contiguous: a 128-row tile holding rows
+ * of several teachers runs one teacher pass per teacher it holds (same
+ * results bit for bit, more work), so grouping rows by teacher is faster.
+ * Workspace: rkl_workspace_bytes(N, V, Hs, Ht).
+ */
+int rkl_forward_hidden_teachers(int64_t N, int64_t V, int64_t Hs, int64_t Ht, int64_t K, const rkl_bf16* h_s,
+                                const rkl_bf16* W_s, const rkl_bf16* h_t, const rkl_bf16* W_t, const int32_t* teacher,
+                                const uint8_t* row_mask, float* loss, float* stats, void* workspace,
+                                size_t workspace_bytes, rkl_stream_t stream);
+
+/* Backward of rkl_forward_hidden_teachers: arguments as rkl_backward_hidden
+ * plus K, W_t [K, V, Ht] and teacher [N] as above. */
+int rkl_backward_hidden_teachers(int64_t N, int64_t V, int64_t Hs, int64_t Ht, int64_t K, const rkl_bf16* h_s,
+                                 const rkl_bf16* W_s, const rkl_bf16* h_t, const rkl_bf16* W_t,
+                                 const int32_t* teacher, const uint8_t* row_mask, const float* grad_loss,
+                                 const float* stats, float* dh_s, float* dW_s, int accumulate_dW, void* workspace,
+                                 size_t workspace_bytes, rkl_stream_t stream);
+
+/*
  * Log-probability of the sampled token and entropy of one projection (slime
  * page, summary: the log-probability / entropy computation of the compact
  * actor path takes the [N, V] logits of the loss-masked rows and returns

@@ -56,6 +56,9 @@ def lib() -> ctypes.CDLL:
         "rkl_forward_logits": ([I64, I64, I64, P, P, P, P, P, P, P, P, SZ, P], I32),
         "rkl_backward_hidden": ([I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, I32, P, SZ, P], I32),
         "rkl_backward_logits": ([I64, I64, I64, P, P, P, P, P, P, P, P, P, I32, P, P, SZ, P], I32),
+        "rkl_forward_hidden_teachers": ([I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+        "rkl_backward_hidden_teachers": ([I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, I32, P, SZ, P],
+                                         I32),
         "rkl_forward_logprob_entropy": ([I64, I64, I64, P, P, P, P, P, P, P, P, SZ, P], I32),
         "rkl_backward_logprob_entropy": ([I64, I64, I64, P, P, P, P, P, P, P, P, P, I32, P, SZ, P], I32),
     }
@@ -367,4 +370,60 @@ def backward_logprob_entropy(h, W, y, stats, grad_logp=None, grad_entropy=None, 
     _check(lib().rkl_backward_logprob_entropy(N, V, H, _ptr(h), _ptr(W), _ptr(y), _ptr(row_mask), _ptr(grad_logp),
                                               _ptr(grad_entropy), _ptr(stats), _ptr(dh), _ptr(dW),
                                               int(bool(accumulate_dW)), _ptr(ws), ws.numel(), _stream(dev)))
+    return dh, dW
+
+
+def forward_hidden_teachers(h_s, W_s, h_t, W_t, teacher, row_mask=None):
+    """Per-row reverse KL with row i's teacher logits h_t[i] W_t[teacher[i]]^T
+    (W_t bf16 [K, V, Ht], teacher int32 [N]).  Returns (loss, stats) as
+    forward_hidden."""
+    torch = _torch()
+    dev = h_s.device
+    N, Hs = h_s.shape
+    K, V, Ht = W_t.shape
+    _need(h_s, "h_s", torch.bfloat16, dev)
+    _need(W_s, "W_s", torch.bfloat16, dev, (V, Hs))
+    _need(h_t, "h_t", torch.bfloat16, dev, (N, Ht))
+    _need(W_t, "W_t", torch.bfloat16, dev)
+    _need(teacher, "teacher", torch.int32, dev, (N,))
+    if row_mask is not None:
+        _need(row_mask, "row_mask", torch.uint8, dev, (N,))
+    loss = torch.empty(N, dtype=torch.float32, device=dev)
+    stats = torch.empty((N, 4), dtype=torch.float32, device=dev)
+    ws = _workspace(dev, workspace_bytes(N, V, Hs, Ht))
+    _check(lib().rkl_forward_hidden_teachers(N, V, Hs, Ht, K, _ptr(h_s), _ptr(W_s), _ptr(h_t), _ptr(W_t),
+                                             _ptr(teacher), _ptr(row_mask), _ptr(loss), _ptr(stats), _ptr(ws),
+                                             ws.numel(), _stream(dev)))
+    return loss, stats
+
+
+def backward_hidden_teachers(h_s, W_s, h_t, W_t, teacher, stats, grad_loss=None, row_mask=None, dW=None,
+                             accumulate_dW=False):
+    """Backward of forward_hidden_teachers: returns (dh_s, dW_s)."""
+    torch = _torch()
+    dev = h_s.device
+    N, Hs = h_s.shape
+    K, V, Ht = W_t.shape
+    _need(h_s, "h_s", torch.bfloat16, dev)
+    _need(W_s, "W_s", torch.bfloat16, dev, (V, Hs))
+    _need(h_t, "h_t", torch.bfloat16, dev, (N, Ht))
+    _need(W_t, "W_t", torch.bfloat16, dev)
+    _need(teacher, "teacher", torch.int32, dev, (N,))
+    _need(stats, "stats", torch.float32, dev, (N, 4))
+    if grad_loss is not None:
+        _need(grad_loss, "grad_loss", torch.float32, dev, (N,))
+    if row_mask is not None:
+        _need(row_mask, "row_mask", torch.uint8, dev, (N,))
+    if dW is None:
+        if accumulate_dW:
+            raise RKLError(RKL_INVALID_ARG, "accumulate_dW needs a dW tensor")
+        dW = torch.empty((V, Hs), dtype=torch.float32, device=dev)
+    else:
+        _need(dW, "dW", torch.float32, dev, (V, Hs))
+    dh = torch.empty((N, Hs), dtype=torch.float32, device=dev)
+    ws = _workspace(dev, workspace_bytes(N, V, Hs, Ht))
+    _check(lib().rkl_backward_hidden_teachers(N, V, Hs, Ht, K, _ptr(h_s), _ptr(W_s), _ptr(h_t), _ptr(W_t),
+                                              _ptr(teacher), _ptr(row_mask), _ptr(grad_loss), _ptr(stats), _ptr(dh),
+                                              _ptr(dW), int(bool(accumulate_dW)), _ptr(ws), ws.numel(),
+                                              _stream(dev)))
     return dh, dW

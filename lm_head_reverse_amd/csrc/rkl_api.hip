@@ -202,14 +202,23 @@ int check_dims(int64_t N, int64_t V, int64_t Hs, int64_t Ht, bool teacher_hidden
 // mode: y != NULL -> log-probability / entropy (out0 = log p(y), out1 =
 // entropy); else reverse KL (out0 = loss) with the teacher as hidden states
 // (z_t NULL) or as logits.
-int mode_of(const float* z_t, const int32_t* y) {
-  return y ? rkl::kModeLogprobEntropy : (z_t ? rkl::kModeTeacherLogits : rkl::kModeHidden);
+int mode_of(const float* z_t, const int32_t* y, const int32_t* teacher) {
+  if (y) return rkl::kModeLogprobEntropy;
+  if (z_t) return rkl::kModeTeacherLogits;
+  return teacher ? rkl::kModeHiddenTeachers : rkl::kModeHidden;
 }
+
+// Per-row teachers: K weights of [V, Ht] each, back to back.
+struct Teachers {
+  const int32_t* teacher = nullptr;   // NULL: one teacher
+  int K = 1;
+  int64_t stride = 0;
+};
 
 int forward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* h_s, const rkl_bf16* W_s,
                   const rkl_bf16* h_t, const rkl_bf16* W_t, const float* z_t, const int32_t* y,
                   const uint8_t* row_mask, float* out0, float* out1, float* stats, void* ws, size_t ws_bytes_given,
-                  hipStream_t s) {
+                  hipStream_t s, Teachers tch = Teachers{}) {
   const size_t need = fwd_ws_bytes(N, V, true);
   if (ws_bytes_given < need)
     return fail(RKL_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes_given, need);
@@ -219,13 +228,14 @@ int forward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* 
   rkl::FwdParams p{};
   p.N = (int)N; p.V = (int)V; p.Hs = (int)Hs; p.Ht = (int)Ht;
   p.h_s = h_s; p.W_s = W_s; p.h_t = h_t; p.W_t = W_t; p.z_t = z_t; p.y = y;
+  p.teacher = tch.teacher; p.K = tch.K; p.wt_stride = tch.stride;
   p.partial = static_cast<float*>(ws);
   p.tiles_per_split = sp.tiles_per_split;
   p.nsplit = sp.nsplit;
   p.ntok = (int)ceil_div(N, rkl::kFwdTileN);
   p.order_gs = fwd_order().gs;
   p.order_tg = fwd_order().tg;
-  const int mode = mode_of(z_t, y);
+  const int mode = mode_of(z_t, y, tch.teacher);
   RKL_TRY(rkl::launch_fwd_tiles(p, mode, fused_waves(), s));
   RKL_TRY(rkl::launch_fwd_combine(p.partial, p.nsplit, p.N, row_mask, mode == rkl::kModeLogprobEntropy, out0, out1,
                                   stats, s));
@@ -235,8 +245,9 @@ int forward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* 
 int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* h_s, const rkl_bf16* W_s,
                    const rkl_bf16* h_t, const rkl_bf16* W_t, const float* z_t, const int32_t* y,
                    const uint8_t* row_mask, const float* grad, const float* grad_h, const float* stats, float* dh,
-                   float* dW, int accumulate, void* ws, size_t ws_bytes_given, hipStream_t s) {
-  const int mode = mode_of(z_t, y);
+                   float* dW, int accumulate, void* ws, size_t ws_bytes_given, hipStream_t s,
+                   Teachers tch = Teachers{}) {
+  const int mode = mode_of(z_t, y, tch.teacher);
   if (N > kMaxPitchElems)
     return fail(RKL_UNSUPPORTED, "N=%lld rows exceed the backward's limit of 2^22 per call", (long long)N);
   const BwdLayout L = bwd_layout(N, V, Hs);
@@ -263,6 +274,7 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
     b.N = (int)N; b.V = (int)V; b.Hs = (int)Hs; b.Ht = (int)Ht;
     b.h_s = h_s; b.W_s = W_s; b.h_t = h_t; b.W_t = W_t; b.z_t = z_t;
     b.row_mask = row_mask; b.grad = grad; b.grad_h = grad_h; b.y = y; b.stats = stats;
+    b.teacher = tch.teacher; b.K = tch.K; b.wt_stride = tch.stride;
     b.gscale = gscale; b.dz = dz; b.w16 = w16; b.ldz = (int)L.ldz; b.c0 = (int)c0; b.kpad = (int)kpad;
     b.ntv = (int)ceil_div(kpad, rkl::kFwdTileV);
     b.tiles_per_group = bwd_tiles_per_group();
@@ -449,6 +461,40 @@ int rkl_backward_logprob_entropy(int64_t N, int64_t V, int64_t H, const rkl_bf16
   }
   return backward_tiled(N, V, H, 0, h, W, nullptr, nullptr, nullptr, y, row_mask, grad_logp, grad_entropy, stats, dh,
                         dW, accumulate_dW != 0, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int rkl_forward_hidden_teachers(int64_t N, int64_t V, int64_t Hs, int64_t Ht, int64_t K, const rkl_bf16* h_s,
+                                const rkl_bf16* W_s, const rkl_bf16* h_t, const rkl_bf16* W_t, const int32_t* teacher,
+                                const uint8_t* row_mask, float* loss, float* stats, void* workspace,
+                                size_t workspace_bytes, rkl_stream_t stream) {
+  if (int rc = check_dims(N, V, Hs, Ht, true, true)) return rc;
+  if (K < 1 || K > 31) return fail(RKL_INVALID_ARG, "K=%lld teachers out of range [1, 31]", (long long)K);
+  if (N > 0) {
+    NEED16(h_s, "h_s"); NEED16(W_s, "W_s"); NEED16(h_t, "h_t"); NEED16(W_t, "W_t"); NEED4(teacher, "teacher");
+    NEED4(loss, "loss"); NEED4(stats, "stats");
+  }
+  Teachers t;
+  t.teacher = teacher; t.K = (int)K; t.stride = V * Ht;
+  return forward_tiled(N, V, Hs, Ht, h_s, W_s, h_t, W_t, nullptr, nullptr, row_mask, loss, nullptr, stats, workspace,
+                       workspace_bytes, static_cast<hipStream_t>(stream), t);
+}
+
+int rkl_backward_hidden_teachers(int64_t N, int64_t V, int64_t Hs, int64_t Ht, int64_t K, const rkl_bf16* h_s,
+                                 const rkl_bf16* W_s, const rkl_bf16* h_t, const rkl_bf16* W_t,
+                                 const int32_t* teacher, const uint8_t* row_mask, const float* grad_loss,
+                                 const float* stats, float* dh_s, float* dW_s, int accumulate_dW, void* workspace,
+                                 size_t workspace_bytes, rkl_stream_t stream) {
+  if (int rc = check_dims(N, V, Hs, Ht, true, true)) return rc;
+  if (K < 1 || K > 31) return fail(RKL_INVALID_ARG, "K=%lld teachers out of range [1, 31]", (long long)K);
+  NEED16(dW_s, "dW_s");
+  if (N > 0) {
+    NEED16(h_s, "h_s"); NEED16(W_s, "W_s"); NEED16(h_t, "h_t"); NEED16(W_t, "W_t"); NEED4(teacher, "teacher");
+    NEED4(stats, "stats"); NEED16(dh_s, "dh_s"); OPT4(grad_loss, "grad_loss");
+  }
+  Teachers t;
+  t.teacher = teacher; t.K = (int)K; t.stride = V * Ht;
+  return backward_tiled(N, V, Hs, Ht, h_s, W_s, h_t, W_t, nullptr, nullptr, row_mask, grad_loss, nullptr, stats, dh_s,
+                        dW_s, accumulate_dW != 0, workspace, workspace_bytes, static_cast<hipStream_t>(stream), t);
 }
 
 }  // extern "C"

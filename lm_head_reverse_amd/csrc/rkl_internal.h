@@ -15,6 +15,9 @@ struct FwdParams {
   const uint16_t* W_t;
   const float* z_t;        // teacher logits [N, V] (teacher-logits payload)
   const int32_t* y;        // sampled token per row (log-probability / entropy)
+  const int32_t* teacher;  // teacher per row (NULL: one teacher)
+  int K;                   // teachers: W_t holds K weights, wt_stride elements apart
+  int64_t wt_stride;
   float* partial;          // [nsplit][5][N]
   int tiles_per_split;     // 256-row vocabulary tiles per split
   int nsplit;
@@ -33,6 +36,9 @@ struct BwdParams {
   const float* grad;       // g of L (reverse KL) or of log p(y) (log-probability / entropy)
   const float* grad_h;     // g of the entropy (log-probability / entropy)
   const int32_t* y;        // sampled token per row (log-probability / entropy)
+  const int32_t* teacher;  // teacher per row (NULL: one teacher)
+  int K;
+  int64_t wt_stride;
   const float* stats;
   const float* gscale;     // [2]: s, 1/s (powers of two); dz is stored as fp16(s * dz)
   uint16_t* dz;            // [ntok * 128, ldz] fp16 chunk workspace (rows past N written as zero)
@@ -84,6 +90,7 @@ enum Mode : int {
   kModeHidden = 0,          // reverse KL, teacher projected from hidden states
   kModeTeacherLogits = 1,   // reverse KL, teacher logits streamed
   kModeLogprobEntropy = 2,  // log p(sampled token) and entropy of one projection
+  kModeHiddenTeachers = 3,  // reverse KL, teacher hidden states, teacher chosen per row
 };
 
 hipError_t launch_fwd_tiles(const FwdParams& p, int mode, int waves, hipStream_t s);

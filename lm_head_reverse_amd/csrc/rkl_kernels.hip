@@ -195,23 +195,44 @@ __device__ __forceinline__ void load_zt(f32x16 (&zt)[FM][FN], const float* __res
 // projections nor the next job restarts the pipeline, and an epilogue
 // overlaps the loads of the next job's first tiles.
 // ---------------------------------------------------------------------------
+// Bit 31 of a tile's teacher set: some row of the tile names no valid teacher.
+constexpr uint32_t kTeacherOutOfRange = 1u << 31;
+
 struct DualOps {
   const uint16_t* W[2];
   const uint16_t* h[2];
   int H[2];
   int nk[2];        // k-tiles per projection; nk[1] = 0 when the teacher is given as logits
   int V, N, n0, v0;  // v0: first row of job 0
+  // Teacher passes of every job: one per set bit k of tset, projecting with
+  // the weight at W[1] + k * wt_stride (one teacher: tset = 1, stride 0).
+  uint32_t tset;
+  int64_t wt_stride;
 };
 
 struct StreamPos {
-  int job, phase, kt;
+  int job, phase, kt, tk;   // tk: teacher of a teacher pass (phase 1)
 };
 
+template <bool MULTI>
 __device__ __forceinline__ void stream_advance(StreamPos& q, const DualOps& o) {
   if (++q.kt == (q.phase ? o.nk[1] : o.nk[0])) {
     q.kt = 0;
-    if (q.phase == 0 && o.nk[1] > 0) {
+    if (!MULTI) {
+      if (q.phase == 0 && o.nk[1] > 0) {
+        q.phase = 1;
+      } else {
+        q.phase = 0;
+        ++q.job;
+      }
+      return;
+    }
+    // the next teacher pass of this job: the next teacher bit of tset
+    const uint32_t ts = o.tset & ~kTeacherOutOfRange;
+    const uint32_t rest = q.phase == 0 ? ts : (ts & ~((2u << q.tk) - 1u));
+    if (o.nk[1] > 0 && rest != 0) {
       q.phase = 1;
+      q.tk = __builtin_ctz(rest);
     } else {
       q.phase = 0;
       ++q.job;
@@ -231,19 +252,28 @@ struct NoTileHook {
 // that tile, and every wave has passed the barrier after which the tile is
 // complete.  The next k-tile's DMA writes `stage`, so a hook that reads it
 // must end with a workgroup barrier whenever it reads.
-template <int NW, class Epi, class Hook = NoTileHook>
+// tkl[fn] = teacher of this lane's token column fn (read only when tset has
+// several bits: a teacher pass then zeroes, in every B fragment, the token
+// columns of the other teachers, so each column accumulates exactly its own
+// teacher's products -- the sum is the same as in a pass over that teacher
+// alone, bit for bit).
+template <int NW, bool MULTI = false, class Epi, class Hook = NoTileHook>
 __device__ __forceinline__ void dual_stream(const DualOps& o, int njobs, char* lds,
                                             f32x16 (&zs)[Fused<NW>::FM][Fused<NW>::FN],
                                             f32x16 (&zt)[Fused<NW>::FM][Fused<NW>::FN], int tid, int arow0, int brow0,
-                                            Epi epi, Hook hook = Hook{}) {
+                                            const int (&tkl)[Fused<NW>::FN], Epi epi, Hook hook = Hook{}) {
   using F = Fused<NW>;
   constexpr int FFM = F::FM, FFN = F::FN, kStreamA = F::kA, kStreamB = F::kB, kStreamND = F::ND;
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int total = njobs * (o.nk[0] + o.nk[1]);
+  // MULTI = false: one teacher (o.tset and o.wt_stride unused)
+  const uint32_t tset = o.tset & ~kTeacherOutOfRange;
+  const int passes = o.nk[1] > 0 ? (MULTI ? __builtin_popcount(tset) : 1) : 0;
+  const bool mixed = MULTI && (passes > 1 || (o.tset & kTeacherOutOfRange) != 0);
+  const int total = njobs * (o.nk[0] + passes * o.nk[1]);
   const uint32_t lbase = lds_addr(lds);
   // stage rotation as byte offsets: reads use lds + offset, the DMA lbase + offset
   int ocur = 0, onxt = FwdStages::kStage, opre = 2 * FwdStages::kStage;
-  StreamPos dp{0, 0, 0};
+  StreamPos dp{0, 0, 0, 0};
   int dissued = 0;
   // Per-lane DMA offsets of the current stream segment (one job's student or
   // teacher k-tiles), relative to the segment's tile base at k-tile 0, with
@@ -257,7 +287,7 @@ __device__ __forceinline__ void dual_stream(const DualOps& o, int njobs, char* l
     const bool t = dp.phase != 0;
     const int ld = t ? o.H[1] : o.H[0];
     const int v0 = o.v0 + dp.job * FBM;
-    segA = (t ? o.W[1] : o.W[0]) + (int64_t)v0 * ld;
+    segA = (t ? o.W[1] + (MULTI ? (int64_t)dp.tk * o.wt_stride : 0) : o.W[0]) + (int64_t)v0 * ld;
     segB = (t ? o.h[1] : o.h[0]) + (int64_t)o.n0 * ld;
     const int nA = o.V - v0, nB = o.N - o.n0;
     const uint32_t ld2 = 2u * (uint32_t)ld;
@@ -278,7 +308,7 @@ __device__ __forceinline__ void dual_stream(const DualOps& o, int njobs, char* l
   };
   auto dma_next = [&]() {
     if (dissued + 1 < total) {
-      stream_advance(dp, o);
+      stream_advance<MULTI>(dp, o);
       if (dp.kt == 0) seg_setup();
     }
     ++dissued;
@@ -297,26 +327,40 @@ __device__ __forceinline__ void dual_stream(const DualOps& o, int njobs, char* l
   for (int f = 0; f < FFM + FFN; ++f)
     load_frag<bf16x8, FFM, FFN>(a[0], b[0], lds + arow0 * kLdsRow, lds + FwdStages::kA + brow0 * kLdsRow, fl, 0, f);
 
-  auto step = [&](f32x16 (&acc)[FFM][FFN]) {
+  auto step = [&](f32x16 (&acc)[FFM][FFN], auto maskb, uint32_t keep) {
     const uint32_t target = lbase + (uint32_t)opre;
-    dma_iter<FBM, FBN, bf16x8, FFM, FFN, kStreamND>(acc, a, b, [&](int q) { dma_all(target, q); }, lds + ocur,
-                                                   lds + onxt, fl, arow0, brow0);
+    dma_iter<FBM, FBN, bf16x8, FFM, FFN, kStreamND, decltype(maskb)::value>(
+        acc, a, b, [&](int q) { dma_all(target, q); }, lds + ocur, lds + onxt, fl, arow0, brow0, keep);
     dma_next();
     const int t = ocur;
     ocur = onxt;
     onxt = opre;
     opre = t;
   };
+  using Plain = std::integral_constant<bool, false>;
+  using Masked = std::integral_constant<bool, true>;
   for (int job = 0; job < njobs; ++job) {
     zero_acc(zs);
     for (int kt = 0; kt < o.nk[0]; ++kt) {
       const char* consumed = lds + ocur;
-      step(zs);
+      step(zs, Plain{}, 0u);
       hook(consumed, job, kt);
     }
-    if (o.nk[1] > 0) {
+    if (passes > 0) {
       zero_acc(zt);
-      for (int kt = 0; kt < o.nk[1]; ++kt) step(zt);
+      if (!MULTI) {
+        for (int kt = 0; kt < o.nk[1]; ++kt) step(zt, Plain{}, 0u);
+      } else {
+        for (uint32_t rest = tset; rest != 0; rest &= rest - 1) {
+          const int k = __builtin_ctz(rest);
+          uint32_t keep = ~0u;   // bit fn: token column fn belongs to teacher k
+          if (mixed) {
+#pragma unroll
+            for (int fn = 0; fn < FFN; ++fn) keep &= ~((uint32_t)(tkl[fn] != k) << fn);
+          }
+          for (int kt = 0; kt < o.nk[1]; ++kt) step(zt, Masked{}, keep);
+        }
+      }
     }
     // the stage just consumed is free until the next k-tile's DMA
     epi(job, lds + opre);
@@ -324,14 +368,48 @@ __device__ __forceinline__ void dual_stream(const DualOps& o, int njobs, char* l
   dma_barrier<0>();
 }
 
+// Teachers of a 128-token tile (reverse KL with a teacher chosen per row):
+// tkl[fn] = teacher of this lane's token column fn (-1 past N), and the
+// returned bitmask holds every teacher id in [0, K) (K <= 31) of the tile's
+// rows, plus bit 31 when one of its rows has an id outside [0, K).  Such a
+// row selects no teacher: every pass over its tile is masked and leaves its
+// teacher logits at 0 (no memory is addressed with the id).  Without per-row
+// teachers (teacher NULL): one teacher, bitmask 1.  Every thread of the
+// workgroup must call it.
+template <int FN>
+__device__ __forceinline__ uint32_t tile_teachers(const int32_t* __restrict__ teacher, int K, int N, int n0, int brow0,
+                                                  int lane, int (&tkl)[FN], uint32_t* tset_lds) {
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) tkl[fn] = 0;
+  if (!teacher) return 1u;
+  uint32_t bits = 0;
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    const int n = n0 + brow0 + fn * 32 + (lane & 31);
+    tkl[fn] = n < N ? teacher[n] : -1;
+    if (tkl[fn] >= 0 && tkl[fn] < K)
+      bits |= 1u << tkl[fn];
+    else if (n < N)
+      bits |= kTeacherOutOfRange;
+  }
+  if (threadIdx.x == 0) *tset_lds = 0u;
+  __syncthreads();
+  if (bits) atomicOr(tset_lds, bits);
+  __syncthreads();
+  return *tset_lds;
+}
+
 // MODE 0: hidden teacher; 1: teacher logits; 2: log-probability / entropy
-// (one projection; the statistics slots hold m, S, B, zy, 0).
+// (one projection; the statistics slots hold m, S, B, zy, 0); 3: hidden
+// teacher chosen per row (as 0, with one teacher pass per teacher present in
+// the token tile).
 template <int MODE, bool VEC4, int NW>
 __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void fwd_tiles(FwdParams p) {
   using F = Fused<NW>;
   constexpr int FFM = F::FM, FFN = F::FN;
   __shared__ __attribute__((aligned(1024))) char lds[3 * FwdStages::kStage];
   __shared__ __attribute__((aligned(16))) float red[F::kRedFloats];
+  __shared__ uint32_t tset_lds;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int logical = xcd_logical(blockIdx.x, p.nsplit * p.ntok);
   int split, tt;
@@ -350,8 +428,11 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void fwd_tiles(FwdParams p)
   const int lrow = 4 * (lane >> 5);
   DualOps o;
   o.W[0] = p.W_s; o.h[0] = p.h_s; o.H[0] = p.Hs; o.nk[0] = p.Hs / kKT;
-  o.W[1] = p.W_t; o.h[1] = p.h_t; o.H[1] = p.Ht; o.nk[1] = MODE == 0 ? p.Ht / kKT : 0;
+  o.W[1] = p.W_t; o.h[1] = p.h_t; o.H[1] = p.Ht; o.nk[1] = (MODE == 0 || MODE == 3) ? p.Ht / kKT : 0;
   o.V = p.V; o.N = p.N; o.n0 = n0; o.v0 = vt0 * FBM;
+  int tkl[FFN];
+  o.tset = tile_teachers<FFN>(MODE == 3 ? p.teacher : nullptr, p.K, p.N, n0, brow0, lane, tkl, &tset_lds);
+  o.wt_stride = p.wt_stride;
   int yv[FFN];   // sampled token of this lane's token columns (MODE 2)
 #pragma unroll
   for (int fn = 0; fn < FFN; ++fn) {
@@ -359,7 +440,7 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void fwd_tiles(FwdParams p)
     yv[fn] = (MODE == 2 && n < p.N) ? p.y[n] : -1;
   }
 
-  dual_stream<NW>(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, [&](int job, char*) {
+  dual_stream<NW, MODE == 3>(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, tkl, [&](int job, char*) {
     const int v0 = (vt0 + job) * FBM;
     if (MODE == 1) load_zt<VEC4>(zt, p.z_t, p.N, p.V, v0 + arow0 + lrow, n0 + brow0 + (lane & 31), lane);
     const int vrow = v0 + arow0 + lrow;
@@ -601,6 +682,7 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
   using F = Fused<NW>;
   constexpr int FFM = F::FM, FFN = F::FN;
   __shared__ __attribute__((aligned(1024))) char lds[3 * FwdStages::kStage];
+  __shared__ uint32_t tset_lds;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int logical = xcd_logical(blockIdx.x, p.ngroups * p.ntok);
   int grp, tt;
@@ -645,8 +727,11 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
   f32x16 zs[FFM][FFN], zt[FFM][FFN];
   DualOps o;
   o.W[0] = p.W_s; o.h[0] = p.h_s; o.H[0] = p.Hs; o.nk[0] = p.Hs / kKT;
-  o.W[1] = p.W_t; o.h[1] = p.h_t; o.H[1] = p.Ht; o.nk[1] = MODE == 0 ? p.Ht / kKT : 0;
+  o.W[1] = p.W_t; o.h[1] = p.h_t; o.H[1] = p.Ht; o.nk[1] = (MODE == 0 || MODE == 3) ? p.Ht / kKT : 0;
   o.V = p.V; o.N = p.N; o.n0 = n0; o.v0 = p.c0 + vt0 * FBM;
+  int tkl[FFN];
+  o.tset = tile_teachers<FFN>(MODE == 3 ? p.teacher : nullptr, p.K, p.N, n0, brow0, lane, tkl, &tset_lds);
+  o.wt_stride = p.wt_stride;
 
   // fp16 copy of this workgroup's share of the W_s chunk for the dh GEMM:
   // of each vocabulary tile's Hs/64 student k-tiles, token tile tt converts
@@ -667,7 +752,7 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
     dma_barrier<63>();
   };
 
-  dual_stream<NW>(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, [&](int job, char* stage) {
+  dual_stream<NW, MODE == 3>(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, tkl, [&](int job, char* stage) {
     const int v0 = p.c0 + (vt0 + job) * FBM;
     if (MODE == 1) load_zt<VEC4>(zt, p.z_t, p.N, p.V, v0 + arow0 + lrow, n0 + brow0 + (lane & 31), lane);
     const int hi = lane >> 5;
@@ -1010,6 +1095,8 @@ static void fwd_tiles_launch(const FwdParams& p, int mode, unsigned nb, hipStrea
   constexpr unsigned nt = Fused<NW>::kThreads;
   if (mode == kModeHidden)
     fwd_tiles<kModeHidden, true, NW><<<nb, nt, 0, s>>>(p);
+  else if (mode == kModeHiddenTeachers)
+    fwd_tiles<kModeHiddenTeachers, true, NW><<<nb, nt, 0, s>>>(p);
   else if (mode == kModeLogprobEntropy)
     fwd_tiles<kModeLogprobEntropy, true, NW><<<nb, nt, 0, s>>>(p);
   else if (p.V % 4 == 0)
@@ -1042,6 +1129,8 @@ static void bwd_dz_launch(const BwdParams& p, int mode, unsigned nb, hipStream_t
   constexpr unsigned nt = Fused<NW>::kThreads;
   if (mode == kModeHidden)
     bwd_dz_tiles<kModeHidden, true, NW><<<nb, nt, 0, s>>>(p);
+  else if (mode == kModeHiddenTeachers)
+    bwd_dz_tiles<kModeHiddenTeachers, true, NW><<<nb, nt, 0, s>>>(p);
   else if (mode == kModeLogprobEntropy)
     bwd_dz_tiles<kModeLogprobEntropy, true, NW><<<nb, nt, 0, s>>>(p);
   else if (p.V % 4 == 0)

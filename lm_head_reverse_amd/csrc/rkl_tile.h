@@ -158,10 +158,12 @@ __device__ __forceinline__ void dma_barrier() {
 // the kBefore DMAs of the tile two ahead issued so far stay in flight: every
 // older one -- all of the next tile's -- has landed.  The caller's prologue
 // issues two whole tiles and waits with ND in flight.
-template <int BM, int BN, typename ELEM, int FM, int FN, int ND, class Issue>
+// MASKB: before its MFMAs, each 16-deep step zeroes the B fragments fn whose
+// bit in `keep` is clear (this lane's token column fn is left out).
+template <int BM, int BN, typename ELEM, int FM, int FN, int ND, bool MASKB = false, class Issue>
 __device__ __forceinline__ void dma_iter(f32x16 (&acc)[FM][FN], ELEM (&a)[2][FM], ELEM (&b)[2][FN], Issue issue,
                                          const char* __restrict__ cur, const char* __restrict__ nxt,
-                                         const FragLanes& fl, int arow0, int brow0) {
+                                         const FragLanes& fl, int arow0, int brow0, uint32_t keep = 0) {
   constexpr int M = FM * FN, R = FM + FN;
   constexpr int kA = BM * kLdsRow;
   constexpr int kBefore = share_lo(ND, 4 * M, 3 * M);   // DMAs of this call issued before its barrier
@@ -169,6 +171,11 @@ __device__ __forceinline__ void dma_iter(f32x16 (&acc)[FM][FN], ELEM (&a)[2][FM]
   for (int ks = 0; ks < 4; ++ks) {
     if (ks == 3) dma_barrier<kBefore>();
     const int fb = ks & 1, nb = fb ^ 1;
+    if (MASKB) {
+#pragma unroll
+      for (int fn = 0; fn < FN; ++fn)
+        if (!((keep >> fn) & 1u)) b[fb][fn] = ELEM{};
+    }
     const char* src = ks == 3 ? nxt : cur;
     const int nks = (ks + 1) & 3;
 #pragma unroll

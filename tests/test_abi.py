@@ -30,6 +30,7 @@ def test_header_declares_the_path():
     for want in ("rkl_compact_rows", "rkl_gather_rows", "rkl_scatter_rows", "rkl_workspace_bytes",
                  "rkl_forward_hidden", "rkl_forward_logits", "rkl_backward_hidden", "rkl_backward_logits",
                  "rkl_forward_logprob_entropy", "rkl_backward_logprob_entropy",
+                 "rkl_forward_hidden_teachers", "rkl_backward_hidden_teachers",
                  "rkl_last_error", "rkl_version"):
         assert want in names
 
@@ -131,6 +132,25 @@ def test_logprob_entropy_rejects():
     # more rows than the backward's per-call limit
     assert bwd((1 << 22) + 1, 100, 64, FAKE, FAKE, FAKE, None, None, None, FAKE, FAKE, FAKE, 0, FAKE, 1 << 62,
                None) == 2
+
+
+def test_hidden_teachers_rejects():
+    L = R.lib()
+    fwd = L.rkl_forward_hidden_teachers
+    # K out of range
+    assert fwd(4, 100, 64, 64, 0, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert fwd(4, 100, 64, 64, 32, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert "K=" in L.rkl_last_error().decode()
+    # teacher ids missing
+    assert fwd(4, 100, 64, 64, 2, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 1 << 30, None) == 1
+    assert "teacher" in L.rkl_last_error().decode()
+    # workspace too small
+    assert fwd(4, 100, 64, 64, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 16, None) == 3
+    bwd = L.rkl_backward_hidden_teachers
+    assert bwd(4, 100, 64, 64, 2, FAKE, FAKE, FAKE, FAKE, MISALIGNED, None, None, FAKE, FAKE, FAKE, 0, FAKE,
+               1 << 30, None) == 1
+    assert bwd((1 << 22) + 1, 100, 64, 64, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 0, FAKE,
+               1 << 62, None) == 2
 
 
 def test_compaction_and_copies_reject():
