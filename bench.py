@@ -18,6 +18,10 @@ log-probability of a sampled token and the entropy of softmax(h_s W_s^T)
 (forward), and the gradients dh, dW of g_lp logp + g_H H (backward), on the
 same student tensors.
 
+--workload teachers times the reverse-KL step with --teachers K teacher
+weights and a teacher chosen per row (--teacher-order grouped: K contiguous
+runs of rows; interleaved: i.i.d. ids, so every tile holds several teachers).
+
 Prints one JSON line (rank 0):
   value = masked tokens/s for forward + backward;
   roofline = the fused forward kernel against the dense bf16 MFMA peak;
@@ -51,8 +55,12 @@ def parse():
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--payload", choices=("hidden", "logits"), default="hidden",
                     help="teacher payload: hidden states (default, the headline) or fp32 logits [N, V]")
-    ap.add_argument("--workload", choices=("reverse_kl", "logprob_entropy"), default="reverse_kl",
-                    help="reverse KL distillation step (default, the headline) or log-probability + entropy")
+    ap.add_argument("--workload", choices=("reverse_kl", "logprob_entropy", "teachers"), default="reverse_kl",
+                    help="reverse KL distillation step (default, the headline), log-probability + entropy, or "
+                         "reverse KL with a teacher chosen per row")
+    ap.add_argument("--teachers", type=int, default=4, help="teachers for --workload teachers")
+    ap.add_argument("--teacher-order", choices=("grouped", "interleaved"), default="grouped",
+                    help="row order for --workload teachers")
     ap.add_argument("--report-c5", action="store_true",
                     help="time compact vs full-row on the long-prompt workload (T=32768, N=4096, Ht=4096)")
     return ap.parse_args()
@@ -334,6 +342,115 @@ def bench_logprob_entropy(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_teachers(args):
+    """Reverse KL on the headline tensors with K teachers chosen per row."""
+    import numpy as np
+    import torch
+
+    import lm_head_reverse_amd as R
+    import synth
+
+    R.lib()
+    dev = torch.device("cuda:0")
+    K = args.teachers
+    print(f"[bench] generating inputs ({K} teachers)", file=sys.stderr, flush=True)
+    case = synth.config("headline")
+    T, V, Hs, Ht = case.T, case.V, case.Hs, case.Ht
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    h_s_all, h_t_all, W_s = bf(case.h_s), bf(case.h_t), bf(case.W_s)
+    W_t = bf(synth.teacher_weights(3, K, V, Ht))
+    tid_all = torch.from_numpy(synth.teacher_ids(3, T, K, args.teacher_order)).to(dev)
+    mask = torch.from_numpy(case.mask).to(dev)
+    N_expected = int(case.mask.sum())
+    grad_pos = torch.full((T,), 1.0 / N_expected, dtype=torch.float32, device=dev)
+    dW = torch.empty((V, Hs), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        idx, N = R.compact_rows(mask)
+        h_s, h_t = R.gather_rows(h_s_all, idx), R.gather_rows(h_t_all, idx)
+        tk, g = R.gather_rows(tid_all, idx), R.gather_rows(grad_pos, idx)
+        loss, stats = R.forward_hidden_teachers(h_s, W_s, h_t, W_t, tk)
+        loss_pos = R.scatter_rows(loss, idx, T)
+        dh, _ = R.backward_hidden_teachers(h_s, W_s, h_t, W_t, tk, stats, grad_loss=g, dW=dW)
+        return N, loss_pos, R.scatter_rows(dh, idx, T)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        N, loss_pos, _ = step()
+    torch.cuda.synchronize()
+    assert N == N_expected and np.all(np.isfinite(loss_pos.cpu().numpy()))
+    print("[bench] timing", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        N, _, _ = step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    idx, _ = R.compact_rows(mask)
+    h_s, h_t = R.gather_rows(h_s_all, idx), R.gather_rows(h_t_all, idx)
+    tk = R.gather_rows(tid_all, idx)
+    g = torch.full((N,), 1.0 / N, dtype=torch.float32, device=dev)
+    _, stats = R.forward_hidden_teachers(h_s, W_s, h_t, W_t, tk)
+    stream = torch.cuda.current_stream(dev)
+    reps = max(args.steps, 5)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(reps):
+        R.forward_hidden_teachers(h_s, W_s, h_t, W_t, tk)
+    ev[1].record(stream)
+    for _ in range(reps):
+        R.backward_hidden_teachers(h_s, W_s, h_t, W_t, tk, stats, grad_loss=g, dW=dW)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = ev[0].elapsed_time(ev[1]) / reps
+    bwd_ms = ev[1].elapsed_time(ev[2]) / reps
+    flop_fwd = 2.0 * N * V * (Hs + Ht)
+    flop_step = 4.0 * N * V * (Hs + Ht) + 4.0 * N * V * Hs
+    achieved_fwd = flop_fwd / (fwd_ms * 1e-3)
+    out = {
+        "metric": "masked tokens/sec fwd+bwd full-vocab reverse KL, teacher per row (H2048,V152k); MFMA % peak",
+        "value": round(N * args.steps / wall, 1),
+        "unit": "masked tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"Qwen3-1.7B-shaped hidden-state teachers, {K} teachers chosen per row "
+                               f"({args.teacher_order}), B=4 S=1025 (T=N=4096 trainable), Hs=Ht=2048, V=151936",
+                   "B": case.B, "S": case.S, "N": int(N), "Hs": Hs, "Ht": Ht, "V": V, "K": K,
+                   "teacher_order": args.teacher_order, "parallelism": "single GPU"},
+        "mfma_peak_frac_fwd_bwd": round(flop_step / (ms_step * 1e-3) / PEAK_BF16, 4),
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "mfma_peak_frac_fwd": round(achieved_fwd / PEAK_BF16, 4),
+        "mfma_peak_frac_bwd": round((flop_step - flop_fwd) / (bwd_ms * 1e-3) / PEAK_BF16, 4),
+        "roofline": {
+            "kernel": "fwd_tiles<3> (fused forward: student + per-row teacher projections + online LSE/KL "
+                      "epilogue; event time of the forward call, which adds the per-row split combine; "
+                      "algorithmic FLOPs only)",
+            "bound": "mfma",
+            "achieved": round(achieved_fwd / 1e12, 2),
+            "peak": round(PEAK_BF16 / 1e12, 1),
+            "unit": "TFLOP/s",
+            "frac": round(achieved_fwd / PEAK_BF16, 4),
+            "traffic": None,
+        },
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.profile_copy:
@@ -346,6 +463,8 @@ def main():
         sys.exit(2)
     if args.workload == "logprob_entropy":
         return bench_logprob_entropy(args)
+    if args.workload == "teachers":
+        return bench_teachers(args)
 
     import numpy as np
     import torch

@@ -225,3 +225,19 @@ def upstream_grads(seed: int, T: int):
     g = _rng(seed, _G).standard_normal(T).astype(np.float32)
     gh = _rng(seed, _GH).uniform(-0.1, 0.1, size=T).astype(np.float32)
     return g, gh
+
+
+# ------------------------------------------------- teacher chosen per row
+
+def teacher_weights(seed: int, K: int, V: int, Ht: int, sigma: float = 0.02) -> np.ndarray:
+    """[K, V, Ht] bf16 bits: K independent output-layer weights N(0, sigma^2)."""
+    return np.stack([_normal_bf16(seed, 16 + k, V, Ht, sigma) for k in range(K)])
+
+
+def teacher_ids(seed: int, T: int, K: int, order: str = "grouped") -> np.ndarray:
+    """int32 [T] teacher id per row: `grouped` gives K contiguous runs of about
+    T/K rows (a batch assembled per teacher), `interleaved` i.i.d. uniform ids
+    (every 128-row tile then holds several teachers)."""
+    if order == "grouped":
+        return (np.arange(T, dtype=np.int64) * K // max(T, 1)).astype(np.int32)
+    return _rng(seed, 15).integers(0, K, size=T, dtype=np.int64).astype(np.int32)
