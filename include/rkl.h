@@ -106,6 +106,15 @@ int rkl_scatter_rows(const void* src, int64_t N, int64_t row_bytes, const int32_
 size_t rkl_workspace_bytes(int64_t N, int64_t V, int64_t Hs, int64_t Ht);
 
 /*
+ * Workspace (bytes) of rkl_forward_hidden_teachers and
+ * rkl_backward_hidden_teachers: rkl_workspace_bytes(N, V, Hs, Ht) plus the
+ * rows regrouped by teacher (h_s, h_t, ids, mask, per-row scalars and dh,
+ * N (6 Hs + 2 Ht + 29) bytes, each piece 256-byte aligned).  Returns 0 on
+ * bad sizes.
+ */
+size_t rkl_workspace_bytes_teachers(int64_t N, int64_t V, int64_t Hs, int64_t Ht);
+
+/*
  * Forward, hidden-state teacher (NeMo-RL page, summary: hidden_states payload).
  *   h_s [N, Hs], W_s [V, Hs], h_t [N, Ht], W_t [V, Ht]   bf16
  *   row_mask  NULL: all N rows are live (compacted input).
@@ -175,10 +184,15 @@ int rkl_backward_logits(int64_t N, int64_t V, int64_t Hs,
  *                         a row gets teacher logits 0 (nothing is addressed
  *                         with the id).
  *   1 <= K <= 31.
- * Rows of one teacher need not be contiguous: a 128-row tile holding rows
- * of several teachers runs one teacher pass per teacher it holds (same
- * results bit for bit, more work), so grouping rows by teacher is faster.
- * Workspace: rkl_workspace_bytes(N, V, Hs, Ht).
+ * Rows of one teacher need not be contiguous.  The call first groups the
+ * rows by teacher id (a stable sort, ids outside [0, K) last) and copies
+ * their h_s, h_t (and mask bytes) into the workspace in that order, so that
+ * a 128-row tile holds one teacher except at group boundaries; a tile that
+ * holds several runs one teacher pass per teacher in it.  Loss and stats are
+ * written back to the caller's row order.  A row's results do not depend on
+ * which rows share its tile, so they are the same bit for bit whatever the
+ * order of the rows.
+ * Workspace: rkl_workspace_bytes_teachers(N, V, Hs, Ht).
  */
 int rkl_forward_hidden_teachers(int64_t N, int64_t V, int64_t Hs, int64_t Ht, int64_t K, const rkl_bf16* h_s,
                                 const rkl_bf16* W_s, const rkl_bf16* h_t, const rkl_bf16* W_t, const int32_t* teacher,
@@ -186,7 +200,10 @@ int rkl_forward_hidden_teachers(int64_t N, int64_t V, int64_t Hs, int64_t Ht, in
                                 size_t workspace_bytes, rkl_stream_t stream);
 
 /* Backward of rkl_forward_hidden_teachers: arguments as rkl_backward_hidden
- * plus K, W_t [K, V, Ht] and teacher [N] as above. */
+ * plus K, W_t [K, V, Ht] and teacher [N] as above.  Rows are grouped by
+ * teacher as in the forward (grad_loss and stats are copied in that order,
+ * dh_s is written back to the caller's); dW_s sums the rows in the grouped
+ * order.  Workspace: rkl_workspace_bytes_teachers(N, V, Hs, Ht). */
 int rkl_backward_hidden_teachers(int64_t N, int64_t V, int64_t Hs, int64_t Ht, int64_t K, const rkl_bf16* h_s,
                                  const rkl_bf16* W_s, const rkl_bf16* h_t, const rkl_bf16* W_t,
                                  const int32_t* teacher, const uint8_t* row_mask, const float* grad_loss,

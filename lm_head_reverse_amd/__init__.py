@@ -17,8 +17,9 @@ import os
 from typing import Optional
 
 __all__ = [
-    "RKLError", "lib", "LIB_PATH", "version", "workspace_bytes", "compact_rows", "gather_rows",
-    "scatter_rows", "forward_hidden", "forward_logits", "backward_hidden", "backward_logits",
+    "RKLError", "lib", "LIB_PATH", "version", "workspace_bytes", "workspace_bytes_teachers", "compact_rows",
+    "gather_rows", "scatter_rows", "forward_hidden", "forward_logits", "backward_hidden", "backward_logits",
+    "forward_hidden_teachers", "backward_hidden_teachers", "forward_logprob_entropy", "backward_logprob_entropy",
     "ReverseKL",
 ]
 
@@ -49,6 +50,7 @@ def lib() -> ctypes.CDLL:
         "rkl_last_error": ([], ctypes.c_char_p),
         "rkl_version": ([], ctypes.c_char_p),
         "rkl_workspace_bytes": ([I64, I64, I64, I64], SZ),
+        "rkl_workspace_bytes_teachers": ([I64, I64, I64, I64], SZ),
         "rkl_compact_rows": ([P, I64, P, P, P, P], I32),
         "rkl_gather_rows": ([P, I64, I64, P, I64, P, P], I32),
         "rkl_scatter_rows": ([P, I64, I64, P, I64, P, P], I32),
@@ -81,6 +83,10 @@ def version() -> str:
 
 def workspace_bytes(N: int, V: int, Hs: int, Ht: int) -> int:
     return int(lib().rkl_workspace_bytes(N, V, Hs, Ht))
+
+
+def workspace_bytes_teachers(N: int, V: int, Hs: int, Ht: int) -> int:
+    return int(lib().rkl_workspace_bytes_teachers(N, V, Hs, Ht))
 
 
 # ---------------------------------------------------------------- torch plumbing
@@ -390,7 +396,7 @@ def forward_hidden_teachers(h_s, W_s, h_t, W_t, teacher, row_mask=None):
         _need(row_mask, "row_mask", torch.uint8, dev, (N,))
     loss = torch.empty(N, dtype=torch.float32, device=dev)
     stats = torch.empty((N, 4), dtype=torch.float32, device=dev)
-    ws = _workspace(dev, workspace_bytes(N, V, Hs, Ht))
+    ws = _workspace(dev, workspace_bytes_teachers(N, V, Hs, Ht))
     _check(lib().rkl_forward_hidden_teachers(N, V, Hs, Ht, K, _ptr(h_s), _ptr(W_s), _ptr(h_t), _ptr(W_t),
                                              _ptr(teacher), _ptr(row_mask), _ptr(loss), _ptr(stats), _ptr(ws),
                                              ws.numel(), _stream(dev)))
@@ -421,7 +427,7 @@ def backward_hidden_teachers(h_s, W_s, h_t, W_t, teacher, stats, grad_loss=None,
     else:
         _need(dW, "dW", torch.float32, dev, (V, Hs))
     dh = torch.empty((N, Hs), dtype=torch.float32, device=dev)
-    ws = _workspace(dev, workspace_bytes(N, V, Hs, Ht))
+    ws = _workspace(dev, workspace_bytes_teachers(N, V, Hs, Ht))
     _check(lib().rkl_backward_hidden_teachers(N, V, Hs, Ht, K, _ptr(h_s), _ptr(W_s), _ptr(h_t), _ptr(W_t),
                                               _ptr(teacher), _ptr(row_mask), _ptr(grad_loss), _ptr(stats), _ptr(dh),
                                               _ptr(dW), int(bool(accumulate_dW)), _ptr(ws), ws.numel(),

@@ -164,6 +164,29 @@ size_t ws_bytes(int64_t N, int64_t V, int64_t Hs, int64_t Ht) {
   return f > b ? f : b;
 }
 
+// Per-row teachers: the rows are first grouped by teacher id (a stable
+// sort) so that a 128-row tile mixes teachers only at group boundaries; the
+// fused kernels then run one teacher pass per tile instead of one per teacher
+// present.  The grouped copies live in front of the regular workspace:
+// [perm][teacher ids][mask bytes][h_s rows][h_t rows][loss or grad][stats][dh].
+struct GroupLayout {
+  size_t off_perm, off_tid, off_mask, off_hs, off_ht, off_row, off_stats, off_dh, total;
+};
+GroupLayout group_layout(int64_t N, int64_t Hs, int64_t Ht) {
+  GroupLayout G{};
+  size_t o = 0;
+  G.off_perm = o;  o += align256((size_t)N * 4);
+  G.off_tid = o;   o += align256((size_t)N * 4);
+  G.off_mask = o;  o += align256((size_t)N);
+  G.off_hs = o;    o += align256((size_t)N * Hs * 2);
+  G.off_ht = o;    o += align256((size_t)N * Ht * 2);
+  G.off_row = o;   o += align256((size_t)N * 4);
+  G.off_stats = o; o += align256((size_t)N * 16);
+  G.off_dh = o;    o += align256((size_t)N * Hs * 4);
+  G.total = o;
+  return G;
+}
+
 int check_dims(int64_t N, int64_t V, int64_t Hs, int64_t Ht, bool teacher_hidden, bool student_hidden) {
   if (N < 0 || N > kMaxDim) return fail(RKL_INVALID_ARG, "N=%lld out of range [0, 2^30]", (long long)N);
   if (V < 1 || V > kMaxDim) return fail(RKL_INVALID_ARG, "V=%lld out of range [1, 2^30]", (long long)V);
@@ -314,6 +337,11 @@ const char* rkl_version(void) { return "rkl 0.1 gfx950"; }
 size_t rkl_workspace_bytes(int64_t N, int64_t V, int64_t Hs, int64_t Ht) {
   if (N < 0 || N > kMaxDim || V < 1 || V > kMaxDim || Hs < 0 || Ht < 0) return 0;
   return ws_bytes(N, V, Hs, Ht);
+}
+
+size_t rkl_workspace_bytes_teachers(int64_t N, int64_t V, int64_t Hs, int64_t Ht) {
+  if (N < 0 || N > kMaxDim || V < 1 || V > kMaxDim || Hs < 0 || Ht < 0) return 0;
+  return group_layout(N, Hs, Ht).total + ws_bytes(N, V, Hs, Ht);
 }
 
 int rkl_compact_rows(const uint8_t* mask, int64_t T, int32_t* row_idx, int32_t* n_rows_dev, int64_t* n_rows_host,
@@ -473,10 +501,32 @@ int rkl_forward_hidden_teachers(int64_t N, int64_t V, int64_t Hs, int64_t Ht, in
     NEED16(h_s, "h_s"); NEED16(W_s, "W_s"); NEED16(h_t, "h_t"); NEED16(W_t, "W_t"); NEED4(teacher, "teacher");
     NEED4(loss, "loss"); NEED4(stats, "stats");
   }
+  const GroupLayout G = group_layout(N, Hs, Ht);
+  const size_t need = G.total + ws_bytes(N, V, Hs, Ht);
+  if (workspace_bytes < need)
+    return fail(RKL_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
+  if (N == 0) return RKL_OK;
+  NEED16(workspace, "workspace");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  char* g = static_cast<char*>(workspace);
+  int32_t* perm = reinterpret_cast<int32_t*>(g + G.off_perm);
+  int32_t* tid = reinterpret_cast<int32_t*>(g + G.off_tid);
+  uint8_t* mask = row_mask ? reinterpret_cast<uint8_t*>(g + G.off_mask) : nullptr;
+  rkl_bf16* hs = reinterpret_cast<rkl_bf16*>(g + G.off_hs);
+  rkl_bf16* ht = reinterpret_cast<rkl_bf16*>(g + G.off_ht);
+  float* loss_g = reinterpret_cast<float*>(g + G.off_row);
+  float* stats_g = reinterpret_cast<float*>(g + G.off_stats);
+  RKL_TRY(rkl::launch_group_by_teacher(teacher, row_mask, (int)N, (int)K, perm, tid, mask, s));
+  RKL_TRY(rkl::launch_gather(h_s, Hs * 2, perm, N, hs, s));
+  RKL_TRY(rkl::launch_gather(h_t, Ht * 2, perm, N, ht, s));
   Teachers t;
-  t.teacher = teacher; t.K = (int)K; t.stride = V * Ht;
-  return forward_tiled(N, V, Hs, Ht, h_s, W_s, h_t, W_t, nullptr, nullptr, row_mask, loss, nullptr, stats, workspace,
-                       workspace_bytes, static_cast<hipStream_t>(stream), t);
+  t.teacher = tid; t.K = (int)K; t.stride = V * Ht;
+  if (int rc = forward_tiled(N, V, Hs, Ht, hs, W_s, ht, W_t, nullptr, nullptr, mask, loss_g, nullptr, stats_g,
+                             g + G.total, workspace_bytes - G.total, s, t))
+    return rc;
+  RKL_TRY(rkl::launch_scatter(loss_g, 4, perm, N, loss, s));
+  RKL_TRY(rkl::launch_scatter(stats_g, 16, perm, N, stats, s));
+  return RKL_OK;
 }
 
 int rkl_backward_hidden_teachers(int64_t N, int64_t V, int64_t Hs, int64_t Ht, int64_t K, const rkl_bf16* h_s,
@@ -491,10 +541,39 @@ int rkl_backward_hidden_teachers(int64_t N, int64_t V, int64_t Hs, int64_t Ht, i
     NEED16(h_s, "h_s"); NEED16(W_s, "W_s"); NEED16(h_t, "h_t"); NEED16(W_t, "W_t"); NEED4(teacher, "teacher");
     NEED4(stats, "stats"); NEED16(dh_s, "dh_s"); OPT4(grad_loss, "grad_loss");
   }
+  if (N > kMaxPitchElems)
+    return fail(RKL_UNSUPPORTED, "N=%lld rows exceed the backward's limit of 2^22 per call", (long long)N);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const GroupLayout G = group_layout(N, Hs, Ht);
+  const size_t need = G.total + bwd_layout(N, V, Hs).total;
+  if (workspace_bytes < need)
+    return fail(RKL_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", workspace_bytes, need);
   Teachers t;
-  t.teacher = teacher; t.K = (int)K; t.stride = V * Ht;
-  return backward_tiled(N, V, Hs, Ht, h_s, W_s, h_t, W_t, nullptr, nullptr, row_mask, grad_loss, nullptr, stats, dh_s,
-                        dW_s, accumulate_dW != 0, workspace, workspace_bytes, static_cast<hipStream_t>(stream), t);
+  t.K = (int)K; t.stride = V * Ht;
+  if (N == 0)   // nothing to group: only dW is written (zeros unless accumulating)
+    return backward_tiled(N, V, Hs, Ht, h_s, W_s, h_t, W_t, nullptr, nullptr, row_mask, grad_loss, nullptr, stats,
+                          dh_s, dW_s, accumulate_dW != 0, workspace, workspace_bytes, s, t);
+  NEED16(workspace, "workspace");
+  char* g = static_cast<char*>(workspace);
+  int32_t* perm = reinterpret_cast<int32_t*>(g + G.off_perm);
+  int32_t* tid = reinterpret_cast<int32_t*>(g + G.off_tid);
+  uint8_t* mask = row_mask ? reinterpret_cast<uint8_t*>(g + G.off_mask) : nullptr;
+  rkl_bf16* hs = reinterpret_cast<rkl_bf16*>(g + G.off_hs);
+  rkl_bf16* ht = reinterpret_cast<rkl_bf16*>(g + G.off_ht);
+  float* grad_g = grad_loss ? reinterpret_cast<float*>(g + G.off_row) : nullptr;
+  float* stats_g = reinterpret_cast<float*>(g + G.off_stats);
+  float* dh_g = reinterpret_cast<float*>(g + G.off_dh);
+  RKL_TRY(rkl::launch_group_by_teacher(teacher, row_mask, (int)N, (int)K, perm, tid, mask, s));
+  RKL_TRY(rkl::launch_gather(h_s, Hs * 2, perm, N, hs, s));
+  RKL_TRY(rkl::launch_gather(h_t, Ht * 2, perm, N, ht, s));
+  if (grad_loss) RKL_TRY(rkl::launch_gather(grad_loss, 4, perm, N, grad_g, s));
+  RKL_TRY(rkl::launch_gather(stats, 16, perm, N, stats_g, s));
+  t.teacher = tid;
+  if (int rc = backward_tiled(N, V, Hs, Ht, hs, W_s, ht, W_t, nullptr, nullptr, mask, grad_g, nullptr, stats_g, dh_g,
+                              dW_s, accumulate_dW != 0, g + G.total, workspace_bytes - G.total, s, t))
+    return rc;
+  RKL_TRY(rkl::launch_scatter(dh_g, Hs * 4, perm, N, dh_s, s));
+  return RKL_OK;
 }
 
 }  // extern "C"

@@ -108,6 +108,9 @@ hipError_t launch_fwd_rows_logits(const float* z_s, const float* z_t, int N, int
 hipError_t launch_bwd_rows_logits(const float* z_s, const float* z_t, int N, int V, const uint8_t* row_mask,
                                   const float* grad, const float* stats, float* dz, hipStream_t s);
 hipError_t launch_compact(const uint8_t* mask, int T, int32_t* row_idx, int32_t* n_out, hipStream_t s);
+// Rows grouped by teacher id (stable; ids outside [0, K) last); K in [1, 31].
+hipError_t launch_group_by_teacher(const int32_t* teacher, const uint8_t* mask, int N, int K, int32_t* perm,
+                                   int32_t* teacher_p, uint8_t* mask_p, hipStream_t s);
 hipError_t launch_gather(const void* src, int64_t row_bytes, const int32_t* row_idx, int64_t N, void* dst,
                          hipStream_t s);
 hipError_t launch_scatter(const void* src, int64_t row_bytes, const int32_t* row_idx, int64_t N, void* dst,

@@ -1058,6 +1058,63 @@ __global__ __launch_bounds__(1024) void compact_kernel(const uint8_t* __restrict
   if (tid == 0) *n_out = base;
 }
 
+// Stable counting sort of rows by teacher id (one workgroup): bucket k holds
+// the rows with id k in [0, K), bucket K those with any other id, each in
+// ascending row order.  perm[j] is the row placed at j; teacher_p[j] and
+// mask_p[j] (when mask is given) are that row's id and mask byte.
+__global__ __launch_bounds__(1024) void group_by_teacher_kernel(const int32_t* __restrict__ teacher,
+                                                                const uint8_t* __restrict__ mask, int N, int K,
+                                                                int32_t* __restrict__ perm,
+                                                                int32_t* __restrict__ teacher_p,
+                                                                uint8_t* __restrict__ mask_p) {
+  __shared__ int start[32];
+  __shared__ int wave_cnt[16][32];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const unsigned long long below = (1ull << lane) - 1ull;
+  if (tid < 32) start[tid] = 0;
+  __syncthreads();
+  for (int i = tid; i < N; i += 1024) {
+    const int k = teacher[i];
+    atomicAdd(&start[(k >= 0 && k < K) ? k : K], 1);
+  }
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int b = 0; b <= K; ++b) {
+      const int c = start[b];
+      start[b] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  for (int base = 0; base < N; base += 1024) {
+    const int i = base + tid;
+    const int id = i < N ? teacher[i] : 0;
+    const int b = i < N ? ((id >= 0 && id < K) ? id : K) : -1;
+    int rank = 0;
+    for (int k = 0; k <= K; ++k) {
+      const unsigned long long bal = __ballot(b == k);
+      if (b == k) rank = __popcll(bal & below);
+      if (lane == 0) wave_cnt[w][k] = __popcll(bal);
+    }
+    __syncthreads();
+    if (b >= 0) {
+      int j = start[b] + rank;
+      for (int u = 0; u < w; ++u) j += wave_cnt[u][b];
+      perm[j] = i;
+      teacher_p[j] = id;
+      if (mask) mask_p[j] = mask[i];
+    }
+    __syncthreads();
+    if (tid <= K) {
+      int c = 0;
+      for (int u = 0; u < 16; ++u) c += wave_cnt[u][tid];
+      start[tid] += c;
+    }
+    __syncthreads();
+  }
+}
+
 template <typename U>
 __global__ __launch_bounds__(256) void gather_kernel(const U* __restrict__ src, int64_t row_units,
                                                      const int32_t* __restrict__ row_idx, U* __restrict__ dst) {
@@ -1195,6 +1252,13 @@ hipError_t launch_bwd_rows_logits(const float* z_s, const float* z_t, int N, int
 
 hipError_t launch_compact(const uint8_t* mask, int T, int32_t* row_idx, int32_t* n_out, hipStream_t s) {
   compact_kernel<<<1, 1024, 0, s>>>(mask, T, row_idx, n_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_group_by_teacher(const int32_t* teacher, const uint8_t* mask, int N, int K, int32_t* perm,
+                                   int32_t* teacher_p, uint8_t* mask_p, hipStream_t s) {
+  if (K < 1 || K > 31) return hipErrorInvalidValue;
+  group_by_teacher_kernel<<<1, 1024, 0, s>>>(teacher, mask, N, K, perm, teacher_p, mask_p);
   return hipGetLastError();
 }
 

@@ -28,6 +28,7 @@ def declared_functions():
 def test_header_declares_the_path():
     names = declared_functions()
     for want in ("rkl_compact_rows", "rkl_gather_rows", "rkl_scatter_rows", "rkl_workspace_bytes",
+                 "rkl_workspace_bytes_teachers",
                  "rkl_forward_hidden", "rkl_forward_logits", "rkl_backward_hidden", "rkl_backward_logits",
                  "rkl_forward_logprob_entropy", "rkl_backward_logprob_entropy",
                  "rkl_forward_hidden_teachers", "rkl_backward_hidden_teachers",
@@ -59,6 +60,12 @@ def test_workspace_sizes():
     assert R.workspace_bytes(32768, 151936, 2048, 2048) <= 32768 * 65536 * 2 + 65536 * 2048 * 2 + 2048 * 32768 * 2 + (1 << 20)
     assert R.workspace_bytes(4096, 151936, 2048, 2048) == R.workspace_bytes(4096, 151936, 2048, 4096)
     assert R.workspace_bytes(-1, 10, 64, 64) == 0
+    # per-row teachers: the regular workspace plus the rows regrouped by
+    # teacher (h_s and h_t bf16, dh fp32, ids, mask and per-row scalars)
+    for N, Hs, Ht in ((4096, 2048, 2048), (300, 128, 192), (0, 64, 64)):
+        extra = R.workspace_bytes_teachers(N, 151936, Hs, Ht) - R.workspace_bytes(N, 151936, Hs, Ht)
+        assert N * (6 * Hs + 2 * Ht + 29) <= extra <= N * (6 * Hs + 2 * Ht + 29) + 8 * 256
+    assert R.workspace_bytes_teachers(-1, 10, 64, 64) == 0
 
 
 def _fwd_hidden(N=4, V=100, Hs=64, Ht=64, p=FAKE, ws=FAKE, nbytes=1 << 30):
@@ -144,13 +151,18 @@ def test_hidden_teachers_rejects():
     # teacher ids missing
     assert fwd(4, 100, 64, 64, 2, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 1 << 30, None) == 1
     assert "teacher" in L.rkl_last_error().decode()
-    # workspace too small
+    # workspace too small: the regular size lacks the regrouped rows
     assert fwd(4, 100, 64, 64, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 16, None) == 3
+    assert fwd(4, 100, 64, 64, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE,
+               R.workspace_bytes(4, 100, 64, 64), None) == 3
+    assert "workspace" in L.rkl_last_error().decode()
     bwd = L.rkl_backward_hidden_teachers
     assert bwd(4, 100, 64, 64, 2, FAKE, FAKE, FAKE, FAKE, MISALIGNED, None, None, FAKE, FAKE, FAKE, 0, FAKE,
                1 << 30, None) == 1
     assert bwd((1 << 22) + 1, 100, 64, 64, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 0, FAKE,
                1 << 62, None) == 2
+    assert bwd(4, 100, 64, 64, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 0, FAKE,
+               R.workspace_bytes(4, 100, 64, 64), None) == 3
 
 
 def test_compaction_and_copies_reject():
