@@ -22,6 +22,14 @@ same student tensors.
 weights and a teacher chosen per row (--teacher-order grouped: K contiguous
 runs of rows; interleaved: i.i.d. ids, so every tile holds several teachers).
 
+--workload vocab_shard times one rank's share of a --shards G-way
+vocabulary-parallel step on the same tensors: the shard forward over its
+V/G vocabulary rows, the merge of all G shards' partials (the other shards'
+already resident, as an all-gather would leave them), the loss scatter, the
+shard backward with the merged stats and the scatter of its dh term.  The
+exchanges between ranks (all-gather of the partials, all-reduce of dh) are
+not part of it.
+
 Prints one JSON line (rank 0):
   value = masked tokens/s for forward + backward;
   roofline = the fused forward kernel against the dense bf16 MFMA peak;
@@ -55,9 +63,12 @@ def parse():
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--payload", choices=("hidden", "logits"), default="hidden",
                     help="teacher payload: hidden states (default, the headline) or fp32 logits [N, V]")
-    ap.add_argument("--workload", choices=("reverse_kl", "logprob_entropy", "teachers"), default="reverse_kl",
-                    help="reverse KL distillation step (default, the headline), log-probability + entropy, or "
-                         "reverse KL with a teacher chosen per row")
+    ap.add_argument("--workload", choices=("reverse_kl", "logprob_entropy", "teachers", "vocab_shard"),
+                    default="reverse_kl",
+                    help="reverse KL distillation step (default, the headline), log-probability + entropy, "
+                         "reverse KL with a teacher chosen per row, or one rank's share of a vocabulary-parallel "
+                         "step")
+    ap.add_argument("--shards", type=int, default=8, help="vocabulary shards for --workload vocab_shard")
     ap.add_argument("--teachers", type=int, default=4, help="teachers for --workload teachers")
     ap.add_argument("--teacher-order", choices=("grouped", "interleaved"), default="grouped",
                     help="row order for --workload teachers")
@@ -451,6 +462,127 @@ def bench_teachers(args):
     print(json.dumps(out), flush=True)
 
 
+def bench_vocab_shard(args):
+    """One rank's share of a G-way vocabulary-parallel reverse-KL step."""
+    import numpy as np
+    import torch
+
+    import lm_head_reverse_amd as R
+    import synth
+
+    R.lib()
+    dev = torch.device("cuda:0")
+    G = args.shards
+    print(f"[bench] generating inputs ({G} vocabulary shards)", file=sys.stderr, flush=True)
+    case = synth.config("headline")
+    T, V, Hs, Ht = case.T, case.V, case.Hs, case.Ht
+    if not 1 <= G <= V:
+        raise SystemExit(f"bench.py: --shards must be in [1, {V}]")
+    q, r = divmod(V, G)
+    bounds = []
+    for k in range(G):
+        a = bounds[-1][1] if bounds else 0
+        bounds.append((a, a + q + (1 if k < r else 0)))
+    v0, v1 = bounds[0]   # this rank's vocabulary rows
+
+    def bf(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    h_s_all, h_t_all, W_s_full, W_t_full = bf(case.h_s), bf(case.h_t), bf(case.W_s), bf(case.W_t)
+    mask = torch.from_numpy(case.mask).to(dev)
+    N_expected = int(case.mask.sum())
+    grad_pos = torch.full((T,), 1.0 / N_expected, dtype=torch.float32, device=dev)
+    # the other ranks' partials, as the all-gather would deliver them
+    idx, N = R.compact_rows(mask)
+    h_s, h_t = R.gather_rows(h_s_all, idx), R.gather_rows(h_t_all, idx)
+    partials = torch.stack([R.forward_hidden_shard(h_s, W_s_full[a:b], h_t, W_t_full[a:b])
+                            for a, b in bounds]).contiguous()
+    W_s, W_t = W_s_full[v0:v1], W_t_full[v0:v1]
+    dW = torch.empty((v1 - v0, Hs), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        idx, N = R.compact_rows(mask)
+        h_s, h_t = R.gather_rows(h_s_all, idx), R.gather_rows(h_t_all, idx)
+        g = R.gather_rows(grad_pos, idx)
+        partials[0] = R.forward_hidden_shard(h_s, W_s, h_t, W_t)
+        loss, stats = R.combine_shards(partials)
+        loss_pos = R.scatter_rows(loss, idx, T)
+        dh, _ = R.backward_hidden(h_s, W_s, h_t, W_t, stats, grad_loss=g, dW=dW)
+        return N, loss_pos, R.scatter_rows(dh, idx, T)
+
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        N, loss_pos, _ = step()
+    torch.cuda.synchronize()
+    assert N == N_expected and np.all(np.isfinite(loss_pos.cpu().numpy()))
+    print("[bench] timing", file=sys.stderr, flush=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        N, _, _ = step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    g = torch.full((N,), 1.0 / N, dtype=torch.float32, device=dev)
+    _, stats = R.combine_shards(partials)
+    stream = torch.cuda.current_stream(dev)
+    reps = max(args.steps, 5)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for _ in range(reps):
+        R.forward_hidden_shard(h_s, W_s, h_t, W_t)
+    ev[1].record(stream)
+    for _ in range(reps):
+        R.backward_hidden(h_s, W_s, h_t, W_t, stats, grad_loss=g, dW=dW)
+    ev[2].record(stream)
+    torch.cuda.synchronize()
+    fwd_ms = ev[0].elapsed_time(ev[1]) / reps
+    bwd_ms = ev[1].elapsed_time(ev[2]) / reps
+    Vs = v1 - v0
+    flop_fwd = 2.0 * N * Vs * (Hs + Ht)
+    flop_step = 4.0 * N * Vs * (Hs + Ht) + 4.0 * N * Vs * Hs
+    achieved_fwd = flop_fwd / (fwd_ms * 1e-3)
+    out = {
+        "metric": "masked tokens/sec fwd+bwd full-vocab reverse KL, one rank of a vocabulary-parallel group "
+                  "(H2048,V152k); MFMA % peak",
+        "value": round(N * args.steps / wall, 1),
+        "unit": "masked tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": f"Qwen3-1.7B-shaped hidden-state teacher, one rank's share of a {G}-way "
+                               f"vocabulary split ({Vs} of 151936 vocabulary rows), B=4 S=1025 (T=N=4096 "
+                               f"trainable), Hs=Ht=2048; inter-rank exchanges excluded",
+                   "B": case.B, "S": case.S, "N": int(N), "Hs": Hs, "Ht": Ht, "V": V, "shards": G,
+                   "V_shard": Vs, "parallelism": "single GPU (one rank's share)"},
+        "mfma_peak_frac_fwd_bwd": round(flop_step / (ms_step * 1e-3) / PEAK_BF16, 4),
+        "fwd_ms": round(fwd_ms, 4),
+        "bwd_ms": round(bwd_ms, 4),
+        "mfma_peak_frac_fwd": round(achieved_fwd / PEAK_BF16, 4),
+        "mfma_peak_frac_bwd": round((flop_step - flop_fwd) / (bwd_ms * 1e-3) / PEAK_BF16, 4),
+        "roofline": {
+            "kernel": "fwd_tiles<0> on the shard (fused forward: both projections + online LSE/KL epilogue; "
+                      "event time of the shard forward call, which adds the split merge; algorithmic FLOPs only)",
+            "bound": "mfma",
+            "achieved": round(achieved_fwd / 1e12, 2),
+            "peak": round(PEAK_BF16 / 1e12, 1),
+            "unit": "TFLOP/s",
+            "frac": round(achieved_fwd / PEAK_BF16, 4),
+            "traffic": None,
+        },
+    }
+    print(json.dumps(out), flush=True)
+
+
 def main():
     args = parse()
     if args.profile_copy:
@@ -465,6 +597,8 @@ def main():
         return bench_logprob_entropy(args)
     if args.workload == "teachers":
         return bench_teachers(args)
+    if args.workload == "vocab_shard":
+        return bench_vocab_shard(args)
 
     import numpy as np
     import torch

@@ -175,6 +175,37 @@ int rkl_backward_logits(int64_t N, int64_t V, int64_t Hs,
                         void* workspace, size_t workspace_bytes, rkl_stream_t stream);
 
 /*
+ * One vocabulary shard of the hidden-state path (NeMo-RL page, implementation
+ * notes: the reverse-KL autograd functions are tensor-parallel over the
+ * vocabulary and the divergence is formed where the vocabulary-parallel group
+ * is held).  A rank owns vocabulary rows [v0, v0 + V) of W_s and W_t; it
+ * passes pointers to those rows and V = its row count.  Arguments as
+ * rkl_forward_hidden, except that nothing is finalised:
+ *   partial [5, N] fp32 out: per row, over the shard's columns only,
+ *       m_s = max z_s, S_s = sum exp(z_s - m_s), A = sum exp(z_s - m_s)(z_s - z_t),
+ *       m_t = max z_t, S_t = sum exp(z_t - m_t)   (planes of N, in that order).
+ * These 20 bytes per row are what the ranks exchange (an all-gather into
+ * [G, 5, N]); rkl_combine_shards then gives every rank the loss and stats.
+ * Workspace: rkl_workspace_bytes(N, V, Hs, Ht) with the shard's V.
+ */
+int rkl_forward_hidden_shard(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* h_s,
+                             const rkl_bf16* W_s, const rkl_bf16* h_t, const rkl_bf16* W_t, float* partial,
+                             void* workspace, size_t workspace_bytes, rkl_stream_t stream);
+
+/*
+ * Merge G shards' partials [G, 5, N] (rkl_forward_hidden_shard's outputs, in
+ * shard order) with the log-sum-exp rule -- M = max_g m_g, S = sum_g S_g
+ * exp(m_g - M), A likewise with the student's factors -- and finalise as
+ * rkl_forward_hidden: loss [N], stats [N, 4] (lse_s, lse_t, L, log p_max over
+ * the whole vocabulary); rows with row_mask 0 get zeros.  1 <= G <= 2^20.
+ * The backward of a shard is rkl_backward_hidden on the shard's rows of W_s
+ * and W_t (V = the shard's count) with these merged stats: it writes the
+ * shard's rows of dW_s and its term of dh_s, which the ranks then sum.
+ */
+int rkl_combine_shards(int64_t G, int64_t N, const float* partials, const uint8_t* row_mask, float* loss,
+                       float* stats, rkl_stream_t stream);
+
+/*
  * Reverse KL with the teacher chosen per row (NeMo-RL page, first-version
  * limits: one teacher checkpoint in that version, with the payload column
  * shaped for a per-row teacher index).  As rkl_forward_hidden, except:

@@ -20,7 +20,7 @@ __all__ = [
     "RKLError", "lib", "LIB_PATH", "version", "workspace_bytes", "workspace_bytes_teachers", "compact_rows",
     "gather_rows", "scatter_rows", "forward_hidden", "forward_logits", "backward_hidden", "backward_logits",
     "forward_hidden_teachers", "backward_hidden_teachers", "forward_logprob_entropy", "backward_logprob_entropy",
-    "ReverseKL",
+    "forward_hidden_shard", "combine_shards", "ReverseKL",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librkl.so")
@@ -58,6 +58,8 @@ def lib() -> ctypes.CDLL:
         "rkl_forward_logits": ([I64, I64, I64, P, P, P, P, P, P, P, P, SZ, P], I32),
         "rkl_backward_hidden": ([I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, I32, P, SZ, P], I32),
         "rkl_backward_logits": ([I64, I64, I64, P, P, P, P, P, P, P, P, P, I32, P, P, SZ, P], I32),
+        "rkl_forward_hidden_shard": ([I64, I64, I64, I64, P, P, P, P, P, P, SZ, P], I32),
+        "rkl_combine_shards": ([I64, I64, P, P, P, P, P], I32),
         "rkl_forward_hidden_teachers": ([I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, SZ, P], I32),
         "rkl_backward_hidden_teachers": ([I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, I32, P, SZ, P],
                                          I32),
@@ -377,6 +379,43 @@ def backward_logprob_entropy(h, W, y, stats, grad_logp=None, grad_entropy=None, 
                                               _ptr(grad_entropy), _ptr(stats), _ptr(dh), _ptr(dW),
                                               int(bool(accumulate_dW)), _ptr(ws), ws.numel(), _stream(dev)))
     return dh, dW
+
+
+def forward_hidden_shard(h_s, W_s, h_t, W_t):
+    """One vocabulary shard's per-row statistics: W_s [V, Hs] and W_t [V, Ht]
+    are the shard's vocabulary rows.  Returns partial fp32 [5, N] = (m_s, S_s,
+    A, m_t, S_t) planes; merge the shards' with combine_shards."""
+    torch = _torch()
+    dev = h_s.device
+    N, Hs = h_s.shape
+    V = W_s.shape[0]
+    Ht = h_t.shape[1]
+    _need(h_s, "h_s", torch.bfloat16, dev)
+    _need(W_s, "W_s", torch.bfloat16, dev, (V, Hs))
+    _need(h_t, "h_t", torch.bfloat16, dev, (N, Ht))
+    _need(W_t, "W_t", torch.bfloat16, dev, (V, Ht))
+    partial = torch.empty((5, N), dtype=torch.float32, device=dev)
+    ws = _workspace(dev, workspace_bytes(N, V, Hs, Ht))
+    _check(lib().rkl_forward_hidden_shard(N, V, Hs, Ht, _ptr(h_s), _ptr(W_s), _ptr(h_t), _ptr(W_t), _ptr(partial),
+                                          _ptr(ws), ws.numel(), _stream(dev)))
+    return partial
+
+
+def combine_shards(partials, row_mask=None):
+    """Merge [G, 5, N] shard partials into (loss [N], stats [N, 4]) over the
+    whole vocabulary, as forward_hidden returns them."""
+    torch = _torch()
+    dev = partials.device
+    G, five, N = partials.shape
+    if five != 5:
+        raise RKLError(RKL_INVALID_ARG, "partials must be [G, 5, N]")
+    _need(partials, "partials", torch.float32, dev)
+    if row_mask is not None:
+        _need(row_mask, "row_mask", torch.uint8, dev, (N,))
+    loss = torch.empty(N, dtype=torch.float32, device=dev)
+    stats = torch.empty((N, 4), dtype=torch.float32, device=dev)
+    _check(lib().rkl_combine_shards(G, N, _ptr(partials), _ptr(row_mask), _ptr(loss), _ptr(stats), _stream(dev)))
+    return loss, stats
 
 
 def forward_hidden_teachers(h_s, W_s, h_t, W_t, teacher, row_mask=None):

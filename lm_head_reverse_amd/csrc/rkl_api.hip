@@ -241,7 +241,7 @@ struct Teachers {
 int forward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* h_s, const rkl_bf16* W_s,
                   const rkl_bf16* h_t, const rkl_bf16* W_t, const float* z_t, const int32_t* y,
                   const uint8_t* row_mask, float* out0, float* out1, float* stats, void* ws, size_t ws_bytes_given,
-                  hipStream_t s, Teachers tch = Teachers{}) {
+                  hipStream_t s, Teachers tch = Teachers{}, float* merged = nullptr) {
   const size_t need = fwd_ws_bytes(N, V, true);
   if (ws_bytes_given < need)
     return fail(RKL_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes_given, need);
@@ -260,6 +260,10 @@ int forward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* 
   p.order_tg = fwd_order().tg;
   const int mode = mode_of(z_t, y, tch.teacher);
   RKL_TRY(rkl::launch_fwd_tiles(p, mode, fused_waves(), s));
+  if (merged) {   // one vocabulary shard: its merged statistics, not finalised
+    RKL_TRY(rkl::launch_fwd_merge(p.partial, p.nsplit, p.N, merged, s));
+    return RKL_OK;
+  }
   RKL_TRY(rkl::launch_fwd_combine(p.partial, p.nsplit, p.N, row_mask, mode == rkl::kModeLogprobEntropy, out0, out1,
                                   stats, s));
   return RKL_OK;
@@ -403,6 +407,30 @@ int rkl_forward_hidden(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_b
   }
   return forward_tiled(N, V, Hs, Ht, h_s, W_s, h_t, W_t, nullptr, nullptr, row_mask, loss, nullptr, stats, workspace,
                        workspace_bytes, static_cast<hipStream_t>(stream));
+}
+
+int rkl_forward_hidden_shard(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* h_s, const rkl_bf16* W_s,
+                             const rkl_bf16* h_t, const rkl_bf16* W_t, float* partial, void* workspace,
+                             size_t workspace_bytes, rkl_stream_t stream) {
+  if (int rc = check_dims(N, V, Hs, Ht, true, true)) return rc;
+  if (N > 0) {
+    NEED16(h_s, "h_s"); NEED16(W_s, "W_s"); NEED16(h_t, "h_t"); NEED16(W_t, "W_t");
+    NEED4(partial, "partial");
+  }
+  return forward_tiled(N, V, Hs, Ht, h_s, W_s, h_t, W_t, nullptr, nullptr, nullptr, nullptr, nullptr, nullptr,
+                       workspace, workspace_bytes, static_cast<hipStream_t>(stream), Teachers{}, partial);
+}
+
+int rkl_combine_shards(int64_t G, int64_t N, const float* partials, const uint8_t* row_mask, float* loss,
+                       float* stats, rkl_stream_t stream) {
+  if (G < 1 || G > ((int64_t)1 << 20)) return fail(RKL_INVALID_ARG, "G=%lld shards out of range [1, 2^20]", (long long)G);
+  if (N < 0 || N > kMaxDim) return fail(RKL_INVALID_ARG, "N=%lld out of range [0, 2^30]", (long long)N);
+  if (G * 5 * N > ((int64_t)1 << 40)) return fail(RKL_INVALID_ARG, "G*N too large");
+  if (N == 0) return RKL_OK;
+  NEED4(partials, "partials"); NEED4(loss, "loss"); NEED4(stats, "stats");
+  RKL_TRY(rkl::launch_fwd_combine(partials, (int)G, (int)N, row_mask, false, loss, nullptr, stats,
+                                  static_cast<hipStream_t>(stream)));
+  return RKL_OK;
 }
 
 int rkl_forward_logits(int64_t N, int64_t V, int64_t Hs, const rkl_bf16* h_s, const rkl_bf16* W_s, const float* z_s,

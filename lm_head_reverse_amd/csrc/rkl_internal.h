@@ -97,6 +97,8 @@ hipError_t launch_fwd_tiles(const FwdParams& p, int mode, int waves, hipStream_t
 // out0: loss (reverse KL) or log p(y); out1: entropy (log-probability / entropy only)
 hipError_t launch_fwd_combine(const float* partial, int nsplit, int N, const uint8_t* row_mask, bool logprob_entropy,
                               float* out0, float* out1, float* stats, hipStream_t s);
+// The splits' merged (m_s, S_s, A, m_t, S_t), not finalised: five planes of N.
+hipError_t launch_fwd_merge(const float* partial, int nsplit, int N, float* merged, hipStream_t s);
 hipError_t launch_bwd_dz(const BwdParams& p, int mode, int waves, hipStream_t s);
 hipError_t launch_grad_scale(const float* grad, const float* grad_h, const uint8_t* row_mask, const float* stats,
                              int N, bool logprob_entropy, float* out, hipStream_t s);

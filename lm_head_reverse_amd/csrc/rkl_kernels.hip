@@ -509,10 +509,13 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void fwd_tiles(FwdParams p)
 // (lse, H, log p(y), log p_max).  32 rows per workgroup; the 8 thread groups
 // each merge every 8th split (coalesced over rows), then group 0 merges the 8
 // results in a fixed order, so the result depends on V (the split plan) only,
-// never on N.
+// never on N.  KIND 0: reverse KL; 1: LPE; 2: no finalisation -- the merged
+// (m_s, S_s, A, m_t, S_t) of all splits go to out0 as five planes of N (one
+// vocabulary shard's contribution, to be merged with the other shards').
 constexpr int kCombRows = 32, kCombWays = 8;
+enum CombineKind : int { kCombineKL = 0, kCombineLPE = 1, kCombineMerged = 2 };
 
-template <bool LPE>
+template <int KIND>
 __global__ __launch_bounds__(256) void fwd_combine(const float* __restrict__ partial, int nsplit, int N,
                                                    const uint8_t* __restrict__ row_mask, float* __restrict__ out0,
                                                    float* __restrict__ out1, float* __restrict__ stats) {
@@ -535,11 +538,19 @@ __global__ __launch_bounds__(256) void fwd_combine(const float* __restrict__ par
     merge3(ms, ss, aa, red[q][0][r], red[q][1][r], red[q][2][r]);
     merge2(mt, st, red[q][3][r], red[q][4][r]);
   }
+  if (KIND == kCombineMerged) {
+    out0[n] = ms;
+    out0[(int64_t)N + n] = ss;
+    out0[(int64_t)2 * N + n] = aa;
+    out0[(int64_t)3 * N + n] = mt;
+    out0[(int64_t)4 * N + n] = st;
+    return;
+  }
   const float log_ss = logf(ss);
   const bool dead = row_mask && row_mask[n] == 0;
   float lse_s = ms + log_ss;
   float lpmax = -log_ss;   // log of the largest student probability
-  if (LPE) {
+  if (KIND == kCombineLPE) {
     float H = lse_s - aa / ss;
     float lpy = mt - lse_s;
     if (dead) { lse_s = 0.f; H = 0.f; lpy = 0.f; lpmax = 0.f; }
@@ -1175,9 +1186,15 @@ hipError_t launch_fwd_combine(const float* partial, int nsplit, int N, const uin
                               float* out0, float* out1, float* stats, hipStream_t s) {
   const unsigned nb = (unsigned)((N + kCombRows - 1) / kCombRows);
   if (logprob_entropy)
-    fwd_combine<true><<<nb, 256, 0, s>>>(partial, nsplit, N, row_mask, out0, out1, stats);
+    fwd_combine<kCombineLPE><<<nb, 256, 0, s>>>(partial, nsplit, N, row_mask, out0, out1, stats);
   else
-    fwd_combine<false><<<nb, 256, 0, s>>>(partial, nsplit, N, row_mask, out0, out1, stats);
+    fwd_combine<kCombineKL><<<nb, 256, 0, s>>>(partial, nsplit, N, row_mask, out0, out1, stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_fwd_merge(const float* partial, int nsplit, int N, float* merged, hipStream_t s) {
+  const unsigned nb = (unsigned)((N + kCombRows - 1) / kCombRows);
+  fwd_combine<kCombineMerged><<<nb, 256, 0, s>>>(partial, nsplit, N, nullptr, merged, nullptr, nullptr);
   return hipGetLastError();
 }
 

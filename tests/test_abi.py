@@ -32,6 +32,7 @@ def test_header_declares_the_path():
                  "rkl_forward_hidden", "rkl_forward_logits", "rkl_backward_hidden", "rkl_backward_logits",
                  "rkl_forward_logprob_entropy", "rkl_backward_logprob_entropy",
                  "rkl_forward_hidden_teachers", "rkl_backward_hidden_teachers",
+                 "rkl_forward_hidden_shard", "rkl_combine_shards",
                  "rkl_last_error", "rkl_version"):
         assert want in names
 
@@ -163,6 +164,22 @@ def test_hidden_teachers_rejects():
                1 << 62, None) == 2
     assert bwd(4, 100, 64, 64, 2, FAKE, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 0, FAKE,
                R.workspace_bytes(4, 100, 64, 64), None) == 3
+
+
+def test_vocab_shard_rejects():
+    L = R.lib()
+    fwd = L.rkl_forward_hidden_shard
+    assert fwd(4, 100, 100, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 2      # Hs % 64
+    assert fwd(4, 100, 64, 64, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1        # partial NULL
+    assert "partial" in L.rkl_last_error().decode()
+    assert fwd(4, 100, 64, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == 3             # workspace
+    comb = L.rkl_combine_shards
+    assert comb(0, 4, FAKE, None, FAKE, FAKE, None) == 1
+    assert "G=" in L.rkl_last_error().decode()
+    assert comb(2, -1, FAKE, None, FAKE, FAKE, None) == 1
+    assert comb(2, 4, None, None, FAKE, FAKE, None) == 1
+    assert comb(2, 4, MISALIGNED, None, FAKE, FAKE, None) == 1
+    assert comb(2, 0, None, None, None, None, None) == 0                                     # nothing to do
 
 
 def test_compaction_and_copies_reject():

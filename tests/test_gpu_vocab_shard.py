@@ -1,0 +1,124 @@
+"""GPU parity of the vocabulary-shard path (through the C ABI) against the
+fp64 oracle (oracle/vocab_shard_oracle.py).
+
+Every shard of a vocabulary runs on this one GPU in turn, as the ranks of a
+vocabulary-parallel group would run theirs; the shards' partials are stacked
+as an all-gather would leave them and merged by rkl_combine_shards.  Each
+shard's backward is rkl_backward_hidden on the shard's weight rows with the
+merged stats.  Bars as in test_gpu_parity; the summed dh uses the same bar.
+"""
+import numpy as np
+import pytest
+
+import lm_head_reverse_amd as R
+import synth
+from gpu_util import bf16, f32, host, say, torch_dev, u8
+from oracle import rkl_oracle as O
+from oracle import vocab_shard_oracle as S
+from tolerances import assert_grad_close, assert_loss_close
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def tdev():
+    torch, dev = torch_dev()
+    R.lib()
+    return torch, dev
+
+
+def _run_shards(torch, hs, Ws, ht, Wt, bounds, g=None, row_mask=None):
+    parts = [R.forward_hidden_shard(hs, Ws[a:b], ht, Wt[a:b]) for a, b in bounds]
+    partials = torch.stack(parts).contiguous()
+    loss, stats = R.combine_shards(partials, row_mask=row_mask)
+    dh_terms, dW_rows = [], []
+    for a, b in bounds:
+        dh, dW = R.backward_hidden(hs, Ws[a:b], ht, Wt[a:b], stats, grad_loss=g, row_mask=row_mask)
+        dh_terms.append(host(dh).astype(np.float64))
+        dW_rows.append(host(dW))
+    torch.cuda.synchronize()
+    return host(partials), host(loss), host(stats), sum(dh_terms), np.concatenate(dW_rows)
+
+
+@pytest.mark.parametrize("bounds", [
+    [(0, 1000), (1000, 1001), (1001, 3001)],     # uneven, with a one-column shard
+    S.shard_bounds(3001, 8),
+])
+def test_shards_against_oracle(tdev, bounds):
+    torch, dev = tdev
+    case = synth.random_case(600, T=300, V=3001, Hs=128, Ht=192, p_mask=1.0, with_grad=True)
+    say("vocab shards", len(bounds))
+    hs, ht, Ws, Wt = bf16(case.h_s, dev), bf16(case.h_t, dev), bf16(case.W_s, dev), bf16(case.W_t, dev)
+    g = f32(case.grad, dev)
+    partials, loss, stats, dh, dW = _run_shards(torch, hs, Ws, ht, Wt, bounds, g)
+    w = {k: O.widen_bf16(getattr(case, k)) for k in ("h_s", "W_s", "h_t", "W_t")}
+    for (a, b), P in zip(bounds, partials):
+        want = S.shard_partials(w["h_s"], w["W_s"], w["h_t"], w["W_t"], a, b)
+        assert_loss_close(P[0] + np.log(P[1]), want[0] + np.log(want[1]), f"shard [{a},{b}) lse_s")
+        assert_loss_close(P[3] + np.log(P[4]), want[3] + np.log(want[4]), f"shard [{a},{b}) lse_t")
+    L, ls, lt, lpmax = S.merge([S.shard_partials(w["h_s"], w["W_s"], w["h_t"], w["W_t"], a, b) for a, b in bounds])
+    assert_loss_close(loss, L, "loss")
+    assert_loss_close(stats[:, 0], ls, "lse_s")
+    assert_loss_close(stats[:, 1], lt, "lse_t")
+    assert np.array_equal(stats[:, 2], loss)
+    assert_loss_close(stats[:, 3], lpmax, "log p_max")
+    full = O.backward(O.Inputs.from_case(case), np.arange(case.T), case.grad.astype(np.float64))
+    assert_grad_close(dh, full["dh"], "dh (sum over shards)")
+    assert_grad_close(dW, full["dW"], "dW (shard rows)")
+
+
+def test_sharded_equals_unsharded_within_tolerance(tdev):
+    torch, dev = tdev
+    case = synth.random_case(601, T=256, V=5000, Hs=64, Ht=64, p_mask=1.0)
+    say("vocab shards vs single device")
+    hs, ht, Ws, Wt = bf16(case.h_s, dev), bf16(case.h_t, dev), bf16(case.W_s, dev), bf16(case.W_t, dev)
+    _, loss, stats, dh, dW = _run_shards(torch, hs, Ws, ht, Wt, S.shard_bounds(5000, 4))
+    loss1, stats1 = R.forward_hidden(hs, Ws, ht, Wt)
+    dh1, dW1 = R.backward_hidden(hs, Ws, ht, Wt, stats1)
+    assert_loss_close(loss, host(loss1).astype(np.float64), "loss")
+    assert_loss_close(stats[:, :2], host(stats1)[:, :2].astype(np.float64), "lse")
+    assert_grad_close(dh, host(dh1).astype(np.float64), "dh")
+    assert_grad_close(dW, host(dW1).astype(np.float64), "dW")
+
+
+def test_one_shard_partial_finalises_like_the_forward(tdev):
+    """G = 1: merging one partial is the single-device forward's own combine
+    over the same split plan, bit for bit."""
+    torch, dev = tdev
+    case = synth.random_case(602, T=200, V=2100, Hs=128, Ht=64, p_mask=1.0)
+    say("vocab one shard")
+    hs, ht, Ws, Wt = bf16(case.h_s, dev), bf16(case.h_t, dev), bf16(case.W_s, dev), bf16(case.W_t, dev)
+    P = R.forward_hidden_shard(hs, Ws, ht, Wt)
+    loss, stats = R.combine_shards(P.unsqueeze(0).contiguous())
+    loss1, stats1 = R.forward_hidden(hs, Ws, ht, Wt)
+    assert np.array_equal(host(loss), host(loss1))
+    assert np.array_equal(host(stats), host(stats1))
+
+
+def test_full_row_mask_in_the_combine(tdev):
+    """Full-row mode: the shards run over all T rows and the combine zeroes
+    the rows whose mask is 0; the live rows equal the compacted rows' results
+    bit for bit (a row's partial depends on the shard's vocabulary only)."""
+    torch, dev = tdev
+    case = synth.random_case(603, T=333, V=2500, Hs=64, Ht=128, p_mask=0.6)
+    say("vocab shards full-row")
+    bounds = S.shard_bounds(2500, 3)
+    mask = u8(case.mask, dev)
+    hs, ht, Ws, Wt = bf16(case.h_s, dev), bf16(case.h_t, dev), bf16(case.W_s, dev), bf16(case.W_t, dev)
+    _, loss_f, stats_f, dh_f, _ = _run_shards(torch, hs, Ws, ht, Wt, bounds, row_mask=mask)
+    idx, N = R.compact_rows(mask)
+    _, loss_c, stats_c, dh_c, _ = _run_shards(torch, R.gather_rows(hs, idx), Ws, R.gather_rows(ht, idx), Wt, bounds)
+    rows, live = host(idx), case.mask != 0
+    assert np.array_equal(loss_f[rows], loss_c) and np.array_equal(stats_f[rows], stats_c)
+    assert np.all(loss_f[~live] == 0.0) and np.all(stats_f[~live] == 0.0)
+    assert np.array_equal(dh_f[rows], dh_c) and np.all(dh_f[~live] == 0.0)
+
+
+def test_empty_rows(tdev):
+    torch, dev = tdev
+    say("vocab shards N=0")
+    z = torch.empty((0, 64), dtype=torch.bfloat16, device=dev)
+    W = torch.zeros((100, 64), dtype=torch.bfloat16, device=dev)
+    P = R.forward_hidden_shard(z, W, z, W)
+    loss, stats = R.combine_shards(torch.stack([P, P]).contiguous())
+    assert loss.shape == (0,) and stats.shape == (0, 4)
