@@ -193,14 +193,28 @@ int rkl_forward_hidden_shard(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const
                              void* workspace, size_t workspace_bytes, rkl_stream_t stream);
 
 /*
- * Merge G shards' partials [G, 5, N] (rkl_forward_hidden_shard's outputs, in
- * shard order) with the log-sum-exp rule -- M = max_g m_g, S = sum_g S_g
- * exp(m_g - M), A likewise with the student's factors -- and finalise as
- * rkl_forward_hidden: loss [N], stats [N, 4] (lse_s, lse_t, L, log p_max over
- * the whole vocabulary); rows with row_mask 0 get zeros.  1 <= G <= 2^20.
- * The backward of a shard is rkl_backward_hidden on the shard's rows of W_s
- * and W_t (V = the shard's count) with these merged stats: it writes the
- * shard's rows of dW_s and its term of dh_s, which the ranks then sum.
+ * The same for the teacher-logits payload: the shard's teacher logits z_t
+ * [N, V] fp32 (its V columns, densely packed) and the student as the shard's
+ * (h_s, W_s) rows or as its fp32 logits z_s [N, V]; arguments otherwise as
+ * rkl_forward_logits.  Workspace: rkl_workspace_bytes(N, V, Hs, 0) (0 when
+ * the student is given as logits).  The shard's backward is
+ * rkl_backward_logits on the shard with the merged stats.
+ */
+int rkl_forward_logits_shard(int64_t N, int64_t V, int64_t Hs, const rkl_bf16* h_s, const rkl_bf16* W_s,
+                             const float* z_s, const float* z_t, float* partial, void* workspace,
+                             size_t workspace_bytes, rkl_stream_t stream);
+
+/*
+ * Merge G shards' partials [G, 5, N] (outputs of rkl_forward_hidden_shard or
+ * rkl_forward_logits_shard, in shard order) with the log-sum-exp rule --
+ * M = max_g m_g, S = sum_g S_g exp(m_g - M), A likewise with the student's
+ * factors -- and finalise as rkl_forward_hidden: loss [N], stats [N, 4]
+ * (lse_s, lse_t, L, log p_max over the whole vocabulary); rows with
+ * row_mask 0 get zeros.  1 <= G <= 2^20.
+ * The backward of a shard is rkl_backward_hidden (or rkl_backward_logits) on
+ * the shard's rows of W_s and W_t, or its logits columns (V = the shard's
+ * count), with these merged stats: it writes the shard's rows of dW_s (or
+ * its dz_s columns) and its term of dh_s, which the ranks then sum.
  */
 int rkl_combine_shards(int64_t G, int64_t N, const float* partials, const uint8_t* row_mask, float* loss,
                        float* stats, rkl_stream_t stream);

@@ -20,7 +20,7 @@ __all__ = [
     "RKLError", "lib", "LIB_PATH", "version", "workspace_bytes", "workspace_bytes_teachers", "compact_rows",
     "gather_rows", "scatter_rows", "forward_hidden", "forward_logits", "backward_hidden", "backward_logits",
     "forward_hidden_teachers", "backward_hidden_teachers", "forward_logprob_entropy", "backward_logprob_entropy",
-    "forward_hidden_shard", "combine_shards", "ReverseKL",
+    "forward_hidden_shard", "forward_logits_shard", "combine_shards", "ReverseKL",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librkl.so")
@@ -59,6 +59,7 @@ def lib() -> ctypes.CDLL:
         "rkl_backward_hidden": ([I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, I32, P, SZ, P], I32),
         "rkl_backward_logits": ([I64, I64, I64, P, P, P, P, P, P, P, P, P, I32, P, P, SZ, P], I32),
         "rkl_forward_hidden_shard": ([I64, I64, I64, I64, P, P, P, P, P, P, SZ, P], I32),
+        "rkl_forward_logits_shard": ([I64, I64, I64, P, P, P, P, P, P, SZ, P], I32),
         "rkl_combine_shards": ([I64, I64, P, P, P, P, P], I32),
         "rkl_forward_hidden_teachers": ([I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, SZ, P], I32),
         "rkl_backward_hidden_teachers": ([I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, I32, P, SZ, P],
@@ -397,6 +398,28 @@ def forward_hidden_shard(h_s, W_s, h_t, W_t):
     partial = torch.empty((5, N), dtype=torch.float32, device=dev)
     ws = _workspace(dev, workspace_bytes(N, V, Hs, Ht))
     _check(lib().rkl_forward_hidden_shard(N, V, Hs, Ht, _ptr(h_s), _ptr(W_s), _ptr(h_t), _ptr(W_t), _ptr(partial),
+                                          _ptr(ws), ws.numel(), _stream(dev)))
+    return partial
+
+
+def forward_logits_shard(z_t, h_s=None, W_s=None, z_s=None):
+    """One vocabulary shard with the teacher given as the shard's fp32 logits
+    z_t [N, V]; the student as the shard's (h_s, W_s) rows or as its fp32
+    logits z_s [N, V].  Returns partial fp32 [5, N] as forward_hidden_shard."""
+    torch = _torch()
+    dev = z_t.device
+    N, V = z_t.shape
+    _need(z_t, "z_t", torch.float32, dev)
+    Hs = 0
+    if z_s is None:
+        Hs = h_s.shape[1]
+        _need(h_s, "h_s", torch.bfloat16, dev, (N, Hs))
+        _need(W_s, "W_s", torch.bfloat16, dev, (V, Hs))
+    else:
+        _need(z_s, "z_s", torch.float32, dev, (N, V))
+    partial = torch.empty((5, N), dtype=torch.float32, device=dev)
+    ws = _workspace(dev, workspace_bytes(N, V, Hs, 0))
+    _check(lib().rkl_forward_logits_shard(N, V, Hs, _ptr(h_s), _ptr(W_s), _ptr(z_s), _ptr(z_t), _ptr(partial),
                                           _ptr(ws), ws.numel(), _stream(dev)))
     return partial
 

@@ -421,6 +421,26 @@ int rkl_forward_hidden_shard(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const
                        workspace, workspace_bytes, static_cast<hipStream_t>(stream), Teachers{}, partial);
 }
 
+int rkl_forward_logits_shard(int64_t N, int64_t V, int64_t Hs, const rkl_bf16* h_s, const rkl_bf16* W_s,
+                             const float* z_s, const float* z_t, float* partial, void* workspace,
+                             size_t workspace_bytes, rkl_stream_t stream) {
+  const bool student_hidden = h_s != nullptr || W_s != nullptr;
+  if (student_hidden && z_s) return fail(RKL_INVALID_ARG, "give the student as (h_s, W_s) or as z_s, not both");
+  if (int rc = check_dims(N, V, Hs, 0, false, student_hidden)) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (N > 0) {
+    NEED16(z_t, "z_t"); NEED4(partial, "partial");
+    if (student_hidden) { NEED16(h_s, "h_s"); NEED16(W_s, "W_s"); }
+    else NEED16(z_s, "z_s");
+  }
+  if (student_hidden)
+    return forward_tiled(N, V, Hs, 0, h_s, W_s, nullptr, nullptr, z_t, nullptr, nullptr, nullptr, nullptr, nullptr,
+                         workspace, workspace_bytes, s, Teachers{}, partial);
+  if (N == 0) return RKL_OK;
+  RKL_TRY(rkl::launch_fwd_rows_logits(z_s, z_t, (int)N, (int)V, nullptr, nullptr, nullptr, partial, s));
+  return RKL_OK;
+}
+
 int rkl_combine_shards(int64_t G, int64_t N, const float* partials, const uint8_t* row_mask, float* loss,
                        float* stats, rkl_stream_t stream) {
   if (G < 1 || G > ((int64_t)1 << 20)) return fail(RKL_INVALID_ARG, "G=%lld shards out of range [1, 2^20]", (long long)G);
@@ -450,7 +470,7 @@ int rkl_forward_logits(int64_t N, int64_t V, int64_t Hs, const rkl_bf16* h_s, co
     return forward_tiled(N, V, Hs, 0, h_s, W_s, nullptr, nullptr, z_t, nullptr, row_mask, loss, nullptr, stats,
                          workspace, workspace_bytes, s);
   if (N == 0) return RKL_OK;
-  RKL_TRY(rkl::launch_fwd_rows_logits(z_s, z_t, (int)N, (int)V, row_mask, loss, stats, s));
+  RKL_TRY(rkl::launch_fwd_rows_logits(z_s, z_t, (int)N, (int)V, row_mask, loss, stats, nullptr, s));
   return RKL_OK;
 }
 

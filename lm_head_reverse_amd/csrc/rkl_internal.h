@@ -105,8 +105,9 @@ hipError_t launch_grad_scale(const float* grad, const float* grad_h, const uint8
 hipError_t launch_transpose_h(const uint16_t* h, int N, int H, uint16_t* hT, int ldT, hipStream_t s);
 hipError_t launch_dw(const DwParams& p, int waves, hipStream_t s);
 hipError_t launch_dh(const DhParams& p, int waves, hipStream_t s);
+// merged != NULL: the unfinalised (m_s, S_s, A, m_t, S_t) planes instead of loss / stats
 hipError_t launch_fwd_rows_logits(const float* z_s, const float* z_t, int N, int V, const uint8_t* row_mask,
-                                  float* loss, float* stats, hipStream_t s);
+                                  float* loss, float* stats, float* merged, hipStream_t s);
 hipError_t launch_bwd_rows_logits(const float* z_s, const float* z_t, int N, int V, const uint8_t* row_mask,
                                   const float* grad, const float* stats, float* dz, hipStream_t s);
 hipError_t launch_compact(const uint8_t* mask, int T, int32_t* row_idx, int32_t* n_out, hipStream_t s);

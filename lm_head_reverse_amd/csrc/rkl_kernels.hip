@@ -959,9 +959,12 @@ __global__ __launch_bounds__(64 * NW, 1) void dh_gemm(DhParams p) {
 // ===========================================================================
 // Both sides given as fp32 logits: one workgroup per row streams z_s, z_t.
 // ===========================================================================
+// merged != NULL: write the row's (m_s, S_s, A, m_t, S_t) to merged as five
+// planes of N (one vocabulary shard's partial) instead of finalising.
 __global__ __launch_bounds__(256) void fwd_rows_logits(const float* __restrict__ z_s, const float* __restrict__ z_t,
                                                        int N, int V, const uint8_t* __restrict__ row_mask,
-                                                       float* __restrict__ loss, float* __restrict__ stats) {
+                                                       float* __restrict__ loss, float* __restrict__ stats,
+                                                       float* __restrict__ merged) {
   __shared__ float red[5][256];
   const int n = blockIdx.x, tid = threadIdx.x;
   const float* rs = z_s + (int64_t)n * V;
@@ -1008,6 +1011,11 @@ __global__ __launch_bounds__(256) void fwd_rows_logits(const float* __restrict__
       red[0][tid] = m1; red[1][tid] = s1; red[2][tid] = a1; red[3][tid] = m2; red[4][tid] = s2;
     }
     __syncthreads();
+  }
+  if (tid == 0 && merged) {
+#pragma unroll
+    for (int c = 0; c < 5; ++c) merged[(int64_t)c * N + n] = red[c][0];
+    return;
   }
   if (tid == 0) {
     const float log_ss = logf(red[1][0]);
@@ -1255,8 +1263,8 @@ hipError_t launch_dh(const DhParams& p, int waves, hipStream_t s) {
 }
 
 hipError_t launch_fwd_rows_logits(const float* z_s, const float* z_t, int N, int V, const uint8_t* row_mask,
-                                  float* loss, float* stats, hipStream_t s) {
-  fwd_rows_logits<<<(unsigned)N, 256, 0, s>>>(z_s, z_t, N, V, row_mask, loss, stats);
+                                  float* loss, float* stats, float* merged, hipStream_t s) {
+  fwd_rows_logits<<<(unsigned)N, 256, 0, s>>>(z_s, z_t, N, V, row_mask, loss, stats, merged);
   return hipGetLastError();
 }
 

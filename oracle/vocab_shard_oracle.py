@@ -43,8 +43,15 @@ from oracle.rkl_oracle import project, reverse_kl_dz
 def shard_partials(h_s, W_s, h_t, W_t, v0: int, v1: int) -> np.ndarray:
     """[5, rows] float64: (m_s, S_s, A, m_t, S_t) of vocabulary columns
     [v0, v1) (float64 inputs: h [rows, H], W [V, H])."""
-    zs = project(h_s, W_s[v0:v1])
-    zt = project(h_t, W_t[v0:v1])
+    return partials_of_logits(project(h_s, W_s[v0:v1]), project(h_t, W_t[v0:v1]))
+
+
+def partials_of_logits(zs, zt) -> np.ndarray:
+    """[5, rows] float64: (m_s, S_s, A, m_t, S_t) of one shard's logits
+    z_s, z_t [rows, shard columns] (the teacher-logits payload, or either
+    side given as logits)."""
+    zs = np.asarray(zs, dtype=np.float64)
+    zt = np.asarray(zt, dtype=np.float64)
     m_s = np.max(zs, axis=1)
     e_s = np.exp(zs - m_s[:, None])
     m_t = np.max(zt, axis=1)

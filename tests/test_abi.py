@@ -32,7 +32,7 @@ def test_header_declares_the_path():
                  "rkl_forward_hidden", "rkl_forward_logits", "rkl_backward_hidden", "rkl_backward_logits",
                  "rkl_forward_logprob_entropy", "rkl_backward_logprob_entropy",
                  "rkl_forward_hidden_teachers", "rkl_backward_hidden_teachers",
-                 "rkl_forward_hidden_shard", "rkl_combine_shards",
+                 "rkl_forward_hidden_shard", "rkl_forward_logits_shard", "rkl_combine_shards",
                  "rkl_last_error", "rkl_version"):
         assert want in names
 
@@ -173,6 +173,10 @@ def test_vocab_shard_rejects():
     assert fwd(4, 100, 64, 64, FAKE, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1        # partial NULL
     assert "partial" in L.rkl_last_error().decode()
     assert fwd(4, 100, 64, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 16, None) == 3             # workspace
+    lg = L.rkl_forward_logits_shard
+    assert lg(4, 100, 64, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 1          # both student forms
+    assert lg(4, 100, 0, None, None, FAKE, None, FAKE, None, 0, None) == 1                 # z_t NULL
+    assert lg(4, 100, 0, None, None, FAKE, FAKE, None, None, 0, None) == 1                 # partial NULL
     comb = L.rkl_combine_shards
     assert comb(0, 4, FAKE, None, FAKE, FAKE, None) == 1
     assert "G=" in L.rkl_last_error().decode()

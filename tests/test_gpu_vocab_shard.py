@@ -4,8 +4,9 @@ fp64 oracle (oracle/vocab_shard_oracle.py).
 Every shard of a vocabulary runs on this one GPU in turn, as the ranks of a
 vocabulary-parallel group would run theirs; the shards' partials are stacked
 as an all-gather would leave them and merged by rkl_combine_shards.  Each
-shard's backward is rkl_backward_hidden on the shard's weight rows with the
-merged stats.  Bars as in test_gpu_parity; the summed dh uses the same bar.
+shard's backward is rkl_backward_hidden on the shard's weight rows (or
+rkl_backward_logits on its logit columns) with the merged stats.  Bars as in
+test_gpu_parity; the summed dh uses the same bar.
 """
 import numpy as np
 import pytest
@@ -122,3 +123,43 @@ def test_empty_rows(tdev):
     P = R.forward_hidden_shard(z, W, z, W)
     loss, stats = R.combine_shards(torch.stack([P, P]).contiguous())
     assert loss.shape == (0,) and stats.shape == (0, 4)
+
+
+@pytest.mark.parametrize("student_logits", [False, True])
+def test_logit_shards_against_oracle(tdev, student_logits):
+    """Teacher-logits payload: each shard gets its own columns of z_t (and of
+    z_s when the student is given as logits) as a dense [N, V_shard] block."""
+    torch, dev = tdev
+    case = synth.random_case(604 + int(student_logits), T=200, V=2600, Hs=128, Ht=0, p_mask=1.0,
+                             student_logits=student_logits, teacher_logits=True, with_grad=True)
+    say("vocab shards, teacher logits, student logits" if student_logits else "vocab shards, teacher logits")
+    bounds = [(0, 1300), (1300, 1301), (1301, 2600)]
+    zt, g = f32(case.z_t, dev), f32(case.grad, dev)
+    if student_logits:
+        zs = f32(case.z_s, dev)
+        side = [dict(z_s=zs[:, a:b].contiguous()) for a, b in bounds]
+    else:
+        hs, Ws = bf16(case.h_s, dev), bf16(case.W_s, dev)
+        side = [dict(h_s=hs, W_s=Ws[a:b]) for a, b in bounds]
+    zt_k = [zt[:, a:b].contiguous() for a, b in bounds]
+    parts = [R.forward_logits_shard(z, **kw) for z, kw in zip(zt_k, side)]
+    loss, stats = R.combine_shards(torch.stack(parts).contiguous())
+    grads = [R.backward_logits(z, stats, grad_loss=g, **kw) for z, kw in zip(zt_k, side)]
+    torch.cuda.synchronize()
+
+    zs_ref = case.z_s.astype(np.float64) if student_logits else O.project(O.widen_bf16(case.h_s),
+                                                                          O.widen_bf16(case.W_s))
+    zt_ref = case.z_t.astype(np.float64)
+    L, ls, lt, lpmax = S.merge([S.partials_of_logits(zs_ref[:, a:b], zt_ref[:, a:b]) for a, b in bounds])
+    assert_loss_close(host(loss), L, "loss")
+    assert_loss_close(host(stats)[:, 0], ls, "lse_s")
+    assert_loss_close(host(stats)[:, 1], lt, "lse_t")
+    assert_loss_close(host(stats)[:, 3], lpmax, "log p_max")
+    gg = case.grad.astype(np.float64)
+    if student_logits:
+        dz = np.concatenate([host(d) for d in grads], axis=1)
+        assert_grad_close(dz, O.reverse_kl_dz(zs_ref, zt_ref, ls, lt, L, gg), "dz (shard columns)")
+    else:
+        full = O.backward(O.Inputs.from_case(case), np.arange(case.T), gg)
+        assert_grad_close(sum(host(d).astype(np.float64) for d, _ in grads), full["dh"], "dh (sum over shards)")
+        assert_grad_close(np.concatenate([host(w) for _, w in grads]), full["dW"], "dW (shard rows)")

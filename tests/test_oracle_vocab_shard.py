@@ -103,3 +103,18 @@ def test_shard_backward_adds_up_to_the_unsharded_backward():
         assert np.allclose(r["dW"], full["dW"][a:b], rtol=1e-10, atol=1e-13)
         dh += r["dh"]
     assert np.allclose(dh, full["dh"], rtol=1e-10, atol=1e-13)
+
+
+def test_logit_shards_equal_the_unsharded_definition():
+    """Either side given as logits: shard partials of column slices merge to
+    the full-row log-sum-exps and reverse KL of the same logits."""
+    rng = np.random.default_rng(6)
+    zs = rng.standard_normal((20, 97)) * 2.0
+    zt = rng.standard_normal((20, 97)) * 2.0
+    zs[:, 50:] += 4.0                       # different maxima per shard
+    bounds = [(0, 13), (13, 50), (50, 51), (51, 97)]
+    L, ls, lt, lpmax = S.merge([S.partials_of_logits(zs[:, a:b], zt[:, a:b]) for a, b in bounds])
+    assert np.allclose(ls, scipy.special.logsumexp(zs, axis=1), rtol=1e-15, atol=1e-13)
+    assert np.allclose(lt, scipy.special.logsumexp(zt, axis=1), rtol=1e-15, atol=1e-13)
+    assert np.allclose(L, O.reverse_kl(zs, zt), rtol=1e-11, atol=1e-13)
+    assert np.allclose(lpmax, O.log_softmax(zs).max(axis=1), rtol=0, atol=1e-13)
