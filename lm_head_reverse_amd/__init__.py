@@ -129,9 +129,11 @@ _ws_cache = {}
 
 
 def _workspace(dev, nbytes: int):
-    """A cached device byte buffer of at least nbytes (grown on demand)."""
+    """A cached device byte buffer of at least nbytes (grown on demand), one
+    per (device, current stream): calls queued on one stream run in order and
+    may share it; calls on different streams may overlap, so they do not."""
     torch = _torch()
-    key = str(dev)
+    key = (str(dev), torch.cuda.current_stream(dev).cuda_stream)
     buf = _ws_cache.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
@@ -296,9 +298,12 @@ class ReverseKL:
     """Per-position reverse KL over a [B, S-1] loss mask with compaction:
     compact -> gather -> fused forward -> scatter, and the matching backward.
 
-        rk = ReverseKL(W_s, W_t)                 # hidden-state teacher
-        loss_pos = rk.forward(h_s, h_t, mask)    # fp32 [T], zeros where mask == 0
-        dh_pos, dW = rk.backward(grad_pos)       # fp32 [T, Hs] and [V, Hs]
+        rk = ReverseKL(W_s, W_t)                     # hidden-state teacher
+        loss_pos = rk.forward(h_s, mask, h_t=h_t)    # fp32 [T], zeros where mask == 0
+        dh_pos, dW = rk.backward(grad_pos)           # fp32 [T, Hs] and [V, Hs]
+
+    With the teacher as fp32 logits: ReverseKL(W_s) and rk.forward(h_s, mask,
+    z_t=z_t), z_t [T, V].
     """
 
     def __init__(self, W_s, W_t=None):
