@@ -346,7 +346,9 @@ __device__ __forceinline__ void dual_stream(const DualOps& o, int njobs, char* l
       step(zs, Plain{}, 0u);
       hook(consumed, job, kt);
     }
-    if (passes > 0) {
+    // per-row teachers: a tile whose rows all have ids outside [0, K) runs no
+    // teacher pass, and its teacher logits are the zeros set here
+    if (MULTI || passes > 0) {
       zero_acc(zt);
       if (!MULTI) {
         for (int kt = 0; kt < o.nk[1]; ++kt) step(zt, Plain{}, 0u);

@@ -154,3 +154,36 @@ def test_full_row_equals_compact(tdev):
         assert np.array_equal(f[i][rows], c[i]), what
         assert np.all(f[i][~m] == 0.0), what
     assert_grad_close(f[4], c[4], "dW full-row vs compact")
+
+
+def test_the_most_teachers_with_out_of_range_ids(tdev):
+    """K = 31, the largest: tile sets use bits 0..30, and ids 31 and -1 (no
+    teacher) set the out-of-range bit.  Every 128-row tile holds many
+    teachers before grouping; rows are compared with a zero teacher for the
+    out-of-range ids, in full-row mode with a partial mask."""
+    torch, dev = tdev
+    K = 31
+    case, W_t, teacher = _problem(506, T=700, V=1300, Hs=64, Ht=64, K=K, p_mask=0.7)
+    teacher[::7] = K
+    teacher[3::11] = -1
+    say("teachers K=31 with out-of-range ids")
+    out = _run(case, W_t, teacher, dev)
+    W_z = np.concatenate([W_t, np.zeros_like(W_t[:1])])
+    t_ref = np.where((teacher >= 0) & (teacher < K), teacher, K)
+    _check(case, W_z, t_ref, out)
+    f = _run(case, W_t, teacher, dev, full_row=True)
+    rows = out[0]
+    for i, what in ((1, "loss"), (2, "stats"), (3, "dh")):
+        assert np.array_equal(f[i][rows], out[i]), what
+
+
+def test_tiles_of_only_out_of_range_ids(tdev):
+    """260 of 400 rows name no teacher: grouped last, they fill whole 128-row
+    tiles that run no teacher pass at all (their teacher logits are 0)."""
+    torch, dev = tdev
+    case, W_t, teacher = _problem(507, T=400, V=900, Hs=64, Ht=128, K=2, p_mask=1.0)
+    teacher[:260] = -5
+    say("teachers: whole tiles of out-of-range ids")
+    out = _run(case, W_t, teacher, dev)
+    W_z = np.concatenate([W_t, np.zeros_like(W_t[:1])])
+    _check(case, W_z, np.where(teacher < 0, 2, teacher), out)
