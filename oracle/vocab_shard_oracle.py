@@ -25,11 +25,22 @@ backward restricted to the shard's columns, with the merged statistics: its
 dz columns and dW rows are the shard's part of the full ones, and its dh is
 one term of a sum over the shards.
 
+The same split applies to the log-probability of a sampled token and the
+entropy (the same notes put these functions beside the distributed entropy
+function): a shard reduces its columns to
+
+    m = max_v z,   S = sum_v exp(z - m),   B = sum_v exp(z - m) z,
+    z_y = z[y] when the sampled token y lies in the shard, else -inf,
+
+and the merge gives lse = M + log S, H = lse - B / S, log p(y) = z_y - lse
+(z_y from the one shard that holds y).
+
 Pins: tests/test_oracle_vocab_shard.py (merged shards against the
-unsharded definition in oracle/rkl_oracle.py for uneven shards, one-column
-shards and a single shard; each shard's m + log S against scipy's
-logsumexp; shard order; the backward's dh adding up over shards and its dW
-rows matching the full dW).
+unsharded definitions in oracle/rkl_oracle.py and
+oracle/logprob_entropy_oracle.py for uneven shards, one-column shards and a
+single shard; each shard's m + log S against scipy's logsumexp; shard
+order; the backward's dh adding up over shards and its dW rows matching the
+full dW).
 """
 from __future__ import annotations
 
@@ -92,3 +103,28 @@ def shard_backward(h_s, W_s, h_t, W_t, v0: int, v1: int, stats, g: Optional[np.n
     zt = project(h_t, W_t[v0:v1])
     dz = reverse_kl_dz(zs, zt, lse_s, lse_t, L, g)
     return {"dz": dz, "dh": dz @ W_s[v0:v1], "dW": dz.T @ h_s}
+
+
+def lpe_shard_partials(h, W, y, v0: int, v1: int) -> np.ndarray:
+    """[4, rows] float64: (m, S, B, z_y) of vocabulary columns [v0, v1) for
+    the projection h W^T and sampled tokens y (global vocabulary indices)."""
+    z = project(h, W[v0:v1])
+    m = np.max(z, axis=1)
+    e = np.exp(z - m[:, None])
+    y = np.asarray(y, dtype=np.int64)
+    inside = (y >= v0) & (y < v1)
+    zy = np.full(z.shape[0], -np.inf)
+    zy[inside] = z[np.nonzero(inside)[0], y[inside] - v0]
+    return np.stack([m, np.sum(e, axis=1), np.sum(e * z, axis=1), zy])
+
+
+def lpe_merge(partials: Sequence[np.ndarray]):
+    """Merge shard partials ([G] of [4, rows]) into per-row (log p(y),
+    entropy, lse, lpmax)."""
+    P = np.stack([np.asarray(p, dtype=np.float64) for p in partials])   # [G, 4, rows]
+    M = np.max(P[:, 0], axis=0)
+    f = np.exp(P[:, 0] - M)
+    S = np.sum(P[:, 1] * f, axis=0)
+    B = np.sum(P[:, 2] * f, axis=0)
+    lse = M + np.log(S)
+    return np.max(P[:, 3], axis=0) - lse, lse - B / S, lse, -np.log(S)

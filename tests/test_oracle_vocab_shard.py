@@ -10,6 +10,7 @@ dropped a shard fails the first check: the shards' maxima differ.
 import numpy as np
 import pytest
 import scipy.special
+import scipy.stats
 
 import synth
 from oracle import rkl_oracle as O
@@ -118,3 +119,39 @@ def test_logit_shards_equal_the_unsharded_definition():
     assert np.allclose(lt, scipy.special.logsumexp(zt, axis=1), rtol=1e-15, atol=1e-13)
     assert np.allclose(L, O.reverse_kl(zs, zt), rtol=1e-11, atol=1e-13)
     assert np.allclose(lpmax, O.log_softmax(zs).max(axis=1), rtol=0, atol=1e-13)
+
+
+@pytest.mark.parametrize("bounds", [
+    [(0, 61)],
+    [(0, 20), (20, 21), (21, 61)],
+    S.shard_bounds(61, 8),
+    [(v, v + 1) for v in range(61)],
+])
+def test_logprob_entropy_shards_equal_the_unsharded_definition(bounds):
+    from oracle import logprob_entropy_oracle as E
+    _, w = _problem(7)
+    n = w["h_s"].shape[0]
+    y = np.random.default_rng(8).integers(0, 61, n)
+    y[:4] = (0, 19, 20, 60)                       # shard edges
+    lp, H, lse, lpmax = S.lpe_merge([S.lpe_shard_partials(w["h_s"], w["W_s"], y, a, b) for a, b in bounds])
+    z = O.project(w["h_s"], w["W_s"])
+    lp0, H0, lse0 = E.logprob_entropy(z, y)
+    assert np.allclose(lse, lse0, rtol=1e-14, atol=1e-13)
+    assert np.allclose(lp, lp0, rtol=1e-12, atol=1e-12)
+    assert np.allclose(H, H0, rtol=1e-11, atol=1e-12)
+    assert np.allclose(H, scipy.stats.entropy(scipy.special.softmax(z, axis=1), axis=1), rtol=1e-10, atol=1e-12)
+    assert np.allclose(lpmax, O.log_softmax(z).max(axis=1), rtol=0, atol=1e-13)
+
+
+def test_logprob_entropy_shard_partial_pieces():
+    _, w = _problem(9)
+    y = np.arange(w["h_s"].shape[0]) * 3 % 61
+    a, b = 10, 37
+    P = S.lpe_shard_partials(w["h_s"], w["W_s"], y, a, b)
+    z = O.project(w["h_s"], w["W_s"][a:b])
+    assert np.allclose(P[0] + np.log(P[1]), scipy.special.logsumexp(z, axis=1), rtol=1e-15, atol=1e-13)
+    p = scipy.special.softmax(z, axis=1)
+    assert np.allclose(P[2] / P[1], np.sum(p * z, axis=1), rtol=1e-12, atol=1e-13)
+    inside = (y >= a) & (y < b)
+    assert np.all(np.isneginf(P[3][~inside]))
+    assert np.array_equal(P[3][inside], z[np.nonzero(inside)[0], y[inside] - a])
