@@ -293,6 +293,36 @@ int rkl_backward_logprob_entropy(int64_t N, int64_t V, int64_t H, const rkl_bf16
                                  const float* grad_entropy, const float* stats, float* dh, float* dW,
                                  int accumulate_dW, void* workspace, size_t workspace_bytes, rkl_stream_t stream);
 
+/*
+ * Log-probability / entropy over one vocabulary shard (NeMo-RL page,
+ * implementation notes: the reverse-KL functions sit beside a distributed,
+ * vocabulary-parallel entropy function).  A rank owns vocabulary rows
+ * [v0, v0 + V) of W and passes those rows with V = its row count, and y in
+ * the shard's own coordinates (y - v0; a row whose token lies in another
+ * shard passes any value outside [0, V), e.g. -1).  Nothing is finalised:
+ *   partial [5, N] fp32 out: per row, over the shard's columns,
+ *       m = max z, S = sum exp(z - m), B = sum exp(z - m) z,
+ *       z_y (the token's logit, or -1e30 when the token is not in the shard), 0
+ *   (planes of N, in that order).
+ * Workspace: rkl_workspace_bytes(N, V, H, 0) with the shard's V.
+ */
+int rkl_forward_logprob_entropy_shard(int64_t N, int64_t V, int64_t H, const rkl_bf16* h, const rkl_bf16* W,
+                                      const int32_t* y, float* partial, void* workspace, size_t workspace_bytes,
+                                      rkl_stream_t stream);
+
+/*
+ * Merge G shards' log-probability / entropy partials [G, 5, N] (in shard
+ * order): M = max_g m_g, S = sum_g S_g exp(m_g - M), B likewise, z_y the
+ * largest of the shards' (the one shard that holds the token); then
+ * finalise as rkl_forward_logprob_entropy: logp [N] = z_y - lse, entropy [N]
+ * = lse - B / S, stats [N, 4] (lse, entropy, logp, log p_max); rows with
+ * row_mask 0 get zeros.  1 <= G <= 2^20.  The backward of a shard is
+ * rkl_backward_logprob_entropy on the shard's rows of W with the shard-local
+ * y and these merged stats: the shard's dW rows and its term of dh.
+ */
+int rkl_combine_shards_logprob_entropy(int64_t G, int64_t N, const float* partials, const uint8_t* row_mask,
+                                       float* logp, float* entropy, float* stats, rkl_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -20,7 +20,8 @@ __all__ = [
     "RKLError", "lib", "LIB_PATH", "version", "workspace_bytes", "workspace_bytes_teachers", "compact_rows",
     "gather_rows", "scatter_rows", "forward_hidden", "forward_logits", "backward_hidden", "backward_logits",
     "forward_hidden_teachers", "backward_hidden_teachers", "forward_logprob_entropy", "backward_logprob_entropy",
-    "forward_hidden_shard", "forward_logits_shard", "combine_shards", "ReverseKL",
+    "forward_hidden_shard", "forward_logits_shard", "combine_shards", "forward_logprob_entropy_shard",
+    "combine_shards_logprob_entropy", "ReverseKL",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librkl.so")
@@ -61,6 +62,8 @@ def lib() -> ctypes.CDLL:
         "rkl_forward_hidden_shard": ([I64, I64, I64, I64, P, P, P, P, P, P, SZ, P], I32),
         "rkl_forward_logits_shard": ([I64, I64, I64, P, P, P, P, P, P, SZ, P], I32),
         "rkl_combine_shards": ([I64, I64, P, P, P, P, P], I32),
+        "rkl_forward_logprob_entropy_shard": ([I64, I64, I64, P, P, P, P, P, SZ, P], I32),
+        "rkl_combine_shards_logprob_entropy": ([I64, I64, P, P, P, P, P, P], I32),
         "rkl_forward_hidden_teachers": ([I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, SZ, P], I32),
         "rkl_backward_hidden_teachers": ([I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, I32, P, SZ, P],
                                          I32),
@@ -444,6 +447,45 @@ def combine_shards(partials, row_mask=None):
     stats = torch.empty((N, 4), dtype=torch.float32, device=dev)
     _check(lib().rkl_combine_shards(G, N, _ptr(partials), _ptr(row_mask), _ptr(loss), _ptr(stats), _stream(dev)))
     return loss, stats
+
+
+def forward_logprob_entropy_shard(h, W, y):
+    """One vocabulary shard of the log-probability / entropy forward: W [V,
+    H] holds the shard's vocabulary rows, y int32 [N] the sampled tokens in
+    the shard's coordinates (outside [0, V) when in another shard).  Returns
+    partial fp32 [5, N] = (m, S, B, z_y, 0) planes; merge the shards' with
+    combine_shards_logprob_entropy."""
+    torch = _torch()
+    dev = h.device
+    N, H = h.shape
+    V = W.shape[0]
+    _need(h, "h", torch.bfloat16, dev)
+    _need(W, "W", torch.bfloat16, dev, (V, H))
+    _need(y, "y", torch.int32, dev, (N,))
+    partial = torch.empty((5, N), dtype=torch.float32, device=dev)
+    ws = _workspace(dev, workspace_bytes(N, V, H, 0))
+    _check(lib().rkl_forward_logprob_entropy_shard(N, V, H, _ptr(h), _ptr(W), _ptr(y), _ptr(partial), _ptr(ws),
+                                                   ws.numel(), _stream(dev)))
+    return partial
+
+
+def combine_shards_logprob_entropy(partials, row_mask=None):
+    """Merge [G, 5, N] log-probability / entropy shard partials into (logp
+    [N], entropy [N], stats [N, 4]) over the whole vocabulary."""
+    torch = _torch()
+    dev = partials.device
+    G, five, N = partials.shape
+    if five != 5:
+        raise RKLError(RKL_INVALID_ARG, "partials must be [G, 5, N]")
+    _need(partials, "partials", torch.float32, dev)
+    if row_mask is not None:
+        _need(row_mask, "row_mask", torch.uint8, dev, (N,))
+    logp = torch.empty(N, dtype=torch.float32, device=dev)
+    ent = torch.empty(N, dtype=torch.float32, device=dev)
+    stats = torch.empty((N, 4), dtype=torch.float32, device=dev)
+    _check(lib().rkl_combine_shards_logprob_entropy(G, N, _ptr(partials), _ptr(row_mask), _ptr(logp), _ptr(ent),
+                                                    _ptr(stats), _stream(dev)))
+    return logp, ent, stats
 
 
 def forward_hidden_teachers(h_s, W_s, h_t, W_t, teacher, row_mask=None):

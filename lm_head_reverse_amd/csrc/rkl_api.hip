@@ -330,8 +330,24 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
   return RKL_OK;
 }
 
+// Merge of G vocabulary shards' partials (rkl_combine_shards*).
+int combine_shards(int64_t G, int64_t N, const float* partials, const uint8_t* row_mask, bool lpe, float* out0,
+                   float* out1, float* stats, hipStream_t s) {
+  if (G < 1 || G > ((int64_t)1 << 20)) return fail(RKL_INVALID_ARG, "G=%lld shards out of range [1, 2^20]", (long long)G);
+  if (N < 0 || N > kMaxDim) return fail(RKL_INVALID_ARG, "N=%lld out of range [0, 2^30]", (long long)N);
+  if (G * 5 * N > ((int64_t)1 << 40)) return fail(RKL_INVALID_ARG, "G*N too large");
+  if (N == 0) return RKL_OK;
+  NEED4(partials, "partials"); NEED4(stats, "stats");
+  if (lpe) { NEED4(out0, "logp"); NEED4(out1, "entropy"); }
+  else NEED4(out0, "loss");
+  RKL_TRY(rkl::launch_fwd_combine(partials, (int)G, (int)N, row_mask, lpe, out0, out1, stats, s));
+  return RKL_OK;
+}
+
 }  // namespace
 
+// The library is built with hidden visibility; only the C ABI is exported.
+#pragma GCC visibility push(default)
 extern "C" {
 
 const char* rkl_last_error(void) { return g_err.c_str(); }
@@ -443,14 +459,23 @@ int rkl_forward_logits_shard(int64_t N, int64_t V, int64_t Hs, const rkl_bf16* h
 
 int rkl_combine_shards(int64_t G, int64_t N, const float* partials, const uint8_t* row_mask, float* loss,
                        float* stats, rkl_stream_t stream) {
-  if (G < 1 || G > ((int64_t)1 << 20)) return fail(RKL_INVALID_ARG, "G=%lld shards out of range [1, 2^20]", (long long)G);
-  if (N < 0 || N > kMaxDim) return fail(RKL_INVALID_ARG, "N=%lld out of range [0, 2^30]", (long long)N);
-  if (G * 5 * N > ((int64_t)1 << 40)) return fail(RKL_INVALID_ARG, "G*N too large");
-  if (N == 0) return RKL_OK;
-  NEED4(partials, "partials"); NEED4(loss, "loss"); NEED4(stats, "stats");
-  RKL_TRY(rkl::launch_fwd_combine(partials, (int)G, (int)N, row_mask, false, loss, nullptr, stats,
-                                  static_cast<hipStream_t>(stream)));
-  return RKL_OK;
+  return combine_shards(G, N, partials, row_mask, false, loss, nullptr, stats, static_cast<hipStream_t>(stream));
+}
+
+int rkl_forward_logprob_entropy_shard(int64_t N, int64_t V, int64_t H, const rkl_bf16* h, const rkl_bf16* W,
+                                      const int32_t* y, float* partial, void* workspace, size_t workspace_bytes,
+                                      rkl_stream_t stream) {
+  if (int rc = check_dims(N, V, H, 0, false, true)) return rc;
+  if (N > 0) {
+    NEED16(h, "h"); NEED16(W, "W"); NEED4(y, "y"); NEED4(partial, "partial");
+  }
+  return forward_tiled(N, V, H, 0, h, W, nullptr, nullptr, nullptr, y, nullptr, nullptr, nullptr, nullptr, workspace,
+                       workspace_bytes, static_cast<hipStream_t>(stream), Teachers{}, partial);
+}
+
+int rkl_combine_shards_logprob_entropy(int64_t G, int64_t N, const float* partials, const uint8_t* row_mask,
+                                       float* logp, float* entropy, float* stats, rkl_stream_t stream) {
+  return combine_shards(G, N, partials, row_mask, true, logp, entropy, stats, static_cast<hipStream_t>(stream));
 }
 
 int rkl_forward_logits(int64_t N, int64_t V, int64_t Hs, const rkl_bf16* h_s, const rkl_bf16* W_s, const float* z_s,
@@ -625,3 +650,4 @@ int rkl_backward_hidden_teachers(int64_t N, int64_t V, int64_t Hs, int64_t Ht, i
 }
 
 }  // extern "C"
+#pragma GCC visibility pop

@@ -4,6 +4,8 @@ with a status and a message before anything is launched."""
 import ctypes
 import os
 import re
+import shutil
+import subprocess
 import threading
 
 import pytest
@@ -33,6 +35,7 @@ def test_header_declares_the_path():
                  "rkl_forward_logprob_entropy", "rkl_backward_logprob_entropy",
                  "rkl_forward_hidden_teachers", "rkl_backward_hidden_teachers",
                  "rkl_forward_hidden_shard", "rkl_forward_logits_shard", "rkl_combine_shards",
+                 "rkl_forward_logprob_entropy_shard", "rkl_combine_shards_logprob_entropy",
                  "rkl_last_error", "rkl_version"):
         assert want in names
 
@@ -42,6 +45,16 @@ def test_library_exports_every_declared_symbol():
     missing = [n for n in declared_functions() if not hasattr(L, n)]
     assert not missing, missing
     assert "gfx950" in R.version()
+
+
+def test_library_exports_nothing_else():
+    """Only the C ABI is visible: the library is built with hidden visibility."""
+    nm = shutil.which("nm")
+    if nm is None:
+        pytest.skip("nm not available")
+    out = subprocess.run([nm, "-D", "--defined-only", R.LIB_PATH], capture_output=True, text=True, check=True).stdout
+    exported = sorted(line.split()[-1] for line in out.splitlines() if line.split()[1:2] == ["T"])
+    assert exported == declared_functions()
 
 
 def test_workspace_sizes():
@@ -184,6 +197,14 @@ def test_vocab_shard_rejects():
     assert comb(2, 4, None, None, FAKE, FAKE, None) == 1
     assert comb(2, 4, MISALIGNED, None, FAKE, FAKE, None) == 1
     assert comb(2, 0, None, None, None, None, None) == 0                                     # nothing to do
+    lf = L.rkl_forward_logprob_entropy_shard
+    assert lf(4, 100, 64, FAKE, FAKE, None, FAKE, FAKE, 1 << 30, None) == 1                  # y NULL
+    assert lf(4, 100, 64, FAKE, FAKE, FAKE, None, FAKE, 1 << 30, None) == 1                  # partial NULL
+    assert lf(4, 100, 96, FAKE, FAKE, FAKE, FAKE, FAKE, 1 << 30, None) == 2                  # H % 64
+    lc = L.rkl_combine_shards_logprob_entropy
+    assert lc(0, 4, FAKE, None, FAKE, FAKE, FAKE, None) == 1
+    assert lc(2, 4, FAKE, None, FAKE, None, FAKE, None) == 1                                 # entropy NULL
+    assert "entropy" in L.rkl_last_error().decode()
 
 
 def test_compaction_and_copies_reject():

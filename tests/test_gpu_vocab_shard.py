@@ -163,3 +163,39 @@ def test_logit_shards_against_oracle(tdev, student_logits):
         full = O.backward(O.Inputs.from_case(case), np.arange(case.T), gg)
         assert_grad_close(sum(host(d).astype(np.float64) for d, _ in grads), full["dh"], "dh (sum over shards)")
         assert_grad_close(np.concatenate([host(w) for _, w in grads]), full["dW"], "dW (shard rows)")
+
+
+def test_logprob_entropy_shards_against_oracle(tdev):
+    """Log-probability / entropy over G = 3 uneven shards (one of a single
+    column): each shard sees its own rows of W and the sampled tokens in its
+    own coordinates (-1 when the token is in another shard)."""
+    from oracle import logprob_entropy_oracle as E
+    torch, dev = tdev
+    case = synth.random_case(610, T=300, V=3001, Hs=128, Ht=64, p_mask=1.0, with_grad=True)
+    rng = np.random.default_rng(611)
+    y = rng.integers(0, 3001, case.T).astype(np.int32)
+    y[:5] = (0, 999, 1000, 1001, 3000)                # both sides of every shard edge
+    g_lp = case.grad
+    g_H = rng.uniform(-0.5, 0.5, case.T).astype(np.float32)
+    bounds = [(0, 1000), (1000, 1001), (1001, 3001)]
+    say("log-probability / entropy shards")
+    h, W = bf16(case.h_s, dev), bf16(case.W_s, dev)
+    y_loc = [torch.from_numpy(np.where((y >= a) & (y < b), y - a, -1).astype(np.int32)).to(dev) for a, b in bounds]
+    parts = [R.forward_logprob_entropy_shard(h, W[a:b], yl) for (a, b), yl in zip(bounds, y_loc)]
+    logp, ent, stats = R.combine_shards_logprob_entropy(torch.stack(parts).contiguous())
+    grads = [R.backward_logprob_entropy(h, W[a:b], yl, stats, grad_logp=f32(g_lp, dev), grad_entropy=f32(g_H, dev))
+             for (a, b), yl in zip(bounds, y_loc)]
+    logp1, ent1, _ = R.forward_logprob_entropy(h, W, torch.from_numpy(y).to(dev))
+    torch.cuda.synchronize()
+
+    wh, wW = O.widen_bf16(case.h_s), O.widen_bf16(case.W_s)
+    lp, H, lse, lpmax = S.lpe_merge([S.lpe_shard_partials(wh, wW, y, a, b) for a, b in bounds])
+    assert_loss_close(host(logp), lp, "logp")
+    assert_loss_close(host(ent), H, "entropy")
+    assert_loss_close(host(stats)[:, 0], lse, "lse")
+    assert_loss_close(host(stats)[:, 3], lpmax, "log p_max")
+    assert_loss_close(host(logp), host(logp1).astype(np.float64), "logp sharded vs single device")
+    assert_loss_close(host(ent), host(ent1).astype(np.float64), "entropy sharded vs single device")
+    full = E.backward(wh, wW, y, g_lp.astype(np.float64), g_H.astype(np.float64))
+    assert_grad_close(sum(host(d).astype(np.float64) for d, _ in grads), full["dh"], "dh (sum over shards)")
+    assert_grad_close(np.concatenate([host(w) for _, w in grads]), full["dW"], "dW (shard rows)")
