@@ -74,6 +74,7 @@ struct DhParams {
   float* dh;
   int accumulate;
   int ntm, ntn;
+  int panel;               // column tiles per panel of the workgroup order
 };
 
 // Tile sizes the host needs for grids and workspace.

@@ -914,8 +914,12 @@ __global__ __launch_bounds__(64 * NW, 1) void dh_gemm(DhParams p) {
   using TB = MN<HBN, NW, HKT>;
   __shared__ __attribute__((aligned(1024))) char lds[HNST * (TA::kBytes + TB::kBytes)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / HGN, wn = w % HGN;
+  // workgroup order: panels of p.panel column tiles, all row tiles of a
+  // panel consecutive (each XCD takes a contiguous run of them)
   const int logical = xcd_logical(blockIdx.x, p.ntm * p.ntn);
-  const int tm = logical / p.ntn, tn = logical - tm * p.ntn;
+  const int per = p.panel * p.ntm, panel = logical / per, r = logical - panel * per;
+  const int width = min(p.panel, p.ntn - panel * p.panel);
+  const int tm = r / width, tn = panel * p.panel + (r - (r / width) * width);
   const int m0 = tm * HBM, n0 = tn * HBN;
   constexpr int FM = HBM / HGM / 32, FN = HBN / HGN / 32;
   f32x16 acc[FM][FN], tot[FM][FN];
