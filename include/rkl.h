@@ -104,9 +104,9 @@ int rkl_scatter_rows(const void* src, int64_t N, int64_t row_bytes, const int32_
  * teacher width Ht (0 = teacher given as logits).  The log-probability /
  * entropy calls pass their H as Hs and 0 as Ht; the per-row-teacher calls
  * need rkl_workspace_bytes_teachers instead.  Returns 0 on bad sizes.
- * Only the backward's need depends on N beyond the row count itself: the
- * fp16 dz of one vocabulary chunk (whole 65536-column segments within
- * 2 GiB) dominates it.
+ * The backward's part dominates: the fp16 dz of one vocabulary chunk
+ * (whole 65536-column segments, at most 2 GiB unless one segment alone is
+ * larger).
  */
 size_t rkl_workspace_bytes(int64_t N, int64_t V, int64_t Hs, int64_t Ht);
 
