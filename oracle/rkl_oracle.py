@@ -183,10 +183,13 @@ def backward(inp: Inputs, rows: np.ndarray, g: Optional[np.ndarray] = None,
     Returns dict with ``dh`` [len(rows), Hs] = dz W_s and ``dW`` [V, Hs] =
     sum_i dz_i^T h_s,i when the student is given as hidden states, and ``dz``
     [len(rows), V] when asked for (or when the student is given as logits).
+    The per-row statistics the backward rebuilt its log-softmaxes from are
+    returned too: ``L``, ``lse_s``, ``lse_t`` (the same values ``forward``
+    gives, from the same projection).
     """
     rows = np.asarray(rows, dtype=np.int64)
     hidden = inp.h_s is not None
-    out = {}
+    out = {"L": np.zeros(rows.shape[0]), "lse_s": np.zeros(rows.shape[0]), "lse_t": np.zeros(rows.shape[0])}
     if hidden:
         out["dh"] = np.zeros((rows.shape[0], inp.h_s.shape[1]))
         out["dW"] = np.zeros(inp.W_s.shape)
@@ -197,6 +200,7 @@ def backward(inp: Inputs, rows: np.ndarray, g: Optional[np.ndarray] = None,
         rr = rows[r0:r0 + row_chunk]
         zs, zt = inp.zs(rr), inp.zt(rr)
         ls, lt, L = row_stats(zs, zt)
+        out["L"][r0:r0 + len(rr)], out["lse_s"][r0:r0 + len(rr)], out["lse_t"][r0:r0 + len(rr)] = L, ls, lt
         gg = None if g is None else np.asarray(g, dtype=np.float64)[r0:r0 + len(rr)]
         dz = reverse_kl_dz(zs, zt, ls, lt, L, gg)
         if "dz" in out:

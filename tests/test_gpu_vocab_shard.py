@@ -1,5 +1,8 @@
 """GPU parity of the vocabulary-shard path (through the C ABI) against the
-fp64 oracle (oracle/vocab_shard_oracle.py).
+plain unsharded fp64 definitions (oracle/rkl_oracle.py,
+oracle/logprob_entropy_oracle.py): each shard's log-sum-exps over its own
+columns, the merged loss and statistics over the whole vocabulary, the
+summed dh and the shards' dW rows.
 
 Every shard of a vocabulary runs on this one GPU in turn, as the ranks of a
 vocabulary-parallel group would run theirs; the shards' partials are stacked
@@ -52,18 +55,21 @@ def test_shards_against_oracle(tdev, bounds):
     hs, ht, Ws, Wt = bf16(case.h_s, dev), bf16(case.h_t, dev), bf16(case.W_s, dev), bf16(case.W_t, dev)
     g = f32(case.grad, dev)
     partials, loss, stats, dh, dW = _run_shards(torch, hs, Ws, ht, Wt, bounds, g)
-    w = {k: O.widen_bf16(getattr(case, k)) for k in ("h_s", "W_s", "h_t", "W_t")}
+    inp = O.Inputs.from_case(case)
+    rows = np.arange(case.T)
     for (a, b), P in zip(bounds, partials):
-        want = S.shard_partials(w["h_s"], w["W_s"], w["h_t"], w["W_t"], a, b)
-        assert_loss_close(P[0] + np.log(P[1]), want[0] + np.log(want[1]), f"shard [{a},{b}) lse_s")
-        assert_loss_close(P[3] + np.log(P[4]), want[3] + np.log(want[4]), f"shard [{a},{b}) lse_t")
-    L, ls, lt, lpmax = S.merge([S.shard_partials(w["h_s"], w["W_s"], w["h_t"], w["W_t"], a, b) for a, b in bounds])
-    assert_loss_close(loss, L, "loss")
-    assert_loss_close(stats[:, 0], ls, "lse_s")
-    assert_loss_close(stats[:, 1], lt, "lse_t")
+        # each shard's m + log S is the log-sum-exp over its own columns
+        cols = np.arange(a, b)
+        assert_loss_close(P[0] + np.log(P[1]), O.logsumexp(inp.zs(rows, cols)), f"shard [{a},{b}) lse_s")
+        assert_loss_close(P[3] + np.log(P[4]), O.logsumexp(inp.zt(rows, cols)), f"shard [{a},{b}) lse_t")
+    # the merged statistics against the plain unsharded definitions
+    full = O.backward(inp, rows, case.grad.astype(np.float64))
+    lpmax = np.max(inp.zs(rows), axis=1) - full["lse_s"]   # log of the largest p_s
+    assert_loss_close(loss, full["L"], "loss")
+    assert_loss_close(stats[:, 0], full["lse_s"], "lse_s")
+    assert_loss_close(stats[:, 1], full["lse_t"], "lse_t")
     assert np.array_equal(stats[:, 2], loss)
     assert_loss_close(stats[:, 3], lpmax, "log p_max")
-    full = O.backward(O.Inputs.from_case(case), np.arange(case.T), case.grad.astype(np.float64))
     assert_grad_close(dh, full["dh"], "dh (sum over shards)")
     assert_grad_close(dW, full["dW"], "dW (shard rows)")
 
@@ -150,7 +156,9 @@ def test_logit_shards_against_oracle(tdev, student_logits):
     zs_ref = case.z_s.astype(np.float64) if student_logits else O.project(O.widen_bf16(case.h_s),
                                                                           O.widen_bf16(case.W_s))
     zt_ref = case.z_t.astype(np.float64)
-    L, ls, lt, lpmax = S.merge([S.partials_of_logits(zs_ref[:, a:b], zt_ref[:, a:b]) for a, b in bounds])
+    # the merged statistics against the plain unsharded definitions
+    L, (ls, lt) = O.reverse_kl(zs_ref, zt_ref), (O.logsumexp(zs_ref), O.logsumexp(zt_ref))
+    lpmax = np.max(zs_ref, axis=1) - ls
     assert_loss_close(host(loss), L, "loss")
     assert_loss_close(host(stats)[:, 0], ls, "lse_s")
     assert_loss_close(host(stats)[:, 1], lt, "lse_t")
@@ -189,7 +197,9 @@ def test_logprob_entropy_shards_against_oracle(tdev):
     torch.cuda.synchronize()
 
     wh, wW = O.widen_bf16(case.h_s), O.widen_bf16(case.W_s)
-    lp, H, lse, lpmax = S.lpe_merge([S.lpe_shard_partials(wh, wW, y, a, b) for a, b in bounds])
+    # the merged statistics against the plain unsharded definitions
+    lp, H, lse = E.forward(wh, wW, y)
+    lpmax = np.max(O.project(wh, wW), axis=1) - lse
     assert_loss_close(host(logp), lp, "logp")
     assert_loss_close(host(ent), H, "entropy")
     assert_loss_close(host(stats)[:, 0], lse, "lse")

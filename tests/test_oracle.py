@@ -243,8 +243,9 @@ def test_dh_dW_finite_differences():
 
     assert np.allclose(out["dh"], _central_diff(loss_h, inp.h_s.copy(), 1e-6), rtol=1e-6, atol=1e-9)
     assert np.allclose(out["dW"], _central_diff(loss_W, inp.W_s.copy(), 1e-6), rtol=1e-6, atol=1e-9)
-    # the teacher side gets no gradient: L moves with W_t but backward reports student grads only
-    assert set(out) == {"dh", "dW"}
+    # the teacher side gets no gradient: L moves with W_t but backward reports
+    # student grads only (beside the row statistics it rebuilt)
+    assert set(out) == {"dh", "dW", "L", "lse_s", "lse_t"}
 
 
 def test_forward_matches_definition_and_chunking():
@@ -261,6 +262,10 @@ def test_forward_matches_definition_and_chunking():
     b1 = O.backward(inp, rows, row_chunk=2)
     b2 = O.backward(inp, rows, row_chunk=100)
     assert np.allclose(b1["dW"], b2["dW"], rtol=0, atol=1e-15) and np.allclose(b1["dh"], b2["dh"], rtol=0, atol=1e-15)
+    # the backward's row statistics are the scipy values too
+    assert np.allclose(b1["L"], want, rtol=1e-12, atol=1e-15)
+    assert np.allclose(b1["lse_s"], scipy.special.logsumexp(zs, axis=1), atol=1e-13)
+    assert np.allclose(b1["lse_t"], scipy.special.logsumexp(zt, axis=1), atol=1e-13)
 
 
 def test_projection_orientation():
@@ -327,7 +332,7 @@ def test_student_logits_backward_is_dz():
     inp = O.Inputs.from_case(case)
     rows = np.arange(10)
     b = O.backward(inp, rows)
-    assert set(b) == {"dz"}
+    assert set(b) == {"dz", "L", "lse_s", "lse_t"}
     fd = _central_diff(lambda z: float(O.reverse_kl(z, inp.zt(rows)).sum()),
                        case.z_s.astype(np.float64), 1e-5)
     assert np.allclose(b["dz"], fd, rtol=1e-6, atol=1e-8)
