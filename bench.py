@@ -30,10 +30,19 @@ shard backward with the merged stats and the scatter of its dh term.  The
 exchanges between ranks (all-gather of the partials, all-reduce of dh) are
 not part of it.
 
-Prints one JSON line (rank 0):
-  value = masked tokens/s for forward + backward;
-  roofline = the fused forward kernel against the dense bf16 MFMA peak;
-  cpu_baseline = the fp64 oracle on a bounded row sample on the host cores.
+Prints one JSON line:
+  value      = masked tokens/s for forward + backward (wall clock over the
+               timed steps, synchronised on both sides);
+  per_kernel = every kernel of the path with its device time per step and
+               per launch, measured in the timed steps with hipEvents that
+               the library records around each launch on its stream, and
+               for the MFMA kernels their algorithmic FLOPs against the
+               dense bf16/fp16 MFMA peak;
+  roofline   = the kernel with the most device time per step, with the HBM
+               traffic per launch from the committed counter record while
+               the kernel sources are unchanged;
+  cpu_baseline = the fp64 oracle on a bounded row sample on the host cores
+               (reverse-KL and log-probability / entropy workloads).
 """
 from __future__ import annotations
 
@@ -50,6 +59,12 @@ METRIC = "masked tokens/sec fwd+bwd full-vocab reverse KL (H2048,V152k); MFMA % 
 # MI355X dense bf16/fp16 MFMA peak: 256 CUs x 4096 FLOP/clk x 2.4 GHz.
 PEAK_BF16 = 256 * 4096 * 2.4e9
 HBM_PEAK = 8.0e12
+DTYPE = "bf16 projections; fp16 dz/dh/dW GEMM operands (power-of-two scaled); fp32 accumulation"
+
+FWD_KERNELS = ("fwd_tiles", "fwd_combine", "fwd_rows_logits")
+BWD_KERNELS = ("grad_scale", "absmax_bf16", "transpose_h", "bwd_dz_tiles", "w_rescale", "dw_gemm", "dh_gemm",
+               "bwd_rows_logits")
+MFMA_KERNELS = ("fwd_tiles", "bwd_dz_tiles", "dw_gemm", "dh_gemm")
 
 
 def parse():
@@ -77,6 +92,8 @@ def parse():
     return ap.parse_args()
 
 
+# ---------------------------------------------------------------- traffic record
+
 def kernel_source_hash() -> str:
     """Hash of the HIP sources with comments and blank space removed: a
     recorded traffic measurement is only reused while the code it was taken
@@ -95,13 +112,14 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd_tiles_headline_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "headline_kernels_hbm_traffic.txt")
 
 
-def recorded_traffic():
-    """HBM bytes per fwd_tiles launch from the committed counter summary
-    (FETCH_SIZE + WRITE_SIZE scaled by the copy-kernel factor), or None if the
-    kernels changed since it was taken."""
+def recorded_traffic() -> dict:
+    """{kernel: record} of HBM bytes per launch on the headline workload from
+    the committed counter summary (FETCH_SIZE + WRITE_SIZE scaled by the
+    copy-kernel factors), for the records taken on the current sources."""
+    out = {}
     try:
         with open(TRAFFIC_FILE) as f:
             for line in f:
@@ -109,10 +127,10 @@ def recorded_traffic():
                 if line.startswith("{"):
                     rec = json.loads(line)
                     if rec.get("kernel_source_hash") == kernel_source_hash():
-                        return rec
+                        out[rec["kernel"]] = rec
     except OSError:
         pass
-    return None
+    return out
 
 
 def profile_copy():
@@ -176,15 +194,75 @@ def report_c5():
     print(json.dumps(out), flush=True)
 
 
+# ---------------------------------------------------------------- CPU baseline
+
+def host_info() -> dict:
+    model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.lower().startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    try:
+        usable = len(os.sched_getaffinity(0))
+    except AttributeError:
+        usable = os.cpu_count()
+    return {"cpu_model": model, "host_logical_cpus": os.cpu_count(), "usable_cpus": usable}
+
+
+def blas_threads() -> int:
+    try:
+        from threadpoolctl import threadpool_info
+        return max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        return os.cpu_count() or 1
+
+
+def grow_sample(run, target_s: float, cap: int, step: int = 32):
+    """Grow the row sample until one run takes about target_s (the per-row
+    cost of a small probe overstates the steady cost)."""
+    n = step
+    t = run(n)
+    while t < target_s / 2 and n < cap:
+        n = int(min(cap, max(n + step, n * target_s / max(t, 1e-3))) // step * step)
+        t = run(n)
+    return n, t
+
+
+def single_core_small() -> dict:
+    """The fp64 oracle on one thread: forward + backward of the tiny logits
+    workload (T=64, V=1024) and of the small hidden-state workload (N=256,
+    Hs=Ht=256, V=8192), in masked tokens/s."""
+    import numpy as np
+    import synth
+    from oracle import rkl_oracle as O
+    from threadpoolctl import threadpool_limits
+    out = {}
+    with threadpool_limits(limits=1):
+        for name in ("c1", "c2"):
+            case = synth.config(name)
+            inp = O.Inputs.from_case(case)
+            rows = O.compact_rows(case.mask)
+            best = float("inf")
+            for _ in range(3):
+                t0 = time.perf_counter()
+                O.forward(inp, rows)
+                O.backward(inp, rows)
+                best = min(best, time.perf_counter() - t0)
+            out[name] = {"masked_tokens": int(rows.shape[0]), "seconds": round(best, 4),
+                         "tokens_per_s": round(rows.shape[0] / best, 1)}
+    out["c1"]["workload"] = "logits both sides, T=64, V=1024"
+    out["c2"]["workload"] = "hidden states, B=2 S=129 (T=256), Hs=Ht=256, V=8192"
+    return out
+
+
 def cpu_baseline(case, target_s: float):
     """Time the fp64 oracle (forward + backward) on a bounded row sample."""
     import numpy as np
     from oracle import rkl_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
 
     def run(nrows):
         inp = O.Inputs(h_s=case.h_s[:nrows], W_s=case.W_s, h_t=case.h_t[:nrows], W_t=case.W_t)
@@ -194,31 +272,21 @@ def cpu_baseline(case, target_s: float):
         O.backward(inp, rows)
         return time.perf_counter() - t0
 
-    # grow the row sample until it takes about target_s (the per-row cost of
-    # a small probe overstates the steady cost)
-    cap = min(4096, case.T)
-    n = 32
-    t = run(n)
-    while t < target_s / 2 and n < cap:
-        n = int(min(cap, max(n + 32, n * target_s / max(t, 1e-3))) // 32 * 32)
-        t = run(n)
-    return {"value": n / t, "unit": "masked tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"fp64 numpy oracle, forward+backward (L, dh, dW) over the first {n} of the {case.T} "
-                      f"positions of this workload, full V={case.V}; {t:.1f} s wall; bf16->fp64 widening "
-                      f"of the weights done once outside the timed region"}
+    n, t = grow_sample(run, target_s, min(4096, case.T))
+    out = {"value": n / t, "unit": "masked tokens/s", "cores": int(blas_threads()), "kind": "oracle",
+           "sample": f"fp64 numpy oracle, forward+backward (L, dh, dW) over the first {n} of the {case.T} "
+                     f"positions of this workload, full V={case.V}; {t:.1f} s wall; bf16->fp64 widening "
+                     f"of the weights done once outside the timed region"}
+    out.update(host_info())
+    out["single_core"] = single_core_small()
+    return out
 
 
 def cpu_baseline_lpe(case, y, target_s: float):
     """Time the fp64 log-probability / entropy oracle (forward + backward) on a
     bounded row sample."""
-    import numpy as np
     from oracle import logprob_entropy_oracle as E
     from oracle import rkl_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        cores = os.cpu_count() or 1
     W = O.widen_bf16(case.W_s)
 
     def run(nrows):
@@ -228,23 +296,207 @@ def cpu_baseline_lpe(case, y, target_s: float):
         E.backward(h, W, y[:nrows])
         return time.perf_counter() - t0
 
-    cap = min(4096, case.T)
-    n = 32
-    t = run(n)
-    while t < target_s / 2 and n < cap:
-        n = int(min(cap, max(n + 32, n * target_s / max(t, 1e-3))) // 32 * 32)
-        t = run(n)
-    return {"value": n / t, "unit": "masked tokens/s", "cores": int(cores), "kind": "oracle",
-            "sample": f"fp64 numpy oracle, log-probability + entropy forward+backward (logp, H, dh, dW) over the "
-                      f"first {n} of the {case.T} positions of this workload, full V={case.V}; {t:.1f} s wall; "
-                      f"bf16->fp64 widening of the weights done once outside the timed region"}
+    n, t = grow_sample(run, target_s, min(4096, case.T))
+    out = {"value": n / t, "unit": "masked tokens/s", "cores": int(blas_threads()), "kind": "oracle",
+           "sample": f"fp64 numpy oracle, log-probability + entropy forward+backward (logp, H, dh, dW) over the "
+                     f"first {n} of the {case.T} positions of this workload, full V={case.V}; {t:.1f} s wall; "
+                     f"bf16->fp64 widening of the weights done once outside the timed region"}
+    out.update(host_info())
+    return out
+
+
+# ---------------------------------------------------------------- timing harness
+
+def run_timed(step, args):
+    """W untimed warm-up steps, then exactly K timed steps bracketed by
+    device synchronisation, with the library's per-kernel event timing on.
+    Returns (N, wall seconds, {kernel: (total ms, launches)})."""
+    import numpy as np
+    import torch
+    import lm_head_reverse_amd as R
+    print("[bench] warmup", file=sys.stderr, flush=True)
+    for _ in range(args.warmup):
+        N, out = step()
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(out.cpu().numpy())), "non-finite output"
+    print("[bench] timing", file=sys.stderr, flush=True)
+    R.kernel_timing(True)
+    R.kernel_times()   # forget the warm-up's records
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        N, _ = step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    times = R.kernel_times()
+    R.kernel_timing(False)
+    return N, wall, times
+
+
+def kernel_report(times, steps, work):
+    """Per-kernel entries and the dominant kernel.  work: {kernel: (FLOPs
+    per step, algorithmic bytes per step)} for the MFMA kernels."""
+    per = []
+    for k, (ms, n) in sorted(times.items(), key=lambda kv: -kv[1][0]):
+        e = {"kernel": k, "launches_per_step": round(n / steps, 3), "ms_per_step": round(ms / steps, 4),
+             "us_per_launch": round(ms * 1e3 / n, 1)}
+        if k in work:
+            flop, nbytes = work[k]
+            launches = n / steps
+            sec = ms * 1e-3 / n
+            e["tflop_per_launch"] = round(flop / launches / 1e12, 4)
+            e["algorithmic_gb_per_launch"] = round(nbytes / launches / 1e9, 4)
+            e["tflops"] = round(flop / launches / sec / 1e12, 2)
+            e["frac"] = round(flop / launches / sec / PEAK_BF16, 4)
+        per.append(e)
+    mfma = [e for e in per if e["kernel"] in work]
+    dom = max(mfma, key=lambda e: e["ms_per_step"]) if mfma else None
+    return per, dom
+
+
+def group_ms(times, steps, names):
+    return sum(ms for k, (ms, _) in times.items() if k in names) / steps
+
+
+def emit(args, metric, N, wall, times, work, flop_fwd, flop_step, config, extra=None, traffic=None):
+    """The JSON line common to every workload."""
+    per, dom = kernel_report(times, args.steps, work)
+    ms_step = wall * 1e3 / args.steps
+    fwd_ms = group_ms(times, args.steps, FWD_KERNELS)
+    bwd_ms = group_ms(times, args.steps, BWD_KERNELS)
+    out = {
+        "metric": metric,
+        "value": round(N * args.steps / wall, 1),
+        "unit": "masked tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": DTYPE,
+        "data": "synthetic",
+        "config": config,
+        "mfma_peak_frac_fwd_bwd": round(flop_step / (ms_step * 1e-3) / PEAK_BF16, 4),
+        "fwd_tokens_per_s": round(N / (fwd_ms * 1e-3), 1),
+        "fwd_kernel_ms": round(fwd_ms, 4),
+        "bwd_kernel_ms": round(bwd_ms, 4),
+        "mfma_peak_frac_fwd": round(flop_fwd / (fwd_ms * 1e-3) / PEAK_BF16, 4),
+        "mfma_peak_frac_bwd": round((flop_step - flop_fwd) / (bwd_ms * 1e-3) / PEAK_BF16, 4),
+        "per_kernel": per,
+    }
+    if dom is not None:
+        rec = (traffic or {}).get(dom["kernel"])
+        out["roofline"] = {
+            "kernel": dom["kernel"] + " (the kernel with the most device time per step; algorithmic FLOPs per "
+                                      "launch over the mean event-timed launch in the timed steps)",
+            "bound": "mfma",
+            "achieved": dom["tflops"],
+            "peak": round(PEAK_BF16 / 1e12, 1),
+            "unit": "TFLOP/s",
+            "frac": dom["frac"],
+            "traffic": None if rec is None else rec["hbm_bytes_per_launch"],
+        }
+        if rec is not None:
+            out["roofline"]["traffic_note"] = ("FETCH_SIZE (L2 misses served by the last-level cache or HBM) + "
+                                               "WRITE_SIZE per launch, copy-calibrated, from " +
+                                               os.path.relpath(TRAFFIC_FILE, ROOT))
+    if extra:
+        out.update(extra)
+    return out
+
+
+def bf16_dev(bits, dev):
+    import numpy as np
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
+
+
+# ---------------------------------------------------------------- workloads
+
+def rkl_work(N, V, Hs, Ht, logits=False, K=1):
+    """Algorithmic FLOPs and bytes per step of the MFMA kernels of one
+    reverse-KL step (Ht = 0 and logits: the teacher as fp32 logits; K
+    teacher weights read)."""
+    t_flop = 0 if logits else 2.0 * N * V * Ht
+    t_read = 4.0 * N * V if logits else 2.0 * K * V * Ht + 2.0 * N * Ht
+    proj = 2.0 * N * V * Hs + t_flop
+    read = 2.0 * V * Hs + 2.0 * N * Hs + t_read
+    return {
+        "fwd_tiles": (proj, read),
+        "bwd_dz_tiles": (proj, read + 2.0 * N * V + 2.0 * V * Hs),   # + fp16 dz, fp16 copy of W_s
+        "dw_gemm": (2.0 * N * V * Hs, 2.0 * N * V + 2.0 * N * Hs + 4.0 * V * Hs),
+        "dh_gemm": (2.0 * N * V * Hs, 2.0 * N * V + 2.0 * V * Hs + 4.0 * N * Hs),
+    }
+
+
+def bench_reverse_kl(args):
+    import numpy as np
+    import torch
+    import lm_head_reverse_amd as R
+    import synth
+
+    R.lib()
+    dev = torch.device("cuda:0")
+    print("[bench] generating inputs", file=sys.stderr, flush=True)
+    case = synth.config("headline")
+    T, V, Hs, Ht = case.T, case.V, case.Hs, case.Ht
+    h_s_all, h_t_all = bf16_dev(case.h_s, dev), bf16_dev(case.h_t, dev)
+    W_s, W_t = bf16_dev(case.W_s, dev), bf16_dev(case.W_t, dev)
+    logits = args.payload == "logits"
+    if logits:
+        # teacher logits payload: z_t = h_t W_t^T formed once in fp32 (input
+        # preparation, outside the timed region); the library streams it
+        z_t_all = h_t_all.float() @ W_t.float().t()
+        del h_t_all, W_t
+    mask = torch.from_numpy(case.mask).to(dev)
+    N_expected = int(case.mask.sum())
+    grad_pos = torch.full((T,), 1.0 / N_expected, dtype=torch.float32, device=dev)   # token-mean upstream
+    dW = torch.empty((V, Hs), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        idx, N = R.compact_rows(mask)
+        h_s = R.gather_rows(h_s_all, idx)
+        t_in = R.gather_rows(z_t_all if logits else h_t_all, idx)
+        g = R.gather_rows(grad_pos, idx)
+        if logits:
+            loss, stats = R.forward_logits(t_in, h_s=h_s, W_s=W_s)
+        else:
+            loss, stats = R.forward_hidden(h_s, W_s, t_in, W_t)
+        loss_pos = R.scatter_rows(loss, idx, T)
+        if logits:
+            dh, _ = R.backward_logits(t_in, stats, h_s=h_s, W_s=W_s, grad_loss=g, dW=dW)
+        else:
+            dh, _ = R.backward_hidden(h_s, W_s, t_in, W_t, stats, grad_loss=g, dW=dW)
+        R.scatter_rows(dh, idx, T)
+        return N, loss_pos
+
+    N, wall, times = run_timed(step, args)
+    assert N == N_expected
+    Ht_eff = 0 if logits else Ht
+    work = rkl_work(N, V, Hs, Ht_eff, logits=logits)
+    flop_fwd = 2.0 * N * V * (Hs + Ht_eff)
+    flop_step = 4.0 * N * V * (Hs + Ht_eff) + 4.0 * N * V * Hs
+    config = {"workload": ("Qwen3-1.7B-shaped fp32 teacher logits [N, V], " if logits else
+                           "Qwen3-1.7B-shaped hidden-state teacher, ") +
+                          "B=4 S=1025 (T=N=4096 trainable), Hs=Ht=2048, V=151936",
+              "B": case.B, "S": case.S, "N": int(N), "Hs": Hs, "Ht": Ht_eff, "V": V,
+              "payload": "logits" if logits else "hidden_states", "parallelism": "single GPU"}
+    if os.environ.get("RKL_VOCAB_CHUNK"):
+        config["backward_vocab_chunk"] = int(os.environ["RKL_VOCAB_CHUNK"])
+    out = emit(args, METRIC, N, wall, times, work, flop_fwd, flop_step, config,
+               traffic=None if logits or os.environ.get("RKL_VOCAB_CHUNK") else recorded_traffic())
+    if not args.no_cpu_baseline and not logits:
+        print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
 
 
 def bench_logprob_entropy(args):
     """The compact actor log-probability / entropy step on the headline tensors."""
-    import numpy as np
     import torch
-
     import lm_head_reverse_amd as R
     import synth
 
@@ -254,8 +506,7 @@ def bench_logprob_entropy(args):
     case = synth.config("headline")
     T, V, H = case.T, case.V, case.Hs
     y_np = synth.sampled_tokens(3, T, V)
-    h_all = torch.from_numpy(case.h_s.view(np.int16)).to(dev).view(torch.bfloat16)
-    W = torch.from_numpy(case.W_s.view(np.int16)).to(dev).view(torch.bfloat16)
+    h_all, W = bf16_dev(case.h_s, dev), bf16_dev(case.W_s, dev)
     y_all = torch.from_numpy(y_np).to(dev)
     mask = torch.from_numpy(case.mask).to(dev)
     N_expected = int(case.mask.sum())
@@ -271,82 +522,20 @@ def bench_logprob_entropy(args):
         y = R.gather_rows(y_all, idx)
         gl, gh = R.gather_rows(g_lp_all, idx), R.gather_rows(g_h_all, idx)
         logp, ent, stats = R.forward_logprob_entropy(h, W, y)
-        lp_pos, ent_pos = R.scatter_rows(logp, idx, T), R.scatter_rows(ent, idx, T)
+        lp_pos = R.scatter_rows(logp, idx, T)
+        R.scatter_rows(ent, idx, T)
         dh, _ = R.backward_logprob_entropy(h, W, y, stats, grad_logp=gl, grad_entropy=gh, dW=dW)
-        return N, lp_pos, ent_pos, R.scatter_rows(dh, idx, T)
+        R.scatter_rows(dh, idx, T)
+        return N, lp_pos
 
-    print("[bench] warmup", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        N, lp_pos, ent_pos, _ = step()
-    torch.cuda.synchronize()
+    N, wall, times = run_timed(step, args)
     assert N == N_expected
-    assert np.all(np.isfinite(lp_pos.cpu().numpy())) and np.all(np.isfinite(ent_pos.cpu().numpy()))
-
-    print("[bench] timing", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        N, _, _, _ = step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    tok_s = N * args.steps / wall
-
-    idx, _ = R.compact_rows(mask)
-    h, y = R.gather_rows(h_all, idx), R.gather_rows(y_all, idx)
-    gl, gh = R.gather_rows(g_lp_all, idx), R.gather_rows(g_h_all, idx)
-    _, _, stats = R.forward_logprob_entropy(h, W, y)
-    stream = torch.cuda.current_stream(dev)
-    reps = max(args.steps, 5)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    torch.cuda.synchronize()
-    ev[0].record(stream)
-    for _ in range(reps):
-        R.forward_logprob_entropy(h, W, y)
-    ev[1].record(stream)
-    for _ in range(reps):
-        R.backward_logprob_entropy(h, W, y, stats, grad_logp=gl, grad_entropy=gh, dW=dW)
-    ev[2].record(stream)
-    torch.cuda.synchronize()
-    fwd_ms = ev[0].elapsed_time(ev[1]) / reps
-    bwd_ms = ev[1].elapsed_time(ev[2]) / reps
-
-    flop_fwd = 2.0 * N * V * H
-    flop_step = 8.0 * N * V * H   # forward + recompute + dh + dW
-    achieved_fwd = flop_fwd / (fwd_ms * 1e-3)
-    out = {
-        "metric": "masked tokens/sec fwd+bwd log-prob + entropy (H2048,V152k); MFMA % peak",
-        "value": round(tok_s, 1),
-        "unit": "masked tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "Qwen3-1.7B-shaped actor log-probability + entropy, B=4 S=1025 (T=N=4096 "
-                               "trainable), H=2048, V=151936, uniform sampled tokens",
-                   "B": case.B, "S": case.S, "N": int(N), "H": H, "V": V, "parallelism": "single GPU"},
-        "mfma_peak_frac_fwd_bwd": round(flop_step / (ms_step * 1e-3) / PEAK_BF16, 4),
-        "fwd_tokens_per_s": round(N / (fwd_ms * 1e-3), 1),
-        "fwd_ms": round(fwd_ms, 4),
-        "bwd_ms": round(bwd_ms, 4),
-        "mfma_peak_frac_fwd": round(achieved_fwd / PEAK_BF16, 4),
-        "mfma_peak_frac_bwd": round((flop_step - flop_fwd) / (bwd_ms * 1e-3) / PEAK_BF16, 4),
-        "roofline": {
-            "kernel": "fwd_tiles<2> (fused forward: one projection + online log-sum-exp / entropy / sampled-logit "
-                      "epilogue; event time of the forward call, which adds the per-row split combine)",
-            "bound": "mfma",
-            "achieved": round(achieved_fwd / 1e12, 2),
-            "peak": round(PEAK_BF16 / 1e12, 1),
-            "unit": "TFLOP/s",
-            "frac": round(achieved_fwd / PEAK_BF16, 4),
-            "traffic": None,
-        },
-    }
+    work = rkl_work(N, V, H, 0)
+    config = {"workload": "Qwen3-1.7B-shaped actor log-probability + entropy, B=4 S=1025 (T=N=4096 "
+                          "trainable), H=2048, V=151936, uniform sampled tokens",
+              "B": case.B, "S": case.S, "N": int(N), "H": H, "V": V, "parallelism": "single GPU"}
+    out = emit(args, "masked tokens/sec fwd+bwd log-prob + entropy (H2048,V152k); MFMA % peak", N, wall, times,
+               work, 2.0 * N * V * H, 8.0 * N * V * H, config)
     if not args.no_cpu_baseline:
         print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline_lpe(case, y_np, args.cpu_seconds)
@@ -355,9 +544,7 @@ def bench_logprob_entropy(args):
 
 def bench_teachers(args):
     """Reverse KL on the headline tensors with K teachers chosen per row."""
-    import numpy as np
     import torch
-
     import lm_head_reverse_amd as R
     import synth
 
@@ -367,12 +554,8 @@ def bench_teachers(args):
     print(f"[bench] generating inputs ({K} teachers)", file=sys.stderr, flush=True)
     case = synth.config("headline")
     T, V, Hs, Ht = case.T, case.V, case.Hs, case.Ht
-
-    def bf(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
-
-    h_s_all, h_t_all, W_s = bf(case.h_s), bf(case.h_t), bf(case.W_s)
-    W_t = bf(synth.teacher_weights(3, K, V, Ht))
+    h_s_all, h_t_all, W_s = bf16_dev(case.h_s, dev), bf16_dev(case.h_t, dev), bf16_dev(case.W_s, dev)
+    W_t = bf16_dev(synth.teacher_weights(3, K, V, Ht), dev)
     tid_all = torch.from_numpy(synth.teacher_ids(3, T, K, args.teacher_order)).to(dev)
     mask = torch.from_numpy(case.mask).to(dev)
     N_expected = int(case.mask.sum())
@@ -387,86 +570,24 @@ def bench_teachers(args):
         loss, stats = R.forward_hidden_teachers(h_s, W_s, h_t, W_t, tk)
         loss_pos = R.scatter_rows(loss, idx, T)
         dh, _ = R.backward_hidden_teachers(h_s, W_s, h_t, W_t, tk, stats, grad_loss=g, dW=dW)
-        return N, loss_pos, R.scatter_rows(dh, idx, T)
+        R.scatter_rows(dh, idx, T)
+        return N, loss_pos
 
-    print("[bench] warmup", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        N, loss_pos, _ = step()
-    torch.cuda.synchronize()
-    assert N == N_expected and np.all(np.isfinite(loss_pos.cpu().numpy()))
-    print("[bench] timing", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        N, _, _ = step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-
-    idx, _ = R.compact_rows(mask)
-    h_s, h_t = R.gather_rows(h_s_all, idx), R.gather_rows(h_t_all, idx)
-    tk = R.gather_rows(tid_all, idx)
-    g = torch.full((N,), 1.0 / N, dtype=torch.float32, device=dev)
-    _, stats = R.forward_hidden_teachers(h_s, W_s, h_t, W_t, tk)
-    stream = torch.cuda.current_stream(dev)
-    reps = max(args.steps, 5)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    torch.cuda.synchronize()
-    ev[0].record(stream)
-    for _ in range(reps):
-        R.forward_hidden_teachers(h_s, W_s, h_t, W_t, tk)
-    ev[1].record(stream)
-    for _ in range(reps):
-        R.backward_hidden_teachers(h_s, W_s, h_t, W_t, tk, stats, grad_loss=g, dW=dW)
-    ev[2].record(stream)
-    torch.cuda.synchronize()
-    fwd_ms = ev[0].elapsed_time(ev[1]) / reps
-    bwd_ms = ev[1].elapsed_time(ev[2]) / reps
-    flop_fwd = 2.0 * N * V * (Hs + Ht)
-    flop_step = 4.0 * N * V * (Hs + Ht) + 4.0 * N * V * Hs
-    achieved_fwd = flop_fwd / (fwd_ms * 1e-3)
-    out = {
-        "metric": "masked tokens/sec fwd+bwd full-vocab reverse KL, teacher per row (H2048,V152k); MFMA % peak",
-        "value": round(N * args.steps / wall, 1),
-        "unit": "masked tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": f"Qwen3-1.7B-shaped hidden-state teachers, {K} teachers chosen per row "
-                               f"({args.teacher_order}), B=4 S=1025 (T=N=4096 trainable), Hs=Ht=2048, V=151936",
-                   "B": case.B, "S": case.S, "N": int(N), "Hs": Hs, "Ht": Ht, "V": V, "K": K,
-                   "teacher_order": args.teacher_order, "parallelism": "single GPU"},
-        "mfma_peak_frac_fwd_bwd": round(flop_step / (ms_step * 1e-3) / PEAK_BF16, 4),
-        "fwd_ms": round(fwd_ms, 4),
-        "bwd_ms": round(bwd_ms, 4),
-        "mfma_peak_frac_fwd": round(achieved_fwd / PEAK_BF16, 4),
-        "mfma_peak_frac_bwd": round((flop_step - flop_fwd) / (bwd_ms * 1e-3) / PEAK_BF16, 4),
-        "roofline": {
-            "kernel": "fwd_tiles<3> (fused forward: student + per-row teacher projections + online LSE/KL "
-                      "epilogue; event time of the forward call, which adds the per-row split combine; "
-                      "algorithmic FLOPs only)",
-            "bound": "mfma",
-            "achieved": round(achieved_fwd / 1e12, 2),
-            "peak": round(PEAK_BF16 / 1e12, 1),
-            "unit": "TFLOP/s",
-            "frac": round(achieved_fwd / PEAK_BF16, 4),
-            "traffic": None,
-        },
-    }
+    N, wall, times = run_timed(step, args)
+    assert N == N_expected
+    config = {"workload": f"Qwen3-1.7B-shaped hidden-state teachers, {K} teachers chosen per row "
+                          f"({args.teacher_order}), B=4 S=1025 (T=N=4096 trainable), Hs=Ht=2048, V=151936",
+              "B": case.B, "S": case.S, "N": int(N), "Hs": Hs, "Ht": Ht, "V": V, "K": K,
+              "teacher_order": args.teacher_order, "parallelism": "single GPU"}
+    out = emit(args, "masked tokens/sec fwd+bwd full-vocab reverse KL, teacher per row (H2048,V152k); MFMA % peak",
+               N, wall, times, rkl_work(N, V, Hs, Ht, K=K), 2.0 * N * V * (Hs + Ht),
+               4.0 * N * V * (Hs + Ht) + 4.0 * N * V * Hs, config)
     print(json.dumps(out), flush=True)
 
 
 def bench_vocab_shard(args):
     """One rank's share of a G-way vocabulary-parallel reverse-KL step."""
-    import numpy as np
     import torch
-
     import lm_head_reverse_amd as R
     import synth
 
@@ -484,11 +605,8 @@ def bench_vocab_shard(args):
         a = bounds[-1][1] if bounds else 0
         bounds.append((a, a + q + (1 if k < r else 0)))
     v0, v1 = bounds[0]   # this rank's vocabulary rows
-
-    def bf(bits):
-        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to(dev).view(torch.bfloat16)
-
-    h_s_all, h_t_all, W_s_full, W_t_full = bf(case.h_s), bf(case.h_t), bf(case.W_s), bf(case.W_t)
+    h_s_all, h_t_all = bf16_dev(case.h_s, dev), bf16_dev(case.h_t, dev)
+    W_s_full, W_t_full = bf16_dev(case.W_s, dev), bf16_dev(case.W_t, dev)
     mask = torch.from_numpy(case.mask).to(dev)
     N_expected = int(case.mask.sum())
     grad_pos = torch.full((T,), 1.0 / N_expected, dtype=torch.float32, device=dev)
@@ -509,77 +627,20 @@ def bench_vocab_shard(args):
         loss, stats = R.combine_shards(partials)
         loss_pos = R.scatter_rows(loss, idx, T)
         dh, _ = R.backward_hidden(h_s, W_s, h_t, W_t, stats, grad_loss=g, dW=dW)
-        return N, loss_pos, R.scatter_rows(dh, idx, T)
+        R.scatter_rows(dh, idx, T)
+        return N, loss_pos
 
-    print("[bench] warmup", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        N, loss_pos, _ = step()
-    torch.cuda.synchronize()
-    assert N == N_expected and np.all(np.isfinite(loss_pos.cpu().numpy()))
-    print("[bench] timing", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        N, _, _ = step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-
-    g = torch.full((N,), 1.0 / N, dtype=torch.float32, device=dev)
-    _, stats = R.combine_shards(partials)
-    stream = torch.cuda.current_stream(dev)
-    reps = max(args.steps, 5)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
-    torch.cuda.synchronize()
-    ev[0].record(stream)
-    for _ in range(reps):
-        R.forward_hidden_shard(h_s, W_s, h_t, W_t)
-    ev[1].record(stream)
-    for _ in range(reps):
-        R.backward_hidden(h_s, W_s, h_t, W_t, stats, grad_loss=g, dW=dW)
-    ev[2].record(stream)
-    torch.cuda.synchronize()
-    fwd_ms = ev[0].elapsed_time(ev[1]) / reps
-    bwd_ms = ev[1].elapsed_time(ev[2]) / reps
+    N, wall, times = run_timed(step, args)
+    assert N == N_expected
     Vs = v1 - v0
-    flop_fwd = 2.0 * N * Vs * (Hs + Ht)
-    flop_step = 4.0 * N * Vs * (Hs + Ht) + 4.0 * N * Vs * Hs
-    achieved_fwd = flop_fwd / (fwd_ms * 1e-3)
-    out = {
-        "metric": "masked tokens/sec fwd+bwd full-vocab reverse KL, one rank of a vocabulary-parallel group "
-                  "(H2048,V152k); MFMA % peak",
-        "value": round(N * args.steps / wall, 1),
-        "unit": "masked tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": f"Qwen3-1.7B-shaped hidden-state teacher, one rank's share of a {G}-way "
-                               f"vocabulary split ({Vs} of 151936 vocabulary rows), B=4 S=1025 (T=N=4096 "
-                               f"trainable), Hs=Ht=2048; inter-rank exchanges excluded",
-                   "B": case.B, "S": case.S, "N": int(N), "Hs": Hs, "Ht": Ht, "V": V, "shards": G,
-                   "V_shard": Vs, "parallelism": "single GPU (one rank's share)"},
-        "mfma_peak_frac_fwd_bwd": round(flop_step / (ms_step * 1e-3) / PEAK_BF16, 4),
-        "fwd_ms": round(fwd_ms, 4),
-        "bwd_ms": round(bwd_ms, 4),
-        "mfma_peak_frac_fwd": round(achieved_fwd / PEAK_BF16, 4),
-        "mfma_peak_frac_bwd": round((flop_step - flop_fwd) / (bwd_ms * 1e-3) / PEAK_BF16, 4),
-        "roofline": {
-            "kernel": "fwd_tiles<0> on the shard (fused forward: both projections + online LSE/KL epilogue; "
-                      "event time of the shard forward call, which adds the split merge; algorithmic FLOPs only)",
-            "bound": "mfma",
-            "achieved": round(achieved_fwd / 1e12, 2),
-            "peak": round(PEAK_BF16 / 1e12, 1),
-            "unit": "TFLOP/s",
-            "frac": round(achieved_fwd / PEAK_BF16, 4),
-            "traffic": None,
-        },
-    }
+    config = {"workload": f"Qwen3-1.7B-shaped hidden-state teacher, one rank's share of a {G}-way "
+                          f"vocabulary split ({Vs} of 151936 vocabulary rows), B=4 S=1025 (T=N=4096 "
+                          f"trainable), Hs=Ht=2048; inter-rank exchanges excluded",
+              "B": case.B, "S": case.S, "N": int(N), "Hs": Hs, "Ht": Ht, "V": V, "shards": G,
+              "V_shard": Vs, "parallelism": "single GPU (one rank's share)"}
+    out = emit(args, "masked tokens/sec fwd+bwd full-vocab reverse KL, one rank of a vocabulary-parallel group "
+                     "(H2048,V152k); MFMA % peak", N, wall, times, rkl_work(N, Vs, Hs, Ht),
+               2.0 * N * Vs * (Hs + Ht), 4.0 * N * Vs * (Hs + Ht) + 4.0 * N * Vs * Hs, config)
     print(json.dumps(out), flush=True)
 
 
@@ -593,153 +654,8 @@ def main():
         print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}); "
               f"the multi-GPU sharding is described but not built", file=sys.stderr)
         sys.exit(2)
-    if args.workload == "logprob_entropy":
-        return bench_logprob_entropy(args)
-    if args.workload == "teachers":
-        return bench_teachers(args)
-    if args.workload == "vocab_shard":
-        return bench_vocab_shard(args)
-
-    import numpy as np
-    import torch
-
-    import lm_head_reverse_amd as R
-    import synth
-
-    R.lib()
-    dev = torch.device("cuda:0")
-    print("[bench] generating inputs", file=sys.stderr, flush=True)
-    case = synth.config("headline")
-    T, V, Hs, Ht = case.T, case.V, case.Hs, case.Ht
-
-    def bf(bits):
-        return torch.from_numpy(bits.view(np.int16)).to(dev).view(torch.bfloat16)
-
-    h_s_all, h_t_all = bf(case.h_s), bf(case.h_t)
-    W_s, W_t = bf(case.W_s), bf(case.W_t)
-    logits = args.payload == "logits"
-    if logits:
-        # teacher logits payload: z_t = h_t W_t^T formed once in fp32 (input
-        # preparation, outside the timed region); the library streams it
-        z_t_all = h_t_all.float() @ W_t.float().t()
-        del h_t_all, W_t
-    mask = torch.from_numpy(case.mask).to(dev)
-    N_expected = int(case.mask.sum())
-    grad_pos = torch.full((T,), 1.0 / N_expected, dtype=torch.float32, device=dev)   # token-mean upstream
-    dW = torch.empty((V, Hs), dtype=torch.float32, device=dev)
-    torch.cuda.synchronize()
-
-    def fwd(h_s, t_in):
-        if logits:
-            return R.forward_logits(t_in, h_s=h_s, W_s=W_s)
-        return R.forward_hidden(h_s, W_s, t_in, W_t)
-
-    def bwd(h_s, t_in, stats, g):
-        if logits:
-            return R.backward_logits(t_in, stats, h_s=h_s, W_s=W_s, grad_loss=g, dW=dW)
-        return R.backward_hidden(h_s, W_s, t_in, W_t, stats, grad_loss=g, dW=dW)
-
-    def step():
-        idx, N = R.compact_rows(mask)
-        h_s = R.gather_rows(h_s_all, idx)
-        t_in = R.gather_rows(z_t_all if logits else h_t_all, idx)
-        g = R.gather_rows(grad_pos, idx)
-        loss, stats = fwd(h_s, t_in)
-        loss_pos = R.scatter_rows(loss, idx, T)
-        dh, _ = bwd(h_s, t_in, stats, g)
-        dh_pos = R.scatter_rows(dh, idx, T)
-        return N, loss_pos, dh_pos
-
-    print("[bench] warmup", file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        N, loss_pos, _ = step()
-    torch.cuda.synchronize()
-    assert N == N_expected
-    lp = loss_pos.cpu().numpy()
-    assert np.all(np.isfinite(lp)), "non-finite loss"
-
-    print("[bench] timing", file=sys.stderr, flush=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        N, _, _ = step()
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    ms_step = wall * 1e3 / args.steps
-    tok_s = N * args.steps / wall
-
-    # per-call device time with events on the stream the library launches on
-    idx, _ = R.compact_rows(mask)
-    h_s = R.gather_rows(h_s_all, idx)
-    t_in = R.gather_rows(z_t_all if logits else h_t_all, idx)
-    g = torch.full((N,), 1.0 / N, dtype=torch.float32, device=dev)
-    loss, stats = fwd(h_s, t_in)
-    stream = torch.cuda.current_stream(dev)
-    reps = max(args.steps, 5)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
-    torch.cuda.synchronize()
-    ev[0].record(stream)
-    for _ in range(reps):
-        fwd(h_s, t_in)
-    ev[1].record(stream)
-    for _ in range(reps):
-        bwd(h_s, t_in, stats, g)
-    ev[2].record(stream)
-    torch.cuda.synchronize()
-    fwd_ms = ev[0].elapsed_time(ev[1]) / reps
-    bwd_ms = ev[1].elapsed_time(ev[2]) / reps
-
-    if logits:
-        flop_fwd = 2.0 * N * V * Hs
-        flop_step = 8.0 * N * V * Hs
-    else:
-        flop_fwd = 2.0 * N * V * (Hs + Ht)
-        flop_step = 4.0 * N * V * (Hs + Ht) + 4.0 * N * V * Hs
-    achieved_fwd = flop_fwd / (fwd_ms * 1e-3)
-    out = {
-        "metric": METRIC,
-        "value": round(tok_s, 1),
-        "unit": "masked tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": ("Qwen3-1.7B-shaped fp32 teacher logits [N, V], " if logits else
-                                "Qwen3-1.7B-shaped hidden-state teacher, ") +
-                               "B=4 S=1025 (T=N=4096 trainable), Hs=Ht=2048, V=151936",
-                   "B": case.B, "S": case.S, "N": int(N), "Hs": Hs, "Ht": 0 if logits else Ht, "V": V,
-                   "payload": "logits" if logits else "hidden_states", "parallelism": "single GPU"},
-        "mfma_peak_frac_fwd_bwd": round(flop_step / (ms_step * 1e-3) / PEAK_BF16, 4),
-        "fwd_tokens_per_s": round(N / (fwd_ms * 1e-3), 1),
-        "fwd_ms": round(fwd_ms, 4),
-        "bwd_ms": round(bwd_ms, 4),
-        "mfma_peak_frac_fwd": round(achieved_fwd / PEAK_BF16, 4),
-        "mfma_peak_frac_bwd": round((flop_step - flop_fwd) / (bwd_ms * 1e-3) / PEAK_BF16, 4),
-        "roofline": {
-            "kernel": ("fwd_tiles<1> (fused forward: student projection + teacher-logit stream + online "
-                       "LSE/KL epilogue" if logits else
-                       "fwd_tiles (fused forward: both projections + online LSE/KL epilogue") +
-                      "; event time of the forward call, which adds the per-row split combine)",
-            "bound": "mfma",
-            "achieved": round(achieved_fwd / 1e12, 2),
-            "peak": round(PEAK_BF16 / 1e12, 1),
-            "unit": "TFLOP/s",
-            "frac": round(achieved_fwd / PEAK_BF16, 4),
-            "traffic": None,
-        },
-    }
-    rec = None if logits else recorded_traffic()
-    if rec is not None:
-        out["roofline"]["traffic"] = rec["hbm_bytes_per_launch"]
-    if not args.no_cpu_baseline and not logits:
-        print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
-    print(json.dumps(out), flush=True)
+    {"reverse_kl": bench_reverse_kl, "logprob_entropy": bench_logprob_entropy, "teachers": bench_teachers,
+     "vocab_shard": bench_vocab_shard}[args.workload](args)
 
 
 if __name__ == "__main__":

@@ -68,6 +68,25 @@ const char* rkl_last_error(void);
 const char* rkl_version(void);
 
 /*
+ * Per-kernel device time, for measurement (the pages define no such call;
+ * it exists so that a benchmark can price each kernel of the path against
+ * the chip's peak).  rkl_kernel_timing(1) turns timing on for the calling
+ * host thread: from then on every kernel that thread's calls launch is
+ * bracketed by two hipEvents recorded on the call's stream (a few
+ * microseconds of host work per launch; no device memory).
+ * rkl_kernel_timing(0) turns it off.  rkl_kernel_times waits for the
+ * recorded events, sums the elapsed time per kernel name and forgets them:
+ * entry k < min(*count, cap) gets names[k] (static storage), total_ms[k] and
+ * launches[k]; *count receives the number of distinct kernels (may exceed
+ * cap).  Host pointers.  Names: fwd_tiles, fwd_combine, bwd_dz_tiles,
+ * dw_gemm, dh_gemm, grad_scale, absmax_bf16, transpose_h, w_rescale,
+ * compact, gather, scatter, fill_zero, fwd_rows_logits, bwd_rows_logits,
+ * group_by_teacher, topk_terms, topk_dz_add.
+ */
+int rkl_kernel_timing(int enable);
+int rkl_kernel_times(int cap, const char** names, double* total_ms, int* launches, int* count);
+
+/*
  * Row compaction (slime page, summary: project only the loss-masked rows).
  *   mask       [T] uint8, nonzero = trainable position (the [B, S-1] layout).
  *   row_idx    [T] int32 capacity; receives the N selected positions in
@@ -82,7 +101,8 @@ int rkl_compact_rows(const uint8_t* mask, int64_t T, int32_t* row_idx, int32_t* 
                      int64_t* n_rows_host, rkl_stream_t stream);
 
 /*
- * Gather: dst[i, :] = src[row_idx[i], :] for i < N, a bit copy of row_bytes
+ * Gather (slime page, summary: the compacted rows are what gets projected):
+ * dst[i, :] = src[row_idx[i], :] for i < N, a bit copy of row_bytes
  * bytes per row.  row_bytes must be a positive multiple of 4; every row_idx
  * entry must lie in [0, T) (not checked on the device).  N = 0 is a no-op.
  */
@@ -99,7 +119,9 @@ int rkl_scatter_rows(const void* src, int64_t N, int64_t row_bytes, const int32_
                      void* dst, rkl_stream_t stream);
 
 /*
- * Device workspace (bytes) that rkl_forward_* and rkl_backward_* need for
+ * Device workspace (NeMo-RL page, implementation notes: chunked functions
+ * that recompute their log-softmaxes in the backward -- the per-chunk
+ * buffers live here) in bytes that rkl_forward_* and rkl_backward_* need for
  * N rows, vocabulary V, student width Hs (0 = student given as logits) and
  * teacher width Ht (0 = teacher given as logits).  The log-probability /
  * entropy calls pass their H as Hs and 0 as Ht; the per-row-teacher calls
@@ -297,6 +319,56 @@ int rkl_backward_logprob_entropy(int64_t N, int64_t V, int64_t H, const rkl_bf16
                                  const int32_t* y, const uint8_t* row_mask, const float* grad_logp,
                                  const float* grad_entropy, const float* stats, float* dh, float* dW,
                                  int accumulate_dW, void* workspace, size_t workspace_bytes, rkl_stream_t stream);
+
+/*
+ * Top-k estimator of the reverse KL (NeMo-RL page, summary: the full
+ * objective is the K = V limit of the top-k estimator -- once the support
+ * spans the whole vocabulary its score-function tail term vanishes).  Per
+ * row i, a support S_i of K vocabulary ids chosen without looking at the
+ * sampled token (e.g. the teacher's top K) and a token y_i sampled from the
+ * student; with f = log p_s - log p_t,
+ *     L_i = sum_{j in S_i} p_s(j) f(j)  +  [y_i not in S_i] f(y_i),
+ * an exact part on the support and a one-sample estimate of the rest, so
+ * that over y_i ~ p_s its expectation is the reverse KL (K = V: exactly the
+ * reverse KL; K = 0: the sampled token's log-probability gap).  Only the
+ * student is projected (hidden states h [N, H], weight W [V, H], bf16); the
+ * teacher arrives as log-probabilities on the support and at the token:
+ *   y              [N] int32 sampled tokens, in [0, V) (not checked on the
+ *                  device).
+ *   support        [N, K] int32 ids per row (distinct; ids outside [0, V)
+ *                  are skipped).  K in [0, V]; NULL when K = 0.
+ *   logpt_support  [N, K] fp32 teacher log-probabilities at those ids.
+ *   logpt_y        [N] fp32 teacher log-probability at y (read only for rows
+ *                  whose y is not in their support).
+ *   row_mask       as rkl_forward_hidden (rows with 0: loss and stats 0).
+ *   loss           [N] fp32 out: L_i.
+ *   stats          [N, 4] fp32 out: (lse, c, sp, bound) -- the student's
+ *                  log-sum-exp, c = sum_{j in S} p_j (f_j + 1) + [y not in S]
+ *                  sp, sp = [y not in S] (f_y + 1), and a bound on |dz| / |g|;
+ *                  all the backward needs besides the inputs.
+ * The student's logits on the support are K dot products per row; the cost
+ * beyond the fused log-sum-exp grows as N K H.
+ * Workspace: rkl_workspace_bytes(N, V, H, 0).  N = 0 launches nothing.
+ */
+int rkl_forward_topk(int64_t N, int64_t V, int64_t H, int64_t K, const rkl_bf16* h, const rkl_bf16* W,
+                     const int32_t* y, const int32_t* support, const float* logpt_support, const float* logpt_y,
+                     const uint8_t* row_mask, float* loss, float* stats, void* workspace, size_t workspace_bytes,
+                     rkl_stream_t stream);
+
+/*
+ * Backward of sum_i g_i L_i for rkl_forward_topk: the exact gradient of the
+ * support part and the score-function estimate of the tail's,
+ *     dz_i[j] = g_i (-p_j c_i + [j in S_i] p_j (f_j + 1) + [j = y_i] sp_i),
+ *     dh = dz W (overwritten),  dW = sum_i dz_i^T h_i (overwritten, or added
+ *     to when accumulate_dW != 0).
+ *   grad_loss [N] fp32 (NULL = all ones); stats from rkl_forward_topk on the
+ *   same inputs.  Other arguments, limits and the workspace as
+ *   rkl_backward_logprob_entropy.
+ */
+int rkl_backward_topk(int64_t N, int64_t V, int64_t H, int64_t K, const rkl_bf16* h, const rkl_bf16* W,
+                      const int32_t* y, const int32_t* support, const float* logpt_support, const uint8_t* row_mask,
+                      const float* grad_loss, const float* stats, float* dh, float* dW, int accumulate_dW,
+                      void* workspace, size_t workspace_bytes, rkl_stream_t stream);
 
 /*
  * Log-probability / entropy over one vocabulary shard (NeMo-RL page,

@@ -17,11 +17,11 @@ import os
 from typing import Optional
 
 __all__ = [
-    "RKLError", "lib", "LIB_PATH", "version", "workspace_bytes", "workspace_bytes_teachers", "compact_rows",
+    "RKLError", "lib", "LIB_PATH", "version", "kernel_timing", "kernel_times", "workspace_bytes", "workspace_bytes_teachers", "compact_rows",
     "gather_rows", "scatter_rows", "forward_hidden", "forward_logits", "backward_hidden", "backward_logits",
     "forward_hidden_teachers", "backward_hidden_teachers", "forward_logprob_entropy", "backward_logprob_entropy",
     "forward_hidden_shard", "forward_logits_shard", "combine_shards", "forward_logprob_entropy_shard",
-    "combine_shards_logprob_entropy", "ReverseKL",
+    "combine_shards_logprob_entropy", "forward_topk", "backward_topk", "ReverseKL",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "librkl.so")
@@ -50,6 +50,8 @@ def lib() -> ctypes.CDLL:
     sig = {
         "rkl_last_error": ([], ctypes.c_char_p),
         "rkl_version": ([], ctypes.c_char_p),
+        "rkl_kernel_timing": ([I32], I32),
+        "rkl_kernel_times": ([I32, P, P, P, P], I32),
         "rkl_workspace_bytes": ([I64, I64, I64, I64], SZ),
         "rkl_workspace_bytes_teachers": ([I64, I64, I64, I64], SZ),
         "rkl_compact_rows": ([P, I64, P, P, P, P], I32),
@@ -68,6 +70,8 @@ def lib() -> ctypes.CDLL:
         "rkl_backward_hidden_teachers": ([I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, I32, P, SZ, P],
                                          I32),
         "rkl_forward_logprob_entropy": ([I64, I64, I64, P, P, P, P, P, P, P, P, SZ, P], I32),
+        "rkl_forward_topk": ([I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+        "rkl_backward_topk": ([I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, I32, P, SZ, P], I32),
         "rkl_backward_logprob_entropy": ([I64, I64, I64, P, P, P, P, P, P, P, P, P, I32, P, SZ, P], I32),
     }
     for name, (args, res) in sig.items():
@@ -85,6 +89,23 @@ def _check(rc: int):
 
 def version() -> str:
     return lib().rkl_version().decode()
+
+
+def kernel_timing(enable: bool) -> None:
+    """Turn per-kernel event timing on or off for this host thread."""
+    _check(lib().rkl_kernel_timing(int(bool(enable))))
+
+
+def kernel_times() -> dict:
+    """{kernel name: (total ms, launches)} recorded since the last call (waits
+    for the recorded events)."""
+    cap = 64
+    names = (ctypes.c_char_p * cap)()
+    ms = (ctypes.c_double * cap)()
+    launches = (ctypes.c_int * cap)()
+    count = ctypes.c_int(0)
+    _check(lib().rkl_kernel_times(cap, names, ms, launches, ctypes.byref(count)))
+    return {names[k].decode(): (ms[k], launches[k]) for k in range(min(count.value, cap))}
 
 
 def workspace_bytes(N: int, V: int, Hs: int, Ht: int) -> int:
@@ -541,4 +562,63 @@ def backward_hidden_teachers(h_s, W_s, h_t, W_t, teacher, stats, grad_loss=None,
                                               _ptr(teacher), _ptr(row_mask), _ptr(grad_loss), _ptr(stats), _ptr(dh),
                                               _ptr(dW), int(bool(accumulate_dW)), _ptr(ws), ws.numel(),
                                               _stream(dev)))
+    return dh, dW
+
+
+def _topk_args(h, W, y, support, logpt_support, row_mask):
+    torch = _torch()
+    dev = h.device
+    N, H = h.shape
+    V = W.shape[0]
+    _need(h, "h", torch.bfloat16, dev)
+    _need(W, "W", torch.bfloat16, dev, (V, H))
+    _need(y, "y", torch.int32, dev, (N,))
+    if support is None:
+        K = 0
+    else:
+        K = support.shape[1]
+        _need(support, "support", torch.int32, dev, (N, K))
+        _need(logpt_support, "logpt_support", torch.float32, dev, (N, K))
+    if row_mask is not None:
+        _need(row_mask, "row_mask", torch.uint8, dev, (N,))
+    return dev, N, V, H, K
+
+
+def forward_topk(h, W, y, support, logpt_support, logpt_y, row_mask=None):
+    """Top-k estimator of the reverse KL per row: the student projected (h
+    [N, H], W [V, H] bf16), y int32 [N] the sampled tokens, support int32
+    [N, K] the support ids (None for K = 0), logpt_support fp32 [N, K] and
+    logpt_y fp32 [N] the teacher's log-probabilities there.  Returns (loss
+    fp32 [N], stats fp32 [N, 4] = (lse, c, sp, bound))."""
+    torch = _torch()
+    dev, N, V, H, K = _topk_args(h, W, y, support, logpt_support, row_mask)
+    _need(logpt_y, "logpt_y", torch.float32, dev, (N,))
+    loss = torch.empty(N, dtype=torch.float32, device=dev)
+    stats = torch.empty((N, 4), dtype=torch.float32, device=dev)
+    ws = _workspace(dev, workspace_bytes(N, V, H, 0))
+    _check(lib().rkl_forward_topk(N, V, H, K, _ptr(h), _ptr(W), _ptr(y), _ptr(support), _ptr(logpt_support),
+                                  _ptr(logpt_y), _ptr(row_mask), _ptr(loss), _ptr(stats), _ptr(ws), ws.numel(),
+                                  _stream(dev)))
+    return loss, stats
+
+
+def backward_topk(h, W, y, support, logpt_support, stats, grad_loss=None, row_mask=None, dW=None,
+                  accumulate_dW=False):
+    """Backward of sum_i g_i L_i for forward_topk: returns (dh fp32 [N, H], dW fp32 [V, H])."""
+    torch = _torch()
+    dev, N, V, H, K = _topk_args(h, W, y, support, logpt_support, row_mask)
+    _need(stats, "stats", torch.float32, dev, (N, 4))
+    if grad_loss is not None:
+        _need(grad_loss, "grad_loss", torch.float32, dev, (N,))
+    if dW is None:
+        if accumulate_dW:
+            raise RKLError(RKL_INVALID_ARG, "accumulate_dW needs a dW tensor")
+        dW = torch.empty((V, H), dtype=torch.float32, device=dev)
+    else:
+        _need(dW, "dW", torch.float32, dev, (V, H))
+    dh = torch.empty((N, H), dtype=torch.float32, device=dev)
+    ws = _workspace(dev, workspace_bytes(N, V, H, 0))
+    _check(lib().rkl_backward_topk(N, V, H, K, _ptr(h), _ptr(W), _ptr(y), _ptr(support), _ptr(logpt_support),
+                                   _ptr(row_mask), _ptr(grad_loss), _ptr(stats), _ptr(dh), _ptr(dW),
+                                   int(bool(accumulate_dW)), _ptr(ws), ws.numel(), _stream(dev)))
     return dh, dW

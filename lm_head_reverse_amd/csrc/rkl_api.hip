@@ -5,7 +5,9 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <string>
+#include <vector>
 
 #include "rkl.h"
 #include "rkl_internal.h"
@@ -28,6 +30,33 @@ int fail(int code, const char* fmt, ...) {
   do {                                                                                  \
     hipError_t e_ = (expr);                                                             \
     if (e_ != hipSuccess) return fail(RKL_DEVICE_ERROR, "%s: %s", #expr, hipGetErrorString(e_)); \
+  } while (0)
+
+// Per-kernel device time (rkl_kernel_timing / rkl_kernel_times): while the
+// calling thread has timing on, every kernel a call launches is bracketed by
+// two events recorded on the call's stream.
+struct TimedLaunch {
+  const char* name;
+  hipEvent_t begin, end;
+};
+thread_local bool g_timing = false;
+thread_local std::vector<TimedLaunch> g_timed;
+
+// A kernel launch (a launch_* call returning hipError_t) on stream `st`, timed
+// when timing is on.
+#define RKL_LAUNCH(name, st, expr)                                                      \
+  do {                                                                                  \
+    hipEvent_t evb_ = nullptr, eve_ = nullptr;                                          \
+    if (g_timing) {                                                                     \
+      RKL_TRY(hipEventCreate(&evb_));                                                   \
+      RKL_TRY(hipEventRecord(evb_, st));                                                \
+    }                                                                                   \
+    RKL_TRY(expr);                                                                      \
+    if (g_timing) {                                                                     \
+      RKL_TRY(hipEventCreate(&eve_));                                                   \
+      RKL_TRY(hipEventRecord(eve_, st));                                                \
+      g_timed.push_back(TimedLaunch{name, evb_, eve_});                                 \
+    }                                                                                   \
   } while (0)
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
@@ -97,23 +126,6 @@ Order read_order(const char* env, Order dflt) {
 }
 Order fwd_order() { return read_order("RKL_FWD_ORDER", Order{2, 16}); }
 
-// Waves per workgroup of the fused kernels: 8 (two waves per SIMD, measured
-// faster) or 4 (RKL_FUSED_WAVES=4).  The fold order of the online statistics
-// follows the wave layout, so the two settings differ in rounding only.
-int fused_waves() {
-  const char* s = std::getenv("RKL_FUSED_WAVES");
-  return (s && std::atoi(s) == 4) ? 4 : 8;
-}
-
-// Waves per workgroup of the dW and dh GEMMs (4 or 8; results are bitwise
-// the same: each output element's k order does not depend on the layout).
-// Measured: dW is faster with 8 (two waves per SIMD), dh with 4.
-int gemm_waves(const char* env, int dflt) {
-  const char* s = std::getenv(env);
-  if (!s) return dflt;
-  const int v = std::atoi(s);
-  return v == 8 ? 8 : (v == 4 ? 4 : dflt);
-}
 Order bwd_order() { return read_order("RKL_BWD_ORDER", Order{4, 8}); }
 
 // Column tiles per panel in the dh GEMM's workgroup order (RKL_DH_PANEL;
@@ -147,19 +159,21 @@ size_t fwd_ws_bytes(int64_t N, int64_t V, bool tiled) {
 }
 
 struct BwdLayout {
-  int64_t ldT, ldz, npad;
+  int64_t ldT, ldz, npad, nchunks;
   size_t off_hT, off_dz, off_w16, off_scale, total;
 };
-// [dz scale: 2 floats][hT: Hs x ldT fp16][dz chunk: npad x ldz fp16]; npad =
-// N rounded up to the 128-token tile (the dz kernel writes those rows as zero)
+// [scale block: rkl::kScaleWmag + nchunks words][hT: Hs x ldT fp16][dz chunk:
+// npad x ldz fp16][fp16 W_s chunk copy]; npad = N rounded up to the 128-token
+// tile (the dz kernel writes those rows as zero)
 BwdLayout bwd_layout(int64_t N, int64_t V, int64_t Hs) {
   BwdLayout L{};
   L.ldT = round_up(N, 64);
   L.npad = round_up(N, rkl::kFwdTileN);
   const int64_t C = vocab_chunk(N);
   L.ldz = round_up(V < C ? V : C, 64);
+  L.nchunks = ceil_div(V, C);
   L.off_scale = 0;
-  L.off_hT = 256;
+  L.off_hT = align256((size_t)(rkl::kScaleWmag + L.nchunks) * 4);
   L.off_dz = L.off_hT + align256((size_t)Hs * L.ldT * 2);
   L.off_w16 = L.off_dz + align256((size_t)L.npad * L.ldz * 2);
   // the fp16 W_s copy covers every 256-row vocabulary tile of a chunk
@@ -270,22 +284,31 @@ int forward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* 
   p.order_gs = fwd_order().gs;
   p.order_tg = fwd_order().tg;
   const int mode = mode_of(z_t, y, tch.teacher);
-  RKL_TRY(rkl::launch_fwd_tiles(p, mode, fused_waves(), s));
+  RKL_LAUNCH("fwd_tiles", s, rkl::launch_fwd_tiles(p, mode, s));
   if (merged) {   // one vocabulary shard: its merged statistics, not finalised
-    RKL_TRY(rkl::launch_fwd_merge(p.partial, p.nsplit, p.N, merged, s));
+    RKL_LAUNCH("fwd_combine", s, rkl::launch_fwd_merge(p.partial, p.nsplit, p.N, merged, s));
     return RKL_OK;
   }
-  RKL_TRY(rkl::launch_fwd_combine(p.partial, p.nsplit, p.N, row_mask, mode == rkl::kModeLogprobEntropy, out0, out1,
+  RKL_LAUNCH("fwd_combine", s, rkl::launch_fwd_combine(p.partial, p.nsplit, p.N, row_mask, mode == rkl::kModeLogprobEntropy, out0, out1,
                                   stats, s));
   return RKL_OK;
 }
+
+// Top-k estimator: the support of every row and the teacher's
+// log-probabilities on it (rkl_*_topk).
+struct TopK {
+  bool on = false;
+  int K = 0;
+  const int32_t* S = nullptr;
+  const float* lpt_S = nullptr;
+};
 
 int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* h_s, const rkl_bf16* W_s,
                    const rkl_bf16* h_t, const rkl_bf16* W_t, const float* z_t, const int32_t* y,
                    const uint8_t* row_mask, const float* grad, const float* grad_h, const float* stats, float* dh,
                    float* dW, int accumulate, void* ws, size_t ws_bytes_given, hipStream_t s,
-                   Teachers tch = Teachers{}) {
-  const int mode = mode_of(z_t, y, tch.teacher);
+                   Teachers tch = Teachers{}, TopK topk = TopK{}) {
+  const int mode = topk.on ? rkl::kModeTopK : mode_of(z_t, y, tch.teacher);
   if (N > kMaxPitchElems)
     return fail(RKL_UNSUPPORTED, "N=%lld rows exceed the backward's limit of 2^22 per call", (long long)N);
   const BwdLayout L = bwd_layout(N, V, Hs);
@@ -293,19 +316,22 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
     return fail(RKL_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes_given, L.total);
   if (N == 0) {
     // an empty selection still produces a (zero) dW unless the caller accumulates
-    if (!accumulate) RKL_TRY(rkl::launch_fill_zero(dW, V * Hs * (int64_t)sizeof(float), s));
+    if (!accumulate) RKL_LAUNCH("fill_zero", s, rkl::launch_fill_zero(dW, V * Hs * (int64_t)sizeof(float), s));
     return RKL_OK;
   }
   NEED16(ws, "workspace");
   char* base = static_cast<char*>(ws);
-  float* gscale = reinterpret_cast<float*>(base + L.off_scale);
+  uint32_t* scales = reinterpret_cast<uint32_t*>(base + L.off_scale);
   uint16_t* hT = reinterpret_cast<uint16_t*>(base + L.off_hT);
   uint16_t* dz = reinterpret_cast<uint16_t*>(base + L.off_dz);
   uint16_t* w16 = reinterpret_cast<uint16_t*>(base + L.off_w16);
-  RKL_TRY(rkl::launch_grad_scale(grad, grad_h, row_mask, stats, (int)N, mode == rkl::kModeLogprobEntropy, gscale, s));
-  RKL_TRY(rkl::launch_transpose_h(h_s, (int)N, (int)Hs, hT, (int)L.ldT, s));
+  RKL_LAUNCH("grad_scale", s, rkl::launch_grad_scale(grad, grad_h, row_mask, stats, (int)N, mode,
+                                 (int)L.nchunks, scales, s));
+  RKL_LAUNCH("absmax_bf16", s, rkl::launch_absmax_bf16(h_s, N * Hs, scales, s));
+  RKL_LAUNCH("transpose_h", s, rkl::launch_transpose_h(h_s, (int)N, (int)Hs, scales, hT, (int)L.ldT, s));
   const int64_t C = vocab_chunk(N);
-  for (int64_t c0 = 0; c0 < V; c0 += C) {
+  for (int64_t c0 = 0, chunk = 0; c0 < V; c0 += C, ++chunk) {
+    uint32_t* wmag = scales + rkl::kScaleWmag + chunk;
     const int64_t width = (V - c0) < C ? (V - c0) : C;
     const int64_t kpad = round_up(width, 64);
     rkl::BwdParams b{};
@@ -313,31 +339,37 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
     b.h_s = h_s; b.W_s = W_s; b.h_t = h_t; b.W_t = W_t; b.z_t = z_t;
     b.row_mask = row_mask; b.grad = grad; b.grad_h = grad_h; b.y = y; b.stats = stats;
     b.teacher = tch.teacher; b.K = tch.K; b.wt_stride = tch.stride;
-    b.gscale = gscale; b.dz = dz; b.w16 = w16; b.ldz = (int)L.ldz; b.c0 = (int)c0; b.kpad = (int)kpad;
+    b.scales = scales; b.wmag = wmag; b.dz = dz; b.w16 = w16; b.ldz = (int)L.ldz; b.c0 = (int)c0;
+    b.kpad = (int)kpad;
     b.ntv = (int)ceil_div(kpad, rkl::kFwdTileV);
     b.tiles_per_group = bwd_tiles_per_group();
     b.ngroups = (int)ceil_div(b.ntv, b.tiles_per_group);
     b.ntok = (int)ceil_div(N, rkl::kFwdTileN);
     b.order_gs = bwd_order().gs;
     b.order_tg = bwd_order().tg;
-    RKL_TRY(rkl::launch_bwd_dz(b, mode, fused_waves(), s));
+    RKL_LAUNCH("bwd_dz_tiles", s, rkl::launch_bwd_dz(b, mode, s));
+    if (topk.on && topk.K > 0)
+      RKL_LAUNCH("topk_dz_add", s, rkl::launch_topk_dz_add(h_s, W_s, (int)N, (int)V, (int)Hs, topk.K, topk.S,
+                                                          topk.lpt_S, row_mask, grad, stats, scales, dz, (int)L.ldz,
+                                                          (int)c0, (int)width, s));
+    RKL_LAUNCH("w_rescale", s, rkl::launch_w_rescale(W_s + c0 * Hs, (int)width, b.ntv, (int)Hs, wmag, w16, s));
 
     rkl::DwParams w{};
-    w.gscale = gscale; w.dz = dz; w.ldz = (int)L.ldz; w.N = (int)N; w.kpad = (int)kpad; w.width = (int)width;
+    w.scales = scales; w.dz = dz; w.ldz = (int)L.ldz; w.N = (int)N; w.kpad = (int)kpad; w.width = (int)width;
     w.hT = hT; w.ldT = (int)L.ldT; w.H = (int)Hs;
     w.dW = dW + c0 * Hs; w.accumulate = accumulate;
     w.ntm = (int)ceil_div(width, rkl::kDwTileM);
     w.ntn = (int)ceil_div(Hs, rkl::kDwTileN);
-    RKL_TRY(rkl::launch_dw(w, gemm_waves("RKL_DW_WAVES", 8), s));
+    RKL_LAUNCH("dw_gemm", s, rkl::launch_dw(w, s));
 
     rkl::DhParams h{};
-    h.gscale = gscale; h.dz = dz; h.ldz = (int)L.ldz; h.N = (int)N; h.npad = (int)L.npad; h.kpad = (int)kpad;
+    h.scales = scales; h.wmag = wmag; h.dz = dz; h.ldz = (int)L.ldz; h.N = (int)N; h.npad = (int)L.npad; h.kpad = (int)kpad;
     h.width = (int)width; h.c0 = (int)c0;
     h.w16 = w16; h.H = (int)Hs; h.dh = dh; h.accumulate = c0 > 0;
     h.ntm = (int)ceil_div(N, rkl::kDhTileM);
     h.ntn = (int)ceil_div(Hs, rkl::kDhTileN);
     h.panel = dh_panel(h.ntn);
-    RKL_TRY(rkl::launch_dh(h, gemm_waves("RKL_DH_WAVES", 4), s));
+    RKL_LAUNCH("dh_gemm", s, rkl::launch_dh(h, s));
   }
   return RKL_OK;
 }
@@ -352,7 +384,7 @@ int combine_shards(int64_t G, int64_t N, const float* partials, const uint8_t* r
   NEED4(partials, "partials"); NEED4(stats, "stats");
   if (lpe) { NEED4(out0, "logp"); NEED4(out1, "entropy"); }
   else NEED4(out0, "loss");
-  RKL_TRY(rkl::launch_fwd_combine(partials, (int)G, (int)N, row_mask, lpe, out0, out1, stats, s));
+  RKL_LAUNCH("fwd_combine", s, rkl::launch_fwd_combine(partials, (int)G, (int)N, row_mask, lpe, out0, out1, stats, s));
   return RKL_OK;
 }
 
@@ -365,6 +397,47 @@ extern "C" {
 const char* rkl_last_error(void) { return g_err.c_str(); }
 
 const char* rkl_version(void) { return "rkl 0.1 gfx950"; }
+
+int rkl_kernel_timing(int enable) {
+  g_timing = enable != 0;
+  return RKL_OK;
+}
+
+int rkl_kernel_times(int cap, const char** names, double* total_ms, int* launches, int* count) {
+  if (cap < 0 || (cap > 0 && (!names || !total_ms || !launches)) || !count)
+    return fail(RKL_INVALID_ARG, "need cap >= 0, arrays of cap entries and a count");
+  std::vector<TimedLaunch> recs;
+  recs.swap(g_timed);
+  int n = 0;
+  int rc = RKL_OK;
+  for (const TimedLaunch& r : recs) {
+    float ms = 0.f;
+    hipError_t e = hipEventSynchronize(r.end);
+    if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.begin, r.end);
+    (void)hipEventDestroy(r.begin);
+    (void)hipEventDestroy(r.end);
+    if (e != hipSuccess) {
+      rc = fail(RKL_DEVICE_ERROR, "kernel timing event: %s", hipGetErrorString(e));
+      continue;
+    }
+    int k = 0;
+    while (k < n && k < cap && std::strcmp(names[k], r.name) != 0) ++k;
+    if (k == n) {
+      if (n < cap) {
+        names[n] = r.name;
+        total_ms[n] = 0.0;
+        launches[n] = 0;
+      }
+      ++n;
+    }
+    if (k < cap) {
+      total_ms[k] += ms;
+      launches[k] += 1;
+    }
+  }
+  *count = n;
+  return rc;
+}
 
 size_t rkl_workspace_bytes(int64_t N, int64_t V, int64_t Hs, int64_t Ht) {
   if (N < 0 || N > kMaxDim || V < 1 || V > kMaxDim || Hs < 0 || Ht < 0) return 0;
@@ -385,7 +458,7 @@ int rkl_compact_rows(const uint8_t* mask, int64_t T, int32_t* row_idx, int32_t* 
     if (!mask) return fail(RKL_INVALID_ARG, "mask is NULL");
     NEED4(row_idx, "row_idx");
   }
-  RKL_TRY(rkl::launch_compact(mask, (int)T, row_idx, n_rows_dev, s));
+  RKL_LAUNCH("compact", s, rkl::launch_compact(mask, (int)T, row_idx, n_rows_dev, s));
   if (n_rows_host) {
     int32_t n = 0;
     RKL_TRY(hipMemcpyAsync(&n, n_rows_dev, sizeof(n), hipMemcpyDeviceToHost, s));
@@ -405,7 +478,7 @@ int rkl_gather_rows(const void* src, int64_t T, int64_t row_bytes, const int32_t
   const bool need16 = row_bytes % 16 == 0;
   if (need16 ? !(aligned16(src) && aligned16(dst)) : !(aligned4(src) && aligned4(dst)))
     return fail(RKL_INVALID_ARG, "src/dst misaligned");
-  RKL_TRY(rkl::launch_gather(src, row_bytes, row_idx, N, dst, static_cast<hipStream_t>(stream)));
+  RKL_LAUNCH("gather", static_cast<hipStream_t>(stream), rkl::launch_gather(src, row_bytes, row_idx, N, dst, static_cast<hipStream_t>(stream)));
   return RKL_OK;
 }
 
@@ -420,8 +493,8 @@ int rkl_scatter_rows(const void* src, int64_t N, int64_t row_bytes, const int32_
   if (need16 ? !(aligned16(dst) && (N == 0 || aligned16(src))) : !(aligned4(dst) && (N == 0 || aligned4(src))))
     return fail(RKL_INVALID_ARG, "src/dst misaligned");
   hipStream_t s = static_cast<hipStream_t>(stream);
-  RKL_TRY(rkl::launch_fill_zero(dst, T * row_bytes, s));
-  if (N > 0) RKL_TRY(rkl::launch_scatter(src, row_bytes, row_idx, N, dst, s));
+  RKL_LAUNCH("fill_zero", s, rkl::launch_fill_zero(dst, T * row_bytes, s));
+  if (N > 0) RKL_LAUNCH("scatter", s, rkl::launch_scatter(src, row_bytes, row_idx, N, dst, s));
   return RKL_OK;
 }
 
@@ -465,7 +538,7 @@ int rkl_forward_logits_shard(int64_t N, int64_t V, int64_t Hs, const rkl_bf16* h
     return forward_tiled(N, V, Hs, 0, h_s, W_s, nullptr, nullptr, z_t, nullptr, nullptr, nullptr, nullptr, nullptr,
                          workspace, workspace_bytes, s, Teachers{}, partial);
   if (N == 0) return RKL_OK;
-  RKL_TRY(rkl::launch_fwd_rows_logits(z_s, z_t, (int)N, (int)V, nullptr, nullptr, nullptr, partial, s));
+  RKL_LAUNCH("fwd_rows_logits", s, rkl::launch_fwd_rows_logits(z_s, z_t, (int)N, (int)V, nullptr, nullptr, nullptr, partial, s));
   return RKL_OK;
 }
 
@@ -507,7 +580,7 @@ int rkl_forward_logits(int64_t N, int64_t V, int64_t Hs, const rkl_bf16* h_s, co
     return forward_tiled(N, V, Hs, 0, h_s, W_s, nullptr, nullptr, z_t, nullptr, row_mask, loss, nullptr, stats,
                          workspace, workspace_bytes, s);
   if (N == 0) return RKL_OK;
-  RKL_TRY(rkl::launch_fwd_rows_logits(z_s, z_t, (int)N, (int)V, row_mask, loss, stats, nullptr, s));
+  RKL_LAUNCH("fwd_rows_logits", s, rkl::launch_fwd_rows_logits(z_s, z_t, (int)N, (int)V, row_mask, loss, stats, nullptr, s));
   return RKL_OK;
 }
 
@@ -546,7 +619,7 @@ int rkl_backward_logits(int64_t N, int64_t V, int64_t Hs, const rkl_bf16* h_s, c
   if (dh_s || dW_s) return fail(RKL_INVALID_ARG, "dh_s and dW_s must be NULL when the student is given as logits");
   if (N == 0) return RKL_OK;
   NEED16(z_s, "z_s"); NEED16(z_t, "z_t"); NEED4(stats, "stats"); NEED16(dz_s, "dz_s"); OPT4(grad_loss, "grad_loss");
-  RKL_TRY(rkl::launch_bwd_rows_logits(z_s, z_t, (int)N, (int)V, row_mask, grad_loss, stats, dz_s, s));
+  RKL_LAUNCH("bwd_rows_logits", s, rkl::launch_bwd_rows_logits(z_s, z_t, (int)N, (int)V, row_mask, grad_loss, stats, dz_s, s));
   return RKL_OK;
 }
 
@@ -576,6 +649,50 @@ int rkl_backward_logprob_entropy(int64_t N, int64_t V, int64_t H, const rkl_bf16
                         dW, accumulate_dW != 0, workspace, workspace_bytes, static_cast<hipStream_t>(stream));
 }
 
+int rkl_forward_topk(int64_t N, int64_t V, int64_t H, int64_t K, const rkl_bf16* h, const rkl_bf16* W,
+                     const int32_t* y, const int32_t* support, const float* logpt_support, const float* logpt_y,
+                     const uint8_t* row_mask, float* loss, float* stats, void* workspace, size_t workspace_bytes,
+                     rkl_stream_t stream) {
+  if (int rc = check_dims(N, V, H, 0, false, true)) return rc;
+  if (K < 0 || K > V) return fail(RKL_INVALID_ARG, "K=%lld support entries out of range [0, V]", (long long)K);
+  if (N * K > ((int64_t)1 << 40)) return fail(RKL_INVALID_ARG, "N*K too large");
+  if (N > 0) {
+    NEED16(h, "h"); NEED16(W, "W"); NEED4(y, "y"); NEED4(logpt_y, "logpt_y");
+    NEED4(loss, "loss"); NEED4(stats, "stats");
+    if (K > 0) { NEED4(support, "support"); NEED4(logpt_support, "logpt_support"); }
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // the student's log-sum-exp and log p(y) over the whole vocabulary (the
+  // log-probability forward; its log p(y) goes to `loss` for the moment)
+  if (int rc = forward_tiled(N, V, H, 0, h, W, nullptr, nullptr, nullptr, y, row_mask, loss, nullptr, stats,
+                             workspace, workspace_bytes, s))
+    return rc;
+  if (N == 0) return RKL_OK;
+  RKL_LAUNCH("topk_terms", s, rkl::launch_topk_terms(h, W, (int)N, (int)V, (int)H, (int)K, y, support, logpt_support,
+                                                    logpt_y, row_mask, loss, stats, s));
+  return RKL_OK;
+}
+
+int rkl_backward_topk(int64_t N, int64_t V, int64_t H, int64_t K, const rkl_bf16* h, const rkl_bf16* W,
+                      const int32_t* y, const int32_t* support, const float* logpt_support, const uint8_t* row_mask,
+                      const float* grad_loss, const float* stats, float* dh, float* dW, int accumulate_dW,
+                      void* workspace, size_t workspace_bytes, rkl_stream_t stream) {
+  if (int rc = check_dims(N, V, H, 0, false, true)) return rc;
+  if (K < 0 || K > V) return fail(RKL_INVALID_ARG, "K=%lld support entries out of range [0, V]", (long long)K);
+  if (N * K > ((int64_t)1 << 40)) return fail(RKL_INVALID_ARG, "N*K too large");
+  NEED16(dW, "dW");
+  if (N > 0) {
+    NEED16(h, "h"); NEED16(W, "W"); NEED4(y, "y"); NEED4(stats, "stats"); NEED16(dh, "dh");
+    OPT4(grad_loss, "grad_loss");
+    if (K > 0) { NEED4(support, "support"); NEED4(logpt_support, "logpt_support"); }
+  }
+  TopK t;
+  t.on = true; t.K = (int)K; t.S = support; t.lpt_S = logpt_support;
+  return backward_tiled(N, V, H, 0, h, W, nullptr, nullptr, nullptr, y, row_mask, grad_loss, nullptr, stats, dh, dW,
+                        accumulate_dW != 0, workspace, workspace_bytes, static_cast<hipStream_t>(stream), Teachers{},
+                        t);
+}
+
 int rkl_forward_hidden_teachers(int64_t N, int64_t V, int64_t Hs, int64_t Ht, int64_t K, const rkl_bf16* h_s,
                                 const rkl_bf16* W_s, const rkl_bf16* h_t, const rkl_bf16* W_t, const int32_t* teacher,
                                 const uint8_t* row_mask, float* loss, float* stats, void* workspace,
@@ -601,16 +718,16 @@ int rkl_forward_hidden_teachers(int64_t N, int64_t V, int64_t Hs, int64_t Ht, in
   rkl_bf16* ht = reinterpret_cast<rkl_bf16*>(g + G.off_ht);
   float* loss_g = reinterpret_cast<float*>(g + G.off_row);
   float* stats_g = reinterpret_cast<float*>(g + G.off_stats);
-  RKL_TRY(rkl::launch_group_by_teacher(teacher, row_mask, (int)N, (int)K, perm, tid, mask, s));
-  RKL_TRY(rkl::launch_gather(h_s, Hs * 2, perm, N, hs, s));
-  RKL_TRY(rkl::launch_gather(h_t, Ht * 2, perm, N, ht, s));
+  RKL_LAUNCH("group_by_teacher", s, rkl::launch_group_by_teacher(teacher, row_mask, (int)N, (int)K, perm, tid, mask, s));
+  RKL_LAUNCH("gather", s, rkl::launch_gather(h_s, Hs * 2, perm, N, hs, s));
+  RKL_LAUNCH("gather", s, rkl::launch_gather(h_t, Ht * 2, perm, N, ht, s));
   Teachers t;
   t.teacher = tid; t.K = (int)K; t.stride = V * Ht;
   if (int rc = forward_tiled(N, V, Hs, Ht, hs, W_s, ht, W_t, nullptr, nullptr, mask, loss_g, nullptr, stats_g,
                              g + G.total, workspace_bytes - G.total, s, t))
     return rc;
-  RKL_TRY(rkl::launch_scatter(loss_g, 4, perm, N, loss, s));
-  RKL_TRY(rkl::launch_scatter(stats_g, 16, perm, N, stats, s));
+  RKL_LAUNCH("scatter", s, rkl::launch_scatter(loss_g, 4, perm, N, loss, s));
+  RKL_LAUNCH("scatter", s, rkl::launch_scatter(stats_g, 16, perm, N, stats, s));
   return RKL_OK;
 }
 
@@ -648,16 +765,16 @@ int rkl_backward_hidden_teachers(int64_t N, int64_t V, int64_t Hs, int64_t Ht, i
   float* grad_g = grad_loss ? reinterpret_cast<float*>(g + G.off_row) : nullptr;
   float* stats_g = reinterpret_cast<float*>(g + G.off_stats);
   float* dh_g = reinterpret_cast<float*>(g + G.off_dh);
-  RKL_TRY(rkl::launch_group_by_teacher(teacher, row_mask, (int)N, (int)K, perm, tid, mask, s));
-  RKL_TRY(rkl::launch_gather(h_s, Hs * 2, perm, N, hs, s));
-  RKL_TRY(rkl::launch_gather(h_t, Ht * 2, perm, N, ht, s));
-  if (grad_loss) RKL_TRY(rkl::launch_gather(grad_loss, 4, perm, N, grad_g, s));
-  RKL_TRY(rkl::launch_gather(stats, 16, perm, N, stats_g, s));
+  RKL_LAUNCH("group_by_teacher", s, rkl::launch_group_by_teacher(teacher, row_mask, (int)N, (int)K, perm, tid, mask, s));
+  RKL_LAUNCH("gather", s, rkl::launch_gather(h_s, Hs * 2, perm, N, hs, s));
+  RKL_LAUNCH("gather", s, rkl::launch_gather(h_t, Ht * 2, perm, N, ht, s));
+  if (grad_loss) RKL_LAUNCH("gather", s, rkl::launch_gather(grad_loss, 4, perm, N, grad_g, s));
+  RKL_LAUNCH("gather", s, rkl::launch_gather(stats, 16, perm, N, stats_g, s));
   t.teacher = tid;
   if (int rc = backward_tiled(N, V, Hs, Ht, hs, W_s, ht, W_t, nullptr, nullptr, mask, grad_g, nullptr, stats_g, dh_g,
                               dW_s, accumulate_dW != 0, g + G.total, workspace_bytes - G.total, s, t))
     return rc;
-  RKL_TRY(rkl::launch_scatter(dh_g, Hs * 4, perm, N, dh_s, s));
+  RKL_LAUNCH("scatter", s, rkl::launch_scatter(dh_g, Hs * 4, perm, N, dh_s, s));
   return RKL_OK;
 }
 

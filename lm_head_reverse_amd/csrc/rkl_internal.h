@@ -40,7 +40,8 @@ struct BwdParams {
   int K;
   int64_t wt_stride;
   const float* stats;
-  const float* gscale;     // [2]: s, 1/s (powers of two); dz is stored as fp16(s * dz)
+  const uint32_t* scales;  // the backward's scale block (kScaleS: dz is stored as fp16(s * dz))
+  uint32_t* wmag;          // this chunk's slot of kScaleWmag: largest |W_s| converted (atomic max)
   uint16_t* dz;            // [ntok * 128, ldz] fp16 chunk workspace (rows past N written as zero)
   uint16_t* w16;           // [ntv * 256, Hs] fp16 copy of the W_s chunk (for dh)
   int ldz;
@@ -54,7 +55,7 @@ struct BwdParams {
 };
 
 struct DwParams {
-  const float* gscale;
+  const uint32_t* scales;  // kScaleKs, kScaleHmag: dW = 2^-(ks + kh) * sum of the fp16 products
   const uint16_t* dz;
   int ldz, N, kpad, width;
   const uint16_t* hT;      // [H, ldT] fp16
@@ -65,7 +66,8 @@ struct DwParams {
 };
 
 struct DhParams {
-  const float* gscale;
+  const uint32_t* scales;  // kScaleKs: dh = 2^-(ks + kw) * sum of the fp16 products
+  const uint32_t* wmag;    // this chunk's largest |W_s| (fixes kw)
   const uint16_t* dz;
   int ldz, N, npad, kpad, width;   // npad: dz workspace rows
   int c0;                          // first vocabulary column of the chunk
@@ -76,6 +78,29 @@ struct DhParams {
   int ntm, ntn;
   int panel;               // column tiles per panel of the workgroup order
 };
+
+// Waves per workgroup: the fused kernels (two waves per SIMD, 64 x 64 of both
+// projections per wave), the dW GEMM (two per SIMD) and the dh GEMM (one per
+// SIMD) -- the layouts measured fastest; no other count is built.
+constexpr int kFusedWaves = 8;
+constexpr int kDwWaves = 8;
+constexpr int kDhWaves = 4;
+
+// The backward's scale block (32-bit words at the front of its workspace).
+// The dz, dW and dh GEMM operands are fp16 copies scaled by powers of two, so
+// every copy is exact wherever fp16 represents the scaled value and the GEMM
+// epilogues undo the scales exactly:
+//   dz   = fp16(2^ks dz),   2^ks puts the largest |g| p_max in [16, 32);
+//   hT   = fp16(2^kh h_s),  2^kh puts the largest |h_s| in [2^14, 2^15);
+//   W16  = fp16(2^kw W_s) per chunk, kw = 0 while the chunk's largest |W_s|
+//          lies in [2^-10, 2^15), else the power of two that puts it in
+//          [2^14, 2^15) (the dz kernel converts with kw = 0 and records the
+//          largest magnitude; w_rescale converts the chunk again when needed).
+constexpr int kScaleS = 0;      // float 2^ks
+constexpr int kScaleKs = 1;     // int ks
+constexpr int kScaleHmag = 2;   // largest |h_s| as bf16 magnitude bits (atomic max)
+constexpr int kScaleWmag = 4;   // first of one slot per chunk: largest |W_s| of the chunk's rows
+constexpr int kMaxExpShift = 100;   // |kh|, |kw| are clamped to this
 
 // Tile sizes the host needs for grids and workspace.
 constexpr int kFwdTileV = 256;
@@ -92,20 +117,41 @@ enum Mode : int {
   kModeTeacherLogits = 1,   // reverse KL, teacher logits streamed
   kModeLogprobEntropy = 2,  // log p(sampled token) and entropy of one projection
   kModeHiddenTeachers = 3,  // reverse KL, teacher hidden states, teacher chosen per row
+  kModeTopK = 4,            // top-k estimator's backward: dense part -p c + spike at the sampled token
 };
 
-hipError_t launch_fwd_tiles(const FwdParams& p, int mode, int waves, hipStream_t s);
+hipError_t launch_fwd_tiles(const FwdParams& p, int mode, hipStream_t s);
 // out0: loss (reverse KL) or log p(y); out1: entropy (log-probability / entropy only)
 hipError_t launch_fwd_combine(const float* partial, int nsplit, int N, const uint8_t* row_mask, bool logprob_entropy,
                               float* out0, float* out1, float* stats, hipStream_t s);
 // The splits' merged (m_s, S_s, A, m_t, S_t), not finalised: five planes of N.
 hipError_t launch_fwd_merge(const float* partial, int nsplit, int N, float* merged, hipStream_t s);
-hipError_t launch_bwd_dz(const BwdParams& p, int mode, int waves, hipStream_t s);
+hipError_t launch_bwd_dz(const BwdParams& p, int mode, hipStream_t s);
+// Writes kScaleS / kScaleKs and clears kScaleHmag and the nchunks kScaleWmag slots.
+// mode: kModeLogprobEntropy, kModeTopK or a reverse-KL mode (the bound on |dz| / |g| differs).
 hipError_t launch_grad_scale(const float* grad, const float* grad_h, const uint8_t* row_mask, const float* stats,
-                             int N, bool logprob_entropy, float* out, hipStream_t s);
-hipError_t launch_transpose_h(const uint16_t* h, int N, int H, uint16_t* hT, int ldT, hipStream_t s);
-hipError_t launch_dw(const DwParams& p, int waves, hipStream_t s);
-hipError_t launch_dh(const DhParams& p, int waves, hipStream_t s);
+                             int N, int mode, int nchunks, uint32_t* scales, hipStream_t s);
+// Top-k estimator, forward: per row, from stats = (lse, -, log p(y), -) of the
+// log-probability forward, the support terms over the K ids of S and the
+// tail at y; writes loss and stats = (lse, c, sp, bound) (see the kernel).
+hipError_t launch_topk_terms(const uint16_t* h, const uint16_t* W, int N, int V, int H, int K, const int32_t* y,
+                             const int32_t* S, const float* lpt_S, const float* lpt_y, const uint8_t* row_mask,
+                             float* loss, float* stats, hipStream_t s);
+// Top-k estimator, backward: adds s g p_j (f_j + 1) for the support ids j of
+// chunk [c0, c0 + width) into the fp16 dz chunk.
+hipError_t launch_topk_dz_add(const uint16_t* h, const uint16_t* W, int N, int V, int H, int K, const int32_t* S,
+                              const float* lpt_S, const uint8_t* row_mask, const float* grad, const float* stats,
+                              const uint32_t* scales, uint16_t* dz, int ldz, int c0, int width, hipStream_t s);
+// scales[kScaleHmag] = max over h [n] of the bf16 magnitude bits (after launch_grad_scale cleared it)
+hipError_t launch_absmax_bf16(const uint16_t* h, int64_t n, uint32_t* scales, hipStream_t s);
+hipError_t launch_transpose_h(const uint16_t* h, int N, int H, const uint32_t* scales, uint16_t* hT, int ldT,
+                              hipStream_t s);
+// The chunk's W16 again with 2^kw when its recorded largest |W_s| (wmag) is out of band; else nothing.
+// W_chunk: the chunk's first row of W_s; rows valid rows, ntv * 256 rows written (zeros past rows).
+hipError_t launch_w_rescale(const uint16_t* W_chunk, int rows, int ntv, int H, const uint32_t* wmag, uint16_t* w16,
+                            hipStream_t s);
+hipError_t launch_dw(const DwParams& p, hipStream_t s);
+hipError_t launch_dh(const DhParams& p, hipStream_t s);
 // merged != NULL: the unfinalised (m_s, S_s, A, m_t, S_t) planes instead of loss / stats
 hipError_t launch_fwd_rows_logits(const float* z_s, const float* z_t, int N, int V, const uint8_t* row_mask,
                                   float* loss, float* stats, float* merged, hipStream_t s);

@@ -53,10 +53,11 @@ using FwdStages = Stages<FBM, FBN>;
 
 // Wave layout of the fused kernels: NW waves as NW/2 rows (vocabulary) x 2
 // columns (tokens) over the 256 x 128 tile; each wave holds FM x FN 32x32
-// blocks of z_s and of z_t.  Four waves: 128 x 64 per wave, 256 accumulator
-// registers, one wave per SIMD.  Eight waves: 64 x 64 per wave, 128
-// accumulator registers, two waves per SIMD (one can issue MFMAs while the
-// other waits on LDS or the DMA), for a third more fragment reads.
+// blocks of z_s and of z_t.  Built with eight waves (kFusedWaves): 64 x 64 per
+// wave, 128 accumulator registers, two waves per SIMD (one can issue MFMAs
+// while the other waits on LDS or the DMA).  (Four waves at 128 x 64 would
+// read a third fewer fragments but need 256 accumulator registers per wave,
+// which spill.)
 template <int NW>
 struct Fused {
   static constexpr int kThreads = 64 * NW;
@@ -159,13 +160,18 @@ __device__ __forceinline__ void fold_lpe(const f32x16 (&zs)[FM][FN], int fn, int
 }
 
 // Teacher logits read into the accumulator layout (teacher-logits payload).
-template <bool VEC4, int FM, int FN>
+// Token columns past N read row N-1 (their results are discarded).  A full
+// vocabulary tile (TAIL false) loads without conditions, from one row
+// pointer per token column and immediate offsets; the last tile clamps each
+// column index to V-1 and zeroes what lies past V.
+// only >= 0 loads token column `only` alone.
+template <bool VEC4, bool TAIL, int FM, int FN>
 __device__ __forceinline__ void load_zt(f32x16 (&zt)[FM][FN], const float* __restrict__ z_t, int N, int V,
-                                        int vrow, int ncol, int lane) {
-  (void)lane;
+                                        int vrow, int ncol, int only = -1) {
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
-    const int n = ncol + fn * 32;
+    if (only >= 0 && fn != only) continue;
+    const int n = min(ncol + fn * 32, N - 1);
     const float* row = z_t + (int64_t)n * V;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
@@ -173,14 +179,24 @@ __device__ __forceinline__ void load_zt(f32x16 (&zt)[FM][FN], const float* __res
       for (int g = 0; g < 4; ++g) {
         const int v = vrow + fm * 32 + 8 * g;
         if (VEC4) {
+          // V % 4 == 0: a group of four is wholly inside or wholly past V
           float4 q = make_float4(0.f, 0.f, 0.f, 0.f);
-          if (n < N && v < V) q = *reinterpret_cast<const float4*>(row + v);
+          if (!TAIL || v < V) q = *reinterpret_cast<const float4*>(row + v);
           zt[fm][fn][4 * g + 0] = q.x; zt[fm][fn][4 * g + 1] = q.y;
           zt[fm][fn][4 * g + 2] = q.z; zt[fm][fn][4 * g + 3] = q.w;
         } else {
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            zt[fm][fn][4 * g + e] = (n < N && v + e < V) ? row[v + e] : 0.f;
+          for (int e = 0; e < 4; ++e) {
+            if (TAIL) {
+              const float x = row[min(v + e, V - 1)];
+              zt[fm][fn][4 * g + e] = v + e < V ? x : 0.f;
+            } else {
+              zt[fm][fn][4 * g + e] = row[v + e];
+            }
+          }
+          // the tail's clamped addresses four at a time (all at once would
+          // hold 64 addresses in registers)
+          if (TAIL) __builtin_amdgcn_sched_barrier(0);
         }
       }
   }
@@ -444,19 +460,27 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void fwd_tiles(FwdParams p)
 
   dual_stream<NW, MODE == 3>(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, tkl, [&](int job, char*) {
     const int v0 = (vt0 + job) * FBM;
-    if (MODE == 1) load_zt<VEC4>(zt, p.z_t, p.N, p.V, v0 + arow0 + lrow, n0 + brow0 + (lane & 31), lane);
     const int vrow = v0 + arow0 + lrow;
     if (v0 + FBM <= p.V) {
+      // teacher logits: the next token column's loads are in flight while
+      // this one folds (with V % 4 != 0 all at once: the unaligned rows need
+      // more registers)
+      if (MODE == 1) load_zt<VEC4, false>(zt, p.z_t, p.N, p.V, vrow, n0 + brow0 + (lane & 31), VEC4 ? 0 : -1);
 #pragma unroll
       for (int fn = 0; fn < FFN; ++fn) {
+        if (MODE == 1 && VEC4 && fn + 1 < FFN)
+          load_zt<VEC4, false>(zt, p.z_t, p.N, p.V, vrow, n0 + brow0 + (lane & 31), fn + 1);
         if (MODE == 2)
           fold_lpe<false>(zs, fn, vrow, p.V, yv[fn], ms[fn], ss[fn], aa[fn], mt[fn]);
         else
           fold_tile<false>(zs, zt, fn, vrow, p.V, ms[fn], ss[fn], aa[fn], mt[fn], st[fn]);
       }
     } else {
+      // the last vocabulary tile: teacher logits one token column at a time
+      // (its clamped loads need an address per entry)
 #pragma unroll
       for (int fn = 0; fn < FFN; ++fn) {
+        if (MODE == 1) load_zt<VEC4, true>(zt, p.z_t, p.N, p.V, vrow, n0 + brow0 + (lane & 31), fn);
         if (MODE == 2)
           fold_lpe<true>(zs, fn, vrow, p.V, yv[fn], ms[fn], ss[fn], aa[fn], mt[fn]);
         else
@@ -557,7 +581,7 @@ __global__ __launch_bounds__(256) void fwd_combine(const float* __restrict__ par
     float lpy = mt - lse_s;
     if (dead) { lse_s = 0.f; H = 0.f; lpy = 0.f; lpmax = 0.f; }
     out0[n] = lpy;
-    out1[n] = H;
+    if (out1) out1[n] = H;
     stats[4 * (int64_t)n + 0] = lse_s;
     stats[4 * (int64_t)n + 1] = H;
     stats[4 * (int64_t)n + 2] = lpy;
@@ -587,10 +611,11 @@ __global__ __launch_bounds__(256) void fwd_combine(const float* __restrict__ par
 // p_v H) <= 2 |g_lp| + |g_H| (1 + H), so that bound takes the place of
 // g * p_max: s * dz stays below 32.
 // ===========================================================================
-template <bool LPE>
+template <int MODE>
 __global__ __launch_bounds__(1024) void grad_scale(const float* __restrict__ grad, const float* __restrict__ grad_h,
                                                    const uint8_t* __restrict__ row_mask,
-                                                   const float* __restrict__ stats, int N, float* __restrict__ out) {
+                                                   const float* __restrict__ stats, int N, int nchunks,
+                                                   uint32_t* __restrict__ scales) {
   __shared__ float red[1024];
   const int tid = threadIdx.x;
   float m = 0.f;
@@ -598,14 +623,19 @@ __global__ __launch_bounds__(1024) void grad_scale(const float* __restrict__ gra
     const bool live = !row_mask || row_mask[n] != 0;
     if (!live) continue;
     const float g = grad ? fabsf(grad[n]) : 1.0f;
-    if (LPE) {
+    if (MODE == kModeLogprobEntropy) {
       const float gh = grad_h ? fabsf(grad_h[n]) : 0.0f;
       m = fmaxf(m, 2.0f * g + gh * (1.0f + fabsf(stats[4 * (int64_t)n + 1])));
+    } else if (MODE == kModeTopK) {
+      m = fmaxf(m, g * stats[4 * (int64_t)n + 3]);   // the row's bound on |dz| / |g|
     } else {
       m = fmaxf(m, g * expf(stats[4 * (int64_t)n + 3]));
     }
   }
   red[tid] = m;
+  // the magnitude records the later kernels take atomic maxima into
+  if (tid == 0) scales[kScaleHmag] = 0u;
+  for (int c = tid; c < nchunks; c += 1024) scales[kScaleWmag + c] = 0u;
   __syncthreads();
   for (int off = 512; off > 0; off >>= 1) {
     if (tid < off) red[tid] = fmaxf(red[tid], red[tid + off]);
@@ -615,8 +645,61 @@ __global__ __launch_bounds__(1024) void grad_scale(const float* __restrict__ gra
     int e = 0;
     if (red[0] > 0.f) frexpf(red[0], &e);     // max in [2^(e-1), 2^e)
     e = e < -100 ? -100 : (e > 100 ? 100 : e);
-    out[0] = ldexpf(1.0f, 5 - e);
-    out[1] = ldexpf(1.0f, e - 5);
+    scales[kScaleS] = __builtin_bit_cast(uint32_t, ldexpf(1.0f, 5 - e));
+    scales[kScaleKs] = (uint32_t)(5 - e);
+  }
+}
+
+// e with |x| in [2^(e-1), 2^e) for the bf16 magnitude bits m (bits & 0x7fff)
+// of a nonzero finite value.
+__device__ __forceinline__ int bf16_mag_exp(uint32_t m) {
+  const int E = (int)(m >> 7);
+  if (E > 0) return E - 126;
+  return (32 - __clz((int)(m & 0x7fu))) - 133;   // subnormal: 0.f x 2^-126
+}
+__device__ __forceinline__ int clamp_shift(int k) { return k < -kMaxExpShift ? -kMaxExpShift : (k > kMaxExpShift ? kMaxExpShift : k); }
+// 2^kh for hT: the largest |h_s| into [2^14, 2^15).
+__device__ __forceinline__ int h_scale_exp(uint32_t m) { return m ? clamp_shift(15 - bf16_mag_exp(m)) : 0; }
+// 2^kw for the W_s copy: 1 while the largest |W_s| is in [2^-10, 2^15) (no
+// overflow, and everything within 2^-4 of fp16's normal range at the top),
+// else as for hT.
+__device__ __forceinline__ int w_scale_exp(uint32_t m) {
+  if (m == 0) return 0;
+  const int e = bf16_mag_exp(m);
+  return (e >= -9 && e <= 15) ? 0 : clamp_shift(15 - e);
+}
+// Largest bf16 magnitude among the 8 values of a 16-byte piece.
+__device__ __forceinline__ uint32_t bf16x8_absmax(u32x4 x) {
+  uint32_t m = 0;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) m = max(m, max(x[e] & 0x7fffu, (x[e] >> 16) & 0x7fffu));
+  return m;
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t m) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+  return m;
+}
+
+// scales[kScaleHmag] = largest bf16 magnitude among n values (n % 8 == 0 not
+// required; 16-byte pieces, then a tail).
+__global__ __launch_bounds__(256) void absmax_bf16(const uint16_t* __restrict__ h, int64_t n,
+                                                   uint32_t* __restrict__ scales) {
+  uint32_t m = 0;
+  const int64_t n8 = n / 8;
+  const u32x4* h8 = reinterpret_cast<const u32x4*>(h);
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256)
+    m = max(m, bf16x8_absmax(h8[i]));
+  for (int64_t i = n8 * 8 + (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+    m = max(m, (uint32_t)h[i] & 0x7fffu);
+  // one atomic per workgroup (atomics on one address serialise in L2)
+  __shared__ uint32_t wmax[4];
+  m = wave_max_u32(m);
+  if ((threadIdx.x & 63) == 0) wmax[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    m = max(max(wmax[0], wmax[1]), max(wmax[2], wmax[3]));
+    if (m) atomicMax(scales + kScaleHmag, m);
   }
 }
 
@@ -630,12 +713,19 @@ __global__ __launch_bounds__(1024) void grad_scale(const float* __restrict__ gra
 // selection, so a dead row stays exactly zero whatever its logits are.
 // vrow = vocabulary index of this lane's row 0 in block fm = 0; elem(z_s,
 // z_t, fn, v) gives s * dz of one entry (v = its vocabulary index).
-template <bool TAIL, int FM, int FN, class Elem>
+// col(fn) runs before token column fn is packed (the teacher-logits payload
+// loads the next column's logits there).
+struct NoColHook {
+  __device__ __forceinline__ void operator()(int) const {}
+};
+
+template <bool TAIL, int FM, int FN, class Elem, class Col = NoColHook>
 __device__ __forceinline__ void dz_pack(const f32x16 (&zs)[FM][FN], const f32x16 (&zt)[FM][FN],
                                         uint32_t (&pk)[FM][FN][2][4], const bool (&live)[FN], int vrow, int V,
-                                        Elem elem) {
+                                        Elem elem, Col col = Col{}) {
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
+    col(fn);
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm) {
       uint32_t w[4][2];   // [gq][dword]
@@ -710,7 +800,9 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
   //   s dz = gs p ((z_s - z_t) - cst),  gs = s g, cst = lse_s - lse_t + L;
   // log-probability / entropy (MODE 2), lp = z - lse:
   //   s dz = gs (1[v = y] - p) - ge p (lp + H) = -p (ge z + cst) + 1[v = y] gs,
-  //   gs = s g_lp, ge = s g_H, cst = gs + ge (H - lse).
+  //   gs = s g_lp, ge = s g_H, cst = gs + ge (H - lse);
+  // top-k estimator (MODE 4): the same form with ge = 0, cst = s g c and the
+  // spike gs = s g sp from the forward's stats (lse, c, sp, bound).
   // css = lse_s log2(e): p = 2^(z log2(e) - css).
   bool live[FFN];
   float gs[FFN], ge[FFN], cst[FFN], css[FFN];
@@ -721,12 +813,19 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
     live[fn] = n < p.N && (!p.row_mask || p.row_mask[n] != 0);
     const int nc = min(n, p.N - 1);
     const float lse_s = p.stats[4 * (int64_t)nc + 0];
-    gs[fn] = (p.grad ? p.grad[nc] : 1.0f) * p.gscale[0];
+    gs[fn] = (p.grad ? p.grad[nc] : 1.0f) * __builtin_bit_cast(float, p.scales[kScaleS]);
     css[fn] = lse_s * kL2E;
     if (MODE == 2) {
       const float H = p.stats[4 * (int64_t)nc + 1];
-      ge[fn] = (p.grad_h ? p.grad_h[nc] : 0.0f) * p.gscale[0];
+      ge[fn] = (p.grad_h ? p.grad_h[nc] : 0.0f) * __builtin_bit_cast(float, p.scales[kScaleS]);
       cst[fn] = gs[fn] + ge[fn] * (H - lse_s);
+      yv[fn] = p.y[nc];
+    } else if (MODE == 4) {
+      // top-k estimator, the dense part and the tail's spike (the support's
+      // own terms are added by topk_dz_add): s dz = -p (gs c) + 1[v = y] gs sp
+      cst[fn] = gs[fn] * p.stats[4 * (int64_t)nc + 1];
+      gs[fn] *= p.stats[4 * (int64_t)nc + 2];
+      ge[fn] = 0.f;
       yv[fn] = p.y[nc];
     } else {
       const float lse_t = p.stats[4 * (int64_t)nc + 1];
@@ -749,17 +848,27 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
   // fp16 copy of this workgroup's share of the W_s chunk for the dh GEMM:
   // of each vocabulary tile's Hs/64 student k-tiles, token tile tt converts
   // those with kt = tt (mod ntok), so every (tile, k-tile) is written once.
-  // Rows past V hold the clamped copies of row V-1 the DMA brought in.
+  // Rows past V hold the clamped copies of row V-1 the DMA brought in.  The
+  // copy is unscaled; the largest magnitude converted goes to the chunk's
+  // record, from which w_rescale decides whether the copy must be made again
+  // with a scale.
   auto convert_w = [&](const char* stage, int job, int kt) {
     if (kt % p.ntok != tt % p.ntok) return;
-    uint16_t* dst = p.w16 + (int64_t)(vt0 + job) * FBM * p.Hs + kt * kKT;
+    // thread tid converts rows r = i * kThreads / 8 + tid / 8, 16-byte piece
+    // tid % 8: a wave-uniform base plus a 32-bit lane offset
+    const int c = tid & 7;
+    const uint32_t loff = (uint32_t)(tid >> 3) * (uint32_t)p.Hs + (uint32_t)(c * 8);
+    uint32_t mag = 0;
 #pragma unroll
     for (int i = 0; i < FBM * 8 / F::kThreads; ++i) {
-      const int pr = tid + i * F::kThreads;
-      const int r = pr >> 3, c = pr & 7;
+      const int r = i * (F::kThreads / 8) + (tid >> 3);
       const u32x4 x = *reinterpret_cast<const u32x4*>(stage + lds_off(r, c));
-      *reinterpret_cast<f16x8*>(dst + (int64_t)r * p.Hs + c * 8) = bf16_to_f16(__builtin_bit_cast(bf16x8, x));
+      mag = max(mag, bf16x8_absmax(x));
+      uint16_t* rb = p.w16 + ((int64_t)(vt0 + job) * FBM + i * (F::kThreads / 8)) * p.Hs + kt * kKT;
+      *reinterpret_cast<f16x8*>(rb + loff) = bf16_to_f16(__builtin_bit_cast(bf16x8, x));
     }
+    mag = wave_max_u32(mag);
+    if (lane == 0 && mag) atomicMax(p.wmag, mag);
     // the next k-tile's DMA writes this stage: every wave's reads first
     // (the condition above is the same for the whole workgroup)
     dma_barrier<63>();
@@ -767,7 +876,6 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
 
   dual_stream<NW, MODE == 3>(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, tkl, [&](int job, char* stage) {
     const int v0 = p.c0 + (vt0 + job) * FBM;
-    if (MODE == 1) load_zt<VEC4>(zt, p.z_t, p.N, p.V, v0 + arow0 + lrow, n0 + brow0 + (lane & 31), lane);
     const int hi = lane >> 5;
     uint32_t pk[FFM][FFN][2][4];   // [fm][fn][run][dword]
     auto kl = [&](float a, float bb, int fn, int) {
@@ -777,16 +885,29 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
       const float d = -ex2(fmaf(a, kL2E, -css[fn])) * fmaf(ge[fn], a, cst[fn]);
       return v == yv[fn] ? d + gs[fn] : d;
     };
-    if (MODE == 2) {
+    if (MODE == 2 || MODE == 4) {
       if (v0 + FBM <= p.V)
         dz_pack<false>(zs, zt, pk, live, v0 + arow0 + lrow, p.V, lpe);
       else
         dz_pack<true>(zs, zt, pk, live, v0 + arow0 + lrow, p.V, lpe);
-    } else {
+    } else if (MODE != 1) {
       if (v0 + FBM <= p.V)
         dz_pack<false>(zs, zt, pk, live, v0 + arow0 + lrow, p.V, kl);
       else
         dz_pack<true>(zs, zt, pk, live, v0 + arow0 + lrow, p.V, kl);
+    } else {
+      // teacher logits, one token column at a time: the next column's loads
+      // are in flight while this one is packed
+      const int vr = v0 + arow0 + lrow, nc = n0 + brow0 + (lane & 31);
+      if (v0 + FBM <= p.V) {
+        load_zt<VEC4, false>(zt, p.z_t, p.N, p.V, vr, nc, 0);
+        dz_pack<false>(zs, zt, pk, live, vr, p.V, kl, [&](int fn) {
+          if (fn + 1 < FFN) load_zt<VEC4, false>(zt, p.z_t, p.N, p.V, vr, nc, fn + 1);
+        });
+      } else {
+        dz_pack<true>(zs, zt, pk, live, vr, p.V, kl,
+                      [&](int fn) { load_zt<VEC4, true>(zt, p.z_t, p.N, p.V, vr, nc, fn); });
+      }
     }
     // Stores go through the free LDS stage, 64 tokens per round: the waves
     // holding those tokens write a [64 token][256 vocabulary] fp16 tile (16-byte
@@ -810,25 +931,34 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
         }
       }
       dma_barrier<63>();
+      // thread tid stores token row tr = it * kThreads / 32 + tid / 32 of the
+      // round, columns col .. col + 7: a wave-uniform row base plus a 32-bit
+      // lane offset (tid / 32) * ldz + (tid % 32) * 8 (no 64-bit per-lane
+      // addresses live across the main loop)
+      const int c = tid & 31;
+      const int col = v0 - p.c0 + c * 8;
+      const uint32_t loff = (uint32_t)(tid >> 5) * (uint32_t)p.ldz + (uint32_t)(c * 8);
 #pragma unroll
       for (int it = 0; it < 64 * 32 / F::kThreads; ++it) {
-        const int lin = it * F::kThreads + tid;
-        const int tr = lin >> 5, c = lin & 31;
-        const int col = v0 - p.c0 + c * 8;
+        const int tr = it * (F::kThreads / 32) + (tid >> 5);
         const u32x4 x = *reinterpret_cast<const u32x4*>(stage + tr * 512 + ((c ^ (tr & 31)) << 4));
-        if (col < p.kpad) *reinterpret_cast<u32x4*>(p.dz + (int64_t)(n0 + round * 64 + tr) * p.ldz + col) = x;
+        uint16_t* rb = p.dz + (int64_t)(n0 + round * 64 + it * (F::kThreads / 32)) * p.ldz + (v0 - p.c0);
+        if (col < p.kpad) *reinterpret_cast<u32x4*>(rb + loff) = x;
       }
       dma_barrier<63>();
     }
   }, convert_w);
 }
 
-// h_s [N, H] bf16 -> hT [H, ldT] fp16 (exact for values in fp16's normal
-// range), zero for token columns in [N, ldT).
+// h_s [N, H] bf16 -> hT [H, ldT] fp16 = fp16(2^kh h_s) (2^kh from the
+// recorded largest |h_s|: exact except for values more than 2^29 below the
+// largest, which fall to fp16 subnormals), zero for token columns in [N, ldT).
 __global__ __launch_bounds__(256) void transpose_h(const uint16_t* __restrict__ h, int N, int H,
-                                                   uint16_t* __restrict__ hT, int ldT) {
+                                                   const uint32_t* __restrict__ scales, uint16_t* __restrict__ hT,
+                                                   int ldT) {
   __shared__ uint16_t tile[64][66];
   const int n0 = blockIdx.x * 64, j0 = blockIdx.y * 64, tid = threadIdx.x;
+  const int kh = h_scale_exp(scales[kScaleHmag]);
   for (int e = tid; e < 64 * 64; e += 256) {
     const int r = e >> 6, c = e & 63;
     tile[r][c] = (n0 + r < N) ? h[(int64_t)(n0 + r) * H + j0 + c] : (uint16_t)0;
@@ -836,8 +966,34 @@ __global__ __launch_bounds__(256) void transpose_h(const uint16_t* __restrict__ 
   __syncthreads();
   for (int e = tid; e < 64 * 64; e += 256) {
     const int r = e >> 6, c = e & 63;
-    const float x = __builtin_bit_cast(float, (uint32_t)tile[c][r] << 16);
+    const float x = ldexpf(__builtin_bit_cast(float, (uint32_t)tile[c][r] << 16), kh);
     hT[(int64_t)(j0 + r) * ldT + n0 + c] = __builtin_bit_cast(uint16_t, (_Float16)x);
+  }
+}
+
+// The fp16 copy of one chunk's W_s rows again, as fp16(2^kw W_s), when the
+// largest magnitude the dz kernel recorded for the chunk lies outside the
+// band where the unscaled copy is exact and finite (kw != 0); rows from
+// `rows` to ntv * 256 are zero (their dz columns are zero).  Otherwise every
+// workgroup returns at once.
+__global__ __launch_bounds__(256) void w_rescale(const uint16_t* __restrict__ W, int rows, int total_rows, int H,
+                                                 const uint32_t* __restrict__ wmag, uint16_t* __restrict__ w16) {
+  const int kw = w_scale_exp(*wmag);
+  if (kw == 0) return;
+  const int64_t n8 = (int64_t)total_rows * H / 8;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    const int64_t row = i * 8 / H;
+    u32x4 o = u32x4{0u, 0u, 0u, 0u};
+    if (row < rows) {
+      const u32x4 x = reinterpret_cast<const u32x4*>(W)[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = ldexpf(__builtin_bit_cast(float, x[e] << 16), kw);
+        const float hi = ldexpf(__builtin_bit_cast(float, x[e] & 0xffff0000u), kw);
+        o[e] = __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2{lo, hi}, f16x2));
+      }
+    }
+    reinterpret_cast<u32x4*>(w16)[i] = o;
   }
 }
 
@@ -852,8 +1008,8 @@ constexpr int WBM = kDwTileM, WBN = kDwTileN, WKT = 32, WNST = 4, WDSTEPS = 1;
 
 template <int NW>
 __global__ __launch_bounds__(64 * NW, 1) void dw_gemm(DwParams p) {
-  // NW = 4: waves 2 x 2, 128 x 128 each; NW = 8: waves 4 (m) x 2 (n), 64 x 128
-  // each (A, read transposed, is the operand with fewer fragments)
+  // NW = 8 (kDwWaves): waves 4 (m) x 2 (n), 64 x 128 each (A, read
+  // transposed, is the operand with fewer fragments)
   constexpr int WGN = 2, WGM = NW / WGN;
   using TA = MN<WBM, NW, WKT>;
   using TB = KM<WBN, NW, WKT>;
@@ -874,7 +1030,8 @@ __global__ __launch_bounds__(64 * NW, 1) void dw_gemm(DwParams p) {
   tb.init(p.hT + (int64_t)n0 * p.ldT, p.ldT, p.H - n0, lane, __builtin_amdgcn_readfirstlane(w));
   gemm_loop<TA, TB, f16x8, false, WNST, false, WDSTEPS>(acc, p.ldT / WKT, lds, ta, tb, 0, tid, wm * (WBM / WGM),
                                                        wn * (WBN / WGN));
-  const float inv = p.gscale[1];
+  // undo both operand scales at once (exact: a power of two)
+  const int unscale = -((int)p.scales[kScaleKs] + h_scale_exp(p.scales[kScaleHmag]));
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
     const int n = n0 + wn * (WBN / WGN) + fn * 32 + (lane & 31);
@@ -886,7 +1043,7 @@ __global__ __launch_bounds__(64 * NW, 1) void dw_gemm(DwParams p) {
         const int m = m0 + wm * (WBM / WGM) + fm * 32 + frag_row(i, lane);
         if (m < p.width) {
           float* o = p.dW + (int64_t)m * p.H + n;
-          const float d = acc[fm][fn][i] * inv;
+          const float d = ldexpf(acc[fm][fn][i], unscale);
           *o = p.accumulate ? *o + d : d;
         }
       }
@@ -908,7 +1065,7 @@ constexpr int HBM = kDhTileM, HBN = kDhTileN, HKT = 64, HNST = 3, HDSTEPS = 3;
 
 template <int NW>
 __global__ __launch_bounds__(64 * NW, 1) void dh_gemm(DhParams p) {
-  // NW = 4: waves 2 x 2, 128 x 64 each; NW = 8: waves 4 (m) x 2 (n), 64 x 64 each
+  // NW = 4 (kDhWaves): waves 2 x 2, 128 x 64 each
   constexpr int HGM = NW / 2, HGN = 2;
   using TA = KM<HBM, NW, HKT>;
   using TB = MN<HBN, NW, HKT>;
@@ -943,7 +1100,8 @@ __global__ __launch_bounds__(64 * NW, 1) void dh_gemm(DhParams p) {
         for (int i = 0; i < 16; ++i) tot[fm][fn][i] = k0 == 0 ? acc[fm][fn][i] : tot[fm][fn][i] + acc[fm][fn][i];
     k0 = k1;
   }
-  const float inv = p.gscale[1];
+  // undo both operand scales at once (exact: a power of two)
+  const int unscale = -((int)p.scales[kScaleKs] + w_scale_exp(*p.wmag));
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
     const int n = n0 + wn * (HBN / HGN) + fn * 32 + (lane & 31);
@@ -955,7 +1113,7 @@ __global__ __launch_bounds__(64 * NW, 1) void dh_gemm(DhParams p) {
         const int m = m0 + wm * (HBM / HGM) + fm * 32 + frag_row(i, lane);
         if (m < p.N) {
           float* o = p.dh + (int64_t)m * p.H + n;
-          const float d = tot[fm][fn][i] * inv;
+          const float d = ldexpf(tot[fm][fn][i], unscale);
           *o = p.accumulate ? *o + d : d;
         }
       }
@@ -1054,6 +1212,115 @@ __global__ __launch_bounds__(256) void bwd_rows_logits(const float* __restrict__
     d = g * ex2(fmaf(a, kL2E, -(lse_s * kL2E))) * ((a - b) - ((lse_s - lse_t) + L));
   }
   dz[(int64_t)n * V + v] = d;
+}
+
+// ===========================================================================
+// Top-k estimator of the reverse KL (NeMo-RL page, summary: the K = V limit
+// of the top-k estimator, whose score-function tail vanishes once the
+// support spans the vocabulary).  Per row t, support ids S[t, 0..K) (ids
+// outside [0, V) are skipped), teacher log-probabilities lpt_S on them and
+// lpt_y at the sampled token y, f = log p_s - log p_t:
+//   L_hat = sum_{j in S} p_j f_j + [y not in S] f_y,
+//   dz_j  = g (-p_j c + [j in S] p_j (f_j + 1) + [j = y, y not in S] sp),
+//   c = sum_{j in S} p_j (f_j + 1) + [y not in S] sp,   sp = f_y + 1.
+// The student logits on the support come from a wave-wide dot product of
+// the row of h with the support's rows of W (fp32, fixed reduction order, so
+// the backward recomputes exactly the forward's values).
+// ===========================================================================
+__device__ __forceinline__ float wave_dot_bf16(const uint16_t* __restrict__ a, const uint16_t* __restrict__ b, int H,
+                                               int lane) {
+  float acc = 0.f;
+  for (int c = lane * 8; c < H; c += 512) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(a + c);
+    const u32x4 w = *reinterpret_cast<const u32x4*>(b + c);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      acc = fmaf(__builtin_bit_cast(float, x[e] << 16), __builtin_bit_cast(float, w[e] << 16), acc);
+      acc = fmaf(__builtin_bit_cast(float, x[e] & 0xffff0000u), __builtin_bit_cast(float, w[e] & 0xffff0000u), acc);
+    }
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
+  return acc;
+}
+
+// One wave per row.  stats on entry: (lse, -, log p(y), -) from the
+// log-probability forward; on exit (lse, c, sp, bound) with bound = |c| + |sp|
+// + max_{j in S} p_j |f_j + 1| >= max_j |dz_j| / |g| (for the backward's fp16
+// scale).  Rows with row_mask 0: loss 0, stats 0.
+__global__ __launch_bounds__(256) void topk_terms(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
+                                                  int N, int V, int H, int K, const int32_t* __restrict__ y,
+                                                  const int32_t* __restrict__ S, const float* __restrict__ lpt_S,
+                                                  const float* __restrict__ lpt_y,
+                                                  const uint8_t* __restrict__ row_mask, float* __restrict__ loss,
+                                                  float* __restrict__ stats) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= N) return;
+  float* st = stats + 4 * (int64_t)t;
+  if (row_mask && row_mask[t] == 0) {
+    if (lane == 0) {
+      loss[t] = 0.f;
+      st[0] = 0.f; st[1] = 0.f; st[2] = 0.f; st[3] = 0.f;
+    }
+    return;
+  }
+  const float lse = st[0], lpy = st[2];
+  const int yt = y[t];
+  float L = 0.f, c = 0.f, bnd = 0.f;
+  bool in = false;
+  for (int k = 0; k < K; ++k) {
+    const int j = S[(int64_t)t * K + k];
+    if (j < 0 || j >= V) continue;
+    const float lp = wave_dot_bf16(h + (int64_t)t * H, W + (int64_t)j * H, H, lane) - lse;
+    const float f = lp - lpt_S[(int64_t)t * K + k];
+    const float pr = expf(lp);
+    L = fmaf(pr, f, L);
+    c = fmaf(pr, f + 1.f, c);
+    bnd = fmaxf(bnd, pr * fabsf(f + 1.f));
+    in = in || j == yt;
+  }
+  float sp = 0.f;
+  if (!in) {
+    const float fy = lpy - lpt_y[t];
+    L += fy;
+    sp = fy + 1.f;
+    c += sp;
+  }
+  if (lane == 0) {
+    loss[t] = L;
+    st[1] = c;
+    st[2] = sp;
+    st[3] = fabsf(c) + fabsf(sp) + bnd;
+  }
+}
+
+// One wave per row: for each support id j in the chunk [c0, c0 + width), add
+// s g p_j (f_j + 1) to the row's fp16 dz entry (lane 0, in support order, so
+// repeated ids add up), saturating at fp16's largest finite value.
+__global__ __launch_bounds__(256) void topk_dz_add(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
+                                                   int N, int V, int H, int K, const int32_t* __restrict__ S,
+                                                   const float* __restrict__ lpt_S,
+                                                   const uint8_t* __restrict__ row_mask,
+                                                   const float* __restrict__ grad, const float* __restrict__ stats,
+                                                   const uint32_t* __restrict__ scales, uint16_t* __restrict__ dz,
+                                                   int ldz, int c0, int width) {
+  const int lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= N || (row_mask && row_mask[t] == 0)) return;
+  const float gs = (grad ? grad[t] : 1.0f) * __builtin_bit_cast(float, scales[kScaleS]);
+  const float lse = stats[4 * (int64_t)t];
+  for (int k = 0; k < K; ++k) {
+    const int j = S[(int64_t)t * K + k];
+    if (j < 0 || j >= V || j < c0 || j >= c0 + width) continue;
+    const float lp = wave_dot_bf16(h + (int64_t)t * H, W + (int64_t)j * H, H, lane) - lse;
+    const float f = lp - lpt_S[(int64_t)t * K + k];
+    if (lane == 0) {
+      uint16_t* e = dz + (int64_t)t * ldz + (j - c0);
+      const float v = (float)__builtin_bit_cast(_Float16, *e) + gs * expf(lp) * (f + 1.f);
+      *e = __builtin_bit_cast(uint16_t, (_Float16)__builtin_amdgcn_fmed3f(v, -65504.f, 65504.f));
+    }
+  }
 }
 
 // ===========================================================================
@@ -1172,8 +1439,9 @@ static inline unsigned grid1(int64_t n, int64_t per, int64_t cap) {
   return (unsigned)g;
 }
 
-template <int NW>
-static void fwd_tiles_launch(const FwdParams& p, int mode, unsigned nb, hipStream_t s) {
+hipError_t launch_fwd_tiles(const FwdParams& p, int mode, hipStream_t s) {
+  const unsigned nb = (unsigned)(p.nsplit * p.ntok);
+  constexpr int NW = kFusedWaves;
   constexpr unsigned nt = Fused<NW>::kThreads;
   if (mode == kModeHidden)
     fwd_tiles<kModeHidden, true, NW><<<nb, nt, 0, s>>>(p);
@@ -1185,14 +1453,6 @@ static void fwd_tiles_launch(const FwdParams& p, int mode, unsigned nb, hipStrea
     fwd_tiles<kModeTeacherLogits, true, NW><<<nb, nt, 0, s>>>(p);
   else
     fwd_tiles<kModeTeacherLogits, false, NW><<<nb, nt, 0, s>>>(p);
-}
-
-hipError_t launch_fwd_tiles(const FwdParams& p, int mode, int waves, hipStream_t s) {
-  const unsigned nb = (unsigned)(p.nsplit * p.ntok);
-  if (waves == 8)
-    fwd_tiles_launch<8>(p, mode, nb, s);
-  else
-    fwd_tiles_launch<4>(p, mode, nb, s);
   return hipGetLastError();
 }
 
@@ -1212,8 +1472,9 @@ hipError_t launch_fwd_merge(const float* partial, int nsplit, int N, float* merg
   return hipGetLastError();
 }
 
-template <int NW>
-static void bwd_dz_launch(const BwdParams& p, int mode, unsigned nb, hipStream_t s) {
+hipError_t launch_bwd_dz(const BwdParams& p, int mode, hipStream_t s) {
+  const unsigned nb = (unsigned)(p.ngroups * p.ntok);
+  constexpr int NW = kFusedWaves;
   constexpr unsigned nt = Fused<NW>::kThreads;
   if (mode == kModeHidden)
     bwd_dz_tiles<kModeHidden, true, NW><<<nb, nt, 0, s>>>(p);
@@ -1221,50 +1482,67 @@ static void bwd_dz_launch(const BwdParams& p, int mode, unsigned nb, hipStream_t
     bwd_dz_tiles<kModeHiddenTeachers, true, NW><<<nb, nt, 0, s>>>(p);
   else if (mode == kModeLogprobEntropy)
     bwd_dz_tiles<kModeLogprobEntropy, true, NW><<<nb, nt, 0, s>>>(p);
+  else if (mode == kModeTopK)
+    bwd_dz_tiles<kModeTopK, true, NW><<<nb, nt, 0, s>>>(p);
   else if (p.V % 4 == 0)
     bwd_dz_tiles<kModeTeacherLogits, true, NW><<<nb, nt, 0, s>>>(p);
   else
     bwd_dz_tiles<kModeTeacherLogits, false, NW><<<nb, nt, 0, s>>>(p);
-}
-
-hipError_t launch_bwd_dz(const BwdParams& p, int mode, int waves, hipStream_t s) {
-  const unsigned nb = (unsigned)(p.ngroups * p.ntok);
-  if (waves == 8)
-    bwd_dz_launch<8>(p, mode, nb, s);
-  else
-    bwd_dz_launch<4>(p, mode, nb, s);
   return hipGetLastError();
 }
 
 hipError_t launch_grad_scale(const float* grad, const float* grad_h, const uint8_t* row_mask, const float* stats,
-                             int N, bool logprob_entropy, float* out, hipStream_t s) {
-  if (logprob_entropy)
-    grad_scale<true><<<1, 1024, 0, s>>>(grad, grad_h, row_mask, stats, N, out);
+                             int N, int mode, int nchunks, uint32_t* scales, hipStream_t s) {
+  if (mode == kModeLogprobEntropy)
+    grad_scale<kModeLogprobEntropy><<<1, 1024, 0, s>>>(grad, grad_h, row_mask, stats, N, nchunks, scales);
+  else if (mode == kModeTopK)
+    grad_scale<kModeTopK><<<1, 1024, 0, s>>>(grad, grad_h, row_mask, stats, N, nchunks, scales);
   else
-    grad_scale<false><<<1, 1024, 0, s>>>(grad, grad_h, row_mask, stats, N, out);
+    grad_scale<kModeHidden><<<1, 1024, 0, s>>>(grad, grad_h, row_mask, stats, N, nchunks, scales);
   return hipGetLastError();
 }
 
-hipError_t launch_transpose_h(const uint16_t* h, int N, int H, uint16_t* hT, int ldT, hipStream_t s) {
+hipError_t launch_topk_terms(const uint16_t* h, const uint16_t* W, int N, int V, int H, int K, const int32_t* y,
+                             const int32_t* S, const float* lpt_S, const float* lpt_y, const uint8_t* row_mask,
+                             float* loss, float* stats, hipStream_t s) {
+  topk_terms<<<(unsigned)((N + 3) / 4), 256, 0, s>>>(h, W, N, V, H, K, y, S, lpt_S, lpt_y, row_mask, loss, stats);
+  return hipGetLastError();
+}
+
+hipError_t launch_topk_dz_add(const uint16_t* h, const uint16_t* W, int N, int V, int H, int K, const int32_t* S,
+                              const float* lpt_S, const uint8_t* row_mask, const float* grad, const float* stats,
+                              const uint32_t* scales, uint16_t* dz, int ldz, int c0, int width, hipStream_t s) {
+  topk_dz_add<<<(unsigned)((N + 3) / 4), 256, 0, s>>>(h, W, N, V, H, K, S, lpt_S, row_mask, grad, stats, scales, dz,
+                                                      ldz, c0, width);
+  return hipGetLastError();
+}
+
+hipError_t launch_absmax_bf16(const uint16_t* h, int64_t n, uint32_t* scales, hipStream_t s) {
+  absmax_bf16<<<grid1(n / 8 + 1, 256 * 4, 256), 256, 0, s>>>(h, n, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_transpose_h(const uint16_t* h, int N, int H, const uint32_t* scales, uint16_t* hT, int ldT,
+                              hipStream_t s) {
   dim3 g((unsigned)(ldT / 64), (unsigned)(H / 64));
-  transpose_h<<<g, 256, 0, s>>>(h, N, H, hT, ldT);
+  transpose_h<<<g, 256, 0, s>>>(h, N, H, scales, hT, ldT);
   return hipGetLastError();
 }
 
-hipError_t launch_dw(const DwParams& p, int waves, hipStream_t s) {
-  if (waves == 8)
-    dw_gemm<8><<<(unsigned)(p.ntm * p.ntn), 512, 0, s>>>(p);
-  else
-    dw_gemm<4><<<(unsigned)(p.ntm * p.ntn), 256, 0, s>>>(p);
+hipError_t launch_w_rescale(const uint16_t* W_chunk, int rows, int ntv, int H, const uint32_t* wmag, uint16_t* w16,
+                            hipStream_t s) {
+  const int64_t n8 = (int64_t)ntv * kFwdTileV * H / 8;
+  w_rescale<<<grid1(n8, 256 * 4, 2048), 256, 0, s>>>(W_chunk, rows, ntv * kFwdTileV, H, wmag, w16);
   return hipGetLastError();
 }
 
-hipError_t launch_dh(const DhParams& p, int waves, hipStream_t s) {
-  const unsigned nb = (unsigned)(p.ntm * p.ntn);
-  if (waves == 8)
-    dh_gemm<8><<<nb, 512, 0, s>>>(p);
-  else
-    dh_gemm<4><<<nb, 256, 0, s>>>(p);
+hipError_t launch_dw(const DwParams& p, hipStream_t s) {
+  dw_gemm<kDwWaves><<<(unsigned)(p.ntm * p.ntn), 64 * kDwWaves, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_dh(const DhParams& p, hipStream_t s) {
+  dh_gemm<kDhWaves><<<(unsigned)(p.ntm * p.ntn), 64 * kDhWaves, 0, s>>>(p);
   return hipGetLastError();
 }
 

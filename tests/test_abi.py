@@ -22,7 +22,8 @@ MISALIGNED = ctypes.c_void_p(0x10002)
 
 
 def declared_functions():
-    src = open(HEADER).read()
+    inc = os.path.dirname(HEADER)
+    src = "".join(open(os.path.join(inc, f)).read() for f in sorted(os.listdir(inc)) if f.endswith(".h"))
     src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
     return sorted(set(re.findall(r"\b(rkl_[a-z_]+)\s*\(", src)))
 

@@ -187,23 +187,39 @@ def test_hidden_multi_chunk_backward(tdev, monkeypatch):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), what
 
 
-@pytest.mark.parametrize("orders", [("1,1", "1,1", "1"), ("3,5", "7,2", "3"), ("64,64", "2,3", "64")],
+@pytest.mark.parametrize("orders", [("1,1", "1,1", "1", "1"), ("3,5", "7,2", "3", "3"), ("64,64", "2,3", "64", "64")],
                          ids=["one_by_one", "ragged_panels", "oversized"])
 def test_tile_order_and_grouping_do_not_change_results(tdev, monkeypatch, orders):
-    """The workgroup order (panel sizes GS x TG) and the vocabulary tiles per
-    backward workgroup only reorder independent work: results are bitwise
-    those of the default settings, for ragged token and vocabulary tails."""
+    """The workgroup orders (the fused kernels' panel sizes GS x TG, the dh
+    GEMM's column tiles per panel) and the vocabulary tiles per backward
+    workgroup only reorder independent work: results are bitwise those of the
+    default settings, for ragged token and vocabulary tails (Hs = 640: five
+    dh column tiles, so panels of 3 leave a ragged last panel)."""
     torch, dev = tdev
-    case = synth.random_case(77, T=700, V=5003, Hs=128, Ht=192, p_mask=0.8, with_grad=True)
+    case = synth.random_case(77, T=700, V=5003, Hs=640, Ht=192, p_mask=0.8, with_grad=True)
     say("orders", orders, case.T, case.V)
     ref = _run_hidden(case, dev, g=case.grad)
-    fo, bo, bt = orders
+    fo, bo, bt, dp = orders
     monkeypatch.setenv("RKL_FWD_ORDER", fo)
     monkeypatch.setenv("RKL_BWD_ORDER", bo)
     monkeypatch.setenv("RKL_BWD_TILES", bt)
+    monkeypatch.setenv("RKL_DH_PANEL", dp)
     got = _run_hidden(case, dev, g=case.grad)
     for a, b, what in zip(got[1:], ref[1:], ("loss", "stats", "dh", "dW")):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), what
+
+
+@pytest.mark.parametrize("tiles", [1, 5, 40])
+def test_forward_split_sizes(tdev, monkeypatch, tiles):
+    """Vocabulary tiles per forward split (1: one split per 256-row tile; 5: a
+    ragged last split; 40: one split over the whole vocabulary): the split
+    plan changes only the order of the log-sum-exp merges, so every setting
+    matches the oracle."""
+    torch, dev = tdev
+    monkeypatch.setenv("RKL_FWD_TILES", str(tiles))
+    case = synth.random_case(79, T=300, V=9001, Hs=128, Ht=192, p_mask=0.7, with_grad=True)
+    say("forward split", tiles, case.T, case.V)
+    _check_against_oracle(case, _run_hidden(case, dev, g=case.grad), g=case.grad)
 
 
 @pytest.mark.parametrize("chunk", [256, 768])
