@@ -33,7 +33,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librkl.so")
-SOURCES = ["rkl_kernels.hip", "rkl_api.hip"]
+SOURCES = ["rkl_kernels.hip", "rkl_api.hip", "rkl_noalloc.hip"]
 ARCH = "gfx950"
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 HOST_NOISE = "'-packed-fp32-ops' is not a recognized feature"

@@ -390,6 +390,11 @@ int combine_shards(int64_t G, int64_t N, const float* partials, const uint8_t* r
 
 }  // namespace
 
+int rkl::set_last_error(int code, const char* msg) {
+  g_err = msg;
+  return code;
+}
+
 // The library is built with hidden visibility; only the C ABI is exported.
 #pragma GCC visibility push(default)
 extern "C" {

@@ -120,6 +120,9 @@ enum Mode : int {
   kModeTopK = 4,            // top-k estimator's backward: dense part -p c + spike at the sampled token
 };
 
+// Sets the calling thread's rkl_last_error message; returns code.
+int set_last_error(int code, const char* msg);
+
 hipError_t launch_fwd_tiles(const FwdParams& p, int mode, hipStream_t s);
 // out0: loss (reverse KL) or log p(y); out1: entropy (log-probability / entropy only)
 hipError_t launch_fwd_combine(const float* partial, int nsplit, int N, const uint8_t* row_mask, bool logprob_entropy,
