@@ -22,6 +22,10 @@ same student tensors.
 weights and a teacher chosen per row (--teacher-order grouped: K contiguous
 runs of rows; interleaved: i.i.d. ids, so every tile holds several teachers).
 
+--workload topk times the top-k estimator of the reverse KL on the same
+student tensors: the teacher's payload is its log-probabilities at its --topk
+K largest logits and at a sampled token per row.
+
 --workload vocab_shard times one rank's share of a --shards G-way
 vocabulary-parallel step on the same tensors: the shard forward over its
 V/G vocabulary rows, the merge of all G shards' partials (the other shards'
@@ -42,7 +46,7 @@ Prints one JSON line:
                traffic per launch from the committed counter record while
                the kernel sources are unchanged;
   cpu_baseline = the fp64 oracle on a bounded row sample on the host cores
-               (reverse-KL and log-probability / entropy workloads).
+               (reverse-KL, log-probability / entropy and top-k workloads).
 """
 from __future__ import annotations
 
@@ -61,9 +65,9 @@ PEAK_BF16 = 256 * 4096 * 2.4e9
 HBM_PEAK = 8.0e12
 DTYPE = "bf16 projections; fp16 dz/dh/dW GEMM operands (power-of-two scaled); fp32 accumulation"
 
-FWD_KERNELS = ("fwd_tiles", "fwd_combine", "fwd_rows_logits")
+FWD_KERNELS = ("fwd_tiles", "fwd_combine", "fwd_rows_logits", "topk_terms")
 BWD_KERNELS = ("grad_scale", "absmax_bf16", "transpose_h", "bwd_dz_tiles", "w_rescale", "dw_gemm", "dh_gemm",
-               "bwd_rows_logits")
+               "bwd_rows_logits", "topk_dz_add")
 MFMA_KERNELS = ("fwd_tiles", "bwd_dz_tiles", "dw_gemm", "dh_gemm")
 
 
@@ -78,11 +82,12 @@ def parse():
                     help="only run a plain 1 GiB device-to-device copy (counter calibration)")
     ap.add_argument("--payload", choices=("hidden", "logits"), default="hidden",
                     help="teacher payload: hidden states (default, the headline) or fp32 logits [N, V]")
-    ap.add_argument("--workload", choices=("reverse_kl", "logprob_entropy", "teachers", "vocab_shard"),
+    ap.add_argument("--workload", choices=("reverse_kl", "logprob_entropy", "teachers", "vocab_shard", "topk"),
                     default="reverse_kl",
                     help="reverse KL distillation step (default, the headline), log-probability + entropy, "
-                         "reverse KL with a teacher chosen per row, or one rank's share of a vocabulary-parallel "
-                         "step")
+                         "reverse KL with a teacher chosen per row, one rank's share of a vocabulary-parallel "
+                         "step, or the top-k estimator")
+    ap.add_argument("--topk", type=int, default=64, help="support size K for --workload topk")
     ap.add_argument("--shards", type=int, default=8, help="vocabulary shards for --workload vocab_shard")
     ap.add_argument("--teachers", type=int, default=4, help="teachers for --workload teachers")
     ap.add_argument("--teacher-order", choices=("grouped", "interleaved"), default="grouped",
@@ -542,6 +547,87 @@ def bench_logprob_entropy(args):
     print(json.dumps(out), flush=True)
 
 
+def cpu_baseline_topk(case, y, S, lpt_S, lpt_y, target_s: float):
+    """Time the fp64 top-k estimator oracle (forward + backward) on a bounded row sample."""
+    from oracle import rkl_oracle as O
+    from oracle import topk_oracle as TK
+    W = O.widen_bf16(case.W_s)
+
+    def run(nrows):
+        h = O.widen_bf16(case.h_s[:nrows])
+        t0 = time.perf_counter()
+        TK.forward_backward(h, W, y[:nrows], S[:nrows], lpt_S[:nrows], lpt_y[:nrows])
+        return time.perf_counter() - t0
+
+    n, t = grow_sample(run, target_s, min(4096, case.T), step=16)
+    out = {"value": n / t, "unit": "masked tokens/s", "cores": int(blas_threads()), "kind": "oracle",
+           "sample": f"fp64 numpy oracle, top-k estimator forward+backward (L, dz, dh, dW) over the first {n} of "
+                     f"the {case.T} positions of this workload, K={S.shape[1]}, full V={case.V}; {t:.1f} s wall; "
+                     f"bf16->fp64 widening of the weight done once outside the timed region"}
+    out.update(host_info())
+    return out
+
+
+def bench_topk(args):
+    """The top-k estimator on the headline student tensors: the teacher's
+    log-probabilities on its top K logits and at the sampled token."""
+    import numpy as np
+    import torch
+    import lm_head_reverse_amd as R
+    import synth
+
+    R.lib()
+    dev = torch.device("cuda:0")
+    K = args.topk
+    print(f"[bench] generating inputs (K = {K})", file=sys.stderr, flush=True)
+    case = synth.config("headline")
+    T, V, H = case.T, case.V, case.Hs
+    h_all, W = bf16_dev(case.h_s, dev), bf16_dev(case.W_s, dev)
+    # teacher payload (input preparation, outside the timed region): log-probabilities of the
+    # teacher logits h_t W_t^T at its K largest logits and at the sampled token
+    with torch.no_grad():
+        z_t = bf16_dev(case.h_t, dev).float() @ bf16_dev(case.W_t, dev).float().t()
+        lpt = torch.log_softmax(z_t, dim=1)
+        del z_t
+        S_all = torch.topk(lpt, K, dim=1).indices.to(torch.int32).contiguous()
+        lptS_all = torch.gather(lpt, 1, S_all.long()).contiguous()
+        y_np = synth.sampled_tokens(3, T, V)
+        y_all = torch.from_numpy(y_np).to(dev)
+        lpty_all = torch.gather(lpt, 1, y_all.long()[:, None])[:, 0].contiguous()
+        del lpt
+    mask = torch.from_numpy(case.mask).to(dev)
+    N_expected = int(case.mask.sum())
+    g_all = torch.full((T,), 1.0 / N_expected, dtype=torch.float32, device=dev)
+    dW = torch.empty((V, H), dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+
+    def step():
+        idx, N = R.compact_rows(mask)
+        h, y = R.gather_rows(h_all, idx), R.gather_rows(y_all, idx)
+        S, lS, ly = R.gather_rows(S_all, idx), R.gather_rows(lptS_all, idx), R.gather_rows(lpty_all, idx)
+        g = R.gather_rows(g_all, idx)
+        loss, stats = R.forward_topk(h, W, y, S, lS, ly)
+        loss_pos = R.scatter_rows(loss, idx, T)
+        dh, _ = R.backward_topk(h, W, y, S, lS, stats, grad_loss=g, dW=dW)
+        R.scatter_rows(dh, idx, T)
+        return N, loss_pos
+
+    N, wall, times = run_timed(step, args)
+    assert N == N_expected
+    work = rkl_work(N, V, H, 0)
+    config = {"workload": f"Qwen3-1.7B-shaped student, top-k estimator with the teacher's top {K} log-probabilities "
+                          f"and uniform sampled tokens, B=4 S=1025 (T=N=4096 trainable), H=2048, V=151936",
+              "B": case.B, "S": case.S, "N": int(N), "H": H, "V": V, "K": K, "parallelism": "single GPU"}
+    out = emit(args, "masked tokens/sec fwd+bwd top-k estimator of the reverse KL (H2048,V152k); MFMA % peak", N,
+               wall, times, work, 2.0 * N * V * H, 8.0 * N * V * H, config)
+    if not args.no_cpu_baseline:
+        print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline_topk(case, y_np, S_all.cpu().numpy().astype(np.int64),
+                                                lptS_all.cpu().numpy().astype(np.float64),
+                                                lpty_all.cpu().numpy().astype(np.float64), args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
 def bench_teachers(args):
     """Reverse KL on the headline tensors with K teachers chosen per row."""
     import torch
@@ -655,7 +741,7 @@ def main():
               f"the multi-GPU sharding is described but not built", file=sys.stderr)
         sys.exit(2)
     {"reverse_kl": bench_reverse_kl, "logprob_entropy": bench_logprob_entropy, "teachers": bench_teachers,
-     "vocab_shard": bench_vocab_shard}[args.workload](args)
+     "vocab_shard": bench_vocab_shard, "topk": bench_topk}[args.workload](args)
 
 
 if __name__ == "__main__":

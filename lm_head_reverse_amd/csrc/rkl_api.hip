@@ -153,6 +153,24 @@ Split fwd_split(int64_t V) {
   return Split{(int)tps, (int)ceil_div(ntv, tps)};
 }
 
+// Splits per forward workgroup: enough that the grid is one workgroup per CU
+// for each token tile's share (256 CUs), so that a workgroup streams many
+// vocabulary tiles without restarting its pipeline.  Measured at N = 4096,
+// H = 2048, V = 151936 (8 groups of 25 splits per token tile, 256
+// workgroups): 4444 us per forward against 4549 us with one split per
+// workgroup; one 75-tile split per workgroup (a different split plan, same
+// grid) took 4427 us, so the 24 extra statistics flushes cost ~0.4 %.  Does
+// not change results.  RKL_FWD_SPLITS_PER_WG overrides it.
+int fwd_splits_per_wg(int nsplit, int64_t ntok) {
+  if (const char* s = std::getenv("RKL_FWD_SPLITS_PER_WG")) {
+    const int v = std::atoi(s);
+    if (v >= 1) return v < nsplit ? v : nsplit;
+  }
+  const int64_t groups_per_tile = ceil_div(256, ntok < 1 ? 1 : ntok);
+  const int64_t spw = ceil_div(nsplit, groups_per_tile);
+  return (int)(spw < 1 ? 1 : spw);
+}
+
 size_t fwd_ws_bytes(int64_t N, int64_t V, bool tiled) {
   if (!tiled) return 0;
   return align256((size_t)fwd_split(V).nsplit * 5 * (size_t)N * sizeof(float));
@@ -281,6 +299,7 @@ int forward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* 
   p.tiles_per_split = sp.tiles_per_split;
   p.nsplit = sp.nsplit;
   p.ntok = (int)ceil_div(N, rkl::kFwdTileN);
+  p.splits_per_wg = fwd_splits_per_wg(p.nsplit, p.ntok);
   p.order_gs = fwd_order().gs;
   p.order_tg = fwd_order().tg;
   const int mode = mode_of(z_t, y, tch.teacher);

@@ -21,6 +21,7 @@ struct FwdParams {
   float* partial;          // [nsplit][5][N]
   int tiles_per_split;     // 256-row vocabulary tiles per split
   int nsplit;
+  int splits_per_wg;       // consecutive splits one workgroup streams through
   int ntok;                // 128-token tiles
   int order_gs, order_tg;  // workgroup order (panel_order)
 };

@@ -26,17 +26,21 @@ constexpr float kNegBig = -1.0e30f;   // "no value seen yet" running max; exp2 o
 __device__ __forceinline__ float ex2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // Merge of two partial (max, sum of exp(z - max), sum of exp(z - max) * d) triples.
+// The sums are written as explicit fmas: left to the compiler, s f1 + s2 f2
+// may be contracted one way for the student's sum and the other way for the
+// teacher's, and identical logits would then no longer give bit-identical
+// log-normalisers (nor a loss of exactly zero).
 __device__ __forceinline__ void merge3(float& m, float& s, float& a, float m2, float s2, float a2) {
   const float M = fmaxf(m, m2);
   const float f1 = ex2((m - M) * kL2E), f2 = ex2((m2 - M) * kL2E);
-  s = s * f1 + s2 * f2;
-  a = a * f1 + a2 * f2;
+  s = fmaf(s, f1, s2 * f2);
+  a = fmaf(a, f1, a2 * f2);
   m = M;
 }
 __device__ __forceinline__ void merge2(float& m, float& s, float m2, float s2) {
   const float M = fmaxf(m, m2);
   const float f1 = ex2((m - M) * kL2E), f2 = ex2((m2 - M) * kL2E);
-  s = s * f1 + s2 * f2;
+  s = fmaf(s, f1, s2 * f2);
   m = M;
 }
 
@@ -429,20 +433,75 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void fwd_tiles(FwdParams p)
   __shared__ __attribute__((aligned(16))) float red[F::kRedFloats];
   __shared__ uint32_t tset_lds;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
-  const int logical = xcd_logical(blockIdx.x, p.nsplit * p.ntok);
-  int split, tt;
-  panel_order(logical, p.nsplit, p.ntok, p.order_gs, p.order_tg, split, tt);
+  // a workgroup takes splits [split0, split1) of token tile tt: their
+  // vocabulary tiles form one stream, and each split's statistics are
+  // written when its last tile is folded (the split plan, and so every
+  // result bit, does not depend on how splits are grouped)
+  const int ngroup = (p.nsplit + p.splits_per_wg - 1) / p.splits_per_wg;
+  const int logical = xcd_logical(blockIdx.x, ngroup * p.ntok);
+  int grp, tt;
+  panel_order(logical, ngroup, p.ntok, p.order_gs, p.order_tg, grp, tt);
   const int n0 = tt * FBN;
   const int ntv = (p.V + FBM - 1) / FBM;
-  const int vt0 = split * p.tiles_per_split;
-  const int vt1 = min(vt0 + p.tiles_per_split, ntv);
+  const int split0 = grp * p.splits_per_wg;
+  const int vt0 = split0 * p.tiles_per_split;
+  const int vt1 = min(min(split0 + p.splits_per_wg, p.nsplit) * p.tiles_per_split, ntv);
 
+  const int arow0 = wm * (FBM / F::kWM), brow0 = wn * (FBN / 2);
   float ms[FFN], ss[FFN], aa[FFN], mt[FFN], st[FFN];
+  auto reset = [&]() {
 #pragma unroll
-  for (int fn = 0; fn < FFN; ++fn) { ms[fn] = kNegBig; ss[fn] = 0.f; aa[fn] = 0.f; mt[fn] = kNegBig; st[fn] = 0.f; }
+    for (int fn = 0; fn < FFN; ++fn) { ms[fn] = kNegBig; ss[fn] = 0.f; aa[fn] = 0.f; mt[fn] = kNegBig; st[fn] = 0.f; }
+  };
+  reset();
+
+  // One split's statistics: merge the two row halves of each 32x32 block
+  // (lanes l and l^32), then the waves that hold the same tokens (wm = 1 ..
+  // kWM-1 into wm = 0, in that order, through LDS), and write the partial.
+  // Every thread calls it; the barriers wait for LDS only, so the DMA of the
+  // next tiles stays in flight.
+  auto flush = [&](int split) {
+#pragma unroll
+    for (int fn = 0; fn < FFN; ++fn) {
+      const float oms = __shfl_xor(ms[fn], 32), oss = __shfl_xor(ss[fn], 32), oaa = __shfl_xor(aa[fn], 32);
+      const float omt = __shfl_xor(mt[fn], 32), ost = __shfl_xor(st[fn], 32);
+      merge3(ms[fn], ss[fn], aa[fn], oms, oss, oaa);
+      merge2(mt[fn], st[fn], omt, ost);
+    }
+    if (wm > 0 && lane < 32) {
+#pragma unroll
+      for (int fn = 0; fn < FFN; ++fn) {
+        float* q = red + ((((wm - 1) * 2 + wn) * FFN + fn) * 32 + lane) * 5;
+        q[0] = ms[fn]; q[1] = ss[fn]; q[2] = aa[fn]; q[3] = mt[fn]; q[4] = st[fn];
+      }
+    }
+    dma_barrier<63>();
+    if (wm == 0 && lane < 32) {
+#pragma unroll
+      for (int fn = 0; fn < FFN; ++fn) {
+#pragma unroll
+        for (int r = 1; r < F::kWM; ++r) {
+          const float* q = red + ((((r - 1) * 2 + wn) * FFN + fn) * 32 + lane) * 5;
+          merge3(ms[fn], ss[fn], aa[fn], q[0], q[1], q[2]);
+          merge2(mt[fn], st[fn], q[3], q[4]);
+        }
+        const int n = n0 + brow0 + fn * 32 + lane;
+        if (n < p.N) {
+          float* P = p.partial + (int64_t)split * 5 * p.N + n;
+          P[0] = ms[fn];
+          P[(int64_t)1 * p.N] = ss[fn];
+          P[(int64_t)2 * p.N] = aa[fn];
+          P[(int64_t)3 * p.N] = mt[fn];
+          P[(int64_t)4 * p.N] = st[fn];
+        }
+      }
+    }
+    // red is written again by the next split's flush
+    dma_barrier<63>();
+    reset();
+  };
 
   f32x16 zs[FFM][FFN], zt[FFM][FFN];
-  const int arow0 = wm * (FBM / F::kWM), brow0 = wn * (FBN / 2);
   const int lrow = 4 * (lane >> 5);
   DualOps o;
   o.W[0] = p.W_s; o.h[0] = p.h_s; o.H[0] = p.Hs; o.nk[0] = p.Hs / kKT;
@@ -487,46 +546,10 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void fwd_tiles(FwdParams p)
           fold_tile<true>(zs, zt, fn, vrow, p.V, ms[fn], ss[fn], aa[fn], mt[fn], st[fn]);
       }
     }
+    // the split's last tile (or the vocabulary's): its statistics are complete
+    const int vt = vt0 + job;
+    if ((vt + 1) % p.tiles_per_split == 0 || vt + 1 == vt1) flush(vt / p.tiles_per_split);
   });
-
-  // merge the two row halves of each 32x32 block (lanes l and l^32)
-#pragma unroll
-  for (int fn = 0; fn < FFN; ++fn) {
-    const float oms = __shfl_xor(ms[fn], 32), oss = __shfl_xor(ss[fn], 32), oaa = __shfl_xor(aa[fn], 32);
-    const float omt = __shfl_xor(mt[fn], 32), ost = __shfl_xor(st[fn], 32);
-    merge3(ms[fn], ss[fn], aa[fn], oms, oss, oaa);
-    merge2(mt[fn], st[fn], omt, ost);
-  }
-  // merge the waves that hold the same tokens (wm = 1 .. kWM-1 into wm = 0,
-  // in that order)
-  if (wm > 0 && lane < 32) {
-#pragma unroll
-    for (int fn = 0; fn < FFN; ++fn) {
-      float* q = red + ((((wm - 1) * 2 + wn) * FFN + fn) * 32 + lane) * 5;
-      q[0] = ms[fn]; q[1] = ss[fn]; q[2] = aa[fn]; q[3] = mt[fn]; q[4] = st[fn];
-    }
-  }
-  __syncthreads();
-  if (wm == 0 && lane < 32) {
-#pragma unroll
-    for (int fn = 0; fn < FFN; ++fn) {
-#pragma unroll
-      for (int r = 1; r < F::kWM; ++r) {
-        const float* q = red + ((((r - 1) * 2 + wn) * FFN + fn) * 32 + lane) * 5;
-        merge3(ms[fn], ss[fn], aa[fn], q[0], q[1], q[2]);
-        merge2(mt[fn], st[fn], q[3], q[4]);
-      }
-      const int n = n0 + brow0 + fn * 32 + lane;
-      if (n < p.N) {
-        float* P = p.partial + (int64_t)split * 5 * p.N + n;
-        P[0] = ms[fn];
-        P[(int64_t)1 * p.N] = ss[fn];
-        P[(int64_t)2 * p.N] = aa[fn];
-        P[(int64_t)3 * p.N] = mt[fn];
-        P[(int64_t)4 * p.N] = st[fn];
-      }
-    }
-  }
 }
 
 // Split combine.  Reverse KL: lse = m + log S per side, L = A / S_s -
@@ -1440,7 +1463,7 @@ static inline unsigned grid1(int64_t n, int64_t per, int64_t cap) {
 }
 
 hipError_t launch_fwd_tiles(const FwdParams& p, int mode, hipStream_t s) {
-  const unsigned nb = (unsigned)(p.nsplit * p.ntok);
+  const unsigned nb = (unsigned)((p.nsplit + p.splits_per_wg - 1) / p.splits_per_wg * p.ntok);
   constexpr int NW = kFusedWaves;
   constexpr unsigned nt = Fused<NW>::kThreads;
   if (mode == kModeHidden)

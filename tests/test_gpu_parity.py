@@ -187,23 +187,27 @@ def test_hidden_multi_chunk_backward(tdev, monkeypatch):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), what
 
 
-@pytest.mark.parametrize("orders", [("1,1", "1,1", "1", "1"), ("3,5", "7,2", "3", "3"), ("64,64", "2,3", "64", "64")],
+@pytest.mark.parametrize("orders", [("1,1", "1,1", "1", "1", "1"), ("3,5", "7,2", "3", "3", "2"),
+                                    ("64,64", "2,3", "64", "64", "1000")],
                          ids=["one_by_one", "ragged_panels", "oversized"])
 def test_tile_order_and_grouping_do_not_change_results(tdev, monkeypatch, orders):
     """The workgroup orders (the fused kernels' panel sizes GS x TG, the dh
-    GEMM's column tiles per panel) and the vocabulary tiles per backward
-    workgroup only reorder independent work: results are bitwise those of the
-    default settings, for ragged token and vocabulary tails (Hs = 640: five
-    dh column tiles, so panels of 3 leave a ragged last panel)."""
+    GEMM's column tiles per panel), the vocabulary tiles per backward
+    workgroup and the forward splits per workgroup only reorder independent
+    work: results are bitwise those of the default settings, for ragged token
+    and vocabulary tails (Hs = 640: five dh column tiles, so panels of 3
+    leave a ragged last panel; 20 forward splits, so groups of 2 and of all
+    of them)."""
     torch, dev = tdev
     case = synth.random_case(77, T=700, V=5003, Hs=640, Ht=192, p_mask=0.8, with_grad=True)
     say("orders", orders, case.T, case.V)
     ref = _run_hidden(case, dev, g=case.grad)
-    fo, bo, bt, dp = orders
+    fo, bo, bt, dp, sp = orders
     monkeypatch.setenv("RKL_FWD_ORDER", fo)
     monkeypatch.setenv("RKL_BWD_ORDER", bo)
     monkeypatch.setenv("RKL_BWD_TILES", bt)
     monkeypatch.setenv("RKL_DH_PANEL", dp)
+    monkeypatch.setenv("RKL_FWD_SPLITS_PER_WG", sp)
     got = _run_hidden(case, dev, g=case.grad)
     for a, b, what in zip(got[1:], ref[1:], ("loss", "stats", "dh", "dW")):
         assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), what
@@ -273,11 +277,17 @@ def test_full_row_equals_compact(tdev):
     assert_grad_close(f[4], c[4], "dW full-row vs compact")
 
 
-def test_self_distillation_is_exactly_zero(tdev):
+@pytest.mark.parametrize("splits_per_wg", [None, "2", "1000"])
+def test_self_distillation_is_exactly_zero(tdev, monkeypatch, splits_per_wg):
+    """Bit-identical teacher: every loss and gradient entry is exactly zero,
+    also when a forward workgroup folds and merges several vocabulary splits
+    in turn (V = 3000: four splits)."""
     torch, dev = tdev
     case = synth.random_case(60, T=100, V=3000, Hs=128, Ht=128, p_mask=0.9)
     case.h_t, case.W_t = case.h_s, case.W_s
-    say("self-distillation small")
+    if splits_per_wg:
+        monkeypatch.setenv("RKL_FWD_SPLITS_PER_WG", splits_per_wg)
+    say("self-distillation small, forward splits per workgroup", splits_per_wg)
     idx, loss, stats, dh, dW = _run_hidden(case, dev)
     assert np.all(loss == 0.0)
     assert np.all(dh == 0.0) and np.all(dW == 0.0)
