@@ -153,22 +153,41 @@ Split fwd_split(int64_t V) {
   return Split{(int)tps, (int)ceil_div(ntv, tps)};
 }
 
-// Splits per forward workgroup: enough that the grid is one workgroup per CU
-// for each token tile's share (256 CUs), so that a workgroup streams many
-// vocabulary tiles without restarting its pipeline.  Measured at N = 4096,
-// H = 2048, V = 151936 (8 groups of 25 splits per token tile, 256
-// workgroups): 4444 us per forward against 4549 us with one split per
-// workgroup; one 75-tile split per workgroup (a different split plan, same
-// grid) took 4427 us, so the 24 extra statistics flushes cost ~0.4 %.  Does
-// not change results.  RKL_FWD_SPLITS_PER_WG overrides it.
-int fwd_splits_per_wg(int nsplit, int64_t ntok) {
+// Splits per forward workgroup.  A workgroup streams its splits' vocabulary
+// tiles as one pipeline, so longer runs save pipeline fills, but the fused
+// kernels hold one workgroup per CU, so a ragged last wave of workgroups
+// costs as long as a full one.  The choice minimises waves of kCUs
+// workgroups x (tiles per workgroup + a fill of about a tenth of a tile),
+// and is taken when it beats one split per workgroup by more than 1 %.
+// Measured forward times at H = 2048, V = 151936 (us, the choice against
+// one split per workgroup, each after warm-up in one process): N = 4096
+// (8 groups of 25 splits, 256 workgroups) 4444 / 4549 on one box and
+// 4296 / 4329 on another; N = 8192 (4 groups of 50) 8468 / 8564; N = 16384
+// (2 groups of 99) 16839 / 17196; N = 1000 (29 groups of 7, 232
+// workgroups: one ragged wave against seven) 1197 / 1240; N = 4224 (groups
+// of 2) 4762 / 4734, within the noise.  Does not change results.
+// RKL_FWD_SPLITS_PER_WG overrides it.
+constexpr int64_t kCUs = 256;   // MI355X compute units
+int fwd_splits_per_wg(int nsplit, int tiles_per_split, int64_t ntok) {
   if (const char* s = std::getenv("RKL_FWD_SPLITS_PER_WG")) {
     const int v = std::atoi(s);
     if (v >= 1) return v < nsplit ? v : nsplit;
   }
-  const int64_t groups_per_tile = ceil_div(256, ntok < 1 ? 1 : ntok);
-  const int64_t spw = ceil_div(nsplit, groups_per_tile);
-  return (int)(spw < 1 ? 1 : spw);
+  if (ntok < 1) ntok = 1;
+  auto cost = [&](int spw) {
+    const int64_t waves = ceil_div(ceil_div(nsplit, spw) * ntok, kCUs);
+    return (double)waves * ((double)spw * tiles_per_split + 0.1);
+  };
+  int best = 1;
+  double best_cost = cost(1);
+  for (int spw = 2; spw <= nsplit; ++spw) {
+    const double c = cost(spw);
+    if (c <= best_cost) {   // ties go to the longer runs
+      best = spw;
+      best_cost = c;
+    }
+  }
+  return best_cost < 0.99 * cost(1) ? best : 1;
 }
 
 size_t fwd_ws_bytes(int64_t N, int64_t V, bool tiled) {
@@ -299,7 +318,7 @@ int forward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* 
   p.tiles_per_split = sp.tiles_per_split;
   p.nsplit = sp.nsplit;
   p.ntok = (int)ceil_div(N, rkl::kFwdTileN);
-  p.splits_per_wg = fwd_splits_per_wg(p.nsplit, p.ntok);
+  p.splits_per_wg = fwd_splits_per_wg(p.nsplit, p.tiles_per_split, p.ntok);
   p.order_gs = fwd_order().gs;
   p.order_tg = fwd_order().tg;
   const int mode = mode_of(z_t, y, tch.teacher);
