@@ -464,17 +464,18 @@ def bench_reverse_kl(args):
     def step():
         idx, N = R.compact_rows(mask)
         h_s = R.gather_rows(h_s_all, idx)
-        t_in = R.gather_rows(z_t_all if logits else h_t_all, idx)
         g = R.gather_rows(grad_pos, idx)
         if logits:
-            loss, stats = R.forward_logits(t_in, h_s=h_s, W_s=W_s)
+            # the kernels read the teacher's logits rows through idx: no copy
+            loss, stats = R.forward_logits(z_t_all, h_s=h_s, W_s=W_s, z_rows=idx)
         else:
-            loss, stats = R.forward_hidden(h_s, W_s, t_in, W_t)
+            h_t = R.gather_rows(h_t_all, idx)
+            loss, stats = R.forward_hidden(h_s, W_s, h_t, W_t)
         loss_pos = R.scatter_rows(loss, idx, T)
         if logits:
-            dh, _ = R.backward_logits(t_in, stats, h_s=h_s, W_s=W_s, grad_loss=g, dW=dW)
+            dh, _ = R.backward_logits(z_t_all, stats, h_s=h_s, W_s=W_s, grad_loss=g, dW=dW, z_rows=idx)
         else:
-            dh, _ = R.backward_hidden(h_s, W_s, t_in, W_t, stats, grad_loss=g, dW=dW)
+            dh, _ = R.backward_hidden(h_s, W_s, h_t, W_t, stats, grad_loss=g, dW=dW)
         R.scatter_rows(dh, idx, T)
         return N, loss_pos
 
@@ -484,7 +485,7 @@ def bench_reverse_kl(args):
     work = rkl_work(N, V, Hs, Ht_eff, logits=logits)
     flop_fwd = 2.0 * N * V * (Hs + Ht_eff)
     flop_step = 4.0 * N * V * (Hs + Ht_eff) + 4.0 * N * V * Hs
-    config = {"workload": ("Qwen3-1.7B-shaped fp32 teacher logits [N, V], " if logits else
+    config = {"workload": ("Qwen3-1.7B-shaped fp32 teacher logits [T, V] read through the row index, " if logits else
                            "Qwen3-1.7B-shaped hidden-state teacher, ") +
                           "B=4 S=1025 (T=N=4096 trainable), Hs=Ht=2048, V=151936",
               "B": case.B, "S": case.S, "N": int(N), "Hs": Hs, "Ht": Ht_eff, "V": V,

@@ -164,11 +164,19 @@ int rkl_forward_hidden(int64_t N, int64_t V, int64_t Hs, int64_t Ht,
  *   z_t [N, V] fp32 teacher logits.
  *   Student either as hidden states (h_s [N, Hs], W_s [V, Hs] bf16, z_s NULL)
  *   or as fp32 logits (z_s [N, V], h_s = W_s = NULL, Hs = 0).
- * Other arguments as rkl_forward_hidden.
+ *   z_rows, T: NULL, 0 for the above.  Otherwise z_t (and z_s) hold T rows
+ *     [T, V] -- e.g. every position of the batch -- and row i of this call
+ *     reads row z_rows[i] of them (z_rows [N] int32, device; typically the
+ *     row_idx of rkl_compact_rows, which spares the gather of the logits
+ *     rows the slime page's compaction would otherwise copy).  1 <= T <=
+ *     2^30.  Values are not checked on the device: they are clamped to
+ *     [0, T), so a wrong index reads a wrong row, never outside the buffers.
+ * Other arguments as rkl_forward_hidden (h_s, row_mask, loss and stats keep
+ * their N rows).
  */
 int rkl_forward_logits(int64_t N, int64_t V, int64_t Hs,
                        const rkl_bf16* h_s, const rkl_bf16* W_s, const float* z_s, const float* z_t,
-                       const uint8_t* row_mask, float* loss, float* stats,
+                       const int32_t* z_rows, int64_t T, const uint8_t* row_mask, float* loss, float* stats,
                        void* workspace, size_t workspace_bytes, rkl_stream_t stream);
 
 /*
@@ -193,12 +201,13 @@ int rkl_backward_hidden(int64_t N, int64_t V, int64_t Hs, int64_t Ht,
  * Backward, logits teacher.  Student as hidden states: outputs dh_s, dW_s as
  * in rkl_backward_hidden (dz_s must be NULL).  Student as logits (h_s = W_s
  * = NULL, Hs = 0): output dz_s [N, V] fp32 = g p_s (w - L), rows with
- * row_mask 0 exactly 0 (dh_s, dW_s must be NULL).
+ * row_mask 0 exactly 0 (dh_s, dW_s must be NULL; dz_s has the call's N rows
+ * also when z_rows indexes the inputs).  z_rows, T as rkl_forward_logits.
  */
 int rkl_backward_logits(int64_t N, int64_t V, int64_t Hs,
                         const rkl_bf16* h_s, const rkl_bf16* W_s, const float* z_s, const float* z_t,
-                        const uint8_t* row_mask, const float* grad_loss, const float* stats,
-                        float* dh_s, float* dW_s, int accumulate_dW, float* dz_s,
+                        const int32_t* z_rows, int64_t T, const uint8_t* row_mask, const float* grad_loss,
+                        const float* stats, float* dh_s, float* dW_s, int accumulate_dW, float* dz_s,
                         void* workspace, size_t workspace_bytes, rkl_stream_t stream);
 
 /*

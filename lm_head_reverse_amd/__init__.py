@@ -58,9 +58,9 @@ def lib() -> ctypes.CDLL:
         "rkl_gather_rows": ([P, I64, I64, P, I64, P, P], I32),
         "rkl_scatter_rows": ([P, I64, I64, P, I64, P, P], I32),
         "rkl_forward_hidden": ([I64, I64, I64, I64, P, P, P, P, P, P, P, P, SZ, P], I32),
-        "rkl_forward_logits": ([I64, I64, I64, P, P, P, P, P, P, P, P, SZ, P], I32),
+        "rkl_forward_logits": ([I64, I64, I64, P, P, P, P, P, I64, P, P, P, P, SZ, P], I32),
         "rkl_backward_hidden": ([I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, I32, P, SZ, P], I32),
-        "rkl_backward_logits": ([I64, I64, I64, P, P, P, P, P, P, P, P, P, I32, P, P, SZ, P], I32),
+        "rkl_backward_logits": ([I64, I64, I64, P, P, P, P, P, I64, P, P, P, P, P, I32, P, P, SZ, P], I32),
         "rkl_forward_hidden_shard": ([I64, I64, I64, I64, P, P, P, P, P, P, SZ, P], I32),
         "rkl_forward_logits_shard": ([I64, I64, I64, P, P, P, P, P, P, SZ, P], I32),
         "rkl_combine_shards": ([I64, I64, P, P, P, P, P], I32),
@@ -228,27 +228,40 @@ def forward_hidden(h_s, W_s, h_t, W_t, row_mask=None):
     return loss, stats
 
 
-def forward_logits(z_t, h_s=None, W_s=None, z_s=None, row_mask=None):
+def _logit_rows(z_t, z_rows, dev):
+    """(N, V, T) of a logits call: z_t holds T rows; without z_rows N = T."""
+    torch = _torch()
+    T, V = z_t.shape
+    if z_rows is None:
+        return T, V, 0
+    _need(z_rows, "z_rows", torch.int32, dev)
+    if z_rows.dim() != 1:
+        raise RKLError(RKL_INVALID_ARG, "z_rows must be one-dimensional")
+    return z_rows.shape[0], V, T
+
+
+def forward_logits(z_t, h_s=None, W_s=None, z_s=None, row_mask=None, z_rows=None):
     """Per-row reverse KL with the teacher given as fp32 logits z_t [N, V]; the
-    student as (h_s, W_s) bf16 or as fp32 logits z_s."""
+    student as (h_s, W_s) bf16 or as fp32 logits z_s.  With z_rows (int32
+    [N]), z_t and z_s hold [T, V] and row i reads their row z_rows[i]."""
     torch = _torch()
     dev = z_t.device
-    N, V = z_t.shape
     _need(z_t, "z_t", torch.float32, dev)
+    N, V, T = _logit_rows(z_t, z_rows, dev)
     Hs = 0
     if z_s is None:
         Hs = h_s.shape[1]
         _need(h_s, "h_s", torch.bfloat16, dev, (N, Hs))
         _need(W_s, "W_s", torch.bfloat16, dev, (V, Hs))
     else:
-        _need(z_s, "z_s", torch.float32, dev, (N, V))
+        _need(z_s, "z_s", torch.float32, dev, tuple(z_t.shape))
     if row_mask is not None:
         _need(row_mask, "row_mask", torch.uint8, dev, (N,))
     loss = torch.empty(N, dtype=torch.float32, device=dev)
     stats = torch.empty((N, 4), dtype=torch.float32, device=dev)
     ws = _workspace(dev, workspace_bytes(N, V, Hs, 0))
-    _check(lib().rkl_forward_logits(N, V, Hs, _ptr(h_s), _ptr(W_s), _ptr(z_s), _ptr(z_t), _ptr(row_mask),
-                                    _ptr(loss), _ptr(stats), _ptr(ws), ws.numel(), _stream(dev)))
+    _check(lib().rkl_forward_logits(N, V, Hs, _ptr(h_s), _ptr(W_s), _ptr(z_s), _ptr(z_t), _ptr(z_rows), T,
+                                    _ptr(row_mask), _ptr(loss), _ptr(stats), _ptr(ws), ws.numel(), _stream(dev)))
     return loss, stats
 
 
@@ -282,22 +295,23 @@ def backward_hidden(h_s, W_s, h_t, W_t, stats, grad_loss=None, row_mask=None, dW
 
 
 def backward_logits(z_t, stats, h_s=None, W_s=None, z_s=None, grad_loss=None, row_mask=None, dW=None,
-                    accumulate_dW=False):
+                    accumulate_dW=False, z_rows=None):
     """Teacher as logits.  Student as (h_s, W_s): returns (dh_s, dW_s).
-    Student as logits z_s: returns dz_s fp32 [N, V]."""
+    Student as logits z_s: returns dz_s fp32 [N, V].  z_rows as
+    forward_logits."""
     torch = _torch()
     dev = z_t.device
-    N, V = z_t.shape
     _need(z_t, "z_t", torch.float32, dev)
+    N, V, T = _logit_rows(z_t, z_rows, dev)
     _need(stats, "stats", torch.float32, dev, (N, 4))
     if grad_loss is not None:
         _need(grad_loss, "grad_loss", torch.float32, dev, (N,))
     if row_mask is not None:
         _need(row_mask, "row_mask", torch.uint8, dev, (N,))
     if z_s is not None:
-        _need(z_s, "z_s", torch.float32, dev, (N, V))
+        _need(z_s, "z_s", torch.float32, dev, tuple(z_t.shape))
         dz = torch.empty((N, V), dtype=torch.float32, device=dev)
-        _check(lib().rkl_backward_logits(N, V, 0, None, None, _ptr(z_s), _ptr(z_t), _ptr(row_mask),
+        _check(lib().rkl_backward_logits(N, V, 0, None, None, _ptr(z_s), _ptr(z_t), _ptr(z_rows), T, _ptr(row_mask),
                                          _ptr(grad_loss), _ptr(stats), None, None, 0, _ptr(dz), None, 0,
                                          _stream(dev)))
         return dz
@@ -312,9 +326,9 @@ def backward_logits(z_t, stats, h_s=None, W_s=None, z_s=None, grad_loss=None, ro
         _need(dW, "dW", torch.float32, dev, (V, Hs))
     dh = torch.empty((N, Hs), dtype=torch.float32, device=dev)
     ws = _workspace(dev, workspace_bytes(N, V, Hs, 0))
-    _check(lib().rkl_backward_logits(N, V, Hs, _ptr(h_s), _ptr(W_s), None, _ptr(z_t), _ptr(row_mask),
-                                     _ptr(grad_loss), _ptr(stats), _ptr(dh), _ptr(dW), int(bool(accumulate_dW)),
-                                     None, _ptr(ws), ws.numel(), _stream(dev)))
+    _check(lib().rkl_backward_logits(N, V, Hs, _ptr(h_s), _ptr(W_s), None, _ptr(z_t), _ptr(z_rows), T,
+                                     _ptr(row_mask), _ptr(grad_loss), _ptr(stats), _ptr(dh), _ptr(dW),
+                                     int(bool(accumulate_dW)), None, _ptr(ws), ws.numel(), _stream(dev)))
     return dh, dW
 
 
@@ -342,8 +356,9 @@ class ReverseKL:
             self.h_t, self.z_t = gather_rows(h_t, self.row_idx), None
             loss, self.stats = forward_hidden(self.h_s, self.W_s, self.h_t, self.W_t)
         else:
-            self.h_t, self.z_t = None, gather_rows(z_t, self.row_idx)
-            loss, self.stats = forward_logits(self.z_t, h_s=self.h_s, W_s=self.W_s)
+            # the logits rows are read through row_idx, not copied
+            self.h_t, self.z_t = None, z_t
+            loss, self.stats = forward_logits(z_t, h_s=self.h_s, W_s=self.W_s, z_rows=self.row_idx)
         return scatter_rows(loss, self.row_idx, T)
 
     def backward(self, grad_pos=None, dW=None, accumulate_dW=False):
@@ -353,7 +368,7 @@ class ReverseKL:
                                      accumulate_dW=accumulate_dW)
         else:
             dh, dW = backward_logits(self.z_t, self.stats, h_s=self.h_s, W_s=self.W_s, grad_loss=g, dW=dW,
-                                     accumulate_dW=accumulate_dW)
+                                     accumulate_dW=accumulate_dW, z_rows=self.row_idx)
         return scatter_rows(dh, self.row_idx, self.T), dW
 
 

@@ -300,10 +300,17 @@ struct Teachers {
   int64_t stride = 0;
 };
 
+// Rows of the given logits (rkl_forward_logits / rkl_backward_logits): token
+// n reads row rows[n] of buffers that hold nrows rows; rows NULL: row n.
+struct ZRows {
+  const int32_t* rows = nullptr;
+  int64_t nrows = 0;
+};
+
 int forward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* h_s, const rkl_bf16* W_s,
                   const rkl_bf16* h_t, const rkl_bf16* W_t, const float* z_t, const int32_t* y,
                   const uint8_t* row_mask, float* out0, float* out1, float* stats, void* ws, size_t ws_bytes_given,
-                  hipStream_t s, Teachers tch = Teachers{}, float* merged = nullptr) {
+                  hipStream_t s, Teachers tch = Teachers{}, float* merged = nullptr, ZRows zr = ZRows{}) {
   const size_t need = fwd_ws_bytes(N, V, true);
   if (ws_bytes_given < need)
     return fail(RKL_WORKSPACE_TOO_SMALL, "workspace %zu bytes < %zu needed", ws_bytes_given, need);
@@ -313,6 +320,7 @@ int forward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* 
   rkl::FwdParams p{};
   p.N = (int)N; p.V = (int)V; p.Hs = (int)Hs; p.Ht = (int)Ht;
   p.h_s = h_s; p.W_s = W_s; p.h_t = h_t; p.W_t = W_t; p.z_t = z_t; p.y = y;
+  p.z_rows = zr.rows; p.z_nrows = (int)(zr.rows ? zr.nrows : N);
   p.teacher = tch.teacher; p.K = tch.K; p.wt_stride = tch.stride;
   p.partial = static_cast<float*>(ws);
   p.tiles_per_split = sp.tiles_per_split;
@@ -345,7 +353,7 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
                    const rkl_bf16* h_t, const rkl_bf16* W_t, const float* z_t, const int32_t* y,
                    const uint8_t* row_mask, const float* grad, const float* grad_h, const float* stats, float* dh,
                    float* dW, int accumulate, void* ws, size_t ws_bytes_given, hipStream_t s,
-                   Teachers tch = Teachers{}, TopK topk = TopK{}) {
+                   Teachers tch = Teachers{}, TopK topk = TopK{}, ZRows zr = ZRows{}) {
   const int mode = topk.on ? rkl::kModeTopK : mode_of(z_t, y, tch.teacher);
   if (N > kMaxPitchElems)
     return fail(RKL_UNSUPPORTED, "N=%lld rows exceed the backward's limit of 2^22 per call", (long long)N);
@@ -375,6 +383,7 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
     rkl::BwdParams b{};
     b.N = (int)N; b.V = (int)V; b.Hs = (int)Hs; b.Ht = (int)Ht;
     b.h_s = h_s; b.W_s = W_s; b.h_t = h_t; b.W_t = W_t; b.z_t = z_t;
+    b.z_rows = zr.rows; b.z_nrows = (int)(zr.rows ? zr.nrows : N);
     b.row_mask = row_mask; b.grad = grad; b.grad_h = grad_h; b.y = y; b.stats = stats;
     b.teacher = tch.teacher; b.K = tch.K; b.wt_stride = tch.stride;
     b.scales = scales; b.wmag = wmag; b.dz = dz; b.w16 = w16; b.ldz = (int)L.ldz; b.c0 = (int)c0;
@@ -581,7 +590,7 @@ int rkl_forward_logits_shard(int64_t N, int64_t V, int64_t Hs, const rkl_bf16* h
     return forward_tiled(N, V, Hs, 0, h_s, W_s, nullptr, nullptr, z_t, nullptr, nullptr, nullptr, nullptr, nullptr,
                          workspace, workspace_bytes, s, Teachers{}, partial);
   if (N == 0) return RKL_OK;
-  RKL_LAUNCH("fwd_rows_logits", s, rkl::launch_fwd_rows_logits(z_s, z_t, (int)N, (int)V, nullptr, nullptr, nullptr, partial, s));
+  RKL_LAUNCH("fwd_rows_logits", s, rkl::launch_fwd_rows_logits(z_s, z_t, nullptr, (int)N, (int)N, (int)V, nullptr, nullptr, nullptr, partial, s));
   return RKL_OK;
 }
 
@@ -606,12 +615,26 @@ int rkl_combine_shards_logprob_entropy(int64_t G, int64_t N, const float* partia
   return combine_shards(G, N, partials, row_mask, true, logp, entropy, stats, static_cast<hipStream_t>(stream));
 }
 
+// z_rows / T of the logits entry points: the row index, and the rows the
+// logits buffers hold.
+static int check_z_rows(int64_t N, const int32_t* z_rows, int64_t T, ZRows& zr) {
+  if (!z_rows) return RKL_OK;
+  if (T < 1 || T > kMaxDim)
+    return fail(RKL_INVALID_ARG, "T=%lld rows of the logits out of range [1, 2^30] with z_rows", (long long)T);
+  if (N > 0) NEED4(z_rows, "z_rows");
+  zr.rows = z_rows;
+  zr.nrows = T;
+  return RKL_OK;
+}
+
 int rkl_forward_logits(int64_t N, int64_t V, int64_t Hs, const rkl_bf16* h_s, const rkl_bf16* W_s, const float* z_s,
-                       const float* z_t, const uint8_t* row_mask, float* loss, float* stats, void* workspace,
-                       size_t workspace_bytes, rkl_stream_t stream) {
+                       const float* z_t, const int32_t* z_rows, int64_t T, const uint8_t* row_mask, float* loss,
+                       float* stats, void* workspace, size_t workspace_bytes, rkl_stream_t stream) {
   const bool student_hidden = h_s != nullptr || W_s != nullptr;
   if (student_hidden && z_s) return fail(RKL_INVALID_ARG, "give the student as (h_s, W_s) or as z_s, not both");
   if (int rc = check_dims(N, V, Hs, 0, false, student_hidden)) return rc;
+  ZRows zr;
+  if (int rc = check_z_rows(N, z_rows, T, zr)) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (N > 0) {
     NEED16(z_t, "z_t");
@@ -621,9 +644,10 @@ int rkl_forward_logits(int64_t N, int64_t V, int64_t Hs, const rkl_bf16* h_s, co
   }
   if (student_hidden)
     return forward_tiled(N, V, Hs, 0, h_s, W_s, nullptr, nullptr, z_t, nullptr, row_mask, loss, nullptr, stats,
-                         workspace, workspace_bytes, s);
+                         workspace, workspace_bytes, s, Teachers{}, nullptr, zr);
   if (N == 0) return RKL_OK;
-  RKL_LAUNCH("fwd_rows_logits", s, rkl::launch_fwd_rows_logits(z_s, z_t, (int)N, (int)V, row_mask, loss, stats, nullptr, s));
+  RKL_LAUNCH("fwd_rows_logits", s, rkl::launch_fwd_rows_logits(z_s, z_t, zr.rows, (int)(zr.rows ? zr.nrows : N), (int)N,
+                                                              (int)V, row_mask, loss, stats, nullptr, s));
   return RKL_OK;
 }
 
@@ -642,12 +666,14 @@ int rkl_backward_hidden(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_
 }
 
 int rkl_backward_logits(int64_t N, int64_t V, int64_t Hs, const rkl_bf16* h_s, const rkl_bf16* W_s, const float* z_s,
-                        const float* z_t, const uint8_t* row_mask, const float* grad_loss, const float* stats,
-                        float* dh_s, float* dW_s, int accumulate_dW, float* dz_s, void* workspace,
-                        size_t workspace_bytes, rkl_stream_t stream) {
+                        const float* z_t, const int32_t* z_rows, int64_t T, const uint8_t* row_mask,
+                        const float* grad_loss, const float* stats, float* dh_s, float* dW_s, int accumulate_dW,
+                        float* dz_s, void* workspace, size_t workspace_bytes, rkl_stream_t stream) {
   const bool student_hidden = h_s != nullptr || W_s != nullptr;
   if (student_hidden && z_s) return fail(RKL_INVALID_ARG, "give the student as (h_s, W_s) or as z_s, not both");
   if (int rc = check_dims(N, V, Hs, 0, false, student_hidden)) return rc;
+  ZRows zr;
+  if (int rc = check_z_rows(N, z_rows, T, zr)) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (student_hidden) {
     if (dz_s) return fail(RKL_INVALID_ARG, "dz_s must be NULL when the student is given as hidden states");
@@ -657,12 +683,13 @@ int rkl_backward_logits(int64_t N, int64_t V, int64_t Hs, const rkl_bf16* h_s, c
       NEED4(stats, "stats"); NEED16(dh_s, "dh_s"); OPT4(grad_loss, "grad_loss");
     }
     return backward_tiled(N, V, Hs, 0, h_s, W_s, nullptr, nullptr, z_t, nullptr, row_mask, grad_loss, nullptr, stats,
-                          dh_s, dW_s, accumulate_dW != 0, workspace, workspace_bytes, s);
+                          dh_s, dW_s, accumulate_dW != 0, workspace, workspace_bytes, s, Teachers{}, TopK{}, zr);
   }
   if (dh_s || dW_s) return fail(RKL_INVALID_ARG, "dh_s and dW_s must be NULL when the student is given as logits");
   if (N == 0) return RKL_OK;
   NEED16(z_s, "z_s"); NEED16(z_t, "z_t"); NEED4(stats, "stats"); NEED16(dz_s, "dz_s"); OPT4(grad_loss, "grad_loss");
-  RKL_LAUNCH("bwd_rows_logits", s, rkl::launch_bwd_rows_logits(z_s, z_t, (int)N, (int)V, row_mask, grad_loss, stats, dz_s, s));
+  RKL_LAUNCH("bwd_rows_logits", s, rkl::launch_bwd_rows_logits(z_s, z_t, zr.rows, (int)(zr.rows ? zr.nrows : N), (int)N,
+                                                              (int)V, row_mask, grad_loss, stats, dz_s, s));
   return RKL_OK;
 }
 

@@ -13,7 +13,9 @@ struct FwdParams {
   const uint16_t* W_s;
   const uint16_t* h_t;
   const uint16_t* W_t;
-  const float* z_t;        // teacher logits [N, V] (teacher-logits payload)
+  const float* z_t;        // teacher logits, rows of V (teacher-logits payload)
+  const int32_t* z_rows;   // row of z_t for token n (NULL: row n)
+  int z_nrows;             // rows z_t holds (z_rows values are clamped to [0, z_nrows))
   const int32_t* y;        // sampled token per row (log-probability / entropy)
   const int32_t* teacher;  // teacher per row (NULL: one teacher)
   int K;                   // teachers: W_t holds K weights, wt_stride elements apart
@@ -33,6 +35,8 @@ struct BwdParams {
   const uint16_t* h_t;
   const uint16_t* W_t;
   const float* z_t;
+  const int32_t* z_rows;   // row of z_t for token n (NULL: row n)
+  int z_nrows;             // rows z_t holds (z_rows values are clamped to [0, z_nrows))
   const uint8_t* row_mask;
   const float* grad;       // g of L (reverse KL) or of log p(y) (log-probability / entropy)
   const float* grad_h;     // g of the entropy (log-probability / entropy)
@@ -157,10 +161,11 @@ hipError_t launch_w_rescale(const uint16_t* W_chunk, int rows, int ntv, int H, c
 hipError_t launch_dw(const DwParams& p, hipStream_t s);
 hipError_t launch_dh(const DhParams& p, hipStream_t s);
 // merged != NULL: the unfinalised (m_s, S_s, A, m_t, S_t) planes instead of loss / stats
-hipError_t launch_fwd_rows_logits(const float* z_s, const float* z_t, int N, int V, const uint8_t* row_mask,
-                                  float* loss, float* stats, float* merged, hipStream_t s);
-hipError_t launch_bwd_rows_logits(const float* z_s, const float* z_t, int N, int V, const uint8_t* row_mask,
-                                  const float* grad, const float* stats, float* dz, hipStream_t s);
+hipError_t launch_fwd_rows_logits(const float* z_s, const float* z_t, const int32_t* z_rows, int z_nrows, int N, int V,
+                                  const uint8_t* row_mask, float* loss, float* stats, float* merged, hipStream_t s);
+hipError_t launch_bwd_rows_logits(const float* z_s, const float* z_t, const int32_t* z_rows, int z_nrows, int N, int V,
+                                  const uint8_t* row_mask, const float* grad, const float* stats, float* dz,
+                                  hipStream_t s);
 hipError_t launch_compact(const uint8_t* mask, int T, int32_t* row_idx, int32_t* n_out, hipStream_t s);
 // Rows grouped by teacher id (stable; ids outside [0, K) last); K in [1, 31].
 hipError_t launch_group_by_teacher(const int32_t* teacher, const uint8_t* mask, int N, int K, int32_t* perm,

@@ -163,20 +163,32 @@ __device__ __forceinline__ void fold_lpe(const f32x16 (&zs)[FM][FN], int fn, int
   }
 }
 
+// The z_t row of each of this lane's token columns: token n reads row
+// z_rows[n] (row n without an index), clamped to [0, nrows); token columns
+// past N read the row of token N-1 (their results are discarded).
+template <int FN>
+__device__ __forceinline__ void zt_rows(const int32_t* __restrict__ z_rows, int nrows, int N, int ncol,
+                                        int (&zr)[FN]) {
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    const int n = min(ncol + fn * 32, N - 1);
+    zr[fn] = z_rows ? min(max(z_rows[n], 0), nrows - 1) : n;
+  }
+}
+
 // Teacher logits read into the accumulator layout (teacher-logits payload).
-// Token columns past N read row N-1 (their results are discarded).  A full
+// zr[fn] = the z_t row of this lane's token column fn (zt_rows).  A full
 // vocabulary tile (TAIL false) loads without conditions, from one row
 // pointer per token column and immediate offsets; the last tile clamps each
 // column index to V-1 and zeroes what lies past V.
 // only >= 0 loads token column `only` alone.
 template <bool VEC4, bool TAIL, int FM, int FN>
-__device__ __forceinline__ void load_zt(f32x16 (&zt)[FM][FN], const float* __restrict__ z_t, int N, int V,
-                                        int vrow, int ncol, int only = -1) {
+__device__ __forceinline__ void load_zt(f32x16 (&zt)[FM][FN], const float* __restrict__ z_t, int V, int vrow,
+                                        const int (&zr)[FN], int only = -1) {
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
     if (only >= 0 && fn != only) continue;
-    const int n = min(ncol + fn * 32, N - 1);
-    const float* row = z_t + (int64_t)n * V;
+    const float* row = z_t + (int64_t)zr[fn] * V;
 #pragma unroll
     for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
@@ -516,6 +528,8 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void fwd_tiles(FwdParams p)
     const int n = n0 + brow0 + fn * 32 + (lane & 31);
     yv[fn] = (MODE == 2 && n < p.N) ? p.y[n] : -1;
   }
+  int zr[FFN];   // z_t row of this lane's token columns (MODE 1)
+  if (MODE == 1) zt_rows<FFN>(p.z_rows, p.z_nrows, p.N, n0 + brow0 + (lane & 31), zr);
 
   dual_stream<NW, MODE == 3>(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, tkl, [&](int job, char*) {
     const int v0 = (vt0 + job) * FBM;
@@ -524,11 +538,11 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void fwd_tiles(FwdParams p)
       // teacher logits: the next token column's loads are in flight while
       // this one folds (with V % 4 != 0 all at once: the unaligned rows need
       // more registers)
-      if (MODE == 1) load_zt<VEC4, false>(zt, p.z_t, p.N, p.V, vrow, n0 + brow0 + (lane & 31), VEC4 ? 0 : -1);
+      if (MODE == 1) load_zt<VEC4, false>(zt, p.z_t, p.V, vrow, zr, VEC4 ? 0 : -1);
 #pragma unroll
       for (int fn = 0; fn < FFN; ++fn) {
         if (MODE == 1 && VEC4 && fn + 1 < FFN)
-          load_zt<VEC4, false>(zt, p.z_t, p.N, p.V, vrow, n0 + brow0 + (lane & 31), fn + 1);
+          load_zt<VEC4, false>(zt, p.z_t, p.V, vrow, zr, fn + 1);
         if (MODE == 2)
           fold_lpe<false>(zs, fn, vrow, p.V, yv[fn], ms[fn], ss[fn], aa[fn], mt[fn]);
         else
@@ -539,7 +553,7 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void fwd_tiles(FwdParams p)
       // (its clamped loads need an address per entry)
 #pragma unroll
       for (int fn = 0; fn < FFN; ++fn) {
-        if (MODE == 1) load_zt<VEC4, true>(zt, p.z_t, p.N, p.V, vrow, n0 + brow0 + (lane & 31), fn);
+        if (MODE == 1) load_zt<VEC4, true>(zt, p.z_t, p.V, vrow, zr, fn);
         if (MODE == 2)
           fold_lpe<true>(zs, fn, vrow, p.V, yv[fn], ms[fn], ss[fn], aa[fn], mt[fn]);
         else
@@ -859,6 +873,9 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
     }
   }
 
+  int zr[FFN];   // z_t row of this lane's token columns (MODE 1)
+  if (MODE == 1) zt_rows<FFN>(p.z_rows, p.z_nrows, p.N, n0 + brow0 + (lane & 31), zr);
+
   f32x16 zs[FFM][FFN], zt[FFM][FFN];
   DualOps o;
   o.W[0] = p.W_s; o.h[0] = p.h_s; o.H[0] = p.Hs; o.nk[0] = p.Hs / kKT;
@@ -921,15 +938,15 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
     } else {
       // teacher logits, one token column at a time: the next column's loads
       // are in flight while this one is packed
-      const int vr = v0 + arow0 + lrow, nc = n0 + brow0 + (lane & 31);
+      const int vr = v0 + arow0 + lrow;
       if (v0 + FBM <= p.V) {
-        load_zt<VEC4, false>(zt, p.z_t, p.N, p.V, vr, nc, 0);
+        load_zt<VEC4, false>(zt, p.z_t, p.V, vr, zr, 0);
         dz_pack<false>(zs, zt, pk, live, vr, p.V, kl, [&](int fn) {
-          if (fn + 1 < FFN) load_zt<VEC4, false>(zt, p.z_t, p.N, p.V, vr, nc, fn + 1);
+          if (fn + 1 < FFN) load_zt<VEC4, false>(zt, p.z_t, p.V, vr, zr, fn + 1);
         });
       } else {
         dz_pack<true>(zs, zt, pk, live, vr, p.V, kl,
-                      [&](int fn) { load_zt<VEC4, true>(zt, p.z_t, p.N, p.V, vr, nc, fn); });
+                      [&](int fn) { load_zt<VEC4, true>(zt, p.z_t, p.V, vr, zr, fn); });
       }
     }
     // Stores go through the free LDS stage, 64 tokens per round: the waves
@@ -1149,13 +1166,15 @@ __global__ __launch_bounds__(64 * NW, 1) void dh_gemm(DhParams p) {
 // merged != NULL: write the row's (m_s, S_s, A, m_t, S_t) to merged as five
 // planes of N (one vocabulary shard's partial) instead of finalising.
 __global__ __launch_bounds__(256) void fwd_rows_logits(const float* __restrict__ z_s, const float* __restrict__ z_t,
-                                                       int N, int V, const uint8_t* __restrict__ row_mask,
+                                                       const int32_t* __restrict__ z_rows, int z_nrows, int N, int V,
+                                                       const uint8_t* __restrict__ row_mask,
                                                        float* __restrict__ loss, float* __restrict__ stats,
                                                        float* __restrict__ merged) {
   __shared__ float red[5][256];
   const int n = blockIdx.x, tid = threadIdx.x;
-  const float* rs = z_s + (int64_t)n * V;
-  const float* rt = z_t + (int64_t)n * V;
+  const int64_t r = z_rows ? min(max(z_rows[n], 0), z_nrows - 1) : n;   // row of z_s and z_t
+  const float* rs = z_s + r * V;
+  const float* rt = z_t + r * V;
   float ms = kNegBig, ss = 0.f, aa = 0.f, mt = kNegBig, st = 0.f;
   for (int v0 = 0; v0 < V; v0 += 4 * 256) {
     float a[4], b[4];
@@ -1220,7 +1239,8 @@ __global__ __launch_bounds__(256) void fwd_rows_logits(const float* __restrict__
 }
 
 __global__ __launch_bounds__(256) void bwd_rows_logits(const float* __restrict__ z_s, const float* __restrict__ z_t,
-                                                       int N, int V, const uint8_t* __restrict__ row_mask,
+                                                       const int32_t* __restrict__ z_rows, int z_nrows, int N, int V,
+                                                       const uint8_t* __restrict__ row_mask,
                                                        const float* __restrict__ grad, const float* __restrict__ stats,
                                                        float* __restrict__ dz) {
   const int n = blockIdx.x;
@@ -1231,7 +1251,8 @@ __global__ __launch_bounds__(256) void bwd_rows_logits(const float* __restrict__
   if (live) {
     const float lse_s = stats[4 * (int64_t)n + 0], lse_t = stats[4 * (int64_t)n + 1], L = stats[4 * (int64_t)n + 2];
     const float g = grad ? grad[n] : 1.0f;
-    const float a = z_s[(int64_t)n * V + v], b = z_t[(int64_t)n * V + v];
+    const int64_t r = z_rows ? min(max(z_rows[n], 0), z_nrows - 1) : n;   // row of z_s and z_t
+    const float a = z_s[r * V + v], b = z_t[r * V + v];
     d = g * ex2(fmaf(a, kL2E, -(lse_s * kL2E))) * ((a - b) - ((lse_s - lse_t) + L));
   }
   dz[(int64_t)n * V + v] = d;
@@ -1569,16 +1590,17 @@ hipError_t launch_dh(const DhParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_fwd_rows_logits(const float* z_s, const float* z_t, int N, int V, const uint8_t* row_mask,
-                                  float* loss, float* stats, float* merged, hipStream_t s) {
-  fwd_rows_logits<<<(unsigned)N, 256, 0, s>>>(z_s, z_t, N, V, row_mask, loss, stats, merged);
+hipError_t launch_fwd_rows_logits(const float* z_s, const float* z_t, const int32_t* z_rows, int z_nrows, int N, int V,
+                                  const uint8_t* row_mask, float* loss, float* stats, float* merged, hipStream_t s) {
+  fwd_rows_logits<<<(unsigned)N, 256, 0, s>>>(z_s, z_t, z_rows, z_nrows, N, V, row_mask, loss, stats, merged);
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_rows_logits(const float* z_s, const float* z_t, int N, int V, const uint8_t* row_mask,
-                                  const float* grad, const float* stats, float* dz, hipStream_t s) {
+hipError_t launch_bwd_rows_logits(const float* z_s, const float* z_t, const int32_t* z_rows, int z_nrows, int N, int V,
+                                  const uint8_t* row_mask, const float* grad, const float* stats, float* dz,
+                                  hipStream_t s) {
   dim3 g((unsigned)N, (unsigned)((V + 255) / 256));
-  bwd_rows_logits<<<g, 256, 0, s>>>(z_s, z_t, N, V, row_mask, grad, stats, dz);
+  bwd_rows_logits<<<g, 256, 0, s>>>(z_s, z_t, z_rows, z_nrows, N, V, row_mask, grad, stats, dz);
   return hipGetLastError();
 }
 

@@ -105,21 +105,27 @@ def test_forward_hidden_rejects(kw, code, msg):
 def test_forward_logits_rejects():
     L = R.lib()
     # student given both ways
-    assert L.rkl_forward_logits(4, 100, 64, FAKE, FAKE, FAKE, FAKE, None, FAKE, FAKE, FAKE, 1 << 20, None) == 1
+    assert L.rkl_forward_logits(4, 100, 64, FAKE, FAKE, FAKE, FAKE, None, 0, None, FAKE, FAKE, FAKE, 1 << 20, None) == 1
     # student as logits but Hs != 0
-    assert L.rkl_forward_logits(4, 100, 64, None, None, FAKE, FAKE, None, FAKE, FAKE, None, 0, None) == 1
+    assert L.rkl_forward_logits(4, 100, 64, None, None, FAKE, FAKE, None, 0, None, FAKE, FAKE, None, 0, None) == 1
     # teacher logits missing
-    assert L.rkl_forward_logits(4, 100, 0, None, None, FAKE, None, None, FAKE, FAKE, None, 0, None) == 1
+    assert L.rkl_forward_logits(4, 100, 0, None, None, FAKE, None, None, 0, None, FAKE, FAKE, None, 0, None) == 1
     assert "z_t" in L.rkl_last_error().decode()
+    # a row index with no row count, or a misaligned one
+    assert L.rkl_forward_logits(4, 100, 0, None, None, FAKE, FAKE, FAKE, 0, None, FAKE, FAKE, None, 0, None) == 1
+    assert "T=" in L.rkl_last_error().decode()
+    assert L.rkl_forward_logits(4, 100, 0, None, None, FAKE, FAKE, MISALIGNED, 8, None, FAKE, FAKE, None, 0,
+                                None) == 1
+    assert "z_rows" in L.rkl_last_error().decode()
 
 
 def test_backward_rejects():
     L = R.lib()
     # student as logits: dh/dW must be NULL
-    assert L.rkl_backward_logits(4, 100, 0, None, None, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 0, FAKE,
+    assert L.rkl_backward_logits(4, 100, 0, None, None, FAKE, FAKE, None, 0, None, None, FAKE, FAKE, FAKE, 0, FAKE,
                                  None, 0, None) == 1
     # student hidden: dz must be NULL
-    assert L.rkl_backward_logits(4, 100, 64, FAKE, FAKE, None, FAKE, None, None, FAKE, FAKE, FAKE, 0, FAKE,
+    assert L.rkl_backward_logits(4, 100, 64, FAKE, FAKE, None, FAKE, None, 0, None, None, FAKE, FAKE, FAKE, 0, FAKE,
                                  FAKE, 1 << 30, None) == 1
     # workspace too small
     assert L.rkl_backward_hidden(4, 100, 64, 64, FAKE, FAKE, FAKE, FAKE, None, None, FAKE, FAKE, FAKE, 0,

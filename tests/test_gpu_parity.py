@@ -246,6 +246,52 @@ def test_student_hidden_teacher_logits(tdev, V):
     _check_against_oracle(case, _run_hidden(case, dev, g=case.grad, teacher_logits=True), g=case.grad)
 
 
+@pytest.mark.parametrize("V", [3000, 1001])
+def test_logits_read_through_row_index(tdev, V):
+    """z_rows: reading the logits rows through an index gives, bit for bit,
+    the results of the same rows gathered first -- for the compacted rows, a
+    shuffled order with repeats, and indices outside [0, T) (read as the
+    clamped row) -- with the student as hidden states (the tiled kernels;
+    V = 1001 takes the unvectorised z_t reads) and as logits (row kernels).
+    Several 128-token tiles with a ragged last one (N = 300 of T = 400)."""
+    torch, dev = tdev
+    T = 400
+    case = synth.random_case(70 + V, T=T, V=V, Hs=128, Ht=0, teacher_logits=True, p_mask=0.7, with_grad=True)
+    zs_case = synth.random_case(80 + V, T=T, V=V, Hs=0, Ht=0, student_logits=True, teacher_logits=True)
+    rng = np.random.default_rng(V)
+    idx_c = O.compact_rows(case.mask).astype(np.int32)
+    idx_s = rng.integers(0, T, size=300).astype(np.int32)
+    idx_o = idx_s.copy()
+    idx_o[::7] = T + 5
+    idx_o[3::11] = -2
+    zt_all = f32(case.z_t, dev)
+    Ws = bf16(case.W_s, dev)
+    zs_all, zt2_all = f32(zs_case.z_s, dev), f32(zs_case.z_t, dev)
+    for name, idx in (("compacted", idx_c), ("shuffled", idx_s), ("out of range", idx_o)):
+        say("logits through z_rows", name, V, idx.shape[0])
+        clamped = np.clip(idx, 0, T - 1).astype(np.int32)
+        rows = torch.from_numpy(idx).to(dev)
+        crow = torch.from_numpy(clamped).to(dev)
+        hs = R.gather_rows(bf16(case.h_s, dev), crow)
+        g = R.gather_rows(f32(case.grad, dev), crow)
+        # student projected
+        zt = R.gather_rows(zt_all, crow)
+        ref = R.forward_logits(zt, h_s=hs, W_s=Ws)
+        ref_b = R.backward_logits(zt, ref[1], h_s=hs, W_s=Ws, grad_loss=g)
+        got = R.forward_logits(zt_all, h_s=hs, W_s=Ws, z_rows=rows)
+        got_b = R.backward_logits(zt_all, got[1], h_s=hs, W_s=Ws, grad_loss=g, z_rows=rows)
+        for a, b, what in zip(got + got_b, ref + ref_b, ("loss", "stats", "dh", "dW")):
+            assert np.array_equal(host(a).view(np.uint32), host(b).view(np.uint32)), (name, what)
+        # student as logits
+        zs, zt2 = R.gather_rows(zs_all, crow), R.gather_rows(zt2_all, crow)
+        ref = R.forward_logits(zt2, z_s=zs)
+        ref_dz = R.backward_logits(zt2, ref[1], z_s=zs, grad_loss=g)
+        got = R.forward_logits(zt2_all, z_s=zs_all, z_rows=rows)
+        got_dz = R.backward_logits(zt2_all, got[1], z_s=zs_all, grad_loss=g, z_rows=rows)
+        for a, b, what in zip(got + (got_dz,), ref + (ref_dz,), ("loss", "stats", "dz")):
+            assert np.array_equal(host(a).view(np.uint32), host(b).view(np.uint32)), (name, what)
+
+
 def test_logits_payload_equals_hidden_payload(tdev):
     """Teacher logits = fp32 rounding of h_t W_t^T: both payload paths agree."""
     torch, dev = tdev
