@@ -1267,25 +1267,50 @@ __global__ __launch_bounds__(256) void bwd_rows_logits(const float* __restrict__
 //   L_hat = sum_{j in S} p_j f_j + [y not in S] f_y,
 //   dz_j  = g (-p_j c + [j in S] p_j (f_j + 1) + [j = y, y not in S] sp),
 //   c = sum_{j in S} p_j (f_j + 1) + [y not in S] sp,   sp = f_y + 1.
-// The student logits on the support come from a wave-wide dot product of
-// the row of h with the support's rows of W (fp32, fixed reduction order, so
-// the backward recomputes exactly the forward's values).
+// The student logits on the support come from wave-wide dot products of the
+// row of h with the support's rows of W, kTopkBatch support ids at a time so
+// that their row loads are in flight together (fp32; each lane accumulates
+// its slice in a fixed order, then a fixed butterfly: the backward
+// recomputes exactly the forward's values).
 // ===========================================================================
-__device__ __forceinline__ float wave_dot_bf16(const uint16_t* __restrict__ a, const uint16_t* __restrict__ b, int H,
-                                               int lane) {
-  float acc = 0.f;
-  for (int c = lane * 8; c < H; c += 512) {
-    const u32x4 x = *reinterpret_cast<const u32x4*>(a + c);
-    const u32x4 w = *reinterpret_cast<const u32x4*>(b + c);
+constexpr int kTopkBatch = 8;
+
+// z[b] = h . W[j[b]] for the ids of one batch (ids outside [0, V) read row 0;
+// their values are not used).
+__device__ __forceinline__ void wave_dots_bf16(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
+                                               const int (&j)[kTopkBatch], int V, int H, int lane,
+                                               float (&z)[kTopkBatch]) {
+  const uint16_t* row[kTopkBatch];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      acc = fmaf(__builtin_bit_cast(float, x[e] << 16), __builtin_bit_cast(float, w[e] << 16), acc);
-      acc = fmaf(__builtin_bit_cast(float, x[e] & 0xffff0000u), __builtin_bit_cast(float, w[e] & 0xffff0000u), acc);
-    }
+  for (int b = 0; b < kTopkBatch; ++b) {
+    z[b] = 0.f;
+    row[b] = W + (int64_t)((j[b] >= 0 && j[b] < V) ? j[b] : 0) * H;
+  }
+  for (int c = lane * 8; c < H; c += 512) {
+    const u32x4 x = *reinterpret_cast<const u32x4*>(h + c);
+    u32x4 w[kTopkBatch];
+#pragma unroll
+    for (int b = 0; b < kTopkBatch; ++b) w[b] = *reinterpret_cast<const u32x4*>(row[b] + c);
+#pragma unroll
+    for (int b = 0; b < kTopkBatch; ++b)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        z[b] = fmaf(__builtin_bit_cast(float, x[e] << 16), __builtin_bit_cast(float, w[b][e] << 16), z[b]);
+        z[b] = fmaf(__builtin_bit_cast(float, x[e] & 0xffff0000u), __builtin_bit_cast(float, w[b][e] & 0xffff0000u),
+                    z[b]);
+      }
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-  return acc;
+  for (int b = 0; b < kTopkBatch; ++b)
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) z[b] += __shfl_xor(z[b], o);
+}
+
+// The support ids k0 .. k0 + kTopkBatch - 1 of row t (-1 past K).
+__device__ __forceinline__ void topk_batch_ids(const int32_t* __restrict__ S, int64_t t, int K, int k0,
+                                               int (&j)[kTopkBatch]) {
+#pragma unroll
+  for (int b = 0; b < kTopkBatch; ++b) j[b] = k0 + b < K ? S[t * K + k0 + b] : -1;
 }
 
 // One wave per row.  stats on entry: (lse, -, log p(y), -) from the
@@ -1313,16 +1338,22 @@ __global__ __launch_bounds__(256) void topk_terms(const uint16_t* __restrict__ h
   const int yt = y[t];
   float L = 0.f, c = 0.f, bnd = 0.f;
   bool in = false;
-  for (int k = 0; k < K; ++k) {
-    const int j = S[(int64_t)t * K + k];
-    if (j < 0 || j >= V) continue;
-    const float lp = wave_dot_bf16(h + (int64_t)t * H, W + (int64_t)j * H, H, lane) - lse;
-    const float f = lp - lpt_S[(int64_t)t * K + k];
-    const float pr = expf(lp);
-    L = fmaf(pr, f, L);
-    c = fmaf(pr, f + 1.f, c);
-    bnd = fmaxf(bnd, pr * fabsf(f + 1.f));
-    in = in || j == yt;
+  for (int k0 = 0; k0 < K; k0 += kTopkBatch) {
+    int j[kTopkBatch];
+    float z[kTopkBatch];
+    topk_batch_ids(S, t, K, k0, j);
+    wave_dots_bf16(h + (int64_t)t * H, W, j, V, H, lane, z);
+#pragma unroll
+    for (int b = 0; b < kTopkBatch; ++b) {
+      if (j[b] < 0 || j[b] >= V) continue;
+      const float lp = z[b] - lse;
+      const float f = lp - lpt_S[(int64_t)t * K + k0 + b];
+      const float pr = expf(lp);
+      L = fmaf(pr, f, L);
+      c = fmaf(pr, f + 1.f, c);
+      bnd = fmaxf(bnd, pr * fabsf(f + 1.f));
+      in = in || j[b] == yt;
+    }
   }
   float sp = 0.f;
   if (!in) {
@@ -1354,15 +1385,28 @@ __global__ __launch_bounds__(256) void topk_dz_add(const uint16_t* __restrict__ 
   if (t >= N || (row_mask && row_mask[t] == 0)) return;
   const float gs = (grad ? grad[t] : 1.0f) * __builtin_bit_cast(float, scales[kScaleS]);
   const float lse = stats[4 * (int64_t)t];
-  for (int k = 0; k < K; ++k) {
-    const int j = S[(int64_t)t * K + k];
-    if (j < 0 || j >= V || j < c0 || j >= c0 + width) continue;
-    const float lp = wave_dot_bf16(h + (int64_t)t * H, W + (int64_t)j * H, H, lane) - lse;
-    const float f = lp - lpt_S[(int64_t)t * K + k];
-    if (lane == 0) {
-      uint16_t* e = dz + (int64_t)t * ldz + (j - c0);
-      const float v = (float)__builtin_bit_cast(_Float16, *e) + gs * expf(lp) * (f + 1.f);
-      *e = __builtin_bit_cast(uint16_t, (_Float16)__builtin_amdgcn_fmed3f(v, -65504.f, 65504.f));
+  for (int k0 = 0; k0 < K; k0 += kTopkBatch) {
+    int j[kTopkBatch];
+    float z[kTopkBatch];
+    topk_batch_ids(S, t, K, k0, j);
+    bool any = false;   // an id of the batch in this chunk (wave-uniform)
+#pragma unroll
+    for (int b = 0; b < kTopkBatch; ++b) {
+      if (j[b] < c0 || j[b] >= c0 + width || j[b] >= V) j[b] = -1;
+      any = any || j[b] >= 0;
+    }
+    if (!any) continue;
+    wave_dots_bf16(h + (int64_t)t * H, W, j, V, H, lane, z);
+#pragma unroll
+    for (int b = 0; b < kTopkBatch; ++b) {
+      if (j[b] < 0) continue;
+      const float lp = z[b] - lse;
+      const float f = lp - lpt_S[(int64_t)t * K + k0 + b];
+      if (lane == 0) {
+        uint16_t* e = dz + (int64_t)t * ldz + (j[b] - c0);
+        const float v = (float)__builtin_bit_cast(_Float16, *e) + gs * expf(lp) * (f + 1.f);
+        *e = __builtin_bit_cast(uint16_t, (_Float16)__builtin_amdgcn_fmed3f(v, -65504.f, 65504.f));
+      }
     }
   }
 }
