@@ -738,8 +738,8 @@ def main():
     if args.report_c5:
         return report_c5()
     if args.gpus != 1:
-        print(f"bench.py: this build runs on exactly one GPU (asked for --gpus {args.gpus}); "
-              f"the multi-GPU sharding is described but not built", file=sys.stderr)
+        print(f"bench.py measures one GPU (asked for --gpus {args.gpus}): the library has no collectives; "
+              f"a vocabulary-parallel rank's share is the vocab_shard workload", file=sys.stderr)
         sys.exit(2)
     {"reverse_kl": bench_reverse_kl, "logprob_entropy": bench_logprob_entropy, "teachers": bench_teachers,
      "vocab_shard": bench_vocab_shard, "topk": bench_topk}[args.workload](args)

@@ -140,8 +140,14 @@ def test_self_distillation_perturbed_logits_vs_hidden(tdev):
     Ll, sl = R.forward_logits(z_t, h_s=h, W_s=Ws)
     dh_l, dW_l = R.backward_logits(z_t, sl, h_s=h, W_s=Ws)
     torch.cuda.synchronize()
-    del z_t
     Ll, sl, dh_l, dW_l = host(Ll), host(sl), host(dh_l), host(dW_l)
+    say("perturbed: logits path through an identity row index")
+    ident = torch.arange(case.T, dtype=torch.int32, device=dev)
+    Li, si = R.forward_logits(z_t, h_s=h, W_s=Ws, z_rows=ident)
+    dh_i, dW_i = R.backward_logits(z_t, si, h_s=h, W_s=Ws, z_rows=ident)
+    for a, b2, what in ((Li, Ll, "loss"), (si, sl, "stats"), (dh_i, dh_l, "dh"), (dW_i, dW_l, "dW")):
+        assert np.array_equal(host(a).view(np.uint32), b2.view(np.uint32)), what
+    del z_t, Li, si, dh_i, dW_i
     assert_loss_close(Ll, Lh, "logits vs hidden loss")
     assert_grad_close(dh_l, dh_h, "logits vs hidden dh")
     assert_grad_close(dW_l, dW_h, "logits vs hidden dW")
