@@ -12,9 +12,9 @@
 // (vocabulary along MFMA rows, tokens along MFMA columns).  In the 32x32 MFMA
 // output layout one lane then holds one token and 16 vocabulary entries per
 // block, so the online log-sum-exp / KL statistics of a token live in that
-// lane's registers for the whole vocabulary sweep; lanes l and l^32 (the two
-// row halves) merge once at the end, then the waves that share tokens merge
-// through LDS.
+// lane's registers for the whole sweep of a vocabulary split; lanes l and
+// l^32 (the two row halves) merge when the split ends, then the waves that
+// share tokens merge through LDS.
 #include "rkl_tile.h"
 #include "rkl_internal.h"
 
@@ -45,9 +45,10 @@ __device__ __forceinline__ void merge2(float& m, float& s, float m2, float s2) {
 }
 
 // ===========================================================================
-// Fused forward: per (vocabulary split, token tile) workgroup, sweep the
-// split's vocabulary tiles; for each tile form z_s (and z_t) in registers with
-// MFMA and fold them into per-lane online statistics
+// Fused forward: per (run of vocabulary splits, token tile) workgroup, sweep
+// the splits' vocabulary tiles; for each tile form z_s (and z_t) in registers
+// with MFMA and fold them into per-lane online statistics, written out per
+// split
 //   m_s, S_s = sum e^{z_s - m_s}, A = sum e^{z_s - m_s} (z_s - z_t), m_t, S_t.
 // Nothing of size [N, V] is written.
 // ===========================================================================
