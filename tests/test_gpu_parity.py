@@ -6,6 +6,8 @@ Bars: per-token |dL| <= 1e-4 + 1e-3|L|; gradients max|d| <= 2e-3 max|ref|;
 compaction, gather and scatter bit-exact; exact zeros where the method gives
 exact zeros (unmasked rows, self-distillation).
 """
+import copy
+
 import numpy as np
 import pytest
 
@@ -151,6 +153,43 @@ def _check_against_oracle(case, out, g=None):
         assert_loss_close(stats[:, 1], lt, "lse_t")
     assert_grad_close(dh, b["dh"], "dh")
     assert_grad_close(dW, b["dW"], "dW")
+
+
+def _random_shapes(n=12, seed=2024):
+    """Seeded random shapes: T in [1, 700], V in [1, 6000] (tails of every
+    size, including V < one 256-row tile), widths multiples of 64 up to 512,
+    mask densities from 0.05 to 1."""
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        T = int(rng.integers(1, 701))
+        V = int(rng.choice([int(rng.integers(1, 257)), int(rng.integers(257, 6001))]))
+        Hs, Ht = (64 * int(rng.integers(1, 9)) for _ in range(2))
+        p = float(rng.choice([0.05, 0.3, 0.7, 1.0]))
+        out.append((i, T, V, Hs, Ht, p))
+    return out
+
+
+@pytest.mark.parametrize("i,T,V,Hs,Ht,p", _random_shapes())
+def test_random_shapes_both_payloads(tdev, i, T, V, Hs, Ht, p):
+    """Seeded random shapes through both payloads (the teacher as hidden
+    states, and as the fp32 rounding of its logits) against the oracle."""
+    torch, dev = tdev
+    case = synth.random_case(5000 + i, T=T, V=V, Hs=Hs, Ht=Ht, p_mask=p, with_grad=True)
+    if int(case.mask.sum()) == 0:
+        case.mask[T // 2] = 1
+    say("random shape", i, T, V, Hs, Ht, p)
+    _check_against_oracle(case, _run_hidden(case, dev, g=case.grad), g=case.grad)
+    lg = copy.copy(case)
+    lg.z_t = O.project_f32(case.h_t, case.W_t)
+    lg.h_t = lg.W_t = None
+    say("random shape, teacher logits", i)
+    idx, loss, stats, dh, dW = _run_hidden(lg, dev, g=lg.grad, teacher_logits=True)
+    rows = O.compact_rows(lg.mask)
+    inp, (L, ls, lt), b = oracle_full(lg, rows, lg.grad[rows])
+    assert_loss_close(loss, L, "loss (teacher logits)")
+    assert_grad_close(dh, b["dh"], "dh (teacher logits)")
+    assert_grad_close(dW, b["dW"], "dW (teacher logits)")
 
 
 def test_hidden_small(tdev):
