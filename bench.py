@@ -11,7 +11,8 @@ every one of the T = B(S-1) = 4096 positions trainable (N = 4096), Hs = Ht =
 2048, V = 151936, bf16 inputs (synthetic, seeded), fp32 accumulation.
 
 --payload logits times the same step with the teacher given as fp32 logits
-[N, V] (formed once from the same tensors) instead of hidden states.
+[T, V] (formed once from the same tensors) instead of hidden states; the
+kernels read the compacted rows through the row index (no [N, V] copy).
 
 --workload logprob_entropy times the compact actor path instead: per row the
 log-probability of a sampled token and the entropy of softmax(h_s W_s^T)
