@@ -22,8 +22,10 @@
  * Conventions shared by every entry point
  *   - Pointers without a "host" note are device pointers (hipMalloc'd or
  *     torch CUDA tensors) on the current device.  Every buffer is owned by
- *     the caller; the library allocates no device memory, keeps no state
- *     between calls, and may be called from several host threads.
+ *     the caller; the library allocates no device memory (the fixed scratch
+ *     array of rkl_noalloc.h aside), keeps no state between calls (the
+ *     events of rkl_kernel_timing aside), and may be called from several
+ *     host threads.
  *   - bf16 values are passed as raw 16-bit patterns (rkl_bf16).  Matrices are
  *     row-major and densely packed: h [rows, H], W [V, H] (the nn.Linear /
  *     output-layer layout), logits [rows, V].
