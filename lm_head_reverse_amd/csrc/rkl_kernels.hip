@@ -950,43 +950,58 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
                       [&](int fn) { load_zt<VEC4, true>(zt, p.z_t, p.V, vr, zr, fn); });
       }
     }
-    // Stores go through the free LDS stage, 64 tokens per round: the waves
-    // holding those tokens write a [64 token][256 vocabulary] fp16 tile (16-byte
-    // chunk c of row t at chunk c ^ (t % 32), so neither side has bank
-    // conflicts), then every thread stores 16-byte pieces of whole rows: 512
-    // contiguous bytes per token row instead of 32 rows per store instruction.
+    // Stores go through LDS: the waves holding a round's tokens write a
+    // [tokens][256 vocabulary] fp16 tile (16-byte chunk c of row t at chunk
+    // c ^ (t % 32), so neither side has bank conflicts), then every thread
+    // stores 16-byte pieces of whole rows: 512 contiguous bytes per token
+    // row instead of 32 rows per store instruction.  Mid-stream only the
+    // free stage (48 KB) can hold the tile: two rounds of 64 tokens.  After
+    // the stream's last k-tile every stage is free once its DMAs have
+    // landed: one round of all 128 tokens, every wave writing at once.
+    auto store = [&](char* buf, auto rounds) {
+      constexpr int NR = decltype(rounds)::value, TPR = FBN / NR;
 #pragma unroll
-    for (int round = 0; round < 2; ++round) {
-      if (wn == round) {
+      for (int round = 0; round < NR; ++round) {
+        if (NR == 1 || wn == round) {
 #pragma unroll
-        for (int fn = 0; fn < FFN; ++fn) {
-          const int tl = fn * 32 + (lane & 31);   // token within the round
+          for (int fn = 0; fn < FFN; ++fn) {
+            const int tl = (NR == 1 ? brow0 : 0) + fn * 32 + (lane & 31);   // token within the round
 #pragma unroll
-          for (int fm = 0; fm < FFM; ++fm)
+            for (int fm = 0; fm < FFM; ++fm)
 #pragma unroll
-            for (int pr = 0; pr < 2; ++pr) {
-              const int c = (arow0 + fm * 32 + 16 * pr + 8 * hi) >> 3;
-              *reinterpret_cast<u32x4*>(stage + tl * 512 + ((c ^ (tl & 31)) << 4)) =
-                  u32x4{pk[fm][fn][pr][0], pk[fm][fn][pr][1], pk[fm][fn][pr][2], pk[fm][fn][pr][3]};
-            }
+              for (int pr = 0; pr < 2; ++pr) {
+                const int c = (arow0 + fm * 32 + 16 * pr + 8 * hi) >> 3;
+                *reinterpret_cast<u32x4*>(buf + tl * 512 + ((c ^ (tl & 31)) << 4)) =
+                    u32x4{pk[fm][fn][pr][0], pk[fm][fn][pr][1], pk[fm][fn][pr][2], pk[fm][fn][pr][3]};
+              }
+          }
         }
-      }
-      dma_barrier<63>();
-      // thread tid stores token row tr = it * kThreads / 32 + tid / 32 of the
-      // round, columns col .. col + 7: a wave-uniform row base plus a 32-bit
-      // lane offset (tid / 32) * ldz + (tid % 32) * 8 (no 64-bit per-lane
-      // addresses live across the main loop)
-      const int c = tid & 31;
-      const int col = v0 - p.c0 + c * 8;
-      const uint32_t loff = (uint32_t)(tid >> 5) * (uint32_t)p.ldz + (uint32_t)(c * 8);
+        dma_barrier<63>();
+        // thread tid stores token row tr = it * kThreads / 32 + tid / 32 of
+        // the round, columns col .. col + 7: a wave-uniform row base plus a
+        // 32-bit lane offset (tid / 32) * ldz + (tid % 32) * 8 (no 64-bit
+        // per-lane addresses live across the main loop)
+        const int c = tid & 31;
+        const int col = v0 - p.c0 + c * 8;
+        const uint32_t loff = (uint32_t)(tid >> 5) * (uint32_t)p.ldz + (uint32_t)(c * 8);
 #pragma unroll
-      for (int it = 0; it < 64 * 32 / F::kThreads; ++it) {
-        const int tr = it * (F::kThreads / 32) + (tid >> 5);
-        const u32x4 x = *reinterpret_cast<const u32x4*>(stage + tr * 512 + ((c ^ (tr & 31)) << 4));
-        uint16_t* rb = p.dz + (int64_t)(n0 + round * 64 + it * (F::kThreads / 32)) * p.ldz + (v0 - p.c0);
-        if (col < p.kpad) *reinterpret_cast<u32x4*>(rb + loff) = x;
+        for (int it = 0; it < TPR * 32 / F::kThreads; ++it) {
+          const int tr = it * (F::kThreads / 32) + (tid >> 5);
+          const u32x4 x = *reinterpret_cast<const u32x4*>(buf + tr * 512 + ((c ^ (tr & 31)) << 4));
+          uint16_t* rb = p.dz + (int64_t)(n0 + round * TPR + it * (F::kThreads / 32)) * p.ldz + (v0 - p.c0);
+          if (col < p.kpad) *reinterpret_cast<u32x4*>(rb + loff) = x;
+        }
+        // buf is written again by the next round or the next k-tile's DMA
+        // (after the last job nothing writes LDS again)
+        if (NR > 1) dma_barrier<63>();
       }
-      dma_barrier<63>();
+    };
+    static_assert(FBN * FBM * 2 <= 3 * FwdStages::kStage, "one round needs the whole tile in the LDS ring");
+    if (vt0 + job + 1 == vt1) {
+      dma_barrier<0>();   // every DMA landed, every fragment read done: the whole ring is free
+      store(lds, std::integral_constant<int, 1>{});
+    } else {
+      store(stage, std::integral_constant<int, 2>{});
     }
   }, convert_w);
 }
