@@ -27,6 +27,10 @@ runs of rows; interleaved: i.i.d. ids, so every tile holds several teachers).
 student tensors: the teacher's payload is its log-probabilities at its --topk
 K largest logits and at a sampled token per row.
 
+--dp-ranks G times one rank's share of a G-way data-parallel group: the
+first T/G positions of the same workload with the weights replicated (the
+rows are independent: no exchange but the trainer's dW all-reduce).
+
 --workload vocab_shard times one rank's share of a --shards G-way
 vocabulary-parallel step on the same tensors: the shard forward over its
 V/G vocabulary rows, the merge of all G shards' partials (the other shards'
@@ -90,6 +94,9 @@ def parse():
                          "step, or the top-k estimator")
     ap.add_argument("--topk", type=int, default=64, help="support size K for --workload topk")
     ap.add_argument("--shards", type=int, default=8, help="vocabulary shards for --workload vocab_shard")
+    ap.add_argument("--dp-ranks", type=int, default=1,
+                    help="reverse_kl workload: time one rank's share of a data-parallel group of this many "
+                         "ranks (the first T/ranks positions, weights replicated)")
     ap.add_argument("--teachers", type=int, default=4, help="teachers for --workload teachers")
     ap.add_argument("--teacher-order", choices=("grouped", "interleaved"), default="grouped",
                     help="row order for --workload teachers")
@@ -447,7 +454,13 @@ def bench_reverse_kl(args):
     dev = torch.device("cuda:0")
     print("[bench] generating inputs", file=sys.stderr, flush=True)
     case = synth.config("headline")
+    G = args.dp_ranks
+    if G < 1 or case.T % G:
+        raise SystemExit(f"bench.py: --dp-ranks must divide T={case.T}")
     T, V, Hs, Ht = case.T, case.V, case.Hs, case.Ht
+    if G > 1:   # one data-parallel rank: its T/G positions, the weights replicated
+        T = case.T // G
+        case.h_s, case.h_t, case.mask = case.h_s[:T], case.h_t[:T], case.mask[:T]
     h_s_all, h_t_all = bf16_dev(case.h_s, dev), bf16_dev(case.h_t, dev)
     W_s, W_t = bf16_dev(case.W_s, dev), bf16_dev(case.W_t, dev)
     logits = args.payload == "logits"
@@ -491,11 +504,15 @@ def bench_reverse_kl(args):
                           "B=4 S=1025 (T=N=4096 trainable), Hs=Ht=2048, V=151936",
               "B": case.B, "S": case.S, "N": int(N), "Hs": Hs, "Ht": Ht_eff, "V": V,
               "payload": "logits" if logits else "hidden_states", "parallelism": "single GPU"}
+    if G > 1:
+        config["workload"] += f"; one rank of {G}-way data parallelism: its {T} positions"
+        config["parallelism"] = f"one rank's share of dp{G}"
     if os.environ.get("RKL_VOCAB_CHUNK"):
         config["backward_vocab_chunk"] = int(os.environ["RKL_VOCAB_CHUNK"])
+    headline = not logits and G == 1 and not os.environ.get("RKL_VOCAB_CHUNK")
     out = emit(args, METRIC, N, wall, times, work, flop_fwd, flop_step, config,
-               traffic=None if logits or os.environ.get("RKL_VOCAB_CHUNK") else recorded_traffic())
-    if not args.no_cpu_baseline and not logits:
+               traffic=recorded_traffic() if headline else None)
+    if not args.no_cpu_baseline and headline:
         print("[bench] oracle cpu baseline", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(case, args.cpu_seconds)
     print(json.dumps(out), flush=True)

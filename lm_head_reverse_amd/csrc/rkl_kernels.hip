@@ -824,6 +824,7 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
   constexpr int FFM = F::FM, FFN = F::FN;
   __shared__ __attribute__((aligned(1024))) char lds[3 * FwdStages::kStage];
   __shared__ uint32_t tset_lds;
+  __shared__ uint32_t wmag_lds[F::kThreads / 64];   // per wave: largest |W_s| bits it converted
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w >> 1, wn = w & 1;
   const int logical = xcd_logical(blockIdx.x, p.ngroups * p.ntok);
   int grp, tt;
@@ -892,7 +893,11 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
   // Rows past V hold the clamped copies of row V-1 the DMA brought in.  The
   // copy is unscaled; the largest magnitude converted goes to the chunk's
   // record, from which w_rescale decides whether the copy must be made again
-  // with a scale.
+  // with a scale: each wave keeps its running maximum in LDS, and the
+  // workgroup takes one atomic maximum at its end (atomics on one address
+  // serialise in L2: one per wave and conversion -- eight per job at 512
+  // rows -- capped the kernel near 1.9 ms whatever N).
+  if (lane == 0) wmag_lds[w] = 0u;
   auto convert_w = [&](const char* stage, int job, int kt) {
     if (kt % p.ntok != tt % p.ntok) return;
     // thread tid converts rows r = i * kThreads / 8 + tid / 8, 16-byte piece
@@ -909,7 +914,7 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
       *reinterpret_cast<f16x8*>(rb + loff) = bf16_to_f16(__builtin_bit_cast(bf16x8, x));
     }
     mag = wave_max_u32(mag);
-    if (lane == 0 && mag) atomicMax(p.wmag, mag);
+    if (lane == 0) wmag_lds[w] = max(wmag_lds[w], mag);   // this wave's slot only
     // the next k-tile's DMA writes this stage: every wave's reads first
     // (the condition above is the same for the whole workgroup)
     dma_barrier<63>();
@@ -1004,6 +1009,13 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
       store(stage, std::integral_constant<int, 2>{});
     }
   }, convert_w);
+  // the stream ended with a workgroup barrier: every wave's slot is final
+  if (tid == 0) {
+    uint32_t m = 0;
+#pragma unroll
+    for (int i = 0; i < F::kThreads / 64; ++i) m = max(m, wmag_lds[i]);
+    if (m) atomicMax(p.wmag, m);
+  }
 }
 
 // h_s [N, H] bf16 -> hT [H, ldT] fp16 = fp16(2^kh h_s) (2^kh from the
