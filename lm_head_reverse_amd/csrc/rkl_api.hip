@@ -82,9 +82,8 @@ bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0
 constexpr int64_t kMaxPitchElems = (int64_t)1 << 22;
 
 // Vocabulary columns per backward chunk for N rows: as many whole
-// kDhSegment-column segments as keep the chunk's fp16 dz within 2 GiB, at
-// least one (262144 columns at N <= 4096, one 65536-column segment for
-// N > 8192).  Fewer chunks mean fewer launches and no narrow tail
+// kChunkUnit (65536) columns as keep the chunk's fp16 dz within 2 GiB, at
+// least one unit (262144 columns at N <= 4096, 65536 for N > 8192).  Fewer chunks mean fewer launches and no narrow tail
 // chunk; chunks on segment boundaries keep dh's bits independent of N.
 // RKL_VOCAB_CHUNK overrides it (a multiple of 256; widths that are not a
 // multiple of kDhSegment change where dh's sum is split, i.e. its rounding).
@@ -96,9 +95,9 @@ int64_t vocab_chunk(int64_t N) {
     return round_up(v, 256);
   }
   const int64_t budget = (int64_t)1 << 31;   // bytes of fp16 dz per chunk
-  int64_t segs = budget / (2 * (N > 0 ? N : 1) * (int64_t)rkl::kDhSegment);
-  if (segs < 1) segs = 1;
-  const int64_t C = segs * rkl::kDhSegment;
+  int64_t units = budget / (2 * (N > 0 ? N : 1) * (int64_t)rkl::kChunkUnit);
+  if (units < 1) units = 1;
+  const int64_t C = units * rkl::kChunkUnit;
   return C < kMaxPitchElems ? C : kMaxPitchElems;
 }
 
@@ -195,13 +194,36 @@ size_t fwd_ws_bytes(int64_t N, int64_t V, bool tiled) {
   return align256((size_t)fwd_split(V).nsplit * 5 * (size_t)N * sizeof(float));
 }
 
+// Whether the dh GEMM runs one workgroup per (tile, vocabulary segment),
+// writing segment sums that a reduce adds in order, instead of one
+// workgroup per tile summing every segment: when the tiles alone would not
+// fill the CUs (N below 4096 at Hs = 2048).  Same bits either way.  Measured
+// at Hs = 2048, V = 151936 (ten 16384-column segments), split against one
+// workgroup per tile: dh 500 against 1921 us at N = 512 (32 tiles), 737
+// against 1903 at N = 1024, 1221 + 34 (the reduce) against 1888 at N = 2048.
+// RKL_DH_SPLIT = 0 / 1 forces it off / on.
+bool dh_split(int64_t N, int64_t Hs) {
+  if (const char* s = std::getenv("RKL_DH_SPLIT")) {
+    if (s[0] == '0') return false;
+    if (s[0] == '1') return true;
+  }
+  return ceil_div(N, rkl::kDhTileM) * ceil_div(Hs, rkl::kDhTileN) < kCUs;
+}
+
+// dh segments a chunk [c0, c0 + width) overlaps (segments end at absolute
+// multiples of kDhSegment).
+int64_t dh_segments(int64_t c0, int64_t width) {
+  return (c0 + width - 1) / rkl::kDhSegment - c0 / rkl::kDhSegment + 1;
+}
+
 struct BwdLayout {
-  int64_t ldT, ldz, npad, nchunks;
-  size_t off_hT, off_dz, off_w16, off_scale, total;
+  int64_t ldT, ldz, npad, nchunks, nseg;
+  size_t off_hT, off_dz, off_w16, off_dhp, off_scale, total;
 };
 // [scale block: rkl::kScaleWmag + nchunks words][hT: Hs x ldT fp16][dz chunk:
-// npad x ldz fp16][fp16 W_s chunk copy]; npad = N rounded up to the 128-token
-// tile (the dz kernel writes those rows as zero)
+// npad x ldz fp16][fp16 W_s chunk copy][dh segment sums nseg x N x Hs fp32,
+// when dh is split]; npad = N rounded up to the 128-token tile (the dz
+// kernel writes those rows as zero)
 BwdLayout bwd_layout(int64_t N, int64_t V, int64_t Hs) {
   BwdLayout L{};
   L.ldT = round_up(N, 64);
@@ -209,12 +231,19 @@ BwdLayout bwd_layout(int64_t N, int64_t V, int64_t Hs) {
   const int64_t C = vocab_chunk(N);
   L.ldz = round_up(V < C ? V : C, 64);
   L.nchunks = ceil_div(V, C);
+  // most segments one chunk overlaps
+  L.nseg = 0;
+  for (int64_t c0 = 0; c0 < V; c0 += C) {
+    const int64_t n = dh_segments(c0, (V - c0) < C ? (V - c0) : C);
+    if (n > L.nseg) L.nseg = n;
+  }
   L.off_scale = 0;
   L.off_hT = align256((size_t)(rkl::kScaleWmag + L.nchunks) * 4);
   L.off_dz = L.off_hT + align256((size_t)Hs * L.ldT * 2);
   L.off_w16 = L.off_dz + align256((size_t)L.npad * L.ldz * 2);
   // the fp16 W_s copy covers every 256-row vocabulary tile of a chunk
-  L.total = L.off_w16 + align256((size_t)round_up(L.ldz, rkl::kFwdTileV) * Hs * 2);
+  L.off_dhp = L.off_w16 + align256((size_t)round_up(L.ldz, rkl::kFwdTileV) * Hs * 2);
+  L.total = L.off_dhp + (dh_split(N, Hs) ? align256((size_t)L.nseg * N * Hs * 4) : 0);
   return L;
 }
 
@@ -416,7 +445,10 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
     h.ntm = (int)ceil_div(N, rkl::kDhTileM);
     h.ntn = (int)ceil_div(Hs, rkl::kDhTileN);
     h.panel = dh_panel(h.ntn);
+    h.nseg = (int)dh_segments(c0, kpad);
+    h.partial = dh_split(N, Hs) ? reinterpret_cast<float*>(base + L.off_dhp) : nullptr;
     RKL_LAUNCH("dh_gemm", s, rkl::launch_dh(h, s));
+    if (h.partial) RKL_LAUNCH("dh_reduce", s, rkl::launch_dh_reduce(h, s));
   }
   return RKL_OK;
 }

@@ -82,6 +82,12 @@ struct DhParams {
   int accumulate;
   int ntm, ntn;
   int panel;               // column tiles per panel of the workgroup order
+  // Split by segment (grids of fewer tiles than CUs): workgroup (tile, s)
+  // writes segment s's raw fp32 sum to partial [nseg][N][H], and dh_reduce
+  // adds them in segment order.  partial NULL: one workgroup per tile sums
+  // every segment itself.
+  float* partial;
+  int nseg;
 };
 
 // Waves per workgroup: the fused kernels (two waves per SIMD, 64 x 64 of both
@@ -113,8 +119,13 @@ constexpr int kFwdTileN = 128;
 constexpr int kDwTileM = 256, kDwTileN = 256;
 constexpr int kDhTileM = 256, kDhTileN = 128;
 // dh's fp32 sum over the vocabulary is split at multiples of this column
-// index (absolute), whatever the backward's chunk width.
-constexpr int kDhSegment = 65536;
+// index (absolute), whatever the backward's chunk width or the dh GEMM's
+// grid: each segment is summed from zero and the segment sums are added in
+// order.
+constexpr int kDhSegment = 16384;
+// The backward's vocabulary chunks are whole multiples of this many columns
+// (a multiple of kDhSegment).
+constexpr int kChunkUnit = 65536;
 
 // What the fused kernels compute.
 enum Mode : int {
@@ -160,6 +171,7 @@ hipError_t launch_w_rescale(const uint16_t* W_chunk, int rows, int ntv, int H, c
                             hipStream_t s);
 hipError_t launch_dw(const DwParams& p, hipStream_t s);
 hipError_t launch_dh(const DhParams& p, hipStream_t s);
+hipError_t launch_dh_reduce(const DhParams& p, hipStream_t s);
 // merged != NULL: the unfinalised (m_s, S_s, A, m_t, S_t) planes instead of loss / stats
 hipError_t launch_fwd_rows_logits(const float* z_s, const float* z_t, const int32_t* z_rows, int z_nrows, int N, int V,
                                   const uint8_t* row_mask, float* loss, float* stats, float* merged, hipStream_t s);

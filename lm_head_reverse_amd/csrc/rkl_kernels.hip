@@ -1127,7 +1127,9 @@ __global__ __launch_bounds__(64 * NW, 1) void dw_gemm(DwParams p) {
 // running total in order.  Chunks that start on segment boundaries thus give
 // the same bits whatever their width (a chunk's total leaves through memory,
 // scaled by the power of two 1/s, which commutes with the additions), so dh
-// does not depend on N through the chunk plan.
+// does not depend on N through the chunk plan.  With fewer tiles than CUs
+// (small N) each (tile, segment) is a workgroup of its own that writes its
+// segment sum, and dh_reduce adds them in the same order: the same bits.
 // ===========================================================================
 constexpr int HBM = kDhTileM, HBN = kDhTileN, HKT = 64, HNST = 3, HDSTEPS = 3;
 
@@ -1140,8 +1142,11 @@ __global__ __launch_bounds__(64 * NW, 1) void dh_gemm(DhParams p) {
   __shared__ __attribute__((aligned(1024))) char lds[HNST * (TA::kBytes + TB::kBytes)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / HGN, wn = w % HGN;
   // workgroup order: panels of p.panel column tiles, all row tiles of a
-  // panel consecutive (each XCD takes a contiguous run of them)
-  const int logical = xcd_logical(blockIdx.x, p.ntm * p.ntn);
+  // panel consecutive (each XCD takes a contiguous run of them); split by
+  // segment, the segment is the slowest index
+  const int ntiles = p.ntm * p.ntn;
+  const int logical0 = xcd_logical(blockIdx.x, ntiles * (p.partial ? p.nseg : 1));
+  const int seg = logical0 / ntiles, logical = logical0 - seg * ntiles;
   const int per = p.panel * p.ntm, panel = logical / per, r = logical - panel * per;
   const int width = min(p.panel, p.ntn - panel * p.panel);
   const int tm = r / width, tn = panel * p.panel + (r - (r / width) * width);
@@ -1151,8 +1156,31 @@ __global__ __launch_bounds__(64 * NW, 1) void dh_gemm(DhParams p) {
   // A: dz rows are tokens (m; npad zero-padded rows), columns vocabulary (k,
   // zero past the chunk width); B: the fp16 copy of the W_s chunk, rows
   // vocabulary (k; the copy covers every k-tile), columns hidden units (n).
-  for (int k0 = 0; k0 < p.kpad;) {
-    const int k1 = min(p.kpad, ((p.c0 + k0) / kDhSegment + 1) * kDhSegment - p.c0);
+  // the two operand scales, undone at once at the end (exact: a power of two)
+  const int unscale = -((int)p.scales[kScaleKs] + w_scale_exp(*p.wmag));
+  // Adding into dh from earlier chunks: the running total starts from dh's
+  // value in this chunk's scale (exact), so each segment is added to the
+  // total one at a time, in order, whatever the chunk plan.
+  const bool carry = p.accumulate && !p.partial;
+  if (carry) {
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int n = n0 + wn * (HBN / HGN) + fn * 32 + (lane & 31);
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = m0 + wm * (HBM / HGM) + fm * 32 + frag_row(i, lane);
+          tot[fm][fn][i] = (m < p.N && n < p.H) ? ldexpf(p.dh[(int64_t)m * p.H + n], -unscale) : 0.f;
+        }
+    }
+  }
+  // Segment sg of the chunk: its columns between absolute multiples of
+  // kDhSegment (chunk-relative [k0, k1); the first one starts at the chunk).
+  const int s0 = p.partial ? seg : 0, s1 = p.partial ? seg + 1 : p.nseg;
+  for (int sg = s0; sg < s1; ++sg) {
+    const int a = (p.c0 / kDhSegment + sg) * kDhSegment;
+    const int k0 = max(a, p.c0) - p.c0, k1 = min(p.kpad, a + kDhSegment - p.c0);
     zero_acc(acc);
     TA ta;
     ta.init(p.dz + (int64_t)m0 * p.ldz + k0, p.ldz, p.npad - m0, lane, __builtin_amdgcn_readfirstlane(w));
@@ -1165,11 +1193,25 @@ __global__ __launch_bounds__(64 * NW, 1) void dh_gemm(DhParams p) {
 #pragma unroll
       for (int fn = 0; fn < FN; ++fn)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) tot[fm][fn][i] = k0 == 0 ? acc[fm][fn][i] : tot[fm][fn][i] + acc[fm][fn][i];
-    k0 = k1;
+        for (int i = 0; i < 16; ++i)
+          tot[fm][fn][i] = (sg == s0 && !carry) ? acc[fm][fn][i] : tot[fm][fn][i] + acc[fm][fn][i];
   }
-  // undo both operand scales at once (exact: a power of two)
-  const int unscale = -((int)p.scales[kScaleKs] + w_scale_exp(*p.wmag));
+  if (p.partial) {   // this segment's raw sum; dh_reduce adds the segments in order
+    float* P = p.partial + (int64_t)seg * p.N * p.H;
+#pragma unroll
+    for (int fn = 0; fn < FN; ++fn) {
+      const int n = n0 + wn * (HBN / HGN) + fn * 32 + (lane & 31);
+      if (n >= p.H) continue;
+#pragma unroll
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int m = m0 + wm * (HBM / HGM) + fm * 32 + frag_row(i, lane);
+          if (m < p.N) P[(int64_t)m * p.H + n] = tot[fm][fn][i];
+        }
+    }
+    return;
+  }
 #pragma unroll
   for (int fn = 0; fn < FN; ++fn) {
     const int n = n0 + wn * (HBN / HGN) + fn * 32 + (lane & 31);
@@ -1179,12 +1221,31 @@ __global__ __launch_bounds__(64 * NW, 1) void dh_gemm(DhParams p) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int m = m0 + wm * (HBM / HGM) + fm * 32 + frag_row(i, lane);
-        if (m < p.N) {
-          float* o = p.dh + (int64_t)m * p.H + n;
-          const float d = ldexpf(tot[fm][fn][i], unscale);
-          *o = p.accumulate ? *o + d : d;
-        }
+        if (m < p.N) p.dh[(int64_t)m * p.H + n] = ldexpf(tot[fm][fn][i], unscale);
       }
+  }
+}
+
+// The segment sums of a split dh GEMM, added in segment order to the running
+// total (dh of the earlier chunks, in this chunk's scale, or the first
+// segment) -- the order the one-workgroup-per-tile GEMM adds them in -- and
+// unscaled into dh.
+__global__ __launch_bounds__(256) void dh_reduce(DhParams p) {
+  const int unscale = -((int)p.scales[kScaleKs] + w_scale_exp(*p.wmag));
+  const int64_t n4 = (int64_t)p.N * p.H / 4, plane = (int64_t)p.N * p.H;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n4; i += (int64_t)gridDim.x * 256) {
+    float4* o = reinterpret_cast<float4*>(p.dh) + i;
+    float4 t = reinterpret_cast<const float4*>(p.partial)[i];
+    if (p.accumulate) {   // the running total starts from dh in this chunk's scale
+      const float4 e = *o;
+      t = make_float4(ldexpf(e.x, -unscale) + t.x, ldexpf(e.y, -unscale) + t.y, ldexpf(e.z, -unscale) + t.z,
+                      ldexpf(e.w, -unscale) + t.w);
+    }
+    for (int sg = 1; sg < p.nseg; ++sg) {
+      const float4 q = reinterpret_cast<const float4*>(p.partial + sg * plane)[i];
+      t.x = t.x + q.x; t.y = t.y + q.y; t.z = t.z + q.z; t.w = t.w + q.w;
+    }
+    *o = make_float4(ldexpf(t.x, unscale), ldexpf(t.y, unscale), ldexpf(t.z, unscale), ldexpf(t.w, unscale));
   }
 }
 
@@ -1658,7 +1719,12 @@ hipError_t launch_dw(const DwParams& p, hipStream_t s) {
 }
 
 hipError_t launch_dh(const DhParams& p, hipStream_t s) {
-  dh_gemm<kDhWaves><<<(unsigned)(p.ntm * p.ntn), 64 * kDhWaves, 0, s>>>(p);
+  dh_gemm<kDhWaves><<<(unsigned)(p.ntm * p.ntn * (p.partial ? p.nseg : 1)), 64 * kDhWaves, 0, s>>>(p);
+  return hipGetLastError();
+}
+
+hipError_t launch_dh_reduce(const DhParams& p, hipStream_t s) {
+  dh_reduce<<<grid1((int64_t)p.N * p.H / 4, 256, 2048), 256, 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -362,6 +362,29 @@ def test_full_row_equals_compact(tdev):
     assert_grad_close(f[4], c[4], "dW full-row vs compact")
 
 
+@pytest.mark.parametrize("T,V,Hs,chunk", [(700, 5003, 640, None), (300, 40000, 128, None), (260, 5003, 256, "768"),
+                                           (129, 16385, 192, "16384")])
+def test_dh_split_by_segment_is_bitwise_the_same(tdev, monkeypatch, T, V, Hs, chunk):
+    """The dh GEMM split into one workgroup per (tile, vocabulary segment)
+    plus an in-order reduce gives dh (and everything else) bit for bit as the
+    one-workgroup-per-tile GEMM: one and several segments per chunk, chunks
+    that do not start on a segment boundary (768 columns), a segment of one
+    column past 16384, several accumulated chunks."""
+    torch, dev = tdev
+    case = synth.random_case(300 + T, T=T, V=V, Hs=Hs, Ht=64, p_mask=0.8, with_grad=True)
+    if chunk:
+        monkeypatch.setenv("RKL_VOCAB_CHUNK", chunk)
+    say("dh split by segment", T, V, Hs, chunk)
+    monkeypatch.setenv("RKL_DH_SPLIT", "0")
+    ref = _run_hidden(case, dev, g=case.grad)
+    monkeypatch.setenv("RKL_DH_SPLIT", "1")
+    got = _run_hidden(case, dev, g=case.grad)
+    for a, b, what in zip(got[1:], ref[1:], ("loss", "stats", "dh", "dW")):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), what
+    if not chunk:
+        _check_against_oracle(case, got, g=case.grad)
+
+
 @pytest.mark.parametrize("splits_per_wg", [None, "2", "1000"])
 def test_self_distillation_is_exactly_zero(tdev, monkeypatch, splits_per_wg):
     """Bit-identical teacher: every loss and gradient entry is exactly zero,
