@@ -129,8 +129,9 @@ int rkl_scatter_rows(const void* src, int64_t N, int64_t row_bytes, const int32_
  * entropy calls pass their H as Hs and 0 as Ht; the per-row-teacher calls
  * need rkl_workspace_bytes_teachers instead.  Returns 0 on bad sizes.
  * The backward's part dominates: the fp16 dz of one vocabulary chunk
- * (whole 65536-column segments, at most 2 GiB unless one segment alone is
- * larger).
+ * (whole 65536-column units, at most 2 GiB unless one unit alone is
+ * larger), and, when dh's tiles are too few to fill the GPU (N * Hs below
+ * about 2^23), dh's fp32 sums per 16384-column vocabulary segment.
  */
 size_t rkl_workspace_bytes(int64_t N, int64_t V, int64_t Hs, int64_t Ht);
 
