@@ -101,12 +101,20 @@ int64_t vocab_chunk(int64_t N) {
   return C < kMaxPitchElems ? C : kMaxPitchElems;
 }
 
-// Vocabulary tiles one backward workgroup sweeps (does not change results;
-// one per workgroup measured fastest: the finer grain balances the last wave).
-int bwd_tiles_per_group() {
-  const char* s = std::getenv("RKL_BWD_TILES");
-  const int v = s ? std::atoi(s) : 1;
-  return v < 1 ? 1 : (v > 64 ? 64 : v);
+// Vocabulary tiles one backward dz workgroup sweeps (does not change
+// results).  Measured at N = 4096, H = 2048, V = 151936: with both
+// projections one per workgroup is fastest (the finer grain balances the
+// last wave; 2 and 3 ran 1.3 and 2.7 % slower); with one projection per job
+// (teacher logits, log-probability / entropy, top-k) the pipeline fill and
+// the epilogue weigh twice as much per job, and two per workgroup ran
+// bwd_dz_tiles 3.1 / 3.7 / 3.5 % faster than one (2790 / 2518 / 2531 us
+// against 2880 / 2614 / 2622).  RKL_BWD_TILES overrides it.
+int bwd_tiles_per_group(int mode) {
+  if (const char* s = std::getenv("RKL_BWD_TILES")) {
+    const int v = std::atoi(s);
+    return v < 1 ? 1 : (v > 64 ? 64 : v);
+  }
+  return (mode == rkl::kModeHidden || mode == rkl::kModeHiddenTeachers) ? 1 : 2;
 }
 
 // Workgroup order of the fused kernels (panel_order): GS vocabulary runs x TG
@@ -418,7 +426,7 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
     b.scales = scales; b.wmag = wmag; b.dz = dz; b.w16 = w16; b.ldz = (int)L.ldz; b.c0 = (int)c0;
     b.kpad = (int)kpad;
     b.ntv = (int)ceil_div(kpad, rkl::kFwdTileV);
-    b.tiles_per_group = bwd_tiles_per_group();
+    b.tiles_per_group = bwd_tiles_per_group(mode);
     b.ngroups = (int)ceil_div(b.ntv, b.tiles_per_group);
     b.ntok = (int)ceil_div(N, rkl::kFwdTileN);
     b.order_gs = bwd_order().gs;
