@@ -625,9 +625,12 @@ def bench_topk(args):
         h, y = R.gather_rows(h_all, idx), R.gather_rows(y_all, idx)
         S, lS, ly = R.gather_rows(S_all, idx), R.gather_rows(lptS_all, idx), R.gather_rows(lpty_all, idx)
         g = R.gather_rows(g_all, idx)
-        loss, stats = R.forward_topk(h, W, y, S, lS, ly)
+        # the student's log-probabilities on the support, kept from the
+        # forward for the backward
+        lps = torch.empty((N, S.shape[1]), dtype=torch.float32, device=dev)
+        loss, stats = R.forward_topk(h, W, y, S, lS, ly, logps_support=lps)
         loss_pos = R.scatter_rows(loss, idx, T)
-        dh, _ = R.backward_topk(h, W, y, S, lS, stats, grad_loss=g, dW=dW)
+        dh, _ = R.backward_topk(h, W, y, S, lS, stats, grad_loss=g, dW=dW, logps_support=lps)
         R.scatter_rows(dh, idx, T)
         return N, loss_pos
 

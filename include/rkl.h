@@ -358,14 +358,19 @@ int rkl_backward_logprob_entropy(int64_t N, int64_t V, int64_t H, const rkl_bf16
  *                  log-sum-exp, c = sum_{j in S} p_j (f_j + 1) + [y not in S]
  *                  sp, sp = [y not in S] (f_y + 1), and a bound on |dz| / |g|;
  *                  all the backward needs besides the inputs.
+ *   logps_support  [N, K] fp32 out, optional (NULL: not written): the
+ *                  student's log-probabilities log p_s(j) on the support (0
+ *                  for ids outside [0, V) and on rows with row_mask 0).
+ *                  Passed to rkl_backward_topk, they spare it the K dot
+ *                  products per row; its results are the same bit for bit.
  * The student's logits on the support are K dot products per row; the cost
  * beyond the fused log-sum-exp grows as N K H.
  * Workspace: rkl_workspace_bytes(N, V, H, 0).  N = 0 launches nothing.
  */
 int rkl_forward_topk(int64_t N, int64_t V, int64_t H, int64_t K, const rkl_bf16* h, const rkl_bf16* W,
                      const int32_t* y, const int32_t* support, const float* logpt_support, const float* logpt_y,
-                     const uint8_t* row_mask, float* loss, float* stats, void* workspace, size_t workspace_bytes,
-                     rkl_stream_t stream);
+                     const uint8_t* row_mask, float* loss, float* stats, float* logps_support, void* workspace,
+                     size_t workspace_bytes, rkl_stream_t stream);
 
 /*
  * Backward of sum_i g_i L_i for rkl_forward_topk: the exact gradient of the
@@ -374,13 +379,14 @@ int rkl_forward_topk(int64_t N, int64_t V, int64_t H, int64_t K, const rkl_bf16*
  *     dh = dz W (overwritten),  dW = sum_i dz_i^T h_i (overwritten, or added
  *     to when accumulate_dW != 0).
  *   grad_loss [N] fp32 (NULL = all ones); stats from rkl_forward_topk on the
- *   same inputs.  Other arguments, limits and the workspace as
- *   rkl_backward_logprob_entropy.
+ *   same inputs; logps_support the forward's optional output on the same
+ *   inputs, or NULL (the dot products are formed again).  Other arguments,
+ *   limits and the workspace as rkl_backward_logprob_entropy.
  */
 int rkl_backward_topk(int64_t N, int64_t V, int64_t H, int64_t K, const rkl_bf16* h, const rkl_bf16* W,
                       const int32_t* y, const int32_t* support, const float* logpt_support, const uint8_t* row_mask,
-                      const float* grad_loss, const float* stats, float* dh, float* dW, int accumulate_dW,
-                      void* workspace, size_t workspace_bytes, rkl_stream_t stream);
+                      const float* grad_loss, const float* stats, const float* logps_support, float* dh, float* dW,
+                      int accumulate_dW, void* workspace, size_t workspace_bytes, rkl_stream_t stream);
 
 /*
  * Log-probability / entropy over one vocabulary shard (NeMo-RL page,

@@ -70,8 +70,8 @@ def lib() -> ctypes.CDLL:
         "rkl_backward_hidden_teachers": ([I64, I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, I32, P, SZ, P],
                                          I32),
         "rkl_forward_logprob_entropy": ([I64, I64, I64, P, P, P, P, P, P, P, P, SZ, P], I32),
-        "rkl_forward_topk": ([I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
-        "rkl_backward_topk": ([I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, I32, P, SZ, P], I32),
+        "rkl_forward_topk": ([I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
+        "rkl_backward_topk": ([I64, I64, I64, I64, P, P, P, P, P, P, P, P, P, P, P, I32, P, SZ, P], I32),
         "rkl_backward_logprob_entropy": ([I64, I64, I64, P, P, P, P, P, P, P, P, P, I32, P, SZ, P], I32),
     }
     for name, (args, res) in sig.items():
@@ -599,30 +599,38 @@ def _topk_args(h, W, y, support, logpt_support, row_mask):
     return dev, N, V, H, K
 
 
-def forward_topk(h, W, y, support, logpt_support, logpt_y, row_mask=None):
+def forward_topk(h, W, y, support, logpt_support, logpt_y, row_mask=None, logps_support=None):
     """Top-k estimator of the reverse KL per row: the student projected (h
     [N, H], W [V, H] bf16), y int32 [N] the sampled tokens, support int32
     [N, K] the support ids (None for K = 0), logpt_support fp32 [N, K] and
     logpt_y fp32 [N] the teacher's log-probabilities there.  Returns (loss
-    fp32 [N], stats fp32 [N, 4] = (lse, c, sp, bound))."""
+    fp32 [N], stats fp32 [N, 4] = (lse, c, sp, bound)).  logps_support: an
+    optional fp32 [N, K] tensor that receives the student's
+    log-probabilities on the support (hand it to backward_topk)."""
     torch = _torch()
     dev, N, V, H, K = _topk_args(h, W, y, support, logpt_support, row_mask)
     _need(logpt_y, "logpt_y", torch.float32, dev, (N,))
+    if logps_support is not None:
+        _need(logps_support, "logps_support", torch.float32, dev, (N, K))
     loss = torch.empty(N, dtype=torch.float32, device=dev)
     stats = torch.empty((N, 4), dtype=torch.float32, device=dev)
     ws = _workspace(dev, workspace_bytes(N, V, H, 0))
     _check(lib().rkl_forward_topk(N, V, H, K, _ptr(h), _ptr(W), _ptr(y), _ptr(support), _ptr(logpt_support),
-                                  _ptr(logpt_y), _ptr(row_mask), _ptr(loss), _ptr(stats), _ptr(ws), ws.numel(),
-                                  _stream(dev)))
+                                  _ptr(logpt_y), _ptr(row_mask), _ptr(loss), _ptr(stats), _ptr(logps_support),
+                                  _ptr(ws), ws.numel(), _stream(dev)))
     return loss, stats
 
 
 def backward_topk(h, W, y, support, logpt_support, stats, grad_loss=None, row_mask=None, dW=None,
-                  accumulate_dW=False):
-    """Backward of sum_i g_i L_i for forward_topk: returns (dh fp32 [N, H], dW fp32 [V, H])."""
+                  accumulate_dW=False, logps_support=None):
+    """Backward of sum_i g_i L_i for forward_topk: returns (dh fp32 [N, H], dW
+    fp32 [V, H]).  logps_support: the forward's optional output on the same
+    inputs (spares the support's dot products; same results)."""
     torch = _torch()
     dev, N, V, H, K = _topk_args(h, W, y, support, logpt_support, row_mask)
     _need(stats, "stats", torch.float32, dev, (N, 4))
+    if logps_support is not None:
+        _need(logps_support, "logps_support", torch.float32, dev, (N, K))
     if grad_loss is not None:
         _need(grad_loss, "grad_loss", torch.float32, dev, (N,))
     if dW is None:
@@ -634,6 +642,6 @@ def backward_topk(h, W, y, support, logpt_support, stats, grad_loss=None, row_ma
     dh = torch.empty((N, H), dtype=torch.float32, device=dev)
     ws = _workspace(dev, workspace_bytes(N, V, H, 0))
     _check(lib().rkl_backward_topk(N, V, H, K, _ptr(h), _ptr(W), _ptr(y), _ptr(support), _ptr(logpt_support),
-                                   _ptr(row_mask), _ptr(grad_loss), _ptr(stats), _ptr(dh), _ptr(dW),
-                                   int(bool(accumulate_dW)), _ptr(ws), ws.numel(), _stream(dev)))
+                                   _ptr(row_mask), _ptr(grad_loss), _ptr(stats), _ptr(logps_support), _ptr(dh),
+                                   _ptr(dW), int(bool(accumulate_dW)), _ptr(ws), ws.numel(), _stream(dev)))
     return dh, dW

@@ -384,6 +384,7 @@ struct TopK {
   int K = 0;
   const int32_t* S = nullptr;
   const float* lpt_S = nullptr;
+  const float* lps = nullptr;   // the student's log-probabilities on S from the forward (NULL: recomputed)
 };
 
 int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* h_s, const rkl_bf16* W_s,
@@ -434,7 +435,8 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
     RKL_LAUNCH("bwd_dz_tiles", s, rkl::launch_bwd_dz(b, mode, s));
     if (topk.on && topk.K > 0)
       RKL_LAUNCH("topk_dz_add", s, rkl::launch_topk_dz_add(h_s, W_s, (int)N, (int)V, (int)Hs, topk.K, topk.S,
-                                                          topk.lpt_S, row_mask, grad, stats, scales, dz, (int)L.ldz,
+                                                          topk.lpt_S, topk.lps, row_mask, grad, stats, scales, dz,
+                                                          (int)L.ldz,
                                                           (int)c0, (int)width, s));
     RKL_LAUNCH("w_rescale", s, rkl::launch_w_rescale(W_s + c0 * Hs, (int)width, b.ntv, (int)Hs, wmag, w16, s));
 
@@ -761,15 +763,15 @@ int rkl_backward_logprob_entropy(int64_t N, int64_t V, int64_t H, const rkl_bf16
 
 int rkl_forward_topk(int64_t N, int64_t V, int64_t H, int64_t K, const rkl_bf16* h, const rkl_bf16* W,
                      const int32_t* y, const int32_t* support, const float* logpt_support, const float* logpt_y,
-                     const uint8_t* row_mask, float* loss, float* stats, void* workspace, size_t workspace_bytes,
-                     rkl_stream_t stream) {
+                     const uint8_t* row_mask, float* loss, float* stats, float* logps_support, void* workspace,
+                     size_t workspace_bytes, rkl_stream_t stream) {
   if (int rc = check_dims(N, V, H, 0, false, true)) return rc;
   if (K < 0 || K > V) return fail(RKL_INVALID_ARG, "K=%lld support entries out of range [0, V]", (long long)K);
   if (N * K > ((int64_t)1 << 40)) return fail(RKL_INVALID_ARG, "N*K too large");
   if (N > 0) {
     NEED16(h, "h"); NEED16(W, "W"); NEED4(y, "y"); NEED4(logpt_y, "logpt_y");
     NEED4(loss, "loss"); NEED4(stats, "stats");
-    if (K > 0) { NEED4(support, "support"); NEED4(logpt_support, "logpt_support"); }
+    if (K > 0) { NEED4(support, "support"); NEED4(logpt_support, "logpt_support"); OPT4(logps_support, "logps_support"); }
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   // the student's log-sum-exp and log p(y) over the whole vocabulary (the
@@ -779,14 +781,15 @@ int rkl_forward_topk(int64_t N, int64_t V, int64_t H, int64_t K, const rkl_bf16*
     return rc;
   if (N == 0) return RKL_OK;
   RKL_LAUNCH("topk_terms", s, rkl::launch_topk_terms(h, W, (int)N, (int)V, (int)H, (int)K, y, support, logpt_support,
-                                                    logpt_y, row_mask, loss, stats, s));
+                                                    logpt_y, row_mask, loss, stats, K > 0 ? logps_support : nullptr,
+                                                    s));
   return RKL_OK;
 }
 
 int rkl_backward_topk(int64_t N, int64_t V, int64_t H, int64_t K, const rkl_bf16* h, const rkl_bf16* W,
                       const int32_t* y, const int32_t* support, const float* logpt_support, const uint8_t* row_mask,
-                      const float* grad_loss, const float* stats, float* dh, float* dW, int accumulate_dW,
-                      void* workspace, size_t workspace_bytes, rkl_stream_t stream) {
+                      const float* grad_loss, const float* stats, const float* logps_support, float* dh, float* dW,
+                      int accumulate_dW, void* workspace, size_t workspace_bytes, rkl_stream_t stream) {
   if (int rc = check_dims(N, V, H, 0, false, true)) return rc;
   if (K < 0 || K > V) return fail(RKL_INVALID_ARG, "K=%lld support entries out of range [0, V]", (long long)K);
   if (N * K > ((int64_t)1 << 40)) return fail(RKL_INVALID_ARG, "N*K too large");
@@ -794,10 +797,10 @@ int rkl_backward_topk(int64_t N, int64_t V, int64_t H, int64_t K, const rkl_bf16
   if (N > 0) {
     NEED16(h, "h"); NEED16(W, "W"); NEED4(y, "y"); NEED4(stats, "stats"); NEED16(dh, "dh");
     OPT4(grad_loss, "grad_loss");
-    if (K > 0) { NEED4(support, "support"); NEED4(logpt_support, "logpt_support"); }
+    if (K > 0) { NEED4(support, "support"); NEED4(logpt_support, "logpt_support"); OPT4(logps_support, "logps_support"); }
   }
   TopK t;
-  t.on = true; t.K = (int)K; t.S = support; t.lpt_S = logpt_support;
+  t.on = true; t.K = (int)K; t.S = support; t.lpt_S = logpt_support; t.lps = K > 0 ? logps_support : nullptr;
   return backward_tiled(N, V, H, 0, h, W, nullptr, nullptr, nullptr, y, row_mask, grad_loss, nullptr, stats, dh, dW,
                         accumulate_dW != 0, workspace, workspace_bytes, static_cast<hipStream_t>(stream), Teachers{},
                         t);

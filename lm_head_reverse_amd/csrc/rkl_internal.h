@@ -155,12 +155,13 @@ hipError_t launch_grad_scale(const float* grad, const float* grad_h, const uint8
 // tail at y; writes loss and stats = (lse, c, sp, bound) (see the kernel).
 hipError_t launch_topk_terms(const uint16_t* h, const uint16_t* W, int N, int V, int H, int K, const int32_t* y,
                              const int32_t* S, const float* lpt_S, const float* lpt_y, const uint8_t* row_mask,
-                             float* loss, float* stats, hipStream_t s);
+                             float* loss, float* stats, float* lps, hipStream_t s);
 // Top-k estimator, backward: adds s g p_j (f_j + 1) for the support ids j of
 // chunk [c0, c0 + width) into the fp16 dz chunk.
 hipError_t launch_topk_dz_add(const uint16_t* h, const uint16_t* W, int N, int V, int H, int K, const int32_t* S,
-                              const float* lpt_S, const uint8_t* row_mask, const float* grad, const float* stats,
-                              const uint32_t* scales, uint16_t* dz, int ldz, int c0, int width, hipStream_t s);
+                              const float* lpt_S, const float* lps, const uint8_t* row_mask, const float* grad,
+                              const float* stats, const uint32_t* scales, uint16_t* dz, int ldz, int c0, int width,
+                              hipStream_t s);
 // scales[kScaleHmag] = max over h [n] of the bf16 magnitude bits (after launch_grad_scale cleared it)
 hipError_t launch_absmax_bf16(const uint16_t* h, int64_t n, uint32_t* scales, hipStream_t s);
 hipError_t launch_transpose_h(const uint16_t* h, int N, int H, const uint32_t* scales, uint16_t* hT, int ldT,

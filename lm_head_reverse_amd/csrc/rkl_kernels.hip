@@ -1411,7 +1411,7 @@ __global__ __launch_bounds__(256) void topk_terms(const uint16_t* __restrict__ h
                                                   const int32_t* __restrict__ S, const float* __restrict__ lpt_S,
                                                   const float* __restrict__ lpt_y,
                                                   const uint8_t* __restrict__ row_mask, float* __restrict__ loss,
-                                                  float* __restrict__ stats) {
+                                                  float* __restrict__ stats, float* __restrict__ lps) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= N) return;
@@ -1421,6 +1421,8 @@ __global__ __launch_bounds__(256) void topk_terms(const uint16_t* __restrict__ h
       loss[t] = 0.f;
       st[0] = 0.f; st[1] = 0.f; st[2] = 0.f; st[3] = 0.f;
     }
+    if (lps)
+      for (int k = lane; k < K; k += 64) lps[(int64_t)t * K + k] = 0.f;
     return;
   }
   const float lse = st[0], lpy = st[2];
@@ -1432,6 +1434,15 @@ __global__ __launch_bounds__(256) void topk_terms(const uint16_t* __restrict__ h
     float z[kTopkBatch];
     topk_batch_ids(S, t, K, k0, j);
     wave_dots_bf16(h + (int64_t)t * H, W, j, V, H, lane, z);
+    // the student's log-probabilities on the support, for the backward
+    // (0 for ids outside [0, V)); lane b writes entry k0 + b
+    if (lps) {
+      float mine = 0.f;
+#pragma unroll
+      for (int b = 0; b < kTopkBatch; ++b)
+        if (lane == b && j[b] >= 0 && j[b] < V) mine = z[b] - lse;
+      if (lane < kTopkBatch && k0 + lane < K) lps[(int64_t)t * K + k0 + lane] = mine;
+    }
 #pragma unroll
     for (int b = 0; b < kTopkBatch; ++b) {
       if (j[b] < 0 || j[b] >= V) continue;
@@ -1464,7 +1475,7 @@ __global__ __launch_bounds__(256) void topk_terms(const uint16_t* __restrict__ h
 // repeated ids add up), saturating at fp16's largest finite value.
 __global__ __launch_bounds__(256) void topk_dz_add(const uint16_t* __restrict__ h, const uint16_t* __restrict__ W,
                                                    int N, int V, int H, int K, const int32_t* __restrict__ S,
-                                                   const float* __restrict__ lpt_S,
+                                                   const float* __restrict__ lpt_S, const float* __restrict__ lps,
                                                    const uint8_t* __restrict__ row_mask,
                                                    const float* __restrict__ grad, const float* __restrict__ stats,
                                                    const uint32_t* __restrict__ scales, uint16_t* __restrict__ dz,
@@ -1485,11 +1496,13 @@ __global__ __launch_bounds__(256) void topk_dz_add(const uint16_t* __restrict__ 
       any = any || j[b] >= 0;
     }
     if (!any) continue;
-    wave_dots_bf16(h + (int64_t)t * H, W, j, V, H, lane, z);
+    // the forward's log-probabilities when given (the same fp32 values),
+    // else the dot products again
+    if (!lps) wave_dots_bf16(h + (int64_t)t * H, W, j, V, H, lane, z);
 #pragma unroll
     for (int b = 0; b < kTopkBatch; ++b) {
       if (j[b] < 0) continue;
-      const float lp = z[b] - lse;
+      const float lp = lps ? lps[(int64_t)t * K + k0 + b] : z[b] - lse;
       const float f = lp - lpt_S[(int64_t)t * K + k0 + b];
       if (lane == 0) {
         uint16_t* e = dz + (int64_t)t * ldz + (j[b] - c0);
@@ -1681,16 +1694,17 @@ hipError_t launch_grad_scale(const float* grad, const float* grad_h, const uint8
 
 hipError_t launch_topk_terms(const uint16_t* h, const uint16_t* W, int N, int V, int H, int K, const int32_t* y,
                              const int32_t* S, const float* lpt_S, const float* lpt_y, const uint8_t* row_mask,
-                             float* loss, float* stats, hipStream_t s) {
-  topk_terms<<<(unsigned)((N + 3) / 4), 256, 0, s>>>(h, W, N, V, H, K, y, S, lpt_S, lpt_y, row_mask, loss, stats);
+                             float* loss, float* stats, float* lps, hipStream_t s) {
+  topk_terms<<<(unsigned)((N + 3) / 4), 256, 0, s>>>(h, W, N, V, H, K, y, S, lpt_S, lpt_y, row_mask, loss, stats, lps);
   return hipGetLastError();
 }
 
 hipError_t launch_topk_dz_add(const uint16_t* h, const uint16_t* W, int N, int V, int H, int K, const int32_t* S,
-                              const float* lpt_S, const uint8_t* row_mask, const float* grad, const float* stats,
-                              const uint32_t* scales, uint16_t* dz, int ldz, int c0, int width, hipStream_t s) {
-  topk_dz_add<<<(unsigned)((N + 3) / 4), 256, 0, s>>>(h, W, N, V, H, K, S, lpt_S, row_mask, grad, stats, scales, dz,
-                                                      ldz, c0, width);
+                              const float* lpt_S, const float* lps, const uint8_t* row_mask, const float* grad,
+                              const float* stats, const uint32_t* scales, uint16_t* dz, int ldz, int c0, int width,
+                              hipStream_t s) {
+  topk_dz_add<<<(unsigned)((N + 3) / 4), 256, 0, s>>>(h, W, N, V, H, K, S, lpt_S, lps, row_mask, grad, stats, scales,
+                                                      dz, ldz, c0, width);
   return hipGetLastError();
 }
 

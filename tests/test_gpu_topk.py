@@ -164,3 +164,35 @@ def test_empty_rows(tdev):
     loss, stats = R.forward_topk(h, W, y, S, lS, torch.empty(0, dtype=torch.float32, device=dev))
     dh, dW = R.backward_topk(h, W, y, S, lS, stats)
     assert loss.shape == (0,) and dh.shape == (0, 64) and int(torch.count_nonzero(dW)) == 0
+
+
+@pytest.mark.parametrize("T,V,H,K", [(300, 3001, 128, 16), (129, 257, 64, 13)])
+def test_support_logprobs_from_the_forward(tdev, T, V, H, K):
+    """The forward's optional output, the student's log-probabilities on the
+    support, matches the fp64 log-softmax there (0 for ids outside [0, V)
+    and on masked rows), and handing it to the backward gives dh and dW bit
+    for bit as forming the support's dot products again (several batches of
+    eight ids per row, and a ragged last batch at K = 13)."""
+    torch, dev = tdev
+    case, y, S, lpt_S, lpt_y = _problem(950 + T, T, V, H, K, p_mask=0.8)
+    S = S.copy()
+    S[::5, 0] = -1
+    S[1::7, K - 1] = V + 3
+    say("top-k support log-probabilities", T, V, H, K)
+    h, W = bf16(case.h_s, dev), bf16(case.W_s, dev)
+    yy = torch.from_numpy(y.astype(np.int32)).to(dev)
+    Sd, lS = torch.from_numpy(np.ascontiguousarray(S)).to(dev), f32(lpt_S, dev)
+    g, rm = f32(case.grad, dev), u8(case.mask, dev)
+    lps = torch.full((T, K), 7.0, dtype=torch.float32, device=dev)
+    loss, stats = R.forward_topk(h, W, yy, Sd, lS, f32(lpt_y, dev), row_mask=rm, logps_support=lps)
+    dh0, dW0 = R.backward_topk(h, W, yy, Sd, lS, stats, grad_loss=g, row_mask=rm)
+    dh1, dW1 = R.backward_topk(h, W, yy, Sd, lS, stats, grad_loss=g, row_mask=rm, logps_support=lps)
+    torch.cuda.synchronize()
+    assert np.array_equal(host(dh0).view(np.uint32), host(dh1).view(np.uint32))
+    assert np.array_equal(host(dW0).view(np.uint32), host(dW1).view(np.uint32))
+    lp = scipy.special.log_softmax(O.widen_bf16(case.h_s) @ O.widen_bf16(case.W_s).T, axis=1)
+    valid = (S >= 0) & (S < V) & (case.mask[:, None] != 0)
+    want = np.where(valid, np.take_along_axis(lp, np.clip(S, 0, V - 1).astype(np.int64), 1), 0.0)
+    got = host(lps)
+    assert np.all(got[~valid] == 0.0)
+    assert_loss_close(got[valid], want[valid], "log p_s on the support")
