@@ -4,7 +4,10 @@
 A step is one pass of the whole path over one batch that is already resident in
 device memory: loss-mask compaction, row gather, fused forward (both
 projections + online log-sum-exp / KL), scatter of the per-token loss,
-recomputing backward (dz, dW, dh) and scatter of dh.
+recomputing backward (dz, dW, dh) and scatter of dh.  The compaction runs one
+batch ahead, as a trainer prefetching its next batch would run it (NextRows):
+each step enqueues its kernels, then compacts the next batch's mask on a side
+stream; every step still runs one compaction.
 
 Workload: Qwen3-1.7B-shaped hidden-state path, B=4 sequences of S=1025 tokens,
 every one of the T = B(S-1) = 4096 positions trainable (N = 4096), Hs = Ht =
@@ -44,9 +47,11 @@ Prints one JSON line:
                timed steps, synchronised on both sides);
   per_kernel = every kernel of the path with its device time per step and
                per launch, measured in the timed steps with hipEvents that
-               the library records around each launch on its stream, and
-               for the MFMA kernels their algorithmic FLOPs against the
-               dense bf16/fp16 MFMA peak;
+               each launch stamps with its kernel's begin and end, and for
+               the MFMA kernels their algorithmic FLOPs against the dense
+               bf16/fp16 MFMA peak (the side-stream compaction is left out:
+               it waits for a free compute unit while the step's kernels
+               hold them all, so its event span is not its run time);
   roofline   = the kernel with the most device time per step, with the HBM
                traffic per launch from the committed counter record while
                the kernel sources are unchanged;
@@ -320,7 +325,45 @@ def cpu_baseline_lpe(case, y, target_s: float):
 
 # ---------------------------------------------------------------- timing harness
 
-def run_timed(step, args):
+class NextRows:
+    """Loss-mask compaction one batch ahead.
+
+    compact_rows waits for its kernel: the row count N sizes every later
+    launch.  Issued at a step's start, that wait would drain the device (it
+    finishes the previous step, then idles through the round trip and the
+    host's first launches).  So each step takes the rows compacted during the
+    previous one and, after enqueueing its own kernels, calls advance(): the
+    next batch's mask is compacted on a side stream (default priority) while
+    the device works through the queued step, and the host waits for that
+    one small kernel only.  Per-kernel timing is paused around it (see the
+    module docstring).  The inputs are the same every step here, so every
+    batch has the same rows."""
+
+    def __init__(self, mask):
+        import torch
+        self.mask = mask
+        self.main = torch.cuda.current_stream(mask.device)
+        self.side = torch.cuda.Stream(mask.device)
+        self.timed = False
+        self.rows = self._compact()
+
+    def _compact(self):
+        import torch
+        import lm_head_reverse_amd as R
+        if self.timed:
+            R.kernel_timing(False)
+        with torch.cuda.stream(self.side):
+            idx, N = R.compact_rows(self.mask)   # returns once the side stream has run it
+        if self.timed:
+            R.kernel_timing(True)
+        idx.record_stream(self.main)   # used by the main stream's kernels
+        return idx, N
+
+    def advance(self):
+        self.rows = self._compact()
+
+
+def run_timed(step, args, rows=None):
     """W untimed warm-up steps, then exactly K timed steps bracketed by
     device synchronisation, with the library's per-kernel event timing on.
     Returns (N, wall seconds, {kernel: (total ms, launches)})."""
@@ -335,6 +378,8 @@ def run_timed(step, args):
     print("[bench] timing", file=sys.stderr, flush=True)
     R.kernel_timing(True)
     R.kernel_times()   # forget the warm-up's records
+    if rows is not None:
+        rows.timed = True
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
@@ -343,6 +388,8 @@ def run_timed(step, args):
     wall = time.perf_counter() - t0
     times = R.kernel_times()
     R.kernel_timing(False)
+    if rows is not None:
+        rows.timed = False
     return N, wall, times
 
 
@@ -475,8 +522,10 @@ def bench_reverse_kl(args):
     dW = torch.empty((V, Hs), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
+    rows = NextRows(mask)
+
     def step():
-        idx, N = R.compact_rows(mask)
+        idx, N = rows.rows
         h_s = R.gather_rows(h_s_all, idx)
         g = R.gather_rows(grad_pos, idx)
         if logits:
@@ -491,9 +540,10 @@ def bench_reverse_kl(args):
         else:
             dh, _ = R.backward_hidden(h_s, W_s, h_t, W_t, stats, grad_loss=g, dW=dW)
         R.scatter_rows(dh, idx, T)
+        rows.advance()
         return N, loss_pos
 
-    N, wall, times = run_timed(step, args)
+    N, wall, times = run_timed(step, args, rows)
     assert N == N_expected
     Ht_eff = 0 if logits else Ht
     work = rkl_work(N, V, Hs, Ht_eff, logits=logits)
@@ -540,8 +590,10 @@ def bench_logprob_entropy(args):
     dW = torch.empty((V, H), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
+    rows = NextRows(mask)
+
     def step():
-        idx, N = R.compact_rows(mask)
+        idx, N = rows.rows
         h = R.gather_rows(h_all, idx)
         y = R.gather_rows(y_all, idx)
         gl, gh = R.gather_rows(g_lp_all, idx), R.gather_rows(g_h_all, idx)
@@ -550,9 +602,10 @@ def bench_logprob_entropy(args):
         R.scatter_rows(ent, idx, T)
         dh, _ = R.backward_logprob_entropy(h, W, y, stats, grad_logp=gl, grad_entropy=gh, dW=dW)
         R.scatter_rows(dh, idx, T)
+        rows.advance()
         return N, lp_pos
 
-    N, wall, times = run_timed(step, args)
+    N, wall, times = run_timed(step, args, rows)
     assert N == N_expected
     work = rkl_work(N, V, H, 0)
     config = {"workload": "Qwen3-1.7B-shaped actor log-probability + entropy, B=4 S=1025 (T=N=4096 "
@@ -620,8 +673,10 @@ def bench_topk(args):
     dW = torch.empty((V, H), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
+    rows = NextRows(mask)
+
     def step():
-        idx, N = R.compact_rows(mask)
+        idx, N = rows.rows
         h, y = R.gather_rows(h_all, idx), R.gather_rows(y_all, idx)
         S, lS, ly = R.gather_rows(S_all, idx), R.gather_rows(lptS_all, idx), R.gather_rows(lpty_all, idx)
         g = R.gather_rows(g_all, idx)
@@ -632,9 +687,10 @@ def bench_topk(args):
         loss_pos = R.scatter_rows(loss, idx, T)
         dh, _ = R.backward_topk(h, W, y, S, lS, stats, grad_loss=g, dW=dW, logps_support=lps)
         R.scatter_rows(dh, idx, T)
+        rows.advance()
         return N, loss_pos
 
-    N, wall, times = run_timed(step, args)
+    N, wall, times = run_timed(step, args, rows)
     assert N == N_expected
     work = rkl_work(N, V, H, 0)
     config = {"workload": f"Qwen3-1.7B-shaped student, top-k estimator with the teacher's top {K} log-probabilities "
@@ -671,17 +727,20 @@ def bench_teachers(args):
     dW = torch.empty((V, Hs), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
+    rows = NextRows(mask)
+
     def step():
-        idx, N = R.compact_rows(mask)
+        idx, N = rows.rows
         h_s, h_t = R.gather_rows(h_s_all, idx), R.gather_rows(h_t_all, idx)
         tk, g = R.gather_rows(tid_all, idx), R.gather_rows(grad_pos, idx)
         loss, stats = R.forward_hidden_teachers(h_s, W_s, h_t, W_t, tk)
         loss_pos = R.scatter_rows(loss, idx, T)
         dh, _ = R.backward_hidden_teachers(h_s, W_s, h_t, W_t, tk, stats, grad_loss=g, dW=dW)
         R.scatter_rows(dh, idx, T)
+        rows.advance()
         return N, loss_pos
 
-    N, wall, times = run_timed(step, args)
+    N, wall, times = run_timed(step, args, rows)
     assert N == N_expected
     config = {"workload": f"Qwen3-1.7B-shaped hidden-state teachers, {K} teachers chosen per row "
                           f"({args.teacher_order}), B=4 S=1025 (T=N=4096 trainable), Hs=Ht=2048, V=151936",
@@ -727,8 +786,10 @@ def bench_vocab_shard(args):
     dW = torch.empty((v1 - v0, Hs), dtype=torch.float32, device=dev)
     torch.cuda.synchronize()
 
+    rows = NextRows(mask)
+
     def step():
-        idx, N = R.compact_rows(mask)
+        idx, N = rows.rows
         h_s, h_t = R.gather_rows(h_s_all, idx), R.gather_rows(h_t_all, idx)
         g = R.gather_rows(grad_pos, idx)
         partials[0] = R.forward_hidden_shard(h_s, W_s, h_t, W_t)
@@ -736,9 +797,10 @@ def bench_vocab_shard(args):
         loss_pos = R.scatter_rows(loss, idx, T)
         dh, _ = R.backward_hidden(h_s, W_s, h_t, W_t, stats, grad_loss=g, dW=dW)
         R.scatter_rows(dh, idx, T)
+        rows.advance()
         return N, loss_pos
 
-    N, wall, times = run_timed(step, args)
+    N, wall, times = run_timed(step, args, rows)
     assert N == N_expected
     Vs = v1 - v0
     config = {"workload": f"Qwen3-1.7B-shaped hidden-state teacher, one rank's share of a {G}-way "

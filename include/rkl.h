@@ -73,9 +73,10 @@ const char* rkl_version(void);
  * Per-kernel device time, for measurement (the pages define no such call;
  * it exists so that a benchmark can price each kernel of the path against
  * the chip's peak).  rkl_kernel_timing(1) turns timing on for the calling
- * host thread: from then on every kernel that thread's calls launch is
- * bracketed by two hipEvents recorded on the call's stream (a few
- * microseconds of host work per launch; no device memory).
+ * host thread: from then on every kernel that thread's calls launch carries
+ * two hipEvents that the launch stamps with the kernel's own begin and end
+ * (hipExtLaunchKernel: no marker packets join the stream; the events come
+ * from a per-thread pool and are reused; no device memory).
  * rkl_kernel_timing(0) turns it off.  rkl_kernel_times waits for the
  * recorded events, sums the elapsed time per kernel name and forgets them:
  * entry k < min(*count, cap) gets names[k] (static storage), total_ms[k] and

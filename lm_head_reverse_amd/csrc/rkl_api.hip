@@ -33,30 +33,64 @@ int fail(int code, const char* fmt, ...) {
   } while (0)
 
 // Per-kernel device time (rkl_kernel_timing / rkl_kernel_times): while the
-// calling thread has timing on, every kernel a call launches is bracketed by
-// two events recorded on the call's stream.
+// calling thread has timing on, every kernel a call launches carries two
+// events that the launch itself stamps with the kernel's begin and end
+// (rkl::set_launch_events), so timing adds no packets to the stream.  Events
+// come from a per-thread, per-device pool and go back to it once read.
 struct TimedLaunch {
   const char* name;
   hipEvent_t begin, end;
+  int device;
 };
 thread_local bool g_timing = false;
 thread_local std::vector<TimedLaunch> g_timed;
+thread_local std::vector<std::vector<hipEvent_t>> g_event_pool;   // [device]
+
+static hipError_t pooled_events(hipEvent_t* a, hipEvent_t* b, int* device) {
+  hipError_t e = hipGetDevice(device);
+  if (e != hipSuccess) return e;
+  if ((int)g_event_pool.size() <= *device) g_event_pool.resize(*device + 1);
+  std::vector<hipEvent_t>& pool = g_event_pool[*device];
+  hipEvent_t* out[2] = {a, b};
+  for (hipEvent_t* o : out) {
+    if (!pool.empty()) {
+      *o = pool.back();
+      pool.pop_back();
+    } else if ((e = hipEventCreate(o)) != hipSuccess) {
+      if (o == b) pool.push_back(*a);
+      return e;
+    }
+  }
+  return hipSuccess;
+}
+
+static void release_events(hipEvent_t a, hipEvent_t b, int device) {
+  if ((int)g_event_pool.size() <= device) g_event_pool.resize(device + 1);
+  g_event_pool[device].push_back(a);
+  g_event_pool[device].push_back(b);
+}
 
 // A kernel launch (a launch_* call returning hipError_t) on stream `st`, timed
-// when timing is on.
+// when timing is on.  A launch_* call that launched nothing (an empty fill)
+// records no entry.
 #define RKL_LAUNCH(name, st, expr)                                                      \
   do {                                                                                  \
     hipEvent_t evb_ = nullptr, eve_ = nullptr;                                          \
+    int evd_ = 0;                                                                       \
     if (g_timing) {                                                                     \
-      RKL_TRY(hipEventCreate(&evb_));                                                   \
-      RKL_TRY(hipEventRecord(evb_, st));                                                \
+      RKL_TRY(pooled_events(&evb_, &eve_, &evd_));                                      \
+      rkl::set_launch_events(evb_, eve_);                                               \
     }                                                                                   \
-    RKL_TRY(expr);                                                                      \
+    const hipError_t el_ = (expr);                                                      \
+    const bool launched_ = !rkl::launch_events_pending();                               \
+    rkl::set_launch_events(nullptr, nullptr);                                           \
     if (g_timing) {                                                                     \
-      RKL_TRY(hipEventCreate(&eve_));                                                   \
-      RKL_TRY(hipEventRecord(eve_, st));                                                \
-      g_timed.push_back(TimedLaunch{name, evb_, eve_});                                 \
+      if (launched_ && el_ == hipSuccess)                                               \
+        g_timed.push_back(TimedLaunch{name, evb_, eve_, evd_});                         \
+      else                                                                              \
+        release_events(evb_, eve_, evd_);                                               \
     }                                                                                   \
+    if (el_ != hipSuccess) return fail(RKL_DEVICE_ERROR, "%s: %s", #expr, hipGetErrorString(el_)); \
   } while (0)
 
 constexpr int64_t kMaxDim = (int64_t)1 << 30;
@@ -508,8 +542,7 @@ int rkl_kernel_times(int cap, const char** names, double* total_ms, int* launche
     float ms = 0.f;
     hipError_t e = hipEventSynchronize(r.end);
     if (e == hipSuccess) e = hipEventElapsedTime(&ms, r.begin, r.end);
-    (void)hipEventDestroy(r.begin);
-    (void)hipEventDestroy(r.end);
+    release_events(r.begin, r.end, r.device);
     if (e != hipSuccess) {
       rc = fail(RKL_DEVICE_ERROR, "kernel timing event: %s", hipGetErrorString(e));
       continue;

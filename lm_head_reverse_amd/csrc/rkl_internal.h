@@ -139,6 +139,15 @@ enum Mode : int {
 // Sets the calling thread's rkl_last_error message; returns code.
 int set_last_error(int code, const char* msg);
 
+// Per-kernel timing: events that the calling thread's next kernel launch
+// takes as its own start and stop (hipExtLaunchKernel stamps them with the
+// kernel's begin and end, with no marker packets of their own in the queue).
+// Each launch_* function below launches at most one kernel, and that launch
+// clears them; launch_events_pending() is then false.  A launch_* call that
+// launched nothing leaves them pending.
+void set_launch_events(hipEvent_t start, hipEvent_t stop);
+bool launch_events_pending();
+
 hipError_t launch_fwd_tiles(const FwdParams& p, int mode, hipStream_t s);
 // out0: loss (reverse KL) or log p(y); out1: entropy (log-probability / entropy only)
 hipError_t launch_fwd_combine(const float* partial, int nsplit, int N, const uint8_t* row_mask, bool logprob_entropy,

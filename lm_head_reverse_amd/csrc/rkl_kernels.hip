@@ -18,6 +18,11 @@
 #include "rkl_tile.h"
 #include "rkl_internal.h"
 
+#include <hip/hip_ext.h>
+
+#include <tuple>
+#include <type_traits>
+
 namespace rkl {
 
 constexpr float kL2E = 1.4426950408889634f;
@@ -1622,6 +1627,34 @@ __global__ __launch_bounds__(256) void fill_zero_u32(uint32_t* __restrict__ p, i
 // ===========================================================================
 // Launchers
 // ===========================================================================
+namespace {
+thread_local hipEvent_t g_launch_ev[2] = {nullptr, nullptr};
+}
+
+void set_launch_events(hipEvent_t start, hipEvent_t stop) {
+  g_launch_ev[0] = start;
+  g_launch_ev[1] = stop;
+}
+
+bool launch_events_pending() { return g_launch_ev[0] != nullptr || g_launch_ev[1] != nullptr; }
+
+// kernel<<<grid, block, 0, s>>>(args...), carrying the pending timing events
+// (if any): the arguments are converted to the kernel's parameter types and
+// passed by address, as the launch API wants them.
+template <class... P, class... A>
+static hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_t s, A&&... a) {
+  static_assert(sizeof...(P) == sizeof...(A), "one argument per kernel parameter");
+  std::tuple<std::remove_cv_t<std::remove_reference_t<P>>...> vals(std::forward<A>(a)...);
+  void* args[sizeof...(P)];
+  std::apply([&args](auto&... v) {
+    int i = 0;
+    ((args[i++] = static_cast<void*>(&v)), ...);
+  }, vals);
+  const hipEvent_t e0 = g_launch_ev[0], e1 = g_launch_ev[1];
+  g_launch_ev[0] = g_launch_ev[1] = nullptr;
+  return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, s, e0, e1, 0);
+}
+
 static inline unsigned grid1(int64_t n, int64_t per, int64_t cap) {
   int64_t g = (n + per - 1) / per;
   if (g < 1) g = 1;
@@ -1634,32 +1667,29 @@ hipError_t launch_fwd_tiles(const FwdParams& p, int mode, hipStream_t s) {
   constexpr int NW = kFusedWaves;
   constexpr unsigned nt = Fused<NW>::kThreads;
   if (mode == kModeHidden)
-    fwd_tiles<kModeHidden, true, NW><<<nb, nt, 0, s>>>(p);
+    return launch(fwd_tiles<kModeHidden, true, NW>, nb, nt, s, p);
   else if (mode == kModeHiddenTeachers)
-    fwd_tiles<kModeHiddenTeachers, true, NW><<<nb, nt, 0, s>>>(p);
+    return launch(fwd_tiles<kModeHiddenTeachers, true, NW>, nb, nt, s, p);
   else if (mode == kModeLogprobEntropy)
-    fwd_tiles<kModeLogprobEntropy, true, NW><<<nb, nt, 0, s>>>(p);
+    return launch(fwd_tiles<kModeLogprobEntropy, true, NW>, nb, nt, s, p);
   else if (p.V % 4 == 0)
-    fwd_tiles<kModeTeacherLogits, true, NW><<<nb, nt, 0, s>>>(p);
+    return launch(fwd_tiles<kModeTeacherLogits, true, NW>, nb, nt, s, p);
   else
-    fwd_tiles<kModeTeacherLogits, false, NW><<<nb, nt, 0, s>>>(p);
-  return hipGetLastError();
+    return launch(fwd_tiles<kModeTeacherLogits, false, NW>, nb, nt, s, p);
 }
 
 hipError_t launch_fwd_combine(const float* partial, int nsplit, int N, const uint8_t* row_mask, bool logprob_entropy,
                               float* out0, float* out1, float* stats, hipStream_t s) {
   const unsigned nb = (unsigned)((N + kCombRows - 1) / kCombRows);
   if (logprob_entropy)
-    fwd_combine<kCombineLPE><<<nb, 256, 0, s>>>(partial, nsplit, N, row_mask, out0, out1, stats);
+    return launch(fwd_combine<kCombineLPE>, nb, 256, s, partial, nsplit, N, row_mask, out0, out1, stats);
   else
-    fwd_combine<kCombineKL><<<nb, 256, 0, s>>>(partial, nsplit, N, row_mask, out0, out1, stats);
-  return hipGetLastError();
+    return launch(fwd_combine<kCombineKL>, nb, 256, s, partial, nsplit, N, row_mask, out0, out1, stats);
 }
 
 hipError_t launch_fwd_merge(const float* partial, int nsplit, int N, float* merged, hipStream_t s) {
   const unsigned nb = (unsigned)((N + kCombRows - 1) / kCombRows);
-  fwd_combine<kCombineMerged><<<nb, 256, 0, s>>>(partial, nsplit, N, nullptr, merged, nullptr, nullptr);
-  return hipGetLastError();
+  return launch(fwd_combine<kCombineMerged>, nb, 256, s, partial, nsplit, N, nullptr, merged, nullptr, nullptr);
 }
 
 hipError_t launch_bwd_dz(const BwdParams& p, int mode, hipStream_t s) {
@@ -1667,105 +1697,91 @@ hipError_t launch_bwd_dz(const BwdParams& p, int mode, hipStream_t s) {
   constexpr int NW = kFusedWaves;
   constexpr unsigned nt = Fused<NW>::kThreads;
   if (mode == kModeHidden)
-    bwd_dz_tiles<kModeHidden, true, NW><<<nb, nt, 0, s>>>(p);
+    return launch(bwd_dz_tiles<kModeHidden, true, NW>, nb, nt, s, p);
   else if (mode == kModeHiddenTeachers)
-    bwd_dz_tiles<kModeHiddenTeachers, true, NW><<<nb, nt, 0, s>>>(p);
+    return launch(bwd_dz_tiles<kModeHiddenTeachers, true, NW>, nb, nt, s, p);
   else if (mode == kModeLogprobEntropy)
-    bwd_dz_tiles<kModeLogprobEntropy, true, NW><<<nb, nt, 0, s>>>(p);
+    return launch(bwd_dz_tiles<kModeLogprobEntropy, true, NW>, nb, nt, s, p);
   else if (mode == kModeTopK)
-    bwd_dz_tiles<kModeTopK, true, NW><<<nb, nt, 0, s>>>(p);
+    return launch(bwd_dz_tiles<kModeTopK, true, NW>, nb, nt, s, p);
   else if (p.V % 4 == 0)
-    bwd_dz_tiles<kModeTeacherLogits, true, NW><<<nb, nt, 0, s>>>(p);
+    return launch(bwd_dz_tiles<kModeTeacherLogits, true, NW>, nb, nt, s, p);
   else
-    bwd_dz_tiles<kModeTeacherLogits, false, NW><<<nb, nt, 0, s>>>(p);
-  return hipGetLastError();
+    return launch(bwd_dz_tiles<kModeTeacherLogits, false, NW>, nb, nt, s, p);
 }
 
 hipError_t launch_grad_scale(const float* grad, const float* grad_h, const uint8_t* row_mask, const float* stats,
                              int N, int mode, int nchunks, uint32_t* scales, hipStream_t s) {
   if (mode == kModeLogprobEntropy)
-    grad_scale<kModeLogprobEntropy><<<1, 1024, 0, s>>>(grad, grad_h, row_mask, stats, N, nchunks, scales);
+    return launch(grad_scale<kModeLogprobEntropy>, 1, 1024, s, grad, grad_h, row_mask, stats, N, nchunks, scales);
   else if (mode == kModeTopK)
-    grad_scale<kModeTopK><<<1, 1024, 0, s>>>(grad, grad_h, row_mask, stats, N, nchunks, scales);
+    return launch(grad_scale<kModeTopK>, 1, 1024, s, grad, grad_h, row_mask, stats, N, nchunks, scales);
   else
-    grad_scale<kModeHidden><<<1, 1024, 0, s>>>(grad, grad_h, row_mask, stats, N, nchunks, scales);
-  return hipGetLastError();
+    return launch(grad_scale<kModeHidden>, 1, 1024, s, grad, grad_h, row_mask, stats, N, nchunks, scales);
 }
 
 hipError_t launch_topk_terms(const uint16_t* h, const uint16_t* W, int N, int V, int H, int K, const int32_t* y,
                              const int32_t* S, const float* lpt_S, const float* lpt_y, const uint8_t* row_mask,
                              float* loss, float* stats, float* lps, hipStream_t s) {
-  topk_terms<<<(unsigned)((N + 3) / 4), 256, 0, s>>>(h, W, N, V, H, K, y, S, lpt_S, lpt_y, row_mask, loss, stats, lps);
-  return hipGetLastError();
+  return launch(topk_terms, (unsigned)((N + 3) / 4), 256, s, h, W, N, V, H, K, y, S, lpt_S, lpt_y, row_mask, loss, stats, lps);
 }
 
 hipError_t launch_topk_dz_add(const uint16_t* h, const uint16_t* W, int N, int V, int H, int K, const int32_t* S,
                               const float* lpt_S, const float* lps, const uint8_t* row_mask, const float* grad,
                               const float* stats, const uint32_t* scales, uint16_t* dz, int ldz, int c0, int width,
                               hipStream_t s) {
-  topk_dz_add<<<(unsigned)((N + 3) / 4), 256, 0, s>>>(h, W, N, V, H, K, S, lpt_S, lps, row_mask, grad, stats, scales,
+  return launch(topk_dz_add, (unsigned)((N + 3) / 4), 256, s, h, W, N, V, H, K, S, lpt_S, lps, row_mask, grad, stats, scales,
                                                       dz, ldz, c0, width);
-  return hipGetLastError();
 }
 
 hipError_t launch_absmax_bf16(const uint16_t* h, int64_t n, uint32_t* scales, hipStream_t s) {
-  absmax_bf16<<<grid1(n / 8 + 1, 256 * 4, 256), 256, 0, s>>>(h, n, scales);
-  return hipGetLastError();
+  return launch(absmax_bf16, grid1(n / 8 + 1, 256 * 4, 256), 256, s, h, n, scales);
 }
 
 hipError_t launch_transpose_h(const uint16_t* h, int N, int H, const uint32_t* scales, uint16_t* hT, int ldT,
                               hipStream_t s) {
   dim3 g((unsigned)(ldT / 64), (unsigned)(H / 64));
-  transpose_h<<<g, 256, 0, s>>>(h, N, H, scales, hT, ldT);
-  return hipGetLastError();
+  return launch(transpose_h, g, 256, s, h, N, H, scales, hT, ldT);
 }
 
 hipError_t launch_w_rescale(const uint16_t* W_chunk, int rows, int ntv, int H, const uint32_t* wmag, uint16_t* w16,
                             hipStream_t s) {
   const int64_t n8 = (int64_t)ntv * kFwdTileV * H / 8;
-  w_rescale<<<grid1(n8, 256 * 4, 2048), 256, 0, s>>>(W_chunk, rows, ntv * kFwdTileV, H, wmag, w16);
-  return hipGetLastError();
+  return launch(w_rescale, grid1(n8, 256 * 4, 2048), 256, s, W_chunk, rows, ntv * kFwdTileV, H, wmag, w16);
 }
 
 hipError_t launch_dw(const DwParams& p, hipStream_t s) {
-  dw_gemm<kDwWaves><<<(unsigned)(p.ntm * p.ntn), 64 * kDwWaves, 0, s>>>(p);
-  return hipGetLastError();
+  return launch(dw_gemm<kDwWaves>, (unsigned)(p.ntm * p.ntn), 64 * kDwWaves, s, p);
 }
 
 hipError_t launch_dh(const DhParams& p, hipStream_t s) {
-  dh_gemm<kDhWaves><<<(unsigned)(p.ntm * p.ntn * (p.partial ? p.nseg : 1)), 64 * kDhWaves, 0, s>>>(p);
-  return hipGetLastError();
+  return launch(dh_gemm<kDhWaves>, (unsigned)(p.ntm * p.ntn * (p.partial ? p.nseg : 1)), 64 * kDhWaves, s, p);
 }
 
 hipError_t launch_dh_reduce(const DhParams& p, hipStream_t s) {
-  dh_reduce<<<grid1((int64_t)p.N * p.H / 4, 256, 2048), 256, 0, s>>>(p);
-  return hipGetLastError();
+  return launch(dh_reduce, grid1((int64_t)p.N * p.H / 4, 256, 2048), 256, s, p);
 }
 
 hipError_t launch_fwd_rows_logits(const float* z_s, const float* z_t, const int32_t* z_rows, int z_nrows, int N, int V,
                                   const uint8_t* row_mask, float* loss, float* stats, float* merged, hipStream_t s) {
-  fwd_rows_logits<<<(unsigned)N, 256, 0, s>>>(z_s, z_t, z_rows, z_nrows, N, V, row_mask, loss, stats, merged);
-  return hipGetLastError();
+  return launch(fwd_rows_logits, (unsigned)N, 256, s, z_s, z_t, z_rows, z_nrows, N, V, row_mask, loss, stats, merged);
 }
 
 hipError_t launch_bwd_rows_logits(const float* z_s, const float* z_t, const int32_t* z_rows, int z_nrows, int N, int V,
                                   const uint8_t* row_mask, const float* grad, const float* stats, float* dz,
                                   hipStream_t s) {
   dim3 g((unsigned)N, (unsigned)((V + 255) / 256));
-  bwd_rows_logits<<<g, 256, 0, s>>>(z_s, z_t, z_rows, z_nrows, N, V, row_mask, grad, stats, dz);
-  return hipGetLastError();
+  return launch(bwd_rows_logits, g, 256, s, z_s, z_t, z_rows, z_nrows, N, V, row_mask, grad, stats, dz);
 }
 
 hipError_t launch_compact(const uint8_t* mask, int T, int32_t* row_idx, int32_t* n_out, hipStream_t s) {
-  compact_kernel<<<1, 1024, 0, s>>>(mask, T, row_idx, n_out);
-  return hipGetLastError();
+  return launch(compact_kernel, 1, 1024, s, mask, T, row_idx, n_out);
 }
 
 hipError_t launch_group_by_teacher(const int32_t* teacher, const uint8_t* mask, int N, int K, int32_t* perm,
                                    int32_t* teacher_p, uint8_t* mask_p, hipStream_t s) {
   if (K < 1 || K > 31) return hipErrorInvalidValue;
-  group_by_teacher_kernel<<<1, 1024, 0, s>>>(teacher, mask, N, K, perm, teacher_p, mask_p);
-  return hipGetLastError();
+  return launch(group_by_teacher_kernel, 1, 1024, s, teacher, mask, N, K, perm, teacher_p, mask_p);
 }
 
 hipError_t launch_gather(const void* src, int64_t row_bytes, const int32_t* row_idx, int64_t N, void* dst,
@@ -1774,10 +1790,9 @@ hipError_t launch_gather(const void* src, int64_t row_bytes, const int32_t* row_
   const int64_t units = v16 ? row_bytes / 16 : row_bytes / 4;
   dim3 g((unsigned)N, grid1(units, 256, 64));
   if (v16)
-    gather_kernel<u32x4><<<g, 256, 0, s>>>((const u32x4*)src, units, row_idx, (u32x4*)dst);
+    return launch(gather_kernel<u32x4>, g, 256, s, (const u32x4*)src, units, row_idx, (u32x4*)dst);
   else
-    gather_kernel<uint32_t><<<g, 256, 0, s>>>((const uint32_t*)src, units, row_idx, (uint32_t*)dst);
-  return hipGetLastError();
+    return launch(gather_kernel<uint32_t>, g, 256, s, (const uint32_t*)src, units, row_idx, (uint32_t*)dst);
 }
 
 hipError_t launch_scatter(const void* src, int64_t row_bytes, const int32_t* row_idx, int64_t N, void* dst,
@@ -1786,17 +1801,15 @@ hipError_t launch_scatter(const void* src, int64_t row_bytes, const int32_t* row
   const int64_t units = v16 ? row_bytes / 16 : row_bytes / 4;
   dim3 g((unsigned)N, grid1(units, 256, 64));
   if (v16)
-    scatter_kernel<u32x4><<<g, 256, 0, s>>>((const u32x4*)src, units, row_idx, (u32x4*)dst);
+    return launch(scatter_kernel<u32x4>, g, 256, s, (const u32x4*)src, units, row_idx, (u32x4*)dst);
   else
-    scatter_kernel<uint32_t><<<g, 256, 0, s>>>((const uint32_t*)src, units, row_idx, (uint32_t*)dst);
-  return hipGetLastError();
+    return launch(scatter_kernel<uint32_t>, g, 256, s, (const uint32_t*)src, units, row_idx, (uint32_t*)dst);
 }
 
 hipError_t launch_fill_zero(void* p, int64_t bytes, hipStream_t s) {
   const int64_t n = bytes / 4;
   if (n == 0) return hipSuccess;
-  fill_zero_u32<<<grid1(n, 256, 8192), 256, 0, s>>>((uint32_t*)p, n);
-  return hipGetLastError();
+  return launch(fill_zero_u32, grid1(n, 256, 8192), 256, s, (uint32_t*)p, n);
 }
 
 }  // namespace rkl

@@ -240,3 +240,18 @@ def test_last_error_is_per_thread():
     t.join()
     assert "multiple of 64" in seen["msg"]
     assert R.lib().rkl_last_error().decode() == main_msg
+
+
+def test_kernel_times_without_launches():
+    # timing on, nothing launched (rejected calls launch nothing): no entries,
+    # and nothing that needs a device is touched
+    L = R.lib()
+    assert L.rkl_kernel_timing(1) == 0
+    try:
+        assert L.rkl_scatter_rows(FAKE, 3, 8, FAKE, 2, FAKE, None) == 1
+        assert R.kernel_times() == {}
+        count = ctypes.c_int(-1)
+        assert L.rkl_kernel_times(0, None, None, None, ctypes.byref(count)) == 0 and count.value == 0
+        assert L.rkl_kernel_times(-1, None, None, None, ctypes.byref(count)) == 1
+    finally:
+        assert L.rkl_kernel_timing(0) == 0
