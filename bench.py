@@ -76,7 +76,7 @@ HBM_PEAK = 8.0e12
 DTYPE = "bf16 projections; fp16 dz/dh/dW GEMM operands (power-of-two scaled); fp32 accumulation"
 
 FWD_KERNELS = ("fwd_tiles", "fwd_combine", "fwd_rows_logits", "topk_terms")
-BWD_KERNELS = ("grad_scale", "absmax_bf16", "transpose_h", "bwd_dz_tiles", "w_rescale", "dw_gemm", "dh_gemm", "dh_reduce",
+BWD_KERNELS = ("grad_scale", "absmax_bf16", "convert_h", "bwd_dz_tiles", "w_rescale", "dw_gemm", "dh_gemm", "dh_reduce",
                "bwd_rows_logits", "topk_dz_add")
 MFMA_KERNELS = ("fwd_tiles", "bwd_dz_tiles", "dw_gemm", "dh_gemm")
 

@@ -82,7 +82,7 @@ const char* rkl_version(void);
  * entry k < min(*count, cap) gets names[k] (static storage), total_ms[k] and
  * launches[k]; *count receives the number of distinct kernels (may exceed
  * cap).  Host pointers.  Names: fwd_tiles, fwd_combine, bwd_dz_tiles,
- * dw_gemm, dh_gemm, dh_reduce, grad_scale, absmax_bf16, transpose_h, w_rescale,
+ * dw_gemm, dh_gemm, dh_reduce, grad_scale, absmax_bf16, convert_h, w_rescale,
  * compact, gather, scatter, fill_zero, fwd_rows_logits, bwd_rows_logits,
  * group_by_teacher, topk_terms, topk_dz_add.
  */

@@ -259,16 +259,16 @@ int64_t dh_segments(int64_t c0, int64_t width) {
 }
 
 struct BwdLayout {
-  int64_t ldT, ldz, npad, nchunks, nseg;
-  size_t off_hT, off_dz, off_w16, off_dhp, off_scale, total;
+  int64_t hrows, ldz, npad, nchunks, nseg;
+  size_t off_h16, off_dz, off_w16, off_dhp, off_scale, total;
 };
-// [scale block: rkl::kScaleWmag + nchunks words][hT: Hs x ldT fp16][dz chunk:
+// [scale block: rkl::kScaleWmag + nchunks words][h16: hrows x Hs fp16][dz chunk:
 // npad x ldz fp16][fp16 W_s chunk copy][dh segment sums nseg x N x Hs fp32,
 // when dh is split]; npad = N rounded up to the 128-token tile (the dz
 // kernel writes those rows as zero)
 BwdLayout bwd_layout(int64_t N, int64_t V, int64_t Hs) {
   BwdLayout L{};
-  L.ldT = round_up(N, 64);
+  L.hrows = round_up(N, 64);
   L.npad = round_up(N, rkl::kFwdTileN);
   const int64_t C = vocab_chunk(N);
   L.ldz = round_up(V < C ? V : C, 64);
@@ -280,8 +280,8 @@ BwdLayout bwd_layout(int64_t N, int64_t V, int64_t Hs) {
     if (n > L.nseg) L.nseg = n;
   }
   L.off_scale = 0;
-  L.off_hT = align256((size_t)(rkl::kScaleWmag + L.nchunks) * 4);
-  L.off_dz = L.off_hT + align256((size_t)Hs * L.ldT * 2);
+  L.off_h16 = align256((size_t)(rkl::kScaleWmag + L.nchunks) * 4);
+  L.off_dz = L.off_h16 + align256((size_t)Hs * L.hrows * 2);
   L.off_w16 = L.off_dz + align256((size_t)L.npad * L.ldz * 2);
   // the fp16 W_s copy covers every 256-row vocabulary tile of a chunk
   L.off_dhp = L.off_w16 + align256((size_t)round_up(L.ldz, rkl::kFwdTileV) * Hs * 2);
@@ -440,13 +440,13 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
   NEED16(ws, "workspace");
   char* base = static_cast<char*>(ws);
   uint32_t* scales = reinterpret_cast<uint32_t*>(base + L.off_scale);
-  uint16_t* hT = reinterpret_cast<uint16_t*>(base + L.off_hT);
+  uint16_t* h16 = reinterpret_cast<uint16_t*>(base + L.off_h16);
   uint16_t* dz = reinterpret_cast<uint16_t*>(base + L.off_dz);
   uint16_t* w16 = reinterpret_cast<uint16_t*>(base + L.off_w16);
   RKL_LAUNCH("grad_scale", s, rkl::launch_grad_scale(grad, grad_h, row_mask, stats, (int)N, mode,
                                  (int)L.nchunks, scales, s));
   RKL_LAUNCH("absmax_bf16", s, rkl::launch_absmax_bf16(h_s, N * Hs, scales, s));
-  RKL_LAUNCH("transpose_h", s, rkl::launch_transpose_h(h_s, (int)N, (int)Hs, scales, hT, (int)L.ldT, s));
+  RKL_LAUNCH("convert_h", s, rkl::launch_convert_h(h_s, (int)N, (int)Hs, scales, h16, (int)L.hrows, s));
   const int64_t C = vocab_chunk(N);
   for (int64_t c0 = 0, chunk = 0; c0 < V; c0 += C, ++chunk) {
     uint32_t* wmag = scales + rkl::kScaleWmag + chunk;
@@ -476,7 +476,7 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
 
     rkl::DwParams w{};
     w.scales = scales; w.dz = dz; w.ldz = (int)L.ldz; w.N = (int)N; w.kpad = (int)kpad; w.width = (int)width;
-    w.hT = hT; w.ldT = (int)L.ldT; w.H = (int)Hs;
+    w.h16 = h16; w.hrows = (int)L.hrows; w.H = (int)Hs;
     w.dW = dW + c0 * Hs; w.accumulate = accumulate;
     w.ntm = (int)ceil_div(width, rkl::kDwTileM);
     w.ntn = (int)ceil_div(Hs, rkl::kDwTileN);

@@ -63,8 +63,8 @@ struct DwParams {
   const uint32_t* scales;  // kScaleKs, kScaleHmag: dW = 2^-(ks + kh) * sum of the fp16 products
   const uint16_t* dz;
   int ldz, N, kpad, width;
-  const uint16_t* hT;      // [H, ldT] fp16
-  int ldT, H;
+  const uint16_t* h16;     // [hrows, H] fp16(2^kh h_s), rows past N zero
+  int hrows, H;
   float* dW;               // dW_s + c0 * H
   int accumulate;
   int ntm, ntn;
@@ -102,7 +102,7 @@ constexpr int kDhWaves = 4;
 // every copy is exact wherever fp16 represents the scaled value and the GEMM
 // epilogues undo the scales exactly:
 //   dz   = fp16(2^ks dz),   2^ks puts the largest |g| p_max in [16, 32);
-//   hT   = fp16(2^kh h_s),  2^kh puts the largest |h_s| in [2^14, 2^15);
+//   h16  = fp16(2^kh h_s),  2^kh puts the largest |h_s| in [2^14, 2^15);
 //   W16  = fp16(2^kw W_s) per chunk, kw = 0 while the chunk's largest |W_s|
 //          lies in [2^-10, 2^15), else the power of two that puts it in
 //          [2^14, 2^15) (the dz kernel converts with kw = 0 and records the
@@ -173,7 +173,7 @@ hipError_t launch_topk_dz_add(const uint16_t* h, const uint16_t* W, int N, int V
                               hipStream_t s);
 // scales[kScaleHmag] = max over h [n] of the bf16 magnitude bits (after launch_grad_scale cleared it)
 hipError_t launch_absmax_bf16(const uint16_t* h, int64_t n, uint32_t* scales, hipStream_t s);
-hipError_t launch_transpose_h(const uint16_t* h, int N, int H, const uint32_t* scales, uint16_t* hT, int ldT,
+hipError_t launch_convert_h(const uint16_t* h, int N, int H, const uint32_t* scales, uint16_t* h16, int hrows,
                               hipStream_t s);
 // The chunk's W16 again with 2^kw when its recorded largest |W_s| (wmag) is out of band; else nothing.
 // W_chunk: the chunk's first row of W_s; rows valid rows, ntv * 256 rows written (zeros past rows).

@@ -701,11 +701,11 @@ __device__ __forceinline__ int bf16_mag_exp(uint32_t m) {
   return (32 - __clz((int)(m & 0x7fu))) - 133;   // subnormal: 0.f x 2^-126
 }
 __device__ __forceinline__ int clamp_shift(int k) { return k < -kMaxExpShift ? -kMaxExpShift : (k > kMaxExpShift ? kMaxExpShift : k); }
-// 2^kh for hT: the largest |h_s| into [2^14, 2^15).
+// 2^kh for h16: the largest |h_s| into [2^14, 2^15).
 __device__ __forceinline__ int h_scale_exp(uint32_t m) { return m ? clamp_shift(15 - bf16_mag_exp(m)) : 0; }
 // 2^kw for the W_s copy: 1 while the largest |W_s| is in [2^-10, 2^15) (no
 // overflow, and everything within 2^-4 of fp16's normal range at the top),
-// else as for hT.
+// else as for h16.
 __device__ __forceinline__ int w_scale_exp(uint32_t m) {
   if (m == 0) return 0;
   const int e = bf16_mag_exp(m);
@@ -1023,24 +1023,28 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
   }
 }
 
-// h_s [N, H] bf16 -> hT [H, ldT] fp16 = fp16(2^kh h_s) (2^kh from the
+// h_s [N, H] bf16 -> h16 [hrows, H] fp16 = fp16(2^kh h_s) (2^kh from the
 // recorded largest |h_s|: exact except for values more than 2^29 below the
-// largest, which fall to fp16 subnormals), zero for token columns in [N, ldT).
-__global__ __launch_bounds__(256) void transpose_h(const uint16_t* __restrict__ h, int N, int H,
-                                                   const uint32_t* __restrict__ scales, uint16_t* __restrict__ hT,
-                                                   int ldT) {
-  __shared__ uint16_t tile[64][66];
-  const int n0 = blockIdx.x * 64, j0 = blockIdx.y * 64, tid = threadIdx.x;
+// largest, which fall to fp16 subnormals), zero rows for tokens in [N, hrows).
+// Same layout as h_s: the dW GEMM reads it as its MN-major operand.
+__global__ __launch_bounds__(256) void convert_h(const uint16_t* __restrict__ h, int N, int H,
+                                                   const uint32_t* __restrict__ scales, uint16_t* __restrict__ h16,
+                                                   int hrows) {
   const int kh = h_scale_exp(scales[kScaleHmag]);
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int r = e >> 6, c = e & 63;
-    tile[r][c] = (n0 + r < N) ? h[(int64_t)(n0 + r) * H + j0 + c] : (uint16_t)0;
-  }
-  __syncthreads();
-  for (int e = tid; e < 64 * 64; e += 256) {
-    const int r = e >> 6, c = e & 63;
-    const float x = ldexpf(__builtin_bit_cast(float, (uint32_t)tile[c][r] << 16), kh);
-    hT[(int64_t)(j0 + r) * ldT + n0 + c] = __builtin_bit_cast(uint16_t, (_Float16)x);
+  const int64_t n8 = (int64_t)hrows * H / 8, live8 = (int64_t)N * H / 8;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += (int64_t)gridDim.x * 256) {
+    u32x4 o = u32x4{0u, 0u, 0u, 0u};
+    if (i < live8) {
+      const u32x4 x = reinterpret_cast<const u32x4*>(h)[i];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float lo = ldexpf(__builtin_bit_cast(float, x[e] << 16), kh);
+        const float hi = ldexpf(__builtin_bit_cast(float, x[e] & 0xFFFF0000u), kh);
+        o[e] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lo) |
+               ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)hi) << 16);
+      }
+    }
+    reinterpret_cast<u32x4*>(h16)[i] = o;
   }
 }
 
@@ -1072,10 +1076,14 @@ __global__ __launch_bounds__(256) void w_rescale(const uint16_t* __restrict__ W,
 
 // ===========================================================================
 // Backward, step 2: dW_s[c0 + m, n] (+)= (1/s) sum_t dz[t, m] h_s[t, n]
-// A = dz (MN-major: token rows, vocabulary contiguous; read transposed),
-// B = hT (K-major).  256 x 256 tiles in 32-deep k-tiles through four LDS
-// stages (128 KB): the DMA runs three k-tiles ahead.  (Three 64-deep stages of
-// a 256 x 256 tile would need 192 KB; with two, memory latency showed.)
+// A = dz and B = h16 = the scaled fp16 copy of h_s, both MN-major (token rows,
+// vocabulary / hidden units contiguous; read transposed): every DMA
+// instruction loads two 512-byte row segments.  (With B as a transposed,
+// K-major copy, the 32-deep k-tiles made 64-byte row segments, which the
+// CU's vector-memory path serves at half the rate: 5 % slower.)  256 x 256
+// tiles in 32-deep k-tiles through four LDS stages (128 KB): the DMA runs
+// three k-tiles ahead.  (Three 64-deep stages of a 256 x 256 tile would need
+// 192 KB; with two, memory latency showed.)
 // ===========================================================================
 constexpr int WBM = kDwTileM, WBN = kDwTileN, WKT = 32, WNST = 4, WDSTEPS = 1;
 
@@ -1085,7 +1093,7 @@ __global__ __launch_bounds__(64 * NW, 1) void dw_gemm(DwParams p) {
   // transposed, is the operand with fewer fragments)
   constexpr int WGN = 2, WGM = NW / WGN;
   using TA = MN<WBM, NW, WKT>;
-  using TB = KM<WBN, NW, WKT>;
+  using TB = MN<WBN, NW, WKT>;
   __shared__ __attribute__((aligned(1024))) char lds[WNST * (TA::kBytes + TB::kBytes)];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, wm = w / WGN, wn = w % WGN;
   const int logical = xcd_logical(blockIdx.x, p.ntm * p.ntn);
@@ -1095,31 +1103,56 @@ __global__ __launch_bounds__(64 * NW, 1) void dw_gemm(DwParams p) {
   f32x16 acc[FM][FN];
   zero_acc(acc);
   // A: dz rows are tokens (k, zero-padded to the workspace's row count >=
-  // ldT), columns vocabulary (m); B: hT rows are hidden units (n), columns
-  // tokens (k, zero past N)
+  // hrows), columns vocabulary (m); B: h16 rows are tokens (k, zero past N),
+  // columns hidden units (n)
   TA ta;
   ta.init(p.dz + m0, p.ldz, p.kpad - m0, lane, __builtin_amdgcn_readfirstlane(w));
   TB tb;
-  tb.init(p.hT + (int64_t)n0 * p.ldT, p.ldT, p.H - n0, lane, __builtin_amdgcn_readfirstlane(w));
-  gemm_loop<TA, TB, f16x8, false, WNST, false, WDSTEPS>(acc, p.ldT / WKT, lds, ta, tb, 0, tid, wm * (WBM / WGM),
+  tb.init(p.h16 + n0, p.H, p.H - n0, lane, __builtin_amdgcn_readfirstlane(w));
+  gemm_loop<TA, TB, f16x8, false, WNST, false, WDSTEPS>(acc, p.hrows / WKT, lds, ta, tb, 0, tid, wm * (WBM / WGM),
                                                        wn * (WBN / WGN));
   // undo both operand scales at once (exact: a power of two)
   const int unscale = -((int)p.scales[kScaleKs] + h_scale_exp(p.scales[kScaleHmag]));
+  // Stores through LDS (free since gemm_loop's last barrier), in two rounds:
+  // round r takes blocks fn = 2r, 2r + 1 of every wave, i.e. the tile's
+  // columns wn * 128 + 64 r .. + 63 for both wn: a [256 rows][128] fp32 image
+  // (128 KB), 16-byte chunk q of row t at chunk q ^ 8 ((t / 4) % 2) (the two
+  // half-waves of a write, rows t and t + 4, then use different banks).  Then
+  // every thread stores 16-byte pieces: 16 lanes cover 64 contiguous columns
+  // of a row (256 bytes), where register-order stores would write one 4-byte
+  // value per lane.
+  static_assert(WBM * 128 * 4 <= WNST * (TA::kBytes + TB::kBytes) && FN == 4, "one round is half the tile");
+  constexpr int kRowB = 128 * 4;
+  auto chunk_at = [](int t, int q) { return q ^ (((t >> 2) & 1) << 3); };
 #pragma unroll
-  for (int fn = 0; fn < FN; ++fn) {
-    const int n = n0 + wn * (WBN / WGN) + fn * 32 + (lane & 31);
-    if (n >= p.H) continue;
+  for (int r = 0; r < 2; ++r) {
 #pragma unroll
-    for (int fm = 0; fm < FM; ++fm)
+    for (int j = 0; j < 2; ++j) {
+      const int fn = 2 * r + j;
+      const int col = wn * 64 + j * 32 + (lane & 31);   // column within the round's image
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int m = m0 + wm * (WBM / WGM) + fm * 32 + frag_row(i, lane);
-        if (m < p.width) {
-          float* o = p.dW + (int64_t)m * p.H + n;
-          const float d = ldexpf(acc[fm][fn][i], unscale);
-          *o = p.accumulate ? *o + d : d;
+      for (int fm = 0; fm < FM; ++fm)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int t = wm * (WBM / WGM) + fm * 32 + frag_row(i, lane);
+          *reinterpret_cast<float*>(lds + t * kRowB + (chunk_at(t, col >> 2) << 4) + (col & 3) * 4) =
+              ldexpf(acc[fm][fn][i], unscale);
         }
+    }
+    dma_barrier<63>();
+    // piece = (row, wn half): 16 threads x 16 bytes
+#pragma unroll 4
+    for (int it = 0; it < WBM * 2 * 16 / (64 * NW); ++it) {
+      const int piece = it * (64 * NW / 16) + (tid >> 4);
+      const int t = piece >> 1, half = piece & 1, q = half * 16 + (tid & 15);
+      const int m = m0 + t, n = n0 + half * 128 + 64 * r + (tid & 15) * 4;
+      const f32x4 v = *reinterpret_cast<const f32x4*>(lds + t * kRowB + (chunk_at(t, q) << 4));
+      if (m < p.width && n < p.H) {
+        f32x4* o = reinterpret_cast<f32x4*>(p.dW + (int64_t)m * p.H + n);
+        *o = p.accumulate ? *o + v : v;
       }
+    }
+    if (r == 0) dma_barrier<63>();   // round 1 writes the image again
   }
 }
 
@@ -1738,10 +1771,9 @@ hipError_t launch_absmax_bf16(const uint16_t* h, int64_t n, uint32_t* scales, hi
   return launch(absmax_bf16, grid1(n / 8 + 1, 256 * 4, 256), 256, s, h, n, scales);
 }
 
-hipError_t launch_transpose_h(const uint16_t* h, int N, int H, const uint32_t* scales, uint16_t* hT, int ldT,
+hipError_t launch_convert_h(const uint16_t* h, int N, int H, const uint32_t* scales, uint16_t* h16, int hrows,
                               hipStream_t s) {
-  dim3 g((unsigned)(ldT / 64), (unsigned)(H / 64));
-  return launch(transpose_h, g, 256, s, h, N, H, scales, hT, ldT);
+  return launch(convert_h, grid1((int64_t)hrows * H / 8, 256, 4096), 256, s, h, N, H, scales, h16, hrows);
 }
 
 hipError_t launch_w_rescale(const uint16_t* W_chunk, int rows, int ntv, int H, const uint32_t* wmag, uint16_t* w16,

@@ -37,7 +37,7 @@ def test_each_launch_is_one_entry(tdev):
         t = R.kernel_times()
     finally:
         R.kernel_timing(False)
-    for k in ("fwd_tiles", "fwd_combine", "bwd_dz_tiles", "dw_gemm", "dh_gemm", "grad_scale", "transpose_h"):
+    for k in ("fwd_tiles", "fwd_combine", "bwd_dz_tiles", "dw_gemm", "dh_gemm", "grad_scale", "convert_h"):
         assert k in t, (k, sorted(t))
         ms, n = t[k]
         assert n >= 1 and ms > 0.0, (k, ms, n)
