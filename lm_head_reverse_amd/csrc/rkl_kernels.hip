@@ -1089,8 +1089,7 @@ constexpr int WBM = kDwTileM, WBN = kDwTileN, WKT = 32, WNST = 4, WDSTEPS = 1;
 
 template <int NW>
 __global__ __launch_bounds__(64 * NW, 1) void dw_gemm(DwParams p) {
-  // NW = 8 (kDwWaves): waves 4 (m) x 2 (n), 64 x 128 each (A, read
-  // transposed, is the operand with fewer fragments)
+  // NW = 8 (kDwWaves): waves 4 (m) x 2 (n), 64 x 128 each
   constexpr int WGN = 2, WGM = NW / WGN;
   using TA = MN<WBM, NW, WKT>;
   using TB = MN<WBN, NW, WKT>;

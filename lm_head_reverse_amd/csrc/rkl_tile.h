@@ -1,22 +1,24 @@
-// rkl_tile.h -- bf16 MFMA tile engine for gfx950 (CDNA4).
+// rkl_tile.h -- bf16 / fp16 MFMA tile engine for gfx950 (CDNA4).
 //
-// One workgroup = 256 threads = 4 wave64s arranged 2 x 2.  A workgroup tile
-// C[BM, BN] (fp32) is the product of two operand tiles that both arrive in
-// LDS as "rows x 64 k" bf16 blocks:  C[m, n] = sum_k A[m, k] * B[n, k].
-// Each wave owns a (BM/2) x (BN/2) sub-tile made of 32 x 32 blocks computed
-// with v_mfma_f32_32x32x16_bf16.
+// A workgroup tile C[BM, BN] (fp32) is the product of two operand tiles that
+// arrive in LDS by direct-to-LDS DMA:  C[m, n] = sum_k A[m, k] * B[n, k].
+// Each wave owns a sub-tile made of 32 x 32 blocks computed with
+// v_mfma_f32_32x32x16_bf16 (or _f16); the kernels set the wave count and
+// the wave layout.
 //
 // Operands may be K-major in memory (k contiguous: hidden states, LM-head
-// weights, dz rows) or MN-major (m or n contiguous: the weight when the
-// contraction runs over the vocabulary, dz when it runs over tokens).  The
-// MN-major loader transposes 4 x 8 blocks in registers so that LDS always
-// holds k-contiguous rows and every MFMA fragment is one 16-byte LDS read.
+// weights, dz rows when the contraction runs over the vocabulary) or MN-major
+// (m or n contiguous: the fp16 weight copy when the contraction runs over
+// the vocabulary, dz and the fp16 copy of h_s when it runs over tokens).
+// K-major tiles land as k-contiguous rows and every MFMA fragment is one
+// 16-byte LDS read; MN-major tiles land as they are in memory and are read
+// back with gfx950's transposing LDS read (two per fragment).
 //
-// LDS rows are 128 bytes (64 bf16).  The 16-byte chunk c of row r lives at
-// chunk c ^ ((r ^ (r >> 3)) & 7): fragment reads by 8 consecutive lanes
-// (8 consecutive rows, one chunk) and the transposing 8-byte writes both
-// spread over all banks, and one direct-to-LDS wave instruction (8 rows of
-// 128 bytes) reads 8 whole 128-byte row segments from global memory.
+// The fused kernels' LDS rows are 128 bytes (64 bf16).  The 16-byte chunk c
+// of row r lives at chunk c ^ ((r ^ (r >> 3)) & 7): fragment reads by 8
+// consecutive lanes (8 consecutive rows, one chunk) spread over all banks,
+// and one direct-to-LDS wave instruction (8 rows of 128 bytes) reads 8 whole
+// 128-byte row segments from global memory.
 #pragma once
 
 #include <hip/hip_runtime.h>

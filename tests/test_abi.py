@@ -67,7 +67,7 @@ def test_workspace_sizes():
     # no fp32 [N, V] logits (4096 x 151936 x 4 B = 2.49 GB) are ever held; the
     # backward keeps an fp16 dz chunk of whole 65536-column segments within
     # 2 GiB (the whole vocabulary at N = 4096), an fp16 copy of that chunk of
-    # W_s and the transposed fp16 h_s
+    # W_s and the scaled fp16 copy of h_s
     assert b < 4096 * 151936 * 4
     assert b <= 4096 * 151936 * 2 + 152064 * 2048 * 2 + 2048 * 4096 * 2 + (1 << 20)
     # N = 8192: two segments (2 GiB of dz); N = 32768: one segment
