@@ -206,14 +206,21 @@ Split fwd_split(int64_t V) {
 // 4296 / 4329 on another; N = 8192 (4 groups of 50) 8468 / 8564; N = 16384
 // (2 groups of 99) 16839 / 17196; N = 1000 (29 groups of 7, 232
 // workgroups: one ragged wave against seven) 1197 / 1240; N = 4224 (groups
-// of 2) 4762 / 4734, within the noise.  Does not change results.
+// of 2) 4762 / 4734, within the noise.  With several teachers chosen per row
+// (uneven), token tiles differ in work -- a tile that straddles a teacher
+// boundary runs a teacher pass per teacher -- and long workgroups would
+// leave the slowest tiles' workgroups running alone: one split per
+// workgroup lets the CUs balance them (K = 4, N = 4096, rows in random
+// order: forward 5.29 against 6.63 ms; in runs of 1024 rows, which no tile
+// straddles, 4.78 against 4.60 ms).  Does not change results.
 // RKL_FWD_SPLITS_PER_WG overrides it.
 constexpr int64_t kCUs = 256;   // MI355X compute units
-int fwd_splits_per_wg(int nsplit, int tiles_per_split, int64_t ntok) {
+int fwd_splits_per_wg(int nsplit, int tiles_per_split, int64_t ntok, bool uneven) {
   if (const char* s = std::getenv("RKL_FWD_SPLITS_PER_WG")) {
     const int v = std::atoi(s);
     if (v >= 1) return v < nsplit ? v : nsplit;
   }
+  if (uneven) return 1;
   if (ntok < 1) ntok = 1;
   auto cost = [&](int spw) {
     const int64_t waves = ceil_div(ceil_div(nsplit, spw) * ntok, kCUs);
@@ -397,7 +404,7 @@ int forward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16* 
   p.tiles_per_split = sp.tiles_per_split;
   p.nsplit = sp.nsplit;
   p.ntok = (int)ceil_div(N, rkl::kFwdTileN);
-  p.splits_per_wg = fwd_splits_per_wg(p.nsplit, p.tiles_per_split, p.ntok);
+  p.splits_per_wg = fwd_splits_per_wg(p.nsplit, p.tiles_per_split, p.ntok, tch.teacher && tch.K > 1);
   p.order_gs = fwd_order().gs;
   p.order_tg = fwd_order().tg;
   const int mode = mode_of(z_t, y, tch.teacher);
