@@ -91,9 +91,14 @@ struct DhParams {
 };
 
 // Waves per workgroup: the fused kernels (two waves per SIMD, 64 x 64 of both
-// projections per wave), the dW GEMM (two per SIMD) and the dh GEMM (one per
-// SIMD) -- the layouts measured fastest; no other count is built.
+// projections per wave), the log-probability / entropy forward and the top-k
+// estimator's dz kernel (one projection: one wave per SIMD, 128 x 64 per wave,
+// six fragments feed eight MFMAs instead of four feeding four), the dW GEMM
+// (two per SIMD) and the dh GEMM (one per SIMD) -- the layouts measured
+// fastest; no other count is built.  (The teacher-logits kernels and the
+// log-probability / entropy dz kernel keep eight: with four they spill.)
 constexpr int kFusedWaves = 8;
+constexpr int kFusedWavesOne = 4;
 constexpr int kDwWaves = 8;
 constexpr int kDhWaves = 4;
 

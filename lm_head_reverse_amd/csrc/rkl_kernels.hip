@@ -63,11 +63,15 @@ using FwdStages = Stages<FBM, FBN>;
 
 // Wave layout of the fused kernels: NW waves as NW/2 rows (vocabulary) x 2
 // columns (tokens) over the 256 x 128 tile; each wave holds FM x FN 32x32
-// blocks of z_s and of z_t.  Built with eight waves (kFusedWaves): 64 x 64 per
-// wave, 128 accumulator registers, two waves per SIMD (one can issue MFMAs
-// while the other waits on LDS or the DMA).  (Four waves at 128 x 64 would
-// read a third fewer fragments but need 256 accumulator registers per wave,
-// which spill.)
+// blocks of z_s and of z_t.  Built with eight waves (kFusedWaves) for the two
+// projections: 64 x 64 per wave, 128 accumulator registers, two waves per
+// SIMD (one can issue MFMAs while the other waits on LDS or the DMA); four
+// waves at 128 x 64 would read a quarter fewer fragments per MFMA but need
+// 256 accumulator registers per wave, which spill.  With one projection the
+// four-wave layout holds 128 and is built (kFusedWavesOne) for the
+// log-probability / entropy forward (-0.6 %) and the top-k estimator's dz
+// (-2.5 %); the log-probability / entropy dz (its entropy term needs a few
+// registers more) spills with four and keeps eight.
 template <int NW>
 struct Fused {
   static constexpr int kThreads = 64 * NW;
@@ -937,10 +941,11 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
       return v == yv[fn] ? d + gs[fn] : d;
     };
     if (MODE == 2 || MODE == 4) {
+      // (one projection: lpe ignores its second operand, so z_s stands in for it)
       if (v0 + FBM <= p.V)
-        dz_pack<false>(zs, zt, pk, live, v0 + arow0 + lrow, p.V, lpe);
+        dz_pack<false>(zs, zs, pk, live, v0 + arow0 + lrow, p.V, lpe);
       else
-        dz_pack<true>(zs, zt, pk, live, v0 + arow0 + lrow, p.V, lpe);
+        dz_pack<true>(zs, zs, pk, live, v0 + arow0 + lrow, p.V, lpe);
     } else if (MODE != 1) {
       if (v0 + FBM <= p.V)
         dz_pack<false>(zs, zt, pk, live, v0 + arow0 + lrow, p.V, kl);
@@ -1703,7 +1708,7 @@ hipError_t launch_fwd_tiles(const FwdParams& p, int mode, hipStream_t s) {
   else if (mode == kModeHiddenTeachers)
     return launch(fwd_tiles<kModeHiddenTeachers, true, NW>, nb, nt, s, p);
   else if (mode == kModeLogprobEntropy)
-    return launch(fwd_tiles<kModeLogprobEntropy, true, NW>, nb, nt, s, p);
+    return launch(fwd_tiles<kModeLogprobEntropy, true, kFusedWavesOne>, nb, Fused<kFusedWavesOne>::kThreads, s, p);
   else if (p.V % 4 == 0)
     return launch(fwd_tiles<kModeTeacherLogits, true, NW>, nb, nt, s, p);
   else
@@ -1735,7 +1740,7 @@ hipError_t launch_bwd_dz(const BwdParams& p, int mode, hipStream_t s) {
   else if (mode == kModeLogprobEntropy)
     return launch(bwd_dz_tiles<kModeLogprobEntropy, true, NW>, nb, nt, s, p);
   else if (mode == kModeTopK)
-    return launch(bwd_dz_tiles<kModeTopK, true, NW>, nb, nt, s, p);
+    return launch(bwd_dz_tiles<kModeTopK, true, kFusedWavesOne>, nb, Fused<kFusedWavesOne>::kThreads, s, p);
   else if (p.V % 4 == 0)
     return launch(bwd_dz_tiles<kModeTeacherLogits, true, NW>, nb, nt, s, p);
   else
