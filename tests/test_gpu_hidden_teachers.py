@@ -80,6 +80,22 @@ def test_against_oracle(tdev, order):
     _check(case, W_t, teacher, _run(case, W_t, teacher, dev))
 
 
+def test_splits_per_workgroup_do_not_change_results(tdev, monkeypatch):
+    """With several teachers per row the forward takes one vocabulary split
+    per workgroup; a workgroup that streams several splits (V = 3001: all
+    twelve one-tile splits, or two) flushes each split's statistics the same
+    way: bit for bit."""
+    torch, dev = tdev
+    case, W_t, teacher = _problem(505, T=300, V=3001, Hs=128, Ht=192, K=3)
+    say("teachers splits per workgroup")
+    ref = _run(case, W_t, teacher, dev)
+    for spw in ("1000", "2"):
+        monkeypatch.setenv("RKL_FWD_SPLITS_PER_WG", spw)
+        got = _run(case, W_t, teacher, dev)
+        for a, b, what in zip(got[1:], ref[1:], ("loss", "stats", "dh", "dW")):
+            assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), (spw, what)
+
+
 def test_one_teacher_equals_single_teacher_path(tdev):
     torch, dev = tdev
     case, W_t, teacher = _problem(501, T=200, V=1500, Hs=128, Ht=64, K=1)
