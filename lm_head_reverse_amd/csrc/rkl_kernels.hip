@@ -1689,6 +1689,8 @@ static hipError_t launch(void (*kernel)(P...), dim3 grid, dim3 block, hipStream_
   }, vals);
   const hipEvent_t e0 = g_launch_ev[0], e1 = g_launch_ev[1];
   g_launch_ev[0] = g_launch_ev[1] = nullptr;
+  // untimed: the plain launch (what kernel<<<>>> does, stream capture included)
+  if (!e0 && !e1) return hipLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, s);
   return hipExtLaunchKernel(reinterpret_cast<const void*>(kernel), grid, block, args, 0, s, e0, e1, 0);
 }
 
