@@ -146,7 +146,8 @@ int set_last_error(int code, const char* msg);
 
 // Per-kernel timing: events that the calling thread's next kernel launch
 // takes as its own start and stop (hipExtLaunchKernel stamps them with the
-// kernel's begin and end, with no marker packets of their own in the queue).
+// kernel's begin and end, with no marker packets of their own in the queue;
+// without events a launch is the plain one).
 // Each launch_* function below launches at most one kernel, and that launch
 // clears them; launch_events_pending() is then false.  A launch_* call that
 // launched nothing leaves them pending.
