@@ -151,6 +151,19 @@ int bwd_tiles_per_group(int mode) {
   return (mode == rkl::kModeHidden || mode == rkl::kModeHiddenTeachers) ? 1 : 2;
 }
 
+// Whether the dz kernel makes its share of the fp16 W_s copy after the
+// stream, from the k-tile loaded again, rather than from the stream's own
+// stage (same bits): when each workgroup runs one job (both projections) and
+// converts at most one k-tile (Hs / 64 <= token tiles).  Mid-stream, the
+// copy's stores hold up the next k-step's barrier.  RKL_LATE_W16=0 turns it
+// off.
+bool late_w16(int mode, int tiles_per_group, int64_t Hs, int64_t ntok) {
+  if (const char* s = std::getenv("RKL_LATE_W16"))
+    if (s[0] == '0') return false;
+  return (mode == rkl::kModeHidden || mode == rkl::kModeHiddenTeachers) && tiles_per_group == 1 &&
+         Hs / 64 <= ntok;   // 64-deep k-tiles
+}
+
 // Workgroup order of the fused kernels (panel_order): GS vocabulary runs x TG
 // token tiles resident together.  Does not change results.  Measured at
 // N = 4096, H = 2048, V = 151936: the forward is fastest with 2 x 16, the
@@ -473,6 +486,7 @@ int backward_tiled(int64_t N, int64_t V, int64_t Hs, int64_t Ht, const rkl_bf16*
     b.ntok = (int)ceil_div(N, rkl::kFwdTileN);
     b.order_gs = bwd_order().gs;
     b.order_tg = bwd_order().tg;
+    b.late_w16 = late_w16(mode, b.tiles_per_group, Hs, b.ntok) ? 1 : 0;
     RKL_LAUNCH("bwd_dz_tiles", s, rkl::launch_bwd_dz(b, mode, s));
     if (topk.on && topk.K > 0)
       RKL_LAUNCH("topk_dz_add", s, rkl::launch_topk_dz_add(h_s, W_s, (int)N, (int)V, (int)Hs, topk.K, topk.S,

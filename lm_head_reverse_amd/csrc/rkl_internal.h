@@ -57,6 +57,7 @@ struct BwdParams {
   int ngroups;             // ceil(ntv / tiles_per_group)
   int ntok;
   int order_gs, order_tg;  // workgroup order (panel_order)
+  int late_w16;            // convert the fp16 W_s copy after the stream (one job, at most one k-tile per workgroup)
 };
 
 struct DwParams {

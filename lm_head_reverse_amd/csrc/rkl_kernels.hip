@@ -827,7 +827,7 @@ __device__ __forceinline__ void dz_pack(const f32x16 (&zs)[FM][FN], const f32x16
 // row_mask 0 are zero.  MODE 2 recomputes the one projection and writes the
 // log-probability / entropy gradient instead (see the per-token constants).
 // ===========================================================================
-template <int MODE, bool VEC4, int NW>
+template <int MODE, bool VEC4, int NW, bool LATE = false>
 __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams p) {
   using F = Fused<NW>;
   constexpr int FFM = F::FM, FFN = F::FN;
@@ -906,9 +906,16 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
   // workgroup takes one atomic maximum at its end (atomics on one address
   // serialise in L2: one per wave and conversion -- eight per job at 512
   // rows -- capped the kernel near 1.9 ms whatever N).
+  //
+  // When the workgroup converts at most one k-tile and runs one job (late_w16),
+  // it converts it after the stream instead: the k-tile's W_s rows are loaded
+  // again into the free LDS ring while the dz math runs, and the copy's stores
+  // go out with the dz stores.  Mid-stream, the next k-step's barrier waits
+  // for the copy's stores (a store and the DMA count in the one vector-memory
+  // counter), about 3 us per workgroup; at the end their wait overlaps the dz
+  // stores'.  The same bits either way.
   if (lane == 0) wmag_lds[w] = 0u;
-  auto convert_w = [&](const char* stage, int job, int kt) {
-    if (kt % p.ntok != tt % p.ntok) return;
+  auto convert_rows = [&](const char* stage, int job, int kt) {
     // thread tid converts rows r = i * kThreads / 8 + tid / 8, 16-byte piece
     // tid % 8: a wave-uniform base plus a 32-bit lane offset
     const int c = tid & 7;
@@ -924,6 +931,11 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
     }
     mag = wave_max_u32(mag);
     if (lane == 0) wmag_lds[w] = max(wmag_lds[w], mag);   // this wave's slot only
+  };
+  constexpr bool late = LATE;
+  auto convert_w = [&](const char* stage, int job, int kt) {
+    if (late || kt % p.ntok != tt % p.ntok) return;
+    convert_rows(stage, job, kt);
     // the next k-tile's DMA writes this stage: every wave's reads first
     // (the condition above is the same for the whole workgroup)
     dma_barrier<63>();
@@ -932,6 +944,24 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
   dual_stream<NW, MODE == 3>(o, vt1 - vt0, lds, zs, zt, tid, arow0, brow0, tkl, [&](int job, char* stage) {
     const int v0 = p.c0 + (vt0 + job) * FBM;
     const int hi = lane >> 5;
+    const bool last = vt0 + job + 1 == vt1;
+    // the late copy's k-tile and where it lands: after the dz tile's 64 KB
+    const int kt_late = tt % p.ntok;
+    const bool conv_late = late && last && kt_late < p.Hs / kKT;
+    constexpr int kLateOff = FBN * FBM * 2;
+    static_assert(kLateOff + FBM * kLdsRow <= 3 * FwdStages::kStage, "the late copy fits beside the dz tile");
+    if (conv_late) {
+      dma_barrier<0>();   // the stream's trailing DMAs landed: the whole ring is free
+      const int wave = __builtin_amdgcn_readfirstlane(w);
+      const uint16_t* src = p.W_s + (int64_t)v0 * p.Hs + kt_late * kKT;
+      const uint32_t dst = lds_addr(lds) + (uint32_t)kLateOff;
+#pragma unroll
+      for (int q = 0; q < F::kA; ++q) {
+        dma16(src, DmaRows<FBM, NW>::lane_off(q, 2u * (uint32_t)p.Hs, p.V - v0, lane, wave),
+              dst + (uint32_t)((wave * F::kA + q) * 1024));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    }
     uint32_t pk[FFM][FFN][2][4];   // [fm][fn][run][dword]
     auto kl = [&](float a, float bb, int fn, int) {
       return gs[fn] * ex2(fmaf(a, kL2E, -css[fn])) * ((a - bb) - cst[fn]);
@@ -991,7 +1021,11 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
               }
           }
         }
-        dma_barrier<63>();
+        // (the late copy's rows must have landed as well)
+        if (conv_late)
+          dma_barrier<0>();
+        else
+          dma_barrier<63>();
         // thread tid stores token row tr = it * kThreads / 32 + tid / 32 of
         // the round, columns col .. col + 7: a wave-uniform row base plus a
         // 32-bit lane offset (tid / 32) * ldz + (tid % 32) * 8 (no 64-bit
@@ -1012,9 +1046,13 @@ __global__ __launch_bounds__(Fused<NW>::kThreads, 1) void bwd_dz_tiles(BwdParams
       }
     };
     static_assert(FBN * FBM * 2 <= 3 * FwdStages::kStage, "one round needs the whole tile in the LDS ring");
-    if (vt0 + job + 1 == vt1) {
-      dma_barrier<0>();   // every DMA landed, every fragment read done: the whole ring is free
+    if (last) {
+      if (!conv_late) dma_barrier<0>();   // every DMA landed, every fragment read done: the whole ring is free
       store(lds, std::integral_constant<int, 1>{});
+      if (conv_late) {
+        __builtin_amdgcn_sched_barrier(0);   // the dz stores' registers first
+        convert_rows(lds + kLateOff, job, kt_late);
+      }
     } else {
       store(stage, std::integral_constant<int, 2>{});
     }
@@ -1735,8 +1773,12 @@ hipError_t launch_bwd_dz(const BwdParams& p, int mode, hipStream_t s) {
   const unsigned nb = (unsigned)(p.ngroups * p.ntok);
   constexpr int NW = kFusedWaves;
   constexpr unsigned nt = Fused<NW>::kThreads;
-  if (mode == kModeHidden)
+  if (mode == kModeHidden && p.late_w16)
+    return launch(bwd_dz_tiles<kModeHidden, true, NW, true>, nb, nt, s, p);
+  else if (mode == kModeHidden)
     return launch(bwd_dz_tiles<kModeHidden, true, NW>, nb, nt, s, p);
+  else if (mode == kModeHiddenTeachers && p.late_w16)
+    return launch(bwd_dz_tiles<kModeHiddenTeachers, true, NW, true>, nb, nt, s, p);
   else if (mode == kModeHiddenTeachers)
     return launch(bwd_dz_tiles<kModeHiddenTeachers, true, NW>, nb, nt, s, p);
   else if (mode == kModeLogprobEntropy)

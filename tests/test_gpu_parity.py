@@ -385,6 +385,23 @@ def test_dh_split_by_segment_is_bitwise_the_same(tdev, monkeypatch, T, V, Hs, ch
         _check_against_oracle(case, got, g=case.grad)
 
 
+@pytest.mark.parametrize("T,V,Hs", [(500, 5003, 192), (1400, 3001, 512), (129, 1000, 64)])
+def test_late_w_copy_is_bitwise_the_same(tdev, monkeypatch, T, V, Hs):
+    """The dz kernel's fp16 copy of W_s made after the stream from the k-tile
+    loaded again (the default when a workgroup converts at most one k-tile)
+    gives dh, dW (and everything else) bit for bit as the copy made from the
+    stream's own stage; ragged vocabulary tails and widths included."""
+    torch, dev = tdev
+    case = synth.random_case(600 + T, T=T, V=V, Hs=Hs, Ht=Hs, p_mask=0.8, with_grad=True)
+    say("late W copy", T, V, Hs)
+    monkeypatch.setenv("RKL_LATE_W16", "0")
+    ref = _run_hidden(case, dev, g=case.grad)
+    monkeypatch.setenv("RKL_LATE_W16", "1")
+    got = _run_hidden(case, dev, g=case.grad)
+    for a, b, what in zip(got[1:], ref[1:], ("loss", "stats", "dh", "dW")):
+        assert np.array_equal(a.view(np.uint32), b.view(np.uint32)), what
+
+
 @pytest.mark.parametrize("splits_per_wg", [None, "2", "1000"])
 def test_self_distillation_is_exactly_zero(tdev, monkeypatch, splits_per_wg):
     """Bit-identical teacher: every loss and gradient entry is exactly zero,
